@@ -1,0 +1,212 @@
+"""fp64 reference of the top-K KL distillation loss and its gradients.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the HIP library never
+imports this module and this module never imports the HIP library.
+
+What is computed, and where it comes from
+-----------------------------------------
+The pages describe the method in words only (their formulas did not survive
+extraction). The quantities below are the plain definition that the fused
+chunked method reorganises exactly:
+
+* "Multiverse Computing ... (iitak.ru), third paragraph" and
+  "Wissensdestillation mit deutlich weniger GPU-Speicher", section
+  "KL-Verlust wird in Blöcken berechnet": the loss consumes the student's
+  final hidden states together with its output projection, works through the
+  sequence block by block, sums each block's contribution and drops the block,
+  and recomputes the blocks in the backward pass. Chunking is therefore a
+  memory schedule, not a change of the function: this oracle has no chunks.
+* Same pages, first and second paragraphs: the teacher is a cache of the
+  top-100 (token id, logit) pairs per position.
+* "Дистилляция и сжатие моделей" (ml-book.com), section "Как это работает:
+  мягкие метки и температура": logits are divided by the temperature T before
+  the softmax, the KL divergence is taken between the two softened
+  distributions, and the KL term is multiplied by T squared.
+
+Readings taken where the pages are silent (each listed in the design notes):
+forward KL(p_t || p_s); the teacher softmax is renormalised over its K cached
+entries; the student is normalised over the full vocabulary; tokens are summed
+(not averaged); duplicate ids inside a row act additively; a teacher logit of
+-inf contributes probability 0 and a zero term.
+
+Per row r, with upstream scale s:
+
+    z_r      = h_r . W_store^T                  (W stored [V, d], as nn.Linear)
+    lse_r    = log sum_v exp(z_rv / T)
+    a_rk     = l_rk / T,  log p_rk = a_rk - logsumexp_k(a_r.),  p_rk = exp(..)
+    row_loss = T^2 * sum_k p_rk * (log p_rk - (z_r,idx_rk / T - lse_r))
+    q_rv     = exp(z_rv / T - lse_r)
+    P_rv     = sum_k p_rk [idx_rk == v]
+    G_rv     = s * T * (q_rv * sum_k p_rk - P_rv)      (= d loss / d z_rv)
+    grad_h_r = G_r . W_store        grad_W_store = G^T . H
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def student_logits(hidden, w_store) -> np.ndarray:
+    """z = hidden . W, with W given in its stored [V, d] layout.
+
+    The loss takes the hidden states and the output projection, not logits
+    ("Wissensdestillation ...", section "KL-Verlust wird in Blöcken berechnet":
+    the output projection is fused into the loss).
+    """
+    return _f64(hidden) @ _f64(w_store).T
+
+
+def logsumexp_rows(u) -> np.ndarray:
+    """Natural-log log-sum-exp of each row, shifted by the row maximum."""
+    u = _f64(u)
+    m = np.max(u, axis=1, keepdims=True)
+    return (m + np.log(np.sum(np.exp(u - m), axis=1, keepdims=True)))[:, 0]
+
+
+def teacher_log_probs(topk_logit, T: float):
+    """Teacher softmax at temperature T, renormalised over the K cached entries.
+
+    Temperature division before the softmax: "Дистилляция и сжатие моделей",
+    section "Как это работает: мягкие метки и температура". Renormalising over
+    the K cached entries is this implementation's reading (the pages do not
+    say what happens to the tail beyond the top-K). Entries equal to -inf get
+    probability 0 (log-probability -inf); a row needs one finite entry.
+
+    Returns (log_p, p), both [N, K] fp64.
+    """
+    a = _f64(topk_logit) / float(T)
+    m = np.max(a, axis=1, keepdims=True)
+    if not np.all(np.isfinite(m)):
+        raise ValueError("every teacher row needs at least one finite logit")
+    with np.errstate(invalid="ignore"):
+        shifted = a - m  # -inf stays -inf
+    log_norm = np.log(np.sum(np.exp(shifted), axis=1, keepdims=True))
+    log_p = shifted - log_norm
+    p = np.exp(log_p)
+    return log_p, p
+
+
+def forward_backward(hidden, w_store, topk_idx, topk_logit, T: float,
+                     grad_scale: float = 1.0, want_grads: bool = True,
+                     block_rows: int = 128) -> dict:
+    """Loss, per-row pieces and gradients of the top-K KL loss, in fp64.
+
+    hidden [N, d], w_store [V, d] (any float dtype; upcast exactly),
+    topk_idx [N, K] integer ids in [0, V), topk_logit [N, K].
+    ``block_rows`` only bounds host memory; the result does not depend on it
+    beyond rounding (rows are independent).
+
+    Returns a dict with ``loss`` (float, math.fsum of rows), ``row_loss`` [N],
+    ``lse`` [N] (natural log of sum exp(z/T)), ``topk_z`` [N, K] (raw z at
+    the ids), and when ``want_grads``: ``grad_hidden`` [N, d] and
+    ``grad_w`` [V, d] (stored layout).
+    """
+    h = _f64(hidden)
+    w = _f64(w_store)
+    idx = np.asarray(topk_idx)
+    n, d = h.shape
+    v = w.shape[0]
+    if w.shape[1] != d or idx.shape != np.shape(topk_logit) or idx.shape[0] != n:
+        raise ValueError("shape mismatch")
+    if idx.size and (idx.min() < 0 or idx.max() >= v):
+        raise ValueError("token id out of range")
+    T = float(T)
+    log_p, p = teacher_log_probs(topk_logit, T)
+
+    row_loss = np.zeros(n)
+    lse = np.zeros(n)
+    topk_z = np.zeros(idx.shape)
+    grad_h = np.zeros((n, d)) if want_grads else None
+    grad_w = np.zeros((v, d)) if want_grads else None
+
+    for r0 in range(0, n, block_rows):
+        r1 = min(n, r0 + block_rows)
+        z = h[r0:r1] @ w.T                     # [R, V]
+        u = z / T
+        lse_b = logsumexp_rows(u)
+        zk = np.take_along_axis(z, idx[r0:r1], axis=1)
+        log_ps = zk / T - lse_b[:, None]       # student log-prob at the ids
+        pb, lpb = p[r0:r1], log_p[r0:r1]
+        # p * (log p - log p_s), with the 0 * log 0 = 0 convention
+        term = np.where(pb > 0, pb * (np.where(pb > 0, lpb, 0.0) - log_ps), 0.0)
+        row_loss[r0:r1] = T * T * term.sum(axis=1)
+        lse[r0:r1] = lse_b
+        topk_z[r0:r1] = zk
+        if want_grads:
+            q = np.exp(u - lse_b[:, None])
+            P = np.zeros_like(q)
+            rows = np.repeat(np.arange(r1 - r0), idx.shape[1])
+            np.add.at(P, (rows, idx[r0:r1].ravel()), pb.ravel())
+            G = grad_scale * T * (q * pb.sum(axis=1, keepdims=True) - P)
+            grad_h[r0:r1] = G @ w
+            grad_w += G.T @ h[r0:r1]
+
+    out = {
+        "loss": math.fsum(row_loss.tolist()),
+        "row_loss": row_loss,
+        "lse": lse,
+        "topk_z": topk_z,
+    }
+    if want_grads:
+        out["grad_hidden"] = grad_h
+        out["grad_w"] = grad_w
+    return out
+
+
+def brute_force(hidden, w_store, topk_idx, topk_logit, T: float,
+                grad_scale: float = 1.0) -> dict:
+    """The same quantities written as scalar Python loops (tiny inputs only).
+
+    No NumPy arithmetic: every sum is ``math.fsum`` over Python floats, so a
+    vectorisation slip in ``forward_backward`` (a transposed operand, a wrong
+    axis) cannot hide behind the same slip here.
+    """
+    H = [[float(x) for x in row] for row in np.asarray(hidden, dtype=np.float64)]
+    W = [[float(x) for x in row] for row in np.asarray(w_store, dtype=np.float64)]
+    I = [[int(x) for x in row] for row in np.asarray(topk_idx)]
+    L = [[float(x) for x in row] for row in np.asarray(topk_logit, dtype=np.float64)]
+    n, d, v = len(H), len(H[0]), len(W)
+    T = float(T)
+    row_loss, lse_all, grad_h = [], [], []
+    grad_w = [[0.0] * d for _ in range(v)]
+    contrib_w = [[[] for _ in range(d)] for _ in range(v)]
+    for r in range(n):
+        z = [math.fsum(H[r][j] * W[c][j] for j in range(d)) for c in range(v)]
+        mz = max(z)
+        lse = mz / T + math.log(math.fsum(math.exp((zc - mz) / T) for zc in z))
+        a = [x / T for x in L[r]]
+        ma = max(a)
+        ln = ma + math.log(math.fsum(math.exp(x - ma) for x in a if x != -math.inf))
+        pt = [0.0 if x == -math.inf else math.exp(x - ln) for x in a]
+        terms = []
+        for k, c in enumerate(I[r]):
+            if pt[k] > 0.0:
+                terms.append(pt[k] * ((a[k] - ln) - (z[c] / T - lse)))
+        row_loss.append(T * T * math.fsum(terms))
+        lse_all.append(lse)
+        sp = math.fsum(pt)
+        G = []
+        for c in range(v):
+            q = math.exp(z[c] / T - lse)
+            Pc = math.fsum(pt[k] for k, cc in enumerate(I[r]) if cc == c)
+            G.append(grad_scale * T * (q * sp - Pc))
+        grad_h.append([math.fsum(G[c] * W[c][j] for c in range(v)) for j in range(d)])
+        for c in range(v):
+            for j in range(d):
+                contrib_w[c][j].append(G[c] * H[r][j])
+    for c in range(v):
+        for j in range(d):
+            grad_w[c][j] = math.fsum(contrib_w[c][j])
+    return {
+        "loss": math.fsum(row_loss),
+        "row_loss": np.array(row_loss),
+        "lse": np.array(lse_all),
+        "grad_hidden": np.array(grad_h),
+        "grad_w": np.array(grad_w),
+    }
