@@ -1,0 +1,141 @@
+/*
+ * fkl.h - C ABI of libfkl: the fused chunked top-K KL distillation loss
+ * (forward and backward) on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * The loss described on the pages "Multiverse Computing ... (iitak.ru)"
+ * (third and fifth paragraphs) and "Wissensdestillation mit deutlich weniger
+ * GPU-Speicher" (section "KL-Verlust wird in Blöcken berechnet"): the student's
+ * output projection is fused into a KL loss against a cached teacher top-K, the
+ * sequence is processed in blocks ("chunks") of rows whose logits are never
+ * kept, and the backward pass recomputes each block. Temperature handling
+ * (logits divided by T before each softmax, KL term scaled by T^2) follows
+ * "Дистилляция и сжатие моделей", section "Как это работает: мягкие метки и
+ * температура". With z = hidden . W^T (W stored [V, d]):
+ *
+ *   lse_r      = ln sum_v exp(z_rv / T)
+ *   p_rk       = softmax_k(topk_logit_r. / T)        (renormalised over K)
+ *   row_loss_r = T^2 sum_k p_rk (ln p_rk - (z_r,idx_rk / T - lse_r))
+ *   loss       = sum_r row_loss_r
+ *   G_rv       = s T (exp(z_rv / T - lse_r) sum_k p_rk - sum_{k: idx_rk = v} p_rk)
+ *   grad_hidden = G . W,   grad_W = H^T . G   (stored [V, d])
+ *
+ * where s is the upstream gradient of ``loss``. Terms with p_rk = 0 (teacher
+ * logit -inf) contribute nothing.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All tensor arguments are DEVICE pointers to dense row-major arrays. The
+ *   caller owns every buffer, including the workspace; the library never
+ *   allocates or frees device memory and keeps no state between calls
+ *   (re-entrant; concurrent calls must use distinct workspaces and outputs).
+ * - Work is enqueued on ``stream`` (a hipStream_t passed as void*; NULL = the
+ *   default stream). Calls return without waiting for the GPU, except under
+ *   FKL_FLAG_VALIDATE_IDX, which synchronises the stream once.
+ * - Arguments are validated before anything is enqueued: a call that returns
+ *   an error has written nothing. No exception or abort crosses the ABI.
+ *   Device faults surface at the caller's next synchronisation.
+ * - Outputs must not alias inputs or each other.
+ * - dtype FKL_BF16: hidden, weight and grad_hidden are bf16 (raw 16-bit);
+ *   FKL_F32: fp32. Ids are int32; teacher logits, lse, loss, row_loss, topk_z
+ *   and grad_weight are fp32 in both modes. Accumulation is fp32.
+ * - Shapes: N >= 0 tokens (rows; N = 0 is an empty batch), d >= 8 with
+ *   d % 8 == 0, V >= 1, 1 <= K <= min(V, 4096), chunk >= 1 rows per pass (the
+ *   result does not depend on it beyond rounding; it bounds the workspace).
+ *   Ids must lie in [0, V) (checked only under FKL_FLAG_VALIDATE_IDX; an id
+ *   out of range without the flag is undefined behaviour). An id repeated
+ *   within a row acts additively: each (id, logit) pair is its own term.
+ * - hidden, weight, grad_hidden, grad_weight and workspace must be 16-byte
+ *   aligned; the fp32/int32 arrays 4-byte aligned.
+ */
+#ifndef FKL_H
+#define FKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FKL_ABI_VERSION 1
+
+/* status codes */
+#define FKL_OK 0            /* success */
+#define FKL_E_ARG 1         /* null/misaligned pointer, bad shape, T not finite or <= 0 */
+#define FKL_E_UNSUPPORTED 2 /* unknown dtype, d % 8 != 0, K > 4096 */
+#define FKL_E_WORKSPACE 3   /* workspace smaller than fkl_workspace_size reports */
+#define FKL_E_HIP 4         /* a HIP launch or runtime call failed (text in fkl_last_error) */
+#define FKL_E_INDEX 5       /* FKL_FLAG_VALIDATE_IDX: an id outside [0, V) */
+
+/* dtypes of hidden / weight / grad_hidden */
+#define FKL_F32 0
+#define FKL_BF16 1
+
+/* flags */
+#define FKL_FLAG_ACCUMULATE_GRAD_W 1u /* backward adds into grad_weight instead of overwriting */
+#define FKL_FLAG_VALIDATE_IDX 2u      /* check ids on the device first (synchronises the stream) */
+
+/* Returns FKL_ABI_VERSION of the loaded library. */
+int32_t fkl_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* fkl_status_string(int32_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). The pointer
+ * stays valid until the next fkl_* call on this thread. */
+const char* fkl_last_error(void);
+
+/* Workspace bytes needed by fkl_forward and fkl_backward for these shapes
+ * (host-only, enqueues nothing). Both grow with chunk * V (the one
+ * chunk-sized logit-gradient buffer of the backward) and with N (per-row
+ * scratch), never with N * V. Either output pointer may be NULL. */
+int32_t fkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                           int32_t dtype, size_t* fwd_bytes, size_t* bwd_bytes);
+
+/* Forward pass.
+ *   hidden     [N, d]  student final hidden states (dtype)
+ *   weight     [V, d]  LM-head weight in nn.Linear layout (dtype)
+ *   topk_idx   [N, K]  int32 teacher top-K token ids
+ *   topk_logit [N, K]  fp32 teacher logits at those ids
+ *   T > 0              temperature;  chunk: rows per pass
+ *   flags              0 or FKL_FLAG_VALIDATE_IDX
+ * Outputs:
+ *   loss       [1]     fp32 sum of row losses (required)
+ *   lse        [N]     fp32 ln sum_v exp(z_rv / T) (required; the backward needs it)
+ *   row_loss   [N]     fp32 per-row loss (may be NULL)
+ *   topk_z     [N, K]  fp32 raw student logits z at the given ids (may be NULL;
+ *                      passing it to fkl_backward saves a recomputation)
+ * The N x V logits are never stored: each chunk's logit tiles live only in
+ * registers. */
+int32_t fkl_forward(const void* hidden, const void* weight, const int32_t* topk_idx,
+                    const float* topk_logit, float T, int64_t chunk, int64_t N, int64_t d,
+                    int64_t V, int32_t K, int32_t dtype, uint32_t flags, float* loss, float* lse,
+                    float* row_loss, float* topk_z, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Backward pass: gradients of s * loss with respect to hidden and weight.
+ *   hidden, weight, topk_idx, topk_logit, T, chunk, N, d, V, K, dtype: as in
+ *                      the forward (same values)
+ *   lse        [N]     from fkl_forward (required)
+ *   topk_z     [N, K]  from fkl_forward, or NULL to recompute it
+ *   grad_loss  [1]     device fp32 upstream gradient s, or NULL for s = 1
+ *   flags              FKL_FLAG_ACCUMULATE_GRAD_W and/or FKL_FLAG_VALIDATE_IDX
+ * Outputs:
+ *   grad_hidden [N, d] (dtype), overwritten
+ *   grad_weight [V, d] fp32, overwritten (or accumulated into)
+ * Each chunk's logits are recomputed tile by tile and turned into the logit
+ * gradient G; G is held for one chunk only (chunk x V in the workspace) and
+ * consumed by the two gradient products. */
+int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk_idx,
+                     const float* topk_logit, const float* lse, const float* topk_z,
+                     const float* grad_loss, float T, int64_t chunk, int64_t N, int64_t d,
+                     int64_t V, int32_t K, int32_t dtype, uint32_t flags, void* grad_hidden,
+                     float* grad_weight, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FKL_H */

@@ -1,0 +1,269 @@
+// C ABI of libfkl: argument validation, workspace planning and the chunk loop.
+// The declarations, argument meanings, layouts and error behaviour are in
+// include/fkl.h.
+#include "fkl.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int64_t chunk_cap;  // rows per pass actually used (<= N, >= 1)
+  int64_t Vpad;       // G row pitch in elements
+  int64_t nslots;     // vocabulary slices holding a partial (valid ones)
+  int64_t slot_cap;   // partial slots allocated per row
+  int64_t gh_splits, gh_len;
+  // forward workspace offsets
+  size_t f_part, f_rowloss, f_topkz, f_flag, f_total;
+  // backward workspace offsets
+  size_t b_G, b_ghpart, b_pcoef, b_acoef, b_lse2, b_zk, b_flag, b_total;
+};
+
+int32_t check_shapes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_t dtype) {
+  if (dtype != FKL_F32 && dtype != FKL_BF16) return fail(FKL_E_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (N < 0) return fail(FKL_E_ARG, "N must be >= 0 (got %lld)", (long long)N);
+  if (d < 8) return fail(FKL_E_ARG, "d must be >= 8 (got %lld)", (long long)d);
+  if (d % 8 != 0) return fail(FKL_E_UNSUPPORTED, "d must be a multiple of 8 (got %lld)", (long long)d);
+  if (V < 1) return fail(FKL_E_ARG, "V must be >= 1 (got %lld)", (long long)V);
+  if (V >= (int64_t(1) << 31)) return fail(FKL_E_ARG, "V must fit in int32");
+  if (K < 1 || K > V) return fail(FKL_E_ARG, "K must be in [1, V] (got %d)", K);
+  if (K > 4096) return fail(FKL_E_UNSUPPORTED, "K > 4096 is not supported (got %d)", K);
+  if (chunk < 1) return fail(FKL_E_ARG, "chunk must be >= 1 (got %lld)", (long long)chunk);
+  return FKL_OK;
+}
+
+Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_t dtype) {
+  using namespace fkl;
+  Plan p{};
+  const int64_t eb = dtype == FKL_BF16 ? 2 : 4;
+  p.chunk_cap = chunk < N ? chunk : N;
+  if (p.chunk_cap < 1) p.chunk_cap = 1;
+  p.Vpad = round_up(V, 8);
+  p.nslots = ceil_div(V, kSliceVocab);
+  p.slot_cap = lse_slots(V);
+  grad_hidden_split(p.chunk_cap, d, p.Vpad, dtype, &p.gh_splits, &p.gh_len);
+
+  size_t off = 0;
+  p.f_part = off;
+  off = align_up(off + static_cast<size_t>(p.slot_cap) * p.chunk_cap * 8);
+  p.f_rowloss = off;
+  off = align_up(off + static_cast<size_t>(N) * 4);
+  p.f_topkz = off;
+  off = align_up(off + static_cast<size_t>(N) * K * 4);
+  p.f_flag = off;
+  off = align_up(off + 4);
+  p.f_total = off;
+
+  off = 0;
+  p.b_G = off;
+  off = align_up(off + static_cast<size_t>(p.chunk_cap) * p.Vpad * eb);
+  p.b_ghpart = off;
+  off = align_up(off + static_cast<size_t>(p.gh_splits) * p.chunk_cap * d * 4);
+  p.b_pcoef = off;
+  off = align_up(off + static_cast<size_t>(p.chunk_cap) * K * 4);
+  p.b_acoef = off;
+  off = align_up(off + static_cast<size_t>(p.chunk_cap) * 4);
+  p.b_lse2 = off;
+  off = align_up(off + static_cast<size_t>(p.chunk_cap) * 4);
+  p.b_zk = off;
+  off = align_up(off + static_cast<size_t>(p.chunk_cap) * K * 4);
+  p.b_flag = off;
+  off = align_up(off + 4);
+  p.b_total = off;
+  return p;
+}
+
+int32_t hip_check(const char* where) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FKL_E_HIP, "%s: %s", where, hipGetErrorString(e));
+  return FKL_OK;
+}
+
+// Runs the device-side id check and waits for its verdict.
+int32_t validate_ids(const int32_t* idx, int64_t N, int32_t K, int64_t V, int32_t* dflag,
+                     hipStream_t s) {
+  fkl::launch_fill_f32(reinterpret_cast<float*>(dflag), 1, 0.0f, s);
+  fkl::launch_validate_idx(idx, N, K, V, dflag, s);
+  int32_t r = hip_check("id validation launch");
+  if (r) return r;
+  int32_t host = 0;
+  hipError_t e = hipMemcpyAsync(&host, dflag, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(FKL_E_HIP, "id validation: %s", hipGetErrorString(e));
+  if (host != 0) return fail(FKL_E_INDEX, "a teacher id is outside [0, V)");
+  return FKL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fkl_abi_version(void) { return FKL_ABI_VERSION; }
+
+const char* fkl_status_string(int32_t status) {
+  switch (status) {
+    case FKL_OK: return "ok";
+    case FKL_E_ARG: return "invalid argument";
+    case FKL_E_UNSUPPORTED: return "unsupported configuration";
+    case FKL_E_WORKSPACE: return "workspace too small";
+    case FKL_E_HIP: return "HIP runtime error";
+    case FKL_E_INDEX: return "invalid teacher id";
+    default: return "unknown status";
+  }
+}
+
+const char* fkl_last_error(void) { return g_last_error; }
+
+int32_t fkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                           int32_t dtype, size_t* fwd_bytes, size_t* bwd_bytes) {
+  g_last_error[0] = 0;
+  const int32_t r = check_shapes(N, d, V, K, chunk, dtype);
+  if (r) return r;
+  const Plan p = make_plan(N, d, V, K, chunk, dtype);
+  if (fwd_bytes) *fwd_bytes = p.f_total;
+  if (bwd_bytes) *bwd_bytes = p.b_total;
+  return FKL_OK;
+}
+
+int32_t fkl_forward(const void* hidden, const void* weight, const int32_t* topk_idx,
+                    const float* topk_logit, float T, int64_t chunk, int64_t N, int64_t d,
+                    int64_t V, int32_t K, int32_t dtype, uint32_t flags, float* loss, float* lse,
+                    float* row_loss, float* topk_z, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  g_last_error[0] = 0;
+  int32_t r = check_shapes(N, d, V, K, chunk, dtype);
+  if (r) return r;
+  if (!std::isfinite(T) || !(T > 0.0f)) return fail(FKL_E_ARG, "T must be finite and > 0");
+  if ((flags & ~FKL_FLAG_VALIDATE_IDX) != 0) return fail(FKL_E_ARG, "unknown forward flag bits");
+  if (!loss || !weight || !workspace) return fail(FKL_E_ARG, "null pointer argument");
+  if (N > 0 && (!hidden || !topk_idx || !topk_logit || !lse))
+    return fail(FKL_E_ARG, "null pointer argument");
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 16))
+    return fail(FKL_E_ARG, "hidden, weight and workspace must be 16-byte aligned");
+  if (!aligned(topk_idx, 4) || !aligned(topk_logit, 4) || !aligned(loss, 4) || !aligned(lse, 4) ||
+      !aligned(row_loss, 4) || !aligned(topk_z, 4))
+    return fail(FKL_E_ARG, "fp32/int32 arrays must be 4-byte aligned");
+  const Plan p = make_plan(N, d, V, K, chunk, dtype);
+  if (workspace_bytes < p.f_total)
+    return fail(FKL_E_WORKSPACE, "forward workspace needs %zu bytes, got %zu", p.f_total,
+                workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  (void)hipGetLastError();
+
+  if (N == 0) {
+    fkl::launch_fill_f32(loss, 1, 0.0f, s);
+    return hip_check("forward (empty batch)");
+  }
+  if (flags & FKL_FLAG_VALIDATE_IDX) {
+    r = validate_ids(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + p.f_flag), s);
+    if (r) return r;
+  }
+  float2* part = reinterpret_cast<float2*>(ws + p.f_part);
+  float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + p.f_rowloss);
+  float* zk = topk_z ? topk_z : reinterpret_cast<float*>(ws + p.f_topkz);
+  const float c2 = 1.4426950408889634f / T;
+
+  fkl::launch_gather_dot(dtype, weight, hidden, topk_idx, d, 0, N, K, zk, s);
+  for (int64_t row0 = 0; row0 < N; row0 += p.chunk_cap) {
+    const int64_t nrows = (N - row0) < p.chunk_cap ? (N - row0) : p.chunk_cap;
+    fkl::launch_logits_lse(dtype, weight, hidden, d, V, row0, nrows, c2, part, p.chunk_cap, s);
+    fkl::launch_merge_loss(part, p.chunk_cap, p.nslots, zk, topk_logit, row0, nrows, K, T, lse, rl,
+                           s);
+  }
+  fkl::launch_reduce_loss(rl, N, loss, s);
+  return hip_check("forward launch");
+}
+
+int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk_idx,
+                     const float* topk_logit, const float* lse, const float* topk_z,
+                     const float* grad_loss, float T, int64_t chunk, int64_t N, int64_t d,
+                     int64_t V, int32_t K, int32_t dtype, uint32_t flags, void* grad_hidden,
+                     float* grad_weight, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  int32_t r = check_shapes(N, d, V, K, chunk, dtype);
+  if (r) return r;
+  if (!std::isfinite(T) || !(T > 0.0f)) return fail(FKL_E_ARG, "T must be finite and > 0");
+  if ((flags & ~(FKL_FLAG_VALIDATE_IDX | FKL_FLAG_ACCUMULATE_GRAD_W)) != 0)
+    return fail(FKL_E_ARG, "unknown backward flag bits");
+  if (!weight || !grad_weight || !workspace) return fail(FKL_E_ARG, "null pointer argument");
+  if (N > 0 && (!hidden || !topk_idx || !topk_logit || !lse || !grad_hidden))
+    return fail(FKL_E_ARG, "null pointer argument");
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 16) ||
+      !aligned(grad_hidden, 16) || !aligned(grad_weight, 16))
+    return fail(FKL_E_ARG, "hidden, weight, gradients and workspace must be 16-byte aligned");
+  if (!aligned(topk_idx, 4) || !aligned(topk_logit, 4) || !aligned(lse, 4) || !aligned(topk_z, 4) ||
+      !aligned(grad_loss, 4))
+    return fail(FKL_E_ARG, "fp32/int32 arrays must be 4-byte aligned");
+  const Plan p = make_plan(N, d, V, K, chunk, dtype);
+  if (workspace_bytes < p.b_total)
+    return fail(FKL_E_WORKSPACE, "backward workspace needs %zu bytes, got %zu", p.b_total,
+                workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  const bool accumulate = (flags & FKL_FLAG_ACCUMULATE_GRAD_W) != 0;
+  (void)hipGetLastError();
+
+  if (N == 0) {
+    if (!accumulate) fkl::launch_fill_f32(grad_weight, V * d, 0.0f, s);
+    return hip_check("backward (empty batch)");
+  }
+  if (flags & FKL_FLAG_VALIDATE_IDX) {
+    r = validate_ids(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + p.b_flag), s);
+    if (r) return r;
+  }
+  void* G = ws + p.b_G;
+  float* ghpart = reinterpret_cast<float*>(ws + p.b_ghpart);
+  float* pcoef = reinterpret_cast<float*>(ws + p.b_pcoef);
+  float* acoef = reinterpret_cast<float*>(ws + p.b_acoef);
+  float* lse2 = reinterpret_cast<float*>(ws + p.b_lse2);
+  float* zk_ws = reinterpret_cast<float*>(ws + p.b_zk);
+  const float c2 = 1.4426950408889634f / T;
+
+  for (int64_t row0 = 0; row0 < N; row0 += p.chunk_cap) {
+    const int64_t nrows = (N - row0) < p.chunk_cap ? (N - row0) : p.chunk_cap;
+    const float* zk;
+    if (topk_z) {
+      zk = topk_z + row0 * K;
+    } else {
+      // recompute z at the ids for this chunk into the workspace (rows 0..nrows)
+      fkl::launch_gather_dot(dtype, weight, static_cast<const unsigned char*>(hidden) +
+                                                row0 * d * (dtype == FKL_BF16 ? 2 : 4),
+                             topk_idx + row0 * K, d, 0, nrows, K, zk_ws, s);
+      zk = zk_ws;
+    }
+    fkl::launch_bwd_prep(topk_logit, lse, grad_loss, row0, nrows, K, T, pcoef, acoef, lse2, s);
+    fkl::launch_gprod(dtype, weight, hidden, d, V, p.Vpad, row0, nrows, c2, acoef, lse2, G, s);
+    fkl::launch_fixup(dtype, G, p.Vpad, topk_idx, zk, pcoef, acoef, lse2, row0, nrows, K, c2, s);
+    fkl::launch_grad_hidden(dtype, G, p.Vpad, weight, d, V, nrows, p.gh_splits, p.gh_len, ghpart,
+                            s);
+    fkl::launch_reduce_grad_hidden(dtype, ghpart, p.gh_splits, nrows, d, grad_hidden, row0, s);
+    fkl::launch_grad_w(dtype, G, p.Vpad, hidden, d, V, row0, nrows, accumulate || row0 > 0,
+                       grad_weight, s);
+  }
+  return hip_check("backward launch");
+}
+
+}  // extern "C"

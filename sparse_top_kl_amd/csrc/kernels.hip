@@ -1,0 +1,610 @@
+// Kernels of the fused chunked top-K KL loss for gfx950.
+//
+// Method: "Multiverse Computing ... (iitak.ru)", third paragraph, and
+// "Wissensdestillation mit deutlich weniger GPU-Speicher", section
+// "KL-Verlust wird in Blöcken berechnet": the output projection is fused into
+// the loss, rows are processed block by block without keeping their logits,
+// and the backward pass recomputes them. Temperature and the T^2 factor:
+// "Дистилляция и сжатие моделей", section "Как это работает: мягкие метки и
+// температура".
+//
+// Forward, per chunk of rows:
+//   k_logits_lse   z tile (MFMA) -> per (128-vocab slice, row) running max and
+//                  sum of 2^(z * log2(e)/T); z never leaves registers.
+//   k_merge_loss   merge the slices into lse, teacher softmax over the K cached
+//                  logits, per-row KL.
+// once: k_gather_dot (z at the teacher ids), k_reduce_loss (fixed-order sum).
+// Backward, per chunk:
+//   k_bwd_prep     teacher probabilities scaled by s*T, lse in base 2.
+//   k_gprod        recompute z tile (same tile code as the forward) and write
+//                  the dense part of the logit gradient, s*T*sum(p)*softmax, as
+//                  one rounding into the chunk-sized G buffer.
+//   k_fixup        subtract s*T*p at the teacher ids (recomputing the same
+//                  value from z at the id, so each entry is rounded once).
+//   k_grad_hidden  split-K MFMA product G . W into fp32 partials;
+//   k_reduce_gh    fixed-order sum of the partials -> grad_hidden rows.
+//   k_grad_w       MFMA product G^T . H accumulated into fp32 grad_W.
+#include <math.h>
+
+#include "gemm_core.hpp"
+#include "kernels.hpp"
+
+namespace fkl {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+#define FKL_GEMM_KERNEL __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------------ forward
+
+template <class P>
+FKL_GEMM_KERNEL void k_logits_lse(const unsigned char* __restrict__ W,
+                                  const unsigned char* __restrict__ H, int64_t d, int64_t V,
+                                  int64_t nrows, int64_t n_vt, int64_t n_tt, float c2,
+                                  float2* __restrict__ part, int64_t part_ld) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  const int64_t total = n_vt * n_tt;
+  const int64_t t = xcd_tile_index(total);
+  if (t >= total) return;
+  const int64_t vt = t / n_tt, tt = t % n_tt;
+  const int64_t rb = d * P::kBytes;
+  // MFMA rows = vocabulary entries (weight rows), columns = tokens, so each
+  // lane's accumulators belong to one token and the reduction over the
+  // vocabulary is mostly in-lane.
+  const Operand A{W, rb, vt * kBM, V, d};
+  const Operand B{H, rb, tt * kBN, nrows, d};
+  f32x16_t acc[kMI][kNI];
+  gemm_tile<P, false, false>(acc, A, B, 0, d, lds);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int64_t v0 = vt * kBM + wm * kWM;
+  if (v0 >= V) return;
+  const int64_t slot = v0 / kSliceVocab;
+  const bool full = v0 + kWM <= V;
+  const int vlim = full ? kWM : static_cast<int>(V - v0);
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (full || acc_row(mi, r, lane) < vlim) m = fmaxf(m, acc[mi][ni][r] * c2);
+    float s = 0.f;
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (full || acc_row(mi, r, lane) < vlim) s += fast_exp2(acc[mi][ni][r] * c2 - m);
+    // the other lane half holds the other 4-row groups of the same token
+    const float mo = __shfl_xor(m, 32);
+    const float so = __shfl_xor(s, 32);
+    const float M = fmaxf(m, mo);
+    const float S = (s > 0.f ? s * fast_exp2(m - M) : 0.f) + (so > 0.f ? so * fast_exp2(mo - M) : 0.f);
+    const int64_t tok = tt * kBN + wn * kWN + ni * 32 + (lane & 31);
+    if (lane < 32 && tok < nrows) part[slot * part_ld + tok] = make_float2(M, S);
+  }
+}
+
+template <class P>
+__device__ __forceinline__ float dot16(u32x4_t a, u32x4_t b, float acc) {
+  if constexpr (P::kBytes == 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(as_f32(a[e] << 16), as_f32(b[e] << 16), acc);
+      acc = fmaf(as_f32(a[e] & 0xffff0000u), as_f32(b[e] & 0xffff0000u), acc);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = fmaf(as_f32(a[e]), as_f32(b[e]), acc);
+  }
+  return acc;
+}
+
+// One wave per row; four 16-lane groups take every fourth teacher id.
+template <class P>
+__global__ __launch_bounds__(256) void k_gather_dot(const unsigned char* __restrict__ W,
+                                                    const unsigned char* __restrict__ H,
+                                                    const int32_t* __restrict__ idx, int64_t d,
+                                                    int64_t nrows, int K, float* __restrict__ zk) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  const int64_t rb = d * P::kBytes;
+  const unsigned char* h = H + row * rb;
+  const int64_t nvec = rb / 16;
+  for (int k = g; k < K; k += 4) {
+    const int64_t v = idx[row * K + k];
+    const unsigned char* wr = W + v * rb;
+    float acc = 0.f;
+    for (int64_t j = li; j < nvec; j += 16) acc = dot16<P>(load16(h + j * 16), load16(wr + j * 16), acc);
+    acc += __shfl_xor(acc, 8);
+    acc += __shfl_xor(acc, 4);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 1);
+    if (li == 0) zk[row * K + k] = acc;
+  }
+}
+
+__device__ __forceinline__ void merge_ms(float& m, float& s, float mo, float so) {
+  if (so <= 0.f) return;
+  if (s <= 0.f) {
+    m = mo;
+    s = so;
+    return;
+  }
+  const float M = fmaxf(m, mo);
+  s = s * fast_exp2(m - M) + so * fast_exp2(mo - M);
+  m = M;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// One wave per row of the chunk.
+__global__ __launch_bounds__(256) void k_merge_loss(const float2* __restrict__ part, int64_t part_ld,
+                                                    int64_t nslots, const float* __restrict__ zk,
+                                                    const float* __restrict__ logit, int64_t nrows,
+                                                    int K, float T, float* __restrict__ lse_out,
+                                                    float* __restrict__ row_loss) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  float m = -INFINITY, s = 0.f;
+  for (int64_t sl = lane; sl < nslots; sl += 64) {
+    const float2 p = part[sl * part_ld + row];
+    merge_ms(m, s, p.x, p.y);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float mo = __shfl_xor(m, o), so = __shfl_xor(s, o);
+    merge_ms(m, s, mo, so);
+  }
+  const float lse = (m + log2f(s)) * kLn2;  // ln sum_v exp(z_v / T)
+
+  const float invT = 1.0f / T;
+  const float* lg = logit + row * K;
+  const float* z = zk + row * K;
+  float ma = -INFINITY;
+  for (int k = lane; k < K; k += 64) ma = fmaxf(ma, lg[k] * invT);
+  ma = wave_max(ma);
+  float zsum = 0.f;
+  for (int k = lane; k < K; k += 64) zsum += expf(lg[k] * invT - ma);
+  zsum = wave_sum(zsum);
+  const float logZ = logf(zsum);
+  float term = 0.f;
+  for (int k = lane; k < K; k += 64) {
+    const float a = lg[k] * invT - ma;
+    const float p = expf(a) / zsum;
+    if (p > 0.f) term += p * ((a - logZ) - (z[k] * invT - lse));
+  }
+  term = wave_sum(term);
+  if (lane == 0) {
+    lse_out[row] = lse;
+    if (row_loss) row_loss[row] = T * T * term;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_reduce_loss(const float* __restrict__ row_loss, int64_t N,
+                                                      float* __restrict__ loss) {
+  __shared__ double sh[1024];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < N; i += 1024) acc += static_cast<double>(row_loss[i]);
+  sh[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = static_cast<float>(sh[0]);
+}
+
+// ------------------------------------------------------------------ backward
+
+// One wave per row: pcoef = s*T*p_k, acoef = s*T*sum_k p_k, lse2 = lse*log2(e).
+__global__ __launch_bounds__(256) void k_bwd_prep(const float* __restrict__ logit,
+                                                  const float* __restrict__ lse,
+                                                  const float* __restrict__ grad_loss,
+                                                  int64_t nrows, int K, float T,
+                                                  float* __restrict__ pcoef,
+                                                  float* __restrict__ acoef,
+                                                  float* __restrict__ lse2) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  const float scale = (grad_loss ? *grad_loss : 1.0f) * T;
+  const float invT = 1.0f / T;
+  const float* lg = logit + row * K;
+  float ma = -INFINITY;
+  for (int k = lane; k < K; k += 64) ma = fmaxf(ma, lg[k] * invT);
+  ma = wave_max(ma);
+  float zsum = 0.f;
+  for (int k = lane; k < K; k += 64) zsum += expf(lg[k] * invT - ma);
+  zsum = wave_sum(zsum);
+  float psum = 0.f;
+  for (int k = lane; k < K; k += 64) {
+    const float p = expf(lg[k] * invT - ma) / zsum;
+    psum += p;
+    pcoef[row * K + k] = scale * p;
+  }
+  psum = wave_sum(psum);
+  if (lane == 0) {
+    acoef[row] = scale * psum;
+    lse2[row] = lse[row] * kLog2e;
+  }
+}
+
+template <class P>
+__device__ __forceinline__ void store4(unsigned char* p, const float (&v)[4]) {
+  if constexpr (P::kBytes == 2) {
+    const uint32_t lo = f32_to_bf16_rne(v[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
+    const uint32_t hi = f32_to_bf16_rne(v[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{lo, hi};
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// Recompute the logit tile and write G_dense = acoef * 2^(z*c2 - lse2) into
+// G[row][v] (row pitch Vpad; columns in [V, Vpad) are written as zero).
+template <class P>
+FKL_GEMM_KERNEL void k_gprod(const unsigned char* __restrict__ W, const unsigned char* __restrict__ H,
+                             int64_t d, int64_t V, int64_t Vpad, int64_t nrows, int64_t n_vt,
+                             int64_t n_tt, float c2, const float* __restrict__ acoef,
+                             const float* __restrict__ lse2, unsigned char* __restrict__ G) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  const int64_t total = n_vt * n_tt;
+  const int64_t t = xcd_tile_index(total);
+  if (t >= total) return;
+  const int64_t vt = t / n_tt, tt = t % n_tt;
+  const int64_t rb = d * P::kBytes;
+  const Operand A{W, rb, vt * kBM, V, d};
+  const Operand B{H, rb, tt * kBN, nrows, d};
+  f32x16_t acc[kMI][kNI];
+  gemm_tile<P, false, false>(acc, A, B, 0, d, lds);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int64_t v0 = vt * kBM + wm * kWM;
+  if (v0 >= Vpad) return;
+  const int64_t gld = Vpad * P::kBytes;
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) {
+    const int64_t tok = tt * kBN + wn * kWN + ni * 32 + (lane & 31);
+    if (tok >= nrows) continue;
+    const float a = acoef[tok];
+    const float l2 = lse2[tok];
+    unsigned char* grow = G + tok * gld;
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int64_t v = v0 + mi * 32 + 8 * g4 + 4 * (lane >> 5);
+        if (v >= Vpad) continue;
+        float vals[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          vals[j] = (v + j < V) ? a * fast_exp2(acc[mi][ni][4 * g4 + j] * c2 - l2) : 0.f;
+        store4<P>(grow + v * P::kBytes, vals);
+      }
+  }
+}
+
+// One wave per row: G[row][idx_k] = acoef * 2^(z_k*c2 - lse2) - sum_{k': idx_k' = idx_k} pcoef_k'.
+template <class P>
+__global__ __launch_bounds__(64) void k_fixup(unsigned char* __restrict__ G, int64_t Vpad,
+                                              const int32_t* __restrict__ idx,
+                                              const float* __restrict__ zk,
+                                              const float* __restrict__ pcoef,
+                                              const float* __restrict__ acoef,
+                                              const float* __restrict__ lse2, int K, float c2) {
+  extern __shared__ int32_t sh_fix[];
+  int32_t* sid = sh_fix;
+  float* sp = reinterpret_cast<float*>(sh_fix + K);
+  const int lane = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  for (int k = lane; k < K; k += 64) {
+    sid[k] = idx[row * K + k];
+    sp[k] = pcoef[row * K + k];
+  }
+  __syncthreads();
+  const float a = acoef[row], l2 = lse2[row];
+  unsigned char* grow = G + row * Vpad * P::kBytes;
+  for (int k = lane; k < K; k += 64) {
+    const int32_t v = sid[k];
+    float sum = 0.f;
+    for (int k2 = 0; k2 < K; ++k2) sum += (sid[k2] == v) ? sp[k2] : 0.f;
+    const float val = a * fast_exp2(zk[row * K + k] * c2 - l2) - sum;
+    if constexpr (P::kBytes == 2)
+      reinterpret_cast<uint16_t*>(grow)[v] = f32_to_bf16_rne(val);
+    else
+      reinterpret_cast<float*>(grow)[v] = val;
+  }
+}
+
+// part[split][row][col] = sum over the split's vocabulary range of G[row][v] W[v][col].
+template <class P>
+FKL_GEMM_KERNEL void k_grad_hidden(const unsigned char* __restrict__ G, int64_t Vpad,
+                                   const unsigned char* __restrict__ W, int64_t d, int64_t V,
+                                   int64_t nrows, int64_t n_tt, int64_t n_dt, int64_t splits,
+                                   int64_t split_len, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  const int64_t total = splits * n_dt * n_tt;
+  const int64_t t = xcd_tile_index(total);
+  if (t >= total) return;
+  const int64_t tt = t % n_tt, rest = t / n_tt;
+  const int64_t dt = rest % n_dt, sp = rest / n_dt;
+  const Operand A{G, Vpad * P::kBytes, tt * kBM, nrows, Vpad};   // [row][v], k = v
+  const Operand B{W, d * P::kBytes, dt * kBN, d, V};             // [v][col], k = v
+  const int64_t k0 = sp * split_len;
+  const int64_t k1 = k0 + split_len < Vpad ? k0 + split_len : Vpad;
+  f32x16_t acc[kMI][kNI];
+  gemm_tile<P, false, true>(acc, A, B, k0, k1, lds);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  float* out = part + sp * nrows * d;
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row = tt * kBM + wm * kWM + acc_row(mi, r, lane);
+      if (row >= nrows) continue;
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni) {
+        const int64_t col = dt * kBN + wn * kWN + ni * 32 + (lane & 31);
+        if (col < d) out[row * d + col] = acc[mi][ni][r];
+      }
+    }
+}
+
+template <class P>
+__global__ __launch_bounds__(256) void k_reduce_gh(const float* __restrict__ part, int64_t splits,
+                                                   int64_t nrows, int64_t d,
+                                                   unsigned char* __restrict__ out) {
+  const int64_t n4 = nrows * d / 4;
+  const int64_t stride = nrows * d;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    float4 s = reinterpret_cast<const float4*>(part)[i];
+    for (int64_t sp = 1; sp < splits; ++sp) {
+      const float4 q = reinterpret_cast<const float4*>(part + sp * stride)[i];
+      s.x += q.x;
+      s.y += q.y;
+      s.z += q.z;
+      s.w += q.w;
+    }
+    const float v[4] = {s.x, s.y, s.z, s.w};
+    store4<P>(out + i * 4 * P::kBytes, v);
+  }
+}
+
+// grad_W[v][col] (+)= sum over the chunk's rows of G[row][v] H[row][col].
+template <class P>
+FKL_GEMM_KERNEL void k_grad_w(const unsigned char* __restrict__ G, int64_t Vpad,
+                              const unsigned char* __restrict__ H, int64_t d, int64_t V,
+                              int64_t nrows, int64_t n_vt, int64_t n_dt, int accumulate,
+                              float* __restrict__ grad_w) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  const int64_t total = n_vt * n_dt;
+  const int64_t t = xcd_tile_index(total);
+  if (t >= total) return;
+  const int64_t vt = t / n_dt, dt = t % n_dt;
+  const Operand A{G, Vpad * P::kBytes, vt * kBM, Vpad, nrows};  // [row][v], k = row
+  const Operand B{H, d * P::kBytes, dt * kBN, d, nrows};        // [row][col], k = row
+  f32x16_t acc[kMI][kNI];
+  gemm_tile<P, true, true>(acc, A, B, 0, nrows, lds);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t v = vt * kBM + wm * kWM + acc_row(mi, r, lane);
+      if (v >= V) continue;
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni) {
+        const int64_t col = dt * kBN + wn * kWN + ni * 32 + (lane & 31);
+        if (col < d) {
+          float* p = grad_w + v * d + col;
+          *p = accumulate ? *p + acc[mi][ni][r] : acc[mi][ni][r];
+        }
+      }
+    }
+}
+
+// ------------------------------------------------------------------ utilities
+
+__global__ void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = v;
+}
+
+// Every id in [0, V).
+__global__ __launch_bounds__(256) void k_validate_idx(const int32_t* __restrict__ idx, int64_t n,
+                                                      int64_t V, int32_t* __restrict__ flag) {
+  int bad = 0;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int32_t v = idx[i];
+    bad |= (v < 0 || v >= V);
+  }
+  if (bad) atomicOr(flag, 1);
+}
+
+// ------------------------------------------------------------------ launchers
+
+static inline unsigned grid_for_tiles(int64_t total) {
+  return static_cast<unsigned>(8 * ceil_div(total, 8));
+}
+
+#define FKL_DISPATCH(dtype, KERNEL, ...)      \
+  do {                                        \
+    if ((dtype) == 1)                         \
+      KERNEL<BF16><<<__VA_ARGS__>>>;          \
+    else                                      \
+      KERNEL<F32><<<__VA_ARGS__>>>;           \
+  } while (0)
+
+void grad_hidden_split(int64_t rows, int64_t d, int64_t Vpad, int dtype, int64_t* splits,
+                       int64_t* len) {
+  const int64_t bk = kRowBytes / (dtype == 1 ? 2 : 4);
+  const int64_t tiles = ceil_div(rows, kBM) * ceil_div(d, kBN);
+  const int64_t stages = ceil_div(Vpad, bk);
+  int64_t sp = ceil_div(512, tiles);
+  if (sp > stages) sp = stages;
+  if (sp < 1) sp = 1;
+  const int64_t l = ceil_div(stages, sp) * bk;
+  *len = l;
+  *splits = ceil_div(Vpad, l);
+}
+
+void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64_t V,
+                       int64_t row0, int64_t nrows, float c2, float2* part, int64_t part_ld,
+                       hipStream_t s) {
+  const int64_t eb = dtype == 1 ? 2 : 4;
+  const int64_t n_vt = ceil_div(V, kBM), n_tt = ceil_div(nrows, kBN);
+  const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
+  if (dtype == 1)
+    k_logits_lse<BF16><<<grid_for_tiles(n_vt * n_tt), kThreads, 0, s>>>(
+        static_cast<const unsigned char*>(W), Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld);
+  else
+    k_logits_lse<F32><<<grid_for_tiles(n_vt * n_tt), kThreads, 0, s>>>(
+        static_cast<const unsigned char*>(W), Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld);
+}
+
+void launch_gather_dot(int dtype, const void* W, const void* H, const int32_t* idx, int64_t d,
+                       int64_t row0, int64_t nrows, int K, float* zk, hipStream_t s) {
+  if (nrows <= 0) return;
+  const int64_t eb = dtype == 1 ? 2 : 4;
+  const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
+  const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, 4));
+  if (dtype == 1)
+    k_gather_dot<BF16><<<blocks, 256, 0, s>>>(static_cast<const unsigned char*>(W), Hc,
+                                               idx + row0 * K, d, nrows, K, zk + row0 * K);
+  else
+    k_gather_dot<F32><<<blocks, 256, 0, s>>>(static_cast<const unsigned char*>(W), Hc,
+                                              idx + row0 * K, d, nrows, K, zk + row0 * K);
+}
+
+void launch_merge_loss(const float2* part, int64_t part_ld, int64_t nslots, const float* zk,
+                       const float* logit, int64_t row0, int64_t nrows, int K, float T,
+                       float* lse, float* row_loss, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, 4));
+  k_merge_loss<<<blocks, 256, 0, s>>>(part, part_ld, nslots, zk + row0 * K, logit + row0 * K,
+                                      nrows, K, T, lse + row0, row_loss ? row_loss + row0 : nullptr);
+}
+
+void launch_reduce_loss(const float* row_loss, int64_t N, float* loss, hipStream_t s) {
+  k_reduce_loss<<<1, 1024, 0, s>>>(row_loss, N, loss);
+}
+
+void launch_bwd_prep(const float* logit, const float* lse, const float* grad_loss, int64_t row0,
+                     int64_t nrows, int K, float T, float* pcoef, float* acoef, float* lse2,
+                     hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, 4));
+  k_bwd_prep<<<blocks, 256, 0, s>>>(logit + row0 * K, lse + row0, grad_loss, nrows, K, T, pcoef,
+                                    acoef, lse2);
+}
+
+void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t Vpad,
+                  int64_t row0, int64_t nrows, float c2, const float* acoef, const float* lse2,
+                  void* G, hipStream_t s) {
+  const int64_t eb = dtype == 1 ? 2 : 4;
+  const int64_t n_vt = ceil_div(Vpad, kBM), n_tt = ceil_div(nrows, kBN);
+  const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
+  if (dtype == 1)
+    k_gprod<BF16><<<grid_for_tiles(n_vt * n_tt), kThreads, 0, s>>>(
+        static_cast<const unsigned char*>(W), Hc, d, V, Vpad, nrows, n_vt, n_tt, c2, acoef, lse2,
+        static_cast<unsigned char*>(G));
+  else
+    k_gprod<F32><<<grid_for_tiles(n_vt * n_tt), kThreads, 0, s>>>(
+        static_cast<const unsigned char*>(W), Hc, d, V, Vpad, nrows, n_vt, n_tt, c2, acoef, lse2,
+        static_cast<unsigned char*>(G));
+}
+
+void launch_fixup(int dtype, void* G, int64_t Vpad, const int32_t* idx, const float* zk,
+                  const float* pcoef, const float* acoef, const float* lse2, int64_t row0,
+                  int64_t nrows, int K, float c2, hipStream_t s) {
+  if (nrows <= 0) return;
+  const size_t shm = static_cast<size_t>(K) * 8;
+  if (dtype == 1)
+    k_fixup<BF16><<<static_cast<unsigned>(nrows), 64, shm, s>>>(
+        static_cast<unsigned char*>(G), Vpad, idx + row0 * K, zk, pcoef, acoef, lse2, K, c2);
+  else
+    k_fixup<F32><<<static_cast<unsigned>(nrows), 64, shm, s>>>(
+        static_cast<unsigned char*>(G), Vpad, idx + row0 * K, zk, pcoef, acoef, lse2, K, c2);
+}
+
+void launch_grad_hidden(int dtype, const void* G, int64_t Vpad, const void* W, int64_t d,
+                        int64_t V, int64_t nrows, int64_t splits, int64_t split_len,
+                        float* part, hipStream_t s) {
+  const int64_t n_tt = ceil_div(nrows, kBM), n_dt = ceil_div(d, kBN);
+  const unsigned grid = grid_for_tiles(splits * n_tt * n_dt);
+  if (dtype == 1)
+    k_grad_hidden<BF16><<<grid, kThreads, 0, s>>>(static_cast<const unsigned char*>(G), Vpad,
+                                                   static_cast<const unsigned char*>(W), d, V,
+                                                   nrows, n_tt, n_dt, splits, split_len, part);
+  else
+    k_grad_hidden<F32><<<grid, kThreads, 0, s>>>(static_cast<const unsigned char*>(G), Vpad,
+                                                  static_cast<const unsigned char*>(W), d, V,
+                                                  nrows, n_tt, n_dt, splits, split_len, part);
+}
+
+void launch_reduce_grad_hidden(int dtype, const float* part, int64_t splits, int64_t nrows,
+                               int64_t d, void* grad_hidden, int64_t row0, hipStream_t s) {
+  const int64_t eb = dtype == 1 ? 2 : 4;
+  unsigned char* out = static_cast<unsigned char*>(grad_hidden) + row0 * d * eb;
+  const int64_t n4 = nrows * d / 4;
+  int64_t blocks = ceil_div(n4, 256);
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) return;
+  if (dtype == 1)
+    k_reduce_gh<BF16><<<static_cast<unsigned>(blocks), 256, 0, s>>>(part, splits, nrows, d, out);
+  else
+    k_reduce_gh<F32><<<static_cast<unsigned>(blocks), 256, 0, s>>>(part, splits, nrows, d, out);
+}
+
+void launch_grad_w(int dtype, const void* G, int64_t Vpad, const void* H, int64_t d, int64_t V,
+                   int64_t row0, int64_t nrows, bool accumulate, float* grad_w, hipStream_t s) {
+  const int64_t eb = dtype == 1 ? 2 : 4;
+  const int64_t n_vt = ceil_div(V, kBM), n_dt = ceil_div(d, kBN);
+  const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
+  const unsigned grid = grid_for_tiles(n_vt * n_dt);
+  if (dtype == 1)
+    k_grad_w<BF16><<<grid, kThreads, 0, s>>>(static_cast<const unsigned char*>(G), Vpad, Hc, d, V,
+                                              nrows, n_vt, n_dt, accumulate ? 1 : 0, grad_w);
+  else
+    k_grad_w<F32><<<grid, kThreads, 0, s>>>(static_cast<const unsigned char*>(G), Vpad, Hc, d, V,
+                                             nrows, n_vt, n_dt, accumulate ? 1 : 0, grad_w);
+}
+
+void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return;
+  int64_t blocks = ceil_div(n, 256);
+  if (blocks > 8192) blocks = 8192;
+  k_fill_f32<<<static_cast<unsigned>(blocks), 256, 0, s>>>(p, n, v);
+}
+
+void launch_validate_idx(const int32_t* idx, int64_t N, int K, int64_t V, int32_t* flag,
+                         hipStream_t s) {
+  const int64_t n = N * K;
+  if (n <= 0) return;
+  int64_t blocks = ceil_div(n, 256);
+  if (blocks > 4096) blocks = 4096;
+  k_validate_idx<<<static_cast<unsigned>(blocks), 256, 0, s>>>(idx, n, V, flag);
+}
+
+}  // namespace fkl

@@ -1,0 +1,59 @@
+// Host-side launchers for the loss kernels (internal to libfkl).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fkl {
+
+// Rows of a (vocab-slice, token) partial: running max and sum of 2^(z*c2).
+constexpr int kSliceVocab = 128;  // vocabulary entries per partial slot
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+// Number of partial slots per token (one per 128-wide vocabulary slice).
+inline int64_t lse_slots(int64_t V) { return ceil_div(V, 256) * 2; }
+
+// Split of the vocabulary contraction of grad_hidden: (splits, split length).
+void grad_hidden_split(int64_t rows, int64_t d, int64_t Vpad, int dtype, int64_t* splits,
+                       int64_t* len);
+
+// Forward, per chunk: partial (max, sum) of 2^(z * c2) per (vocab slice, token).
+void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64_t V,
+                       int64_t row0, int64_t nrows, float c2, float2* part, int64_t part_ld,
+                       hipStream_t s);
+// z at the teacher ids for rows [row0, row0 + nrows).
+void launch_gather_dot(int dtype, const void* W, const void* H, const int32_t* idx, int64_t d,
+                       int64_t row0, int64_t nrows, int K, float* zk, hipStream_t s);
+// Merge partials into lse, teacher softmax and per-row loss for one chunk.
+void launch_merge_loss(const float2* part, int64_t part_ld, int64_t nslots, const float* zk,
+                       const float* logit, int64_t row0, int64_t nrows, int K, float T,
+                       float* lse, float* row_loss, hipStream_t s);
+// loss = sum of row_loss in a fixed order (fp64 accumulation).
+void launch_reduce_loss(const float* row_loss, int64_t N, float* loss, hipStream_t s);
+
+// Backward, per chunk.
+void launch_bwd_prep(const float* logit, const float* lse, const float* grad_loss, int64_t row0,
+                     int64_t nrows, int K, float T, float* pcoef, float* acoef, float* lse2,
+                     hipStream_t s);
+void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t Vpad,
+                  int64_t row0, int64_t nrows, float c2, const float* acoef, const float* lse2,
+                  void* G, hipStream_t s);
+void launch_fixup(int dtype, void* G, int64_t Vpad, const int32_t* idx, const float* zk,
+                  const float* pcoef, const float* acoef, const float* lse2, int64_t row0,
+                  int64_t nrows, int K, float c2, hipStream_t s);
+void launch_grad_hidden(int dtype, const void* G, int64_t Vpad, const void* W, int64_t d,
+                        int64_t V, int64_t nrows, int64_t splits, int64_t split_len,
+                        float* part, hipStream_t s);
+void launch_reduce_grad_hidden(int dtype, const float* part, int64_t splits, int64_t nrows,
+                               int64_t d, void* grad_hidden, int64_t row0, hipStream_t s);
+void launch_grad_w(int dtype, const void* G, int64_t Vpad, const void* H, int64_t d, int64_t V,
+                   int64_t row0, int64_t nrows, bool accumulate, float* grad_w, hipStream_t s);
+
+// Utilities.
+void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+void launch_validate_idx(const int32_t* idx, int64_t N, int K, int64_t V, int32_t* flag,
+                         hipStream_t s);
+
+}  // namespace fkl

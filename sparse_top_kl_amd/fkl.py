@@ -1,0 +1,241 @@
+"""ctypes binding of libfkl (include/fkl.h), plus an autograd wrapper.
+
+Argument marshalling only: tensors become device pointers, torch's current
+HIP stream is passed through, and the library's status codes become
+exceptions. Every step of the loss runs in libfkl's HIP kernels; there is no
+CPU or PyTorch fallback. If the library is not built this module raises.
+
+Functions with the ``fkl_`` prefix mirror the C entry points one to one;
+``fused_chunked_kl`` is the user-facing loss with autograd.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfkl.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "fkl.h")
+
+
+def _header_constants() -> dict:
+    consts = {}
+    with open(HEADER_PATH) as f:
+        for m in re.finditer(r"#define\s+(FKL_\w+)\s+(\d+)u?", f.read()):
+            consts[m.group(1)] = int(m.group(2))
+    return consts
+
+
+_C = _header_constants()
+FKL_OK = _C["FKL_OK"]
+FKL_E_ARG = _C["FKL_E_ARG"]
+FKL_E_UNSUPPORTED = _C["FKL_E_UNSUPPORTED"]
+FKL_E_WORKSPACE = _C["FKL_E_WORKSPACE"]
+FKL_E_HIP = _C["FKL_E_HIP"]
+FKL_E_INDEX = _C["FKL_E_INDEX"]
+FKL_F32 = _C["FKL_F32"]
+FKL_BF16 = _C["FKL_BF16"]
+FKL_FLAG_ACCUMULATE_GRAD_W = _C["FKL_FLAG_ACCUMULATE_GRAD_W"]
+FKL_FLAG_VALIDATE_IDX = _C["FKL_FLAG_VALIDATE_IDX"]
+
+
+class FklError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libfkl status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_u32 = ctypes.c_uint32
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "fkl_abi_version": (_i32, []),
+    "fkl_status_string": (ctypes.c_char_p, [_i32]),
+    "fkl_last_error": (ctypes.c_char_p, []),
+    "fkl_workspace_size": (_i32, [_i64, _i64, _i64, _i32, _i64, _i32,
+                                  ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "fkl_forward": (_i32, [_p, _p, _p, _p, _f32, _i64, _i64, _i64, _i64, _i32, _i32, _u32,
+                           _p, _p, _p, _p, _p, _sz, _p]),
+    "fkl_backward": (_i32, [_p, _p, _p, _p, _p, _p, _p, _f32, _i64, _i64, _i64, _i64, _i32,
+                            _i32, _u32, _p, _p, _p, _sz, _p]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfkl.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m sparse_top_kl_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != FKL_OK:
+        raise FklError(status, f"{fkl_status_string(status)}: {fkl_last_error()}")
+
+
+def fkl_abi_version() -> int:
+    return lib().fkl_abi_version()
+
+
+def fkl_status_string(status: int) -> str:
+    return lib().fkl_status_string(status).decode()
+
+
+def fkl_last_error() -> str:
+    return lib().fkl_last_error().decode()
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return FKL_BF16
+    if dt == torch.float32:
+        return FKL_F32
+    raise FklError(FKL_E_UNSUPPORTED, f"hidden/weight dtype {dt} (bf16 or fp32 only)")
+
+
+def fkl_workspace_size(N, d, V, K, chunk, dtype) -> tuple[int, int]:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    f, b = _sz(0), _sz(0)
+    _check(lib().fkl_workspace_size(N, d, V, K, chunk, code, ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _require(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise FklError(FKL_E_ARG, f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise FklError(FKL_E_ARG, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise FklError(FKL_E_ARG, f"{name} must be {dtype}, got {t.dtype}")
+
+
+@dataclass
+class ForwardResult:
+    loss: torch.Tensor       # [] fp32
+    lse: torch.Tensor        # [N] fp32
+    row_loss: torch.Tensor   # [N] fp32
+    topk_z: torch.Tensor     # [N, K] fp32
+
+
+def fkl_forward(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Tensor,
+                topk_logit: torch.Tensor, T: float, chunk: int, *, validate: bool = False,
+                workspace: torch.Tensor | None = None) -> ForwardResult:
+    """Forward pass on [N, d] hidden, [V, d] weight, [N, K] int32 ids and fp32 logits."""
+    N, d = hidden.shape
+    V, K = weight.shape[0], topk_idx.shape[1]
+    code = dtype_code(hidden.dtype)
+    for t, n, dt in ((hidden, "hidden", None), (weight, "weight", hidden.dtype),
+                     (topk_idx, "topk_idx", torch.int32), (topk_logit, "topk_logit", torch.float32)):
+        _require(t, n, dt)
+    dev = hidden.device
+    fw, _ = fkl_workspace_size(N, d, V, K, chunk, code)
+    ws = workspace if workspace is not None else _workspace(fw, dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    row_loss = torch.empty(N, dtype=torch.float32, device=dev)
+    topk_z = torch.empty(N, K, dtype=torch.float32, device=dev)
+    flags = FKL_FLAG_VALIDATE_IDX if validate else 0
+    _check(lib().fkl_forward(_ptr(hidden), _ptr(weight), _ptr(topk_idx), _ptr(topk_logit),
+                             float(T), chunk, N, d, V, K, code, flags, _ptr(loss), _ptr(lse),
+                             _ptr(row_loss), _ptr(topk_z), _ptr(ws), ws.numel(), _stream(dev)))
+    return ForwardResult(loss, lse, row_loss, topk_z)
+
+
+def fkl_backward(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Tensor,
+                 topk_logit: torch.Tensor, lse: torch.Tensor, T: float, chunk: int, *,
+                 topk_z: torch.Tensor | None = None, grad_loss: torch.Tensor | None = None,
+                 grad_weight: torch.Tensor | None = None, accumulate: bool = False,
+                 validate: bool = False, workspace: torch.Tensor | None = None):
+    """Backward pass; returns (grad_hidden [N, d] in hidden's dtype, grad_weight [V, d] fp32)."""
+    N, d = hidden.shape
+    V, K = weight.shape[0], topk_idx.shape[1]
+    code = dtype_code(hidden.dtype)
+    for t, n, dt in ((hidden, "hidden", None), (weight, "weight", hidden.dtype),
+                     (topk_idx, "topk_idx", torch.int32), (topk_logit, "topk_logit", torch.float32),
+                     (lse, "lse", torch.float32)):
+        _require(t, n, dt)
+    if topk_z is not None:
+        _require(topk_z, "topk_z", torch.float32)
+    if grad_loss is not None:
+        _require(grad_loss, "grad_loss", torch.float32)
+    dev = hidden.device
+    _, bw = fkl_workspace_size(N, d, V, K, chunk, code)
+    ws = workspace if workspace is not None else _workspace(bw, dev)
+    grad_hidden = torch.empty_like(hidden)
+    if grad_weight is None:
+        grad_weight = torch.empty(V, d, dtype=torch.float32, device=dev)
+    else:
+        _require(grad_weight, "grad_weight", torch.float32)
+    flags = (FKL_FLAG_ACCUMULATE_GRAD_W if accumulate else 0) | \
+        (FKL_FLAG_VALIDATE_IDX if validate else 0)
+    _check(lib().fkl_backward(_ptr(hidden), _ptr(weight), _ptr(topk_idx), _ptr(topk_logit),
+                              _ptr(lse), _ptr(topk_z), _ptr(grad_loss), float(T), chunk, N, d, V,
+                              K, code, flags, _ptr(grad_hidden), _ptr(grad_weight), _ptr(ws),
+                              ws.numel(), _stream(dev)))
+    return grad_hidden, grad_weight
+
+
+class FusedChunkedKL(torch.autograd.Function):
+    """Autograd wrapper: saves lse and the gathered logits, not the N x V logits."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, topk_idx, topk_logit, T, chunk):
+        shape = hidden.shape
+        h2 = hidden.reshape(-1, shape[-1]).contiguous()
+        idx = topk_idx.reshape(h2.shape[0], -1).to(torch.int32).contiguous()
+        lg = topk_logit.reshape(h2.shape[0], -1).to(torch.float32).contiguous()
+        w = weight.contiguous()
+        out = fkl_forward(h2, w, idx, lg, T, chunk)
+        ctx.save_for_backward(h2, w, idx, lg, out.lse, out.topk_z)
+        ctx.T, ctx.chunk, ctx.shape = T, chunk, shape
+        return out.loss
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        h2, w, idx, lg, lse, zk = ctx.saved_tensors
+        g = grad_loss.to(torch.float32).reshape(()).contiguous()
+        gh, gw = fkl_backward(h2, w, idx, lg, lse, ctx.T, ctx.chunk, topk_z=zk, grad_loss=g)
+        return gh.reshape(ctx.shape), gw.to(w.dtype), None, None, None, None
+
+
+def fused_chunked_kl(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Tensor,
+                     topk_logit: torch.Tensor, T: float = 1.0, chunk: int = 2048) -> torch.Tensor:
+    """Sum over tokens of T^2 KL(teacher top-K softmax || student softmax) at temperature T.
+
+    hidden [..., d] (bf16 or fp32), weight [V, d] (LM head, nn.Linear layout),
+    topk_idx / topk_logit [..., K]. Returns a 0-d fp32 tensor; gradients flow to
+    hidden and weight.
+    """
+    return FusedChunkedKL.apply(hidden, weight, topk_idx, topk_logit, float(T), int(chunk))

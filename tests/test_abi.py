@@ -1,0 +1,139 @@
+"""The C ABI without a GPU: symbols, constants, workspace planning, validation.
+
+Validation happens before anything is enqueued, so calls that must fail can
+be made here with placeholder (never dereferenced) device addresses.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_top_kl_amd import fkl
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fkl.h")
+
+
+def _declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fkl_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = fkl.lib()
+    names = _declared_functions()
+    assert {"fkl_forward", "fkl_backward", "fkl_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in fkl.h but not exported"
+
+
+def test_binding_covers_every_declared_function():
+    for n in _declared_functions():
+        assert callable(getattr(fkl, n)), n
+
+
+def test_abi_version_and_status_strings():
+    assert fkl.fkl_abi_version() == 1
+    assert fkl.fkl_status_string(fkl.FKL_OK) == "ok"
+    assert fkl.fkl_status_string(fkl.FKL_E_WORKSPACE) == "workspace too small"
+    assert fkl.fkl_status_string(12345) == "unknown status"
+
+
+def test_workspace_is_linear_in_rows_and_never_rows_times_vocab():
+    d, V, K, chunk = 3072, 128256, 100, 2048
+    f1, b1 = fkl.fkl_workspace_size(32768, d, V, K, chunk, fkl.FKL_BF16)
+    f2, b2 = fkl.fkl_workspace_size(65536, d, V, K, chunk, fkl.FKL_BF16)
+    per_row_f = (f2 - f1) / 32768
+    per_row_b = (b2 - b1) / 32768
+    assert per_row_f < 8 * K        # per-row scratch only (row loss, gathered logits)
+    assert per_row_b == 0           # the backward's scratch is chunk-sized
+    # the only chunk x V object is the bf16 logit-gradient buffer
+    assert b1 < chunk * V * 2 * 1.5
+    assert b1 < 32768 * V * 2 / 8
+    # it scales with the chunk
+    _, b3 = fkl.fkl_workspace_size(32768, d, V, K, 4096, fkl.FKL_BF16)
+    assert b3 > 1.5 * b1
+
+
+def test_workspace_size_rejects_bad_shapes():
+    with pytest.raises(fkl.FklError) as e:
+        fkl.fkl_workspace_size(10, 12, 100, 5, 4, fkl.FKL_BF16)
+    assert e.value.status == fkl.FKL_E_UNSUPPORTED
+    with pytest.raises(fkl.FklError) as e:
+        fkl.fkl_workspace_size(10, 16, 100, 101, 4, fkl.FKL_BF16)
+    assert e.value.status == fkl.FKL_E_ARG
+    with pytest.raises(fkl.FklError) as e:
+        fkl.fkl_workspace_size(10, 16, 100, 5, 0, fkl.FKL_BF16)
+    assert e.value.status == fkl.FKL_E_ARG
+    with pytest.raises(fkl.FklError) as e:
+        fkl.fkl_workspace_size(10, 16, 100, 5, 4, 7)
+    assert e.value.status == fkl.FKL_E_UNSUPPORTED
+
+
+# placeholder addresses: 16-byte aligned, never dereferenced on the error paths
+A = 0x10000
+
+
+def _fwd(**over):
+    args = dict(hidden=A, weight=A, idx=A, logit=A, T=1.0, chunk=4, N=10, d=16, V=100, K=5,
+                dtype=fkl.FKL_BF16, flags=0, loss=A, lse=A, row_loss=None, topk_z=None,
+                ws=A, ws_bytes=1 << 40, stream=None)
+    args.update(over)
+    return fkl.lib().fkl_forward(*args.values())
+
+
+def _bwd(**over):
+    args = dict(hidden=A, weight=A, idx=A, logit=A, lse=A, topk_z=None, grad_loss=None, T=1.0,
+                chunk=4, N=10, d=16, V=100, K=5, dtype=fkl.FKL_BF16, flags=0, gh=A, gw=A, ws=A,
+                ws_bytes=1 << 40, stream=None)
+    args.update(over)
+    return fkl.lib().fkl_backward(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(hidden=None), fkl.FKL_E_ARG),
+    (dict(loss=None), fkl.FKL_E_ARG),
+    (dict(lse=None), fkl.FKL_E_ARG),
+    (dict(hidden=A + 2), fkl.FKL_E_ARG),
+    (dict(lse=A + 2), fkl.FKL_E_ARG),
+    (dict(T=0.0), fkl.FKL_E_ARG),
+    (dict(T=-1.0), fkl.FKL_E_ARG),
+    (dict(T=float("nan")), fkl.FKL_E_ARG),
+    (dict(T=float("inf")), fkl.FKL_E_ARG),
+    (dict(chunk=0), fkl.FKL_E_ARG),
+    (dict(N=-1), fkl.FKL_E_ARG),
+    (dict(K=0), fkl.FKL_E_ARG),
+    (dict(K=101), fkl.FKL_E_ARG),
+    (dict(d=12), fkl.FKL_E_UNSUPPORTED),
+    (dict(dtype=5), fkl.FKL_E_UNSUPPORTED),
+    (dict(flags=1), fkl.FKL_E_ARG),
+    (dict(ws_bytes=16), fkl.FKL_E_WORKSPACE),
+])
+def test_forward_validation(over, code):
+    assert _fwd(**over) == code
+    assert fkl.fkl_last_error() != ""
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(gh=None), fkl.FKL_E_ARG),
+    (dict(gw=None), fkl.FKL_E_ARG),
+    (dict(lse=None), fkl.FKL_E_ARG),
+    (dict(gw=A + 4), fkl.FKL_E_ARG),
+    (dict(grad_loss=A + 1), fkl.FKL_E_ARG),
+    (dict(T=0.0), fkl.FKL_E_ARG),
+    (dict(flags=4), fkl.FKL_E_ARG),
+    (dict(K=5000, V=10000), fkl.FKL_E_UNSUPPORTED),
+    (dict(ws_bytes=1024), fkl.FKL_E_WORKSPACE),
+])
+def test_backward_validation(over, code):
+    assert _bwd(**over) == code
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(fkl, "_lib", None)
+    monkeypatch.setattr(fkl, "LIB_PATH", "/nonexistent/libfkl.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        fkl.lib()
