@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused chunked top-K KL loss (forward + backward) on one MI355X.
+
+One step = fkl_forward + fkl_backward over all rows of the workload (every
+chunk), inputs resident in HBM, workspaces allocated before timing. Prints one
+JSON line: throughput in tokens/s, the MFMA roofline of the dominant kernel
+(its average launch time measured with HIP events inside the timed region),
+peak HBM of one step, a sampled parity check against the fp64 oracle and the
+oracle's own host throughput on a bounded sample of the same rows.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "fused KL fwd+bwd tokens/s + % bf16 MFMA peak; peak HBM GiB at 32K tokens"
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}
+PEAK_HBM_GBS = 8000.0
+GEMM_KERNELS = ("k_logits_lse", "k_gprod", "k_grad_hidden", "k_grad_w")
+# figures printed on the pages (context only, other hardware, other scope)
+PAGE_CONTEXT = {
+    "isolated_32k_loss_peak_GiB": {"dense": 85.2, "fused_chunked": 5.45},
+    "h200_8k_training_peak_GB": {"online": 102.8, "fully_chunked": 58.3},
+    "gptoss20b_32768_step_s": {"before": 57.0, "after": 12.23},
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_top_kl_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, gpu_rows: dict, budget_s: float):
+    """Time the fp64 oracle (as it stands) on a bounded prefix of the rows and
+    compare its outputs for those rows with the GPU's."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    w = inp["workload"]
+
+    def run(n):
+        t0 = time.perf_counter()
+        out = oracle.forward_backward(inp["hidden"][:n], inp["weight"], inp["topk_idx"][:n],
+                                      inp["topk_logit"][:n], w.T)
+        return out, time.perf_counter() - t0
+
+    # calibrate on two sizes (the fixed per-call cost is large), then fill the budget
+    _, t1 = run(16)
+    _, t2 = run(64)
+    per_row = max((t2 - t1) / 48, 1e-6)
+    n = int(max(64, min(w.N, (budget_s - max(t1 - 16 * per_row, 0.0)) / per_row)))
+    n = max(16, (n // 16) * 16)
+    out, t = run(n)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    tol = 1e-3 if w.dtype == "bf16" else 1e-5
+    gtol = 2e-2 if w.dtype == "bf16" else 1e-4
+    lse_err = float(np.max(np.abs(gpu_rows["lse"][:n] - out["lse"]) / np.abs(out["lse"])))
+    rl_err = float(np.max(np.abs(gpu_rows["row_loss"][:n] - out["row_loss"]) /
+                          np.maximum(np.abs(out["row_loss"]), 1.0)))
+    gh_err = float(np.max(np.abs(gpu_rows["grad_hidden"][:n] - out["grad_hidden"])) /
+                   np.max(np.abs(out["grad_hidden"])))
+    parity = {
+        "rows": n,
+        "lse_rel_err": lse_err,
+        "row_loss_rel_err": rl_err,
+        "grad_hidden_err_over_max": gh_err,
+        "ok": bool(lse_err <= tol and rl_err <= tol and gh_err <= gtol),
+    }
+    base = {
+        "value": n / t,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {n} of {w.N} rows of {w.name}, forward+backward in fp64 "
+                  f"(NumPy BLAS), {t:.1f} s; grad_W restricted to those rows",
+    }
+    return base, parity
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="long32k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this loss is benchmarked on a single MI355X "
+              "(row sharding across GPUs would add one grad_W all-reduce; not built). "
+              f"Got --gpus {args.gpus}, WORLD_SIZE {world}.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_top_kl_amd import fkl, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    log(f"[bench] generating {w.name}: N={w.N} d={w.d} V={w.V} K={w.K} T={w.T} "
+        f"chunk={w.chunk} {w.dtype}")
+    inp = synth.make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    h = torch.from_numpy(inp["hidden"]).to(dev).to(dt).contiguous()
+    W = torch.from_numpy(inp["weight"]).to(dev).to(dt).contiguous()
+    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    lg = torch.from_numpy(inp["topk_logit"]).to(dev)
+    torch.cuda.synchronize()
+    input_bytes = sum(t.numel() * t.element_size() for t in (h, W, idx, lg))
+
+    fw, bw = fkl.fkl_workspace_size(w.N, w.d, w.V, w.K, w.chunk, dt)
+    ws_f = torch.empty(fw, dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(bw, dtype=torch.uint8, device=dev)
+    gw = torch.empty(w.V, w.d, dtype=torch.float32, device=dev)
+
+    def step():
+        out = fkl.fkl_forward(h, W, idx, lg, w.T, w.chunk, workspace=ws_f)
+        gh, _ = fkl.fkl_backward(h, W, idx, lg, out.lse, w.T, w.chunk, topk_z=out.topk_z,
+                                 grad_weight=gw, workspace=ws_b)
+        return out, gh
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # peak HBM of one step (inputs, outputs, workspaces, grad_W)
+    del ws_f, ws_b
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    ws_f = torch.empty(fw, dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(bw, dtype=torch.uint8, device=dev)
+    out, gh = step()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev)
+    largest_ws = max(fw, bw)
+    gpu_rows = {
+        "lse": out.lse.double().cpu().numpy(),
+        "row_loss": out.row_loss.double().cpu().numpy(),
+        "grad_hidden": gh.double().cpu().numpy(),
+    }
+    loss_val = out.loss.item()
+    del out, gh
+
+    log(f"[bench] timing {args.steps} steps")
+    fkl.fkl_timing_reset()
+    fkl.fkl_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fkl.fkl_timing_enable(False)
+    ktimes = fkl.kernel_times()
+    log(f"[bench] {elapsed / args.steps * 1e3:.2f} ms/step")
+
+    flops_step = 8.0 * w.N * w.d * w.V
+    ms_step = elapsed / args.steps * 1e3
+    kernels = {k: {"launches_per_step": n / args.steps, "avg_ms": ms / n,
+                   "ms_per_step": ms / args.steps} for k, (n, ms) in ktimes.items()}
+    dom = max(ktimes, key=lambda k: ktimes[k][1])
+    n_launch, dom_ms = ktimes[dom]
+    avg_ms = dom_ms / n_launch
+    peak_tf = PEAK_TFLOPS[w.dtype]
+    if dom in GEMM_KERNELS:
+        rows_per_launch = w.N / (n_launch / args.steps)
+        flops_launch = 2.0 * rows_per_launch * w.d * w.V
+        achieved = flops_launch / (avg_ms * 1e-3) / 1e12
+        traffic = load_traffic(dom, w.name)
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak_tf,
+                    "unit": "TFLOP/s", "frac": achieved / peak_tf, "traffic": traffic,
+                    "flops_per_launch": flops_launch, "avg_launch_ms": avg_ms}
+    else:
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": None, "traffic": load_traffic(dom, w.name),
+                    "avg_launch_ms": avg_ms}
+
+    if args.no_cpu_baseline:
+        base, parity = None, None
+    else:
+        log("[bench] oracle on the host (cpu_baseline and sampled parity)")
+        base, parity = cpu_baseline(inp, gpu_rows, args.cpu_seconds)
+
+    tokens_s = w.N * args.steps / elapsed
+    result = {
+        "metric": METRIC,
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "N": w.N, "d": w.d, "V": w.V,
+                   "K": w.K, "T": w.T, "chunk": w.chunk, "teacher_ids": w.ids},
+        "mfma_frac_step": flops_step / (ms_step * 1e-3) / (peak_tf * 1e12),
+        "flops_per_step": flops_step,
+        "roofline": roofline,
+        "cpu_baseline": base,
+        "parity_sampled": parity,
+        "peak_hbm_gib": peak / 2**30,
+        "peak_hbm_path_gib": (peak - input_bytes) / 2**30,
+        "largest_workspace_gib": largest_ws / 2**30,
+        "dense_nxv_fp32_gib": w.N * w.V * 4 / 2**30,
+        "loss": loss_val,
+        "kernels": kernels,
+        "source_hash": source_hash(),
+        "context_pages": PAGE_CONTEXT,
+    }
+    if not math.isfinite(loss_val):
+        log("[bench] non-finite loss")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

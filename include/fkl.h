@@ -134,6 +134,24 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
                      int64_t V, int32_t K, int32_t dtype, uint32_t flags, void* grad_hidden,
                      float* grad_weight, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Per-kernel timing, a profiling aid (off by default). While enabled, every
+ * kernel launch the library makes is bracketed by two HIP events recorded on
+ * the launch stream; the events cost a few microseconds of GPU time each.
+ * Kernel ids run from 0 to fkl_kernel_count() - 1.
+ *   fkl_timing_enable: on = 1 enables, 0 disables; returns the previous state.
+ *   fkl_timing_reset:  waits for outstanding events and zeroes all totals.
+ *   fkl_timing_read:   waits for outstanding events (host-blocking) and writes
+ *                      the launch count and summed milliseconds of one kernel
+ *                      since the last reset; FKL_E_ARG for an unknown id.
+ *   fkl_kernel_name:   static name of a kernel id, NULL if unknown.
+ * Timing state is process-wide; concurrent library calls on several streams
+ * are timed correctly but share the totals. */
+int32_t fkl_timing_enable(int32_t on);
+int32_t fkl_timing_reset(void);
+int32_t fkl_timing_read(int32_t kernel, int64_t* launches, double* total_ms);
+int32_t fkl_kernel_count(void);
+const char* fkl_kernel_name(int32_t kernel);
+
 #ifdef __cplusplus
 }
 #endif

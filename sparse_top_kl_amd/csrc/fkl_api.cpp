@@ -11,6 +11,7 @@
 #include <cstring>
 
 #include "kernels.hpp"
+#include "timing.hpp"
 
 namespace {
 
@@ -265,5 +266,23 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
   }
   return hip_check("backward launch");
 }
+
+int32_t fkl_timing_enable(int32_t on) { return fkl::timing_set(on != 0) ? 1 : 0; }
+
+int32_t fkl_timing_reset(void) {
+  fkl::timing_reset();
+  return FKL_OK;
+}
+
+int32_t fkl_timing_read(int32_t kernel, int64_t* launches, double* total_ms) {
+  g_last_error[0] = 0;
+  if (!fkl::timing_read(kernel, launches, total_ms))
+    return fail(FKL_E_ARG, "unknown kernel id %d", kernel);
+  return FKL_OK;
+}
+
+int32_t fkl_kernel_count(void) { return fkl::KID_COUNT; }
+
+const char* fkl_kernel_name(int32_t kernel) { return fkl::kernel_name(kernel); }
 
 }  // extern "C"

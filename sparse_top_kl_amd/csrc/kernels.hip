@@ -28,6 +28,7 @@
 
 #include "gemm_core.hpp"
 #include "kernels.hpp"
+#include "timing.hpp"
 
 namespace fkl {
 
@@ -474,6 +475,7 @@ void grad_hidden_split(int64_t rows, int64_t d, int64_t Vpad, int dtype, int64_t
 void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64_t V,
                        int64_t row0, int64_t nrows, float c2, float2* part, int64_t part_ld,
                        hipStream_t s) {
+  ScopedTimer timer_(KID_LOGITS_LSE, s);
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(V, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
@@ -488,6 +490,7 @@ void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64
 void launch_gather_dot(int dtype, const void* W, const void* H, const int32_t* idx, int64_t d,
                        int64_t row0, int64_t nrows, int K, float* zk, hipStream_t s) {
   if (nrows <= 0) return;
+  ScopedTimer timer_(KID_GATHER_DOT, s);
   const int64_t eb = dtype == 1 ? 2 : 4;
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
   const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, 4));
@@ -502,18 +505,21 @@ void launch_gather_dot(int dtype, const void* W, const void* H, const int32_t* i
 void launch_merge_loss(const float2* part, int64_t part_ld, int64_t nslots, const float* zk,
                        const float* logit, int64_t row0, int64_t nrows, int K, float T,
                        float* lse, float* row_loss, hipStream_t s) {
+  ScopedTimer timer_(KID_MERGE_LOSS, s);
   const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, 4));
   k_merge_loss<<<blocks, 256, 0, s>>>(part, part_ld, nslots, zk + row0 * K, logit + row0 * K,
                                       nrows, K, T, lse + row0, row_loss ? row_loss + row0 : nullptr);
 }
 
 void launch_reduce_loss(const float* row_loss, int64_t N, float* loss, hipStream_t s) {
+  ScopedTimer timer_(KID_REDUCE_LOSS, s);
   k_reduce_loss<<<1, 1024, 0, s>>>(row_loss, N, loss);
 }
 
 void launch_bwd_prep(const float* logit, const float* lse, const float* grad_loss, int64_t row0,
                      int64_t nrows, int K, float T, float* pcoef, float* acoef, float* lse2,
                      hipStream_t s) {
+  ScopedTimer timer_(KID_BWD_PREP, s);
   const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, 4));
   k_bwd_prep<<<blocks, 256, 0, s>>>(logit + row0 * K, lse + row0, grad_loss, nrows, K, T, pcoef,
                                     acoef, lse2);
@@ -522,6 +528,7 @@ void launch_bwd_prep(const float* logit, const float* lse, const float* grad_los
 void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t Vpad,
                   int64_t row0, int64_t nrows, float c2, const float* acoef, const float* lse2,
                   void* G, hipStream_t s) {
+  ScopedTimer timer_(KID_GPROD, s);
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(Vpad, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
@@ -539,6 +546,7 @@ void launch_fixup(int dtype, void* G, int64_t Vpad, const int32_t* idx, const fl
                   const float* pcoef, const float* acoef, const float* lse2, int64_t row0,
                   int64_t nrows, int K, float c2, hipStream_t s) {
   if (nrows <= 0) return;
+  ScopedTimer timer_(KID_FIXUP, s);
   const size_t shm = static_cast<size_t>(K) * 8;
   if (dtype == 1)
     k_fixup<BF16><<<static_cast<unsigned>(nrows), 64, shm, s>>>(
@@ -551,6 +559,7 @@ void launch_fixup(int dtype, void* G, int64_t Vpad, const int32_t* idx, const fl
 void launch_grad_hidden(int dtype, const void* G, int64_t Vpad, const void* W, int64_t d,
                         int64_t V, int64_t nrows, int64_t splits, int64_t split_len,
                         float* part, hipStream_t s) {
+  ScopedTimer timer_(KID_GRAD_HIDDEN, s);
   const int64_t n_tt = ceil_div(nrows, kBM), n_dt = ceil_div(d, kBN);
   const unsigned grid = grid_for_tiles(splits * n_tt * n_dt);
   if (dtype == 1)
@@ -571,6 +580,7 @@ void launch_reduce_grad_hidden(int dtype, const float* part, int64_t splits, int
   int64_t blocks = ceil_div(n4, 256);
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) return;
+  ScopedTimer timer_(KID_REDUCE_GH, s);
   if (dtype == 1)
     k_reduce_gh<BF16><<<static_cast<unsigned>(blocks), 256, 0, s>>>(part, splits, nrows, d, out);
   else
@@ -579,6 +589,7 @@ void launch_reduce_grad_hidden(int dtype, const float* part, int64_t splits, int
 
 void launch_grad_w(int dtype, const void* G, int64_t Vpad, const void* H, int64_t d, int64_t V,
                    int64_t row0, int64_t nrows, bool accumulate, float* grad_w, hipStream_t s) {
+  ScopedTimer timer_(KID_GRAD_W, s);
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(V, kBM), n_dt = ceil_div(d, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
@@ -593,6 +604,7 @@ void launch_grad_w(int dtype, const void* G, int64_t Vpad, const void* H, int64_
 
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
   if (n <= 0) return;
+  ScopedTimer timer_(KID_FILL, s);
   int64_t blocks = ceil_div(n, 256);
   if (blocks > 8192) blocks = 8192;
   k_fill_f32<<<static_cast<unsigned>(blocks), 256, 0, s>>>(p, n, v);
@@ -602,6 +614,7 @@ void launch_validate_idx(const int32_t* idx, int64_t N, int K, int64_t V, int32_
                          hipStream_t s) {
   const int64_t n = N * K;
   if (n <= 0) return;
+  ScopedTimer timer_(KID_VALIDATE, s);
   int64_t blocks = ceil_div(n, 256);
   if (blocks > 4096) blocks = 4096;
   k_validate_idx<<<static_cast<unsigned>(blocks), 256, 0, s>>>(idx, n, V, flag);

@@ -69,6 +69,11 @@ _SIGNATURES = {
                            _p, _p, _p, _p, _p, _sz, _p]),
     "fkl_backward": (_i32, [_p, _p, _p, _p, _p, _p, _p, _f32, _i64, _i64, _i64, _i64, _i32,
                             _i32, _u32, _p, _p, _p, _sz, _p]),
+    "fkl_timing_enable": (_i32, [_i32]),
+    "fkl_timing_reset": (_i32, []),
+    "fkl_timing_read": (_i32, [_i32, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]),
+    "fkl_kernel_count": (_i32, []),
+    "fkl_kernel_name": (ctypes.c_char_p, [_i32]),
 }
 
 
@@ -205,6 +210,41 @@ def fkl_backward(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Ten
                               K, code, flags, _ptr(grad_hidden), _ptr(grad_weight), _ptr(ws),
                               ws.numel(), _stream(dev)))
     return grad_hidden, grad_weight
+
+
+def fkl_timing_enable(on: bool) -> bool:
+    """Turns per-kernel event timing on or off; returns the previous state."""
+    return bool(lib().fkl_timing_enable(1 if on else 0))
+
+
+def fkl_timing_reset() -> None:
+    _check(lib().fkl_timing_reset())
+
+
+def fkl_timing_read(kernel: int) -> tuple[int, float]:
+    """(launches, total milliseconds) of one kernel since the last reset."""
+    n, ms = _i64(0), ctypes.c_double(0.0)
+    _check(lib().fkl_timing_read(kernel, ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
+
+
+def fkl_kernel_count() -> int:
+    return lib().fkl_kernel_count()
+
+
+def fkl_kernel_name(kernel: int) -> str | None:
+    r = lib().fkl_kernel_name(kernel)
+    return None if r is None else r.decode()
+
+
+def kernel_times() -> dict:
+    """{kernel name: (launches, total ms)} for every kernel since the last reset."""
+    out = {}
+    for k in range(fkl_kernel_count()):
+        n, ms = fkl_timing_read(k)
+        if n:
+            out[fkl_kernel_name(k)] = (n, ms)
+    return out
 
 
 class FusedChunkedKL(torch.autograd.Function):
