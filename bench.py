@@ -205,8 +205,8 @@ def main():
     avg_ms = dom_ms / n_launch
     peak_tf = PEAK_TFLOPS[w.dtype]
     if dom in GEMM_KERNELS:
-        rows_per_launch = w.N / (n_launch / args.steps)
-        flops_launch = 2.0 * rows_per_launch * w.d * w.V
+        # each of the four contractions covers all N x V logits once per step
+        flops_launch = 2.0 * w.N * w.d * w.V / (n_launch / args.steps)
         achieved = flops_launch / (avg_ms * 1e-3) / 1e12
         traffic = load_traffic(dom, w.name)
         roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak_tf,

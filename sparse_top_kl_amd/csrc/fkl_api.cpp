@@ -30,17 +30,67 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Largest offset a buffer load may reach: 2 GiB less a margin.
+constexpr int64_t kMaxBlockBytes = (int64_t(1) << 31) - (int64_t(1) << 20);
+
+// The backward keeps one block of the logit gradient G, bw_rows x bw_pitch,
+// with bw_rows * bw_pitch <= chunk * Vpad (the memory the chunk size allows).
+// grad_W is read-modified-written once per extra row block and the fp32
+// grad_hidden accumulator once per extra vocabulary slice, so the shape
+// minimising (row blocks - 1) * V + (slices - 1) * N is chosen.
 struct Plan {
-  int64_t chunk_cap;  // rows per pass actually used (<= N, >= 1)
-  int64_t Vpad;       // G row pitch in elements
+  int64_t chunk_cap;  // forward rows per pass (<= N, >= 1)
+  int64_t Vpad;       // vocabulary rounded up to 8
   int64_t nslots;     // vocabulary slices holding a partial (valid ones)
   int64_t slot_cap;   // partial slots allocated per row
-  int64_t gh_splits, gh_len;
+  // backward blocking: row blocks of bw_rows x vocabulary slices of bw_pitch
+  int64_t bw_rows, bw_pitch;
   // forward workspace offsets
   size_t f_part, f_rowloss, f_topkz, f_flag, f_total;
   // backward workspace offsets
-  size_t b_G, b_ghpart, b_pcoef, b_acoef, b_lse2, b_zk, b_flag, b_total;
+  size_t b_G, b_ghacc, b_pcoef, b_acoef, b_lse2, b_zk, b_flag, b_total;
 };
+
+void plan_backward_blocks(int64_t N, int64_t V, int64_t Vpad, int64_t chunk_cap, int64_t eb,
+                          int64_t* rows, int64_t* pitch) {
+  int64_t budget = chunk_cap * Vpad;
+  if (budget > kMaxBlockBytes / eb) budget = kMaxBlockBytes / eb;
+  if (budget >= N * Vpad) {  // one block covers everything
+    *rows = N;
+    *pitch = Vpad;
+    return;
+  }
+  double best = 1e300;
+  *rows = 1;
+  *pitch = Vpad;
+  const int64_t max_blocks = fkl::ceil_div(N, 256);
+  for (int64_t nb = 1; nb <= max_blocks; ++nb) {
+    const int64_t rc = nb == 1 ? N : fkl::round_up(fkl::ceil_div(N, nb), 256);
+    if (rc > N || rc * 256 > budget) continue;
+    const int64_t vs_max = budget / rc;
+    int64_t ns, vs;
+    if (vs_max >= Vpad) {
+      ns = 1;
+      vs = Vpad;
+    } else {
+      const int64_t vm = vs_max / 256 * 256;
+      ns = fkl::ceil_div(Vpad, vm);
+      vs = fkl::round_up(fkl::ceil_div(Vpad, ns), 256);
+      if (vs > vm) continue;
+    }
+    const int64_t nblk = fkl::ceil_div(N, rc);
+    const double cost = double(nblk - 1) * V + double(ns - 1) * N + 1024.0 * nblk * ns;
+    if (cost < best) {
+      best = cost;
+      *rows = rc;
+      *pitch = vs;
+    }
+  }
+  if (best == 1e300) {  // tiny budget: one row per block, whole vocabulary
+    *rows = budget / Vpad > 0 ? (budget / Vpad < N ? budget / Vpad : N) : 1;
+    *pitch = Vpad;
+  }
+}
 
 int32_t check_shapes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_t dtype) {
   if (dtype != FKL_F32 && dtype != FKL_BF16) return fail(FKL_E_UNSUPPORTED, "unknown dtype %d", dtype);
@@ -52,6 +102,9 @@ int32_t check_shapes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, 
   if (K < 1 || K > V) return fail(FKL_E_ARG, "K must be in [1, V] (got %d)", K);
   if (K > 4096) return fail(FKL_E_UNSUPPORTED, "K > 4096 is not supported (got %d)", K);
   if (chunk < 1) return fail(FKL_E_ARG, "chunk must be >= 1 (got %lld)", (long long)chunk);
+  const int64_t eb = dtype == FKL_BF16 ? 2 : 4;
+  if (V * d * eb > kMaxBlockBytes)
+    return fail(FKL_E_UNSUPPORTED, "weight larger than 2 GiB is not supported");
   return FKL_OK;
 }
 
@@ -64,7 +117,7 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_
   p.Vpad = round_up(V, 8);
   p.nslots = ceil_div(V, kSliceVocab);
   p.slot_cap = lse_slots(V);
-  grad_hidden_split(p.chunk_cap, d, p.Vpad, dtype, &p.gh_splits, &p.gh_len);
+  plan_backward_blocks(N > 0 ? N : 1, V, p.Vpad, p.chunk_cap, eb, &p.bw_rows, &p.bw_pitch);
 
   size_t off = 0;
   p.f_part = off;
@@ -77,19 +130,20 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_
   off = align_up(off + 4);
   p.f_total = off;
 
+  const size_t rows = static_cast<size_t>(p.bw_rows);
   off = 0;
   p.b_G = off;
-  off = align_up(off + static_cast<size_t>(p.chunk_cap) * p.Vpad * eb);
-  p.b_ghpart = off;
-  off = align_up(off + static_cast<size_t>(p.gh_splits) * p.chunk_cap * d * 4);
+  off = align_up(off + rows * p.bw_pitch * eb);
+  p.b_ghacc = off;
+  off = align_up(off + rows * d * 4);
   p.b_pcoef = off;
-  off = align_up(off + static_cast<size_t>(p.chunk_cap) * K * 4);
+  off = align_up(off + rows * K * 4);
   p.b_acoef = off;
-  off = align_up(off + static_cast<size_t>(p.chunk_cap) * 4);
+  off = align_up(off + rows * 4);
   p.b_lse2 = off;
-  off = align_up(off + static_cast<size_t>(p.chunk_cap) * 4);
+  off = align_up(off + rows * 4);
   p.b_zk = off;
-  off = align_up(off + static_cast<size_t>(p.chunk_cap) * K * 4);
+  off = align_up(off + rows * K * 4);
   p.b_flag = off;
   off = align_up(off + 4);
   p.b_total = off;
@@ -236,33 +290,39 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
     if (r) return r;
   }
   void* G = ws + p.b_G;
-  float* ghpart = reinterpret_cast<float*>(ws + p.b_ghpart);
+  float* ghacc = reinterpret_cast<float*>(ws + p.b_ghacc);
   float* pcoef = reinterpret_cast<float*>(ws + p.b_pcoef);
   float* acoef = reinterpret_cast<float*>(ws + p.b_acoef);
   float* lse2 = reinterpret_cast<float*>(ws + p.b_lse2);
   float* zk_ws = reinterpret_cast<float*>(ws + p.b_zk);
   const float c2 = 1.4426950408889634f / T;
+  const int64_t eb = dtype == FKL_BF16 ? 2 : 4;
 
-  for (int64_t row0 = 0; row0 < N; row0 += p.chunk_cap) {
-    const int64_t nrows = (N - row0) < p.chunk_cap ? (N - row0) : p.chunk_cap;
+  for (int64_t row0 = 0; row0 < N; row0 += p.bw_rows) {
+    const int64_t nrows = (N - row0) < p.bw_rows ? (N - row0) : p.bw_rows;
     const float* zk;
     if (topk_z) {
       zk = topk_z + row0 * K;
     } else {
-      // recompute z at the ids for this chunk into the workspace (rows 0..nrows)
-      fkl::launch_gather_dot(dtype, weight, static_cast<const unsigned char*>(hidden) +
-                                                row0 * d * (dtype == FKL_BF16 ? 2 : 4),
+      // recompute z at the ids for this block into the workspace (rows 0..nrows)
+      fkl::launch_gather_dot(dtype, weight, static_cast<const unsigned char*>(hidden) + row0 * d * eb,
                              topk_idx + row0 * K, d, 0, nrows, K, zk_ws, s);
       zk = zk_ws;
     }
     fkl::launch_bwd_prep(topk_logit, lse, grad_loss, row0, nrows, K, T, pcoef, acoef, lse2, s);
-    fkl::launch_gprod(dtype, weight, hidden, d, V, p.Vpad, row0, nrows, c2, acoef, lse2, G, s);
-    fkl::launch_fixup(dtype, G, p.Vpad, topk_idx, zk, pcoef, acoef, lse2, row0, nrows, K, c2, s);
-    fkl::launch_grad_hidden(dtype, G, p.Vpad, weight, d, V, nrows, p.gh_splits, p.gh_len, ghpart,
-                            s);
-    fkl::launch_reduce_grad_hidden(dtype, ghpart, p.gh_splits, nrows, d, grad_hidden, row0, s);
-    fkl::launch_grad_w(dtype, G, p.Vpad, hidden, d, V, row0, nrows, accumulate || row0 > 0,
-                       grad_weight, s);
+    for (int64_t v0 = 0; v0 < p.Vpad; v0 += p.bw_pitch) {
+      const int64_t Vw = (p.Vpad - v0) < p.bw_pitch ? (p.Vpad - v0) : p.bw_pitch;
+      const int64_t Vlim = (V - v0) < Vw ? (V - v0) : Vw;
+      fkl::launch_gprod(dtype, weight, hidden, d, V, v0, Vw, p.bw_pitch, row0, nrows, c2, acoef,
+                        lse2, G, s);
+      fkl::launch_fixup(dtype, G, p.bw_pitch, v0, Vw, topk_idx, zk, pcoef, acoef, lse2, row0, nrows,
+                        K, c2, s);
+      fkl::launch_grad_hidden(dtype, G, p.bw_pitch, weight, d, v0, Vw, Vlim, nrows, v0 > 0, ghacc,
+                              s);
+      fkl::launch_grad_w(dtype, G, p.bw_pitch, hidden, d, v0, Vw, Vlim, row0, nrows,
+                         accumulate || row0 > 0, grad_weight, s);
+    }
+    fkl::launch_reduce_grad_hidden(dtype, ghacc, 1, nrows, d, grad_hidden, row0, s);
   }
   return hip_check("backward launch");
 }

@@ -3,21 +3,25 @@
 // Every contraction of the loss (the logit tile z = W_tile . H_tile^T, its
 // recompute in the backward, grad_hidden = G . W and grad_W = G^T . H) runs
 // through gemm_tile(). Operands are staged through LDS in a k-contiguous
-// layout with a padded row pitch; an operand whose storage is contiguous along
-// its m/n index instead ("MN-major", e.g. W read as [v][d] when v is the
-// contraction index) is transposed in registers on the way into LDS, so the
-// fragment reads are always one 16-byte ds_read per lane.
+// layout with a padded row pitch; an operand stored contiguous along its m/n
+// index ("MN-major", e.g. W read as [v][d] when v is the contraction index) is
+// transposed in registers on its way into LDS, so every fragment read is one
+// 16-byte ds_read per lane.
 //
-// Tile shape: 256 threads = 4 wave64s in a 2x2 grid, each wave owning a
-// 128x128 sub-tile as 4x4 MFMA blocks of 32x32 (bf16: v_mfma_f32_32x32x16_bf16;
-// fp32: v_mfma_f32_32x32x2_f32). One pipeline stage covers 128 bytes of K per
-// row (64 bf16 or 32 fp32); two stages are double-buffered in LDS (144 KiB),
-// with the next stage's global loads in flight during the current stage's
-// MFMAs.
+// Global reads are raw buffer loads: the buffer's record count makes reads
+// past the end of the operand return zero, and lanes whose element lies
+// outside the operand use an offset beyond the record count, so tails need no
+// branches.
 //
-// Accumulator layout (32x32 MFMA result, as documented for CDNA3/CDNA4):
-// element r of block (mi, ni) in lane l is row
-//   mi*32 + 8*(r/4) + 4*(l/32) + (r%4)   and column   ni*32 + (l%32)
+// Pipeline (one workgroup, two LDS stages of 128 bytes of K per row):
+//   the registers of each thread hold the global data of stage t+1 while the
+//   waves run the MFMAs of stage t; early in stage t those registers are
+//   written to the other LDS buffer and refilled with stage t+2. Inside a
+//   stage the fragments of k-step s+1 are read from LDS while the MFMAs of
+//   k-step s run. One barrier per stage.
+//
+// Accumulator layout (32x32 MFMA result): element r of block (mi, ni) in lane
+// l is row  mi*32 + 8*(r/4) + 4*(l/32) + (r%4)  and column  ni*32 + (l%32)
 // of the wave's sub-tile.
 #pragma once
 
@@ -30,17 +34,27 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kBM = 256;  // tile rows (MFMA A side)
-constexpr int kBN = 256;  // tile columns (MFMA B side)
-constexpr int kWM = 128;  // wave sub-tile rows
-constexpr int kWN = 128;  // wave sub-tile columns
-constexpr int kMI = kWM / 32;
-constexpr int kNI = kWN / 32;
+constexpr int kBM = 256;                           // tile rows (MFMA A side)
+constexpr int kBN = 256;                           // tile columns (MFMA B side)
 constexpr int kRowBytes = 128;                     // K bytes per stage and row
 constexpr int kPitch = kRowBytes + 16;             // padded LDS row pitch
 constexpr int kStageBytes = (kBM + kBN) * kPitch;  // 73728
 constexpr int kLdsBytes = 2 * kStageBytes;         // 147456 (of 160 KiB)
+constexpr uint32_t kOOB = 0x80000000u;             // offset past any record count
+
+// Wave grid of a workgroup: WM x WN waves, each owning (256/WM) x (256/WN).
+template <int WM, int WN>
+struct TileCfg {
+  static constexpr int kWavesM = WM;
+  static constexpr int kWavesN = WN;
+  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int kWM = kBM / WM;
+  static constexpr int kWN = kBN / WN;
+  static constexpr int kMI = kWM / 32;
+  static constexpr int kNI = kWN / 32;
+  __device__ static int wave_m() { return static_cast<int>(threadIdx.x >> 6) / WN; }
+  __device__ static int wave_n() { return static_cast<int>(threadIdx.x >> 6) % WN; }
+};
 
 // Element kinds. bf16 is carried as raw 16-bit patterns.
 struct BF16 {
@@ -54,87 +68,128 @@ struct F32 {
   static constexpr int kVec = 4;
 };
 
-// A stored matrix seen as an operand indexed (mn, k).
-//   k-major  (KC): element (mn, k) at base + mn*ld + k*bytes   (stored [mn][k])
-//   mn-major (MC): element (mn, k) at base + k*ld + mn*bytes   (stored [k][mn])
-// Reads with mn >= mn_lim or k >= k_lim return zero. For KC, k_lim must be a
-// multiple of the vector width; for MC, mn_lim must be.
-struct Operand {
-  const unsigned char* base;
-  int64_t ld;  // bytes between consecutive stored rows
-  int64_t mn0;
-  int64_t mn_lim;
-  int64_t k_lim;
-};
-
 // Bit-level reinterpretation of one 32-bit lane value. Taking the argument
 // by value matters: applying __builtin_bit_cast directly to a vector-element
 // subscript (v[e]) reads element 0 regardless of e with this compiler.
 __device__ __forceinline__ float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
 
+__device__ __forceinline__ u32x4_t lds_load16(const unsigned char* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ void lds_store16(unsigned char* p, u32x4_t v) {
+  *reinterpret_cast<u32x4_t*>(p) = v;
+}
 __device__ __forceinline__ u32x4_t load16(const unsigned char* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
-__device__ __forceinline__ void store16(unsigned char* p, u32x4_t v) {
-  *reinterpret_cast<u32x4_t*>(p) = v;
+
+// A stored matrix seen as an operand indexed (mn, k), restricted to one tile:
+//   k-major  (KC): element (mn, k) at base + mn*ld + k*bytes   (stored [mn][k])
+//   mn-major (MC): element (mn, k) at base + k*ld + mn*bytes   (stored [k][mn])
+// with base pointing at the tile's first mn (and first k). Elements with
+// mn >= mn_count or k >= k_lim read as zero. For KC, k_lim must be a multiple
+// of the vector width; for MC, mn_count must be. Every byte offset the tile
+// can reach from base must stay below 2^31 (checked on the host); invalid
+// elements use an offset past the record count, which the hardware returns
+// as zero.
+struct Operand {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t ld;
+  int32_t mn_count;
+  int32_t k_lim;
+};
+
+__device__ __forceinline__ int32_t clamp_i32(int64_t x) {
+  return static_cast<int32_t>(x < 0 ? 0 : (x > 0x7fffffffLL ? 0x7fffffffLL : x));
 }
 
-// k-major operand: each thread moves (BX * 128 / 16) / 256 16-byte vectors.
-template <class P, int BX>
+__device__ __forceinline__ Operand make_operand(const unsigned char* base, int64_t ld,
+                                                int64_t mn_count, int64_t k_lim) {
+  Operand op;
+  op.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0,
+                                             0x7fffffff, 0x00020000);
+  op.ld = static_cast<uint32_t>(ld);
+  op.mn_count = clamp_i32(mn_count);
+  op.k_lim = clamp_i32(k_lim);
+  return op;
+}
+
+__device__ __forceinline__ u32x4_t buffer_load16(const Operand& op, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(op.rsrc, off, 0, 0));
+}
+
+// k-major operand: each thread moves 16-byte vectors of BX rows x 128 bytes.
+template <class P, int BX, int NT>
 struct StageKC {
-  static constexpr int kN = BX * (kRowBytes / 16) / kThreads;
+  static constexpr int kN = BX * (kRowBytes / 16) / NT;
   u32x4_t r[kN];
-  __device__ __forceinline__ void load(const Operand& op, int64_t k0, int tid) {
+  uint32_t off[kN];  // byte offset of the thread's vector at k = 0 (kOOB if its row is invalid)
+  int kc[kN];        // k index of the vector within a stage
+  __device__ __forceinline__ void init(const Operand& op, int tid) {
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c >> 3, kc = c & 7;
-      const int64_t mn = op.mn0 + row;
-      const int64_t k = k0 + kc * P::kVec;
-      if (mn < op.mn_lim && k < op.k_lim)
-        r[i] = load16(op.base + mn * op.ld + k * P::kBytes);
-      else
-        r[i] = u32x4_t{0u, 0u, 0u, 0u};
+      const int c = tid + i * NT;
+      const int row = c >> 3;
+      kc[i] = (c & 7) * P::kVec;
+      off[i] = row < op.mn_count ? static_cast<uint32_t>(row) * op.ld + kc[i] * P::kBytes : kOOB;
+    }
+  }
+  __device__ __forceinline__ void load(const Operand& op, int k0) {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const uint32_t o = (k0 + kc[i] < op.k_lim) ? off[i] + k0 * P::kBytes : kOOB;
+      r[i] = buffer_load16(op, o);
     }
   }
   __device__ __forceinline__ void store(unsigned char* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
-      const int c = tid + i * kThreads;
-      store16(lds + (c >> 3) * kPitch + (c & 7) * 16, r[i]);
+      const int c = tid + i * NT;
+      lds_store16(lds + (c >> 3) * kPitch + (c & 7) * 16, r[i]);
     }
   }
 };
 
 // mn-major operand: each thread moves kVec x kVec blocks (kVec k-rows of one
 // 16-byte mn-vector), transposes them in registers and writes kVec LDS rows.
-// Lane mapping (kb fastest) keeps both the global reads (8 lanes per 128-byte
-// row segment) and the LDS writes (8 lanes per LDS row) conflict-free.
-template <class P, int BX>
+// Lane mapping (k-block fastest) keeps both the global reads (8 lanes per
+// 128-byte row segment) and the LDS writes (8 lanes per LDS row) conflict-free.
+template <class P, int BX, int NT>
 struct StageMC {
   static constexpr int V = P::kVec;
-  static constexpr int kN = (kRowBytes / 16) * (BX / V) / kThreads;
+  static constexpr int kBlocks = (kRowBytes / 16) * (BX / V);
+  static constexpr int kN = (kBlocks + NT - 1) / NT;  // blocks per thread (threads past kBlocks idle)
   u32x4_t r[kN][V];
-  __device__ __forceinline__ void load(const Operand& op, int64_t k0, int tid) {
+  uint32_t off[kN];  // byte offset of the block's first element at k = 0 (kOOB if invalid)
+  int kb[kN];        // first k of the block within a stage
+  __device__ __forceinline__ void init(const Operand& op, int tid) {
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
-      const int b = tid + i * kThreads;
-      const int kb = b & 7, mb = b >> 3;
-      const int64_t mn = op.mn0 + mb * V;
+      const int b = tid + i * NT;
+      const int mb = b >> 3;
+      kb[i] = (b & 7) * V;
+      off[i] = (b < kBlocks && mb * V < op.mn_count)
+                   ? static_cast<uint32_t>(kb[i]) * op.ld + mb * V * P::kBytes
+                   : kOOB;
+    }
+  }
+  __device__ __forceinline__ void load(const Operand& op, int k0) {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const uint32_t base = off[i] + static_cast<uint32_t>(k0) * op.ld;
+      const bool ok = off[i] != kOOB;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const int64_t k = k0 + kb * V + e;
-        if (mn < op.mn_lim && k < op.k_lim)
-          r[i][e] = load16(op.base + k * op.ld + mn * P::kBytes);
-        else
-          r[i][e] = u32x4_t{0u, 0u, 0u, 0u};
+        const bool v = ok && (k0 + kb[i] + e < op.k_lim);
+        r[i][e] = buffer_load16(op, v ? base + e * op.ld : kOOB);
       }
     }
   }
   __device__ __forceinline__ void store(unsigned char* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
-      const int b = tid + i * kThreads;
+      const int b = tid + i * NT;
+      if (kBlocks % NT != 0 && b >= kBlocks) continue;
       const int kb = b & 7, mb = b >> 3;
 #pragma unroll
       for (int j = 0; j < V; ++j) {
@@ -145,14 +200,13 @@ struct StageMC {
           for (int w = 0; w < 4; ++w) {
             const uint32_t lo = r[i][2 * w][j >> 1];
             const uint32_t hi = r[i][2 * w + 1][j >> 1];
-            o[w] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                           : ((lo & 0xffffu) | (hi << 16));
+            o[w] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
           }
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = r[i][e][j];
         }
-        store16(lds + (mb * V + j) * kPitch + kb * 16, o);
+        lds_store16(lds + (mb * V + j) * kPitch + kb * 16, o);
       }
     }
   }
@@ -170,78 +224,158 @@ __device__ __forceinline__ void mfma_16B(f32x16_t& c, u32x4_t a, u32x4_t b) {
   }
 }
 
-// One LDS stage: 4 k-steps of 32 bytes per row; lane half h reads the 16-byte
-// chunk 2s+h of its row, the same k-positions for both operands.
-template <class P>
-__device__ __forceinline__ void compute_stage(f32x16_t (&acc)[kMI][kNI], const unsigned char* la,
-                                              const unsigned char* lb, int wm, int wn, int lane) {
-  const unsigned char* pa = la + (wm * kWM + (lane & 31)) * kPitch + (lane >> 5) * 16;
-  const unsigned char* pb = lb + (wn * kWN + (lane & 31)) * kPitch + (lane >> 5) * 16;
-#pragma unroll
-  for (int s = 0; s < kRowBytes / 32; ++s) {
-    u32x4_t a[kMI], b[kNI];
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) a[mi] = load16(pa + mi * 32 * kPitch + s * 32);
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) b[ni] = load16(pb + ni * 32 * kPitch + s * 32);
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < kNI; ++ni) mfma_16B<P>(acc[mi][ni], a[mi], b[ni]);
-  }
-}
-
-template <bool MC, class P, int BX>
+template <bool MC, class P, int BX, int NT>
 struct StageSel {
-  typedef StageKC<P, BX> type;
+  typedef StageKC<P, BX, NT> type;
 };
-template <class P, int BX>
-struct StageSel<true, P, BX> {
-  typedef StageMC<P, BX> type;
+template <class P, int BX, int NT>
+struct StageSel<true, P, BX, NT> {
+  typedef StageMC<P, BX, NT> type;
 };
 
-// acc = A[mn tile, k_begin:k_end] . B[mn tile, k_begin:k_end]^T
-// k_begin must be a multiple of the stage depth unless it is 0; steps past
-// k_end read zeros only if the operands' k_lim says so (callers split K on
-// stage boundaries and end the last split at k_lim).
-template <class P, bool A_MC, bool B_MC>
-__device__ __forceinline__ void gemm_tile(f32x16_t (&acc)[kMI][kNI], const Operand& A,
-                                          const Operand& B, int64_t k_begin, int64_t k_end,
-                                          unsigned char* lds) {
-  constexpr int BK = kRowBytes / P::kBytes;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
-#pragma unroll
-  for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+template <class P, class C, bool A_MC, bool B_MC>
+struct TileLoop {
+  static constexpr int BK = kRowBytes / P::kBytes;
+  typedef typename StageSel<A_MC, P, kBM, C::kThreads>::type SA;
+  typedef typename StageSel<B_MC, P, kBN, C::kThreads>::type SB;
 
-  const int64_t nk = (k_end - k_begin + BK - 1) / BK;
-  if (nk <= 0) return;
-  typename StageSel<A_MC, P, kBM>::type sa;
-  typename StageSel<B_MC, P, kBN>::type sb;
-  sa.load(A, k_begin, tid);
-  sb.load(B, k_begin, tid);
-  sa.store(lds, tid);
-  sb.store(lds + kBM * kPitch, tid);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    unsigned char* cur = lds + (kt & 1) * kStageBytes;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      sa.load(A, k_begin + (kt + 1) * BK, tid);
-      sb.load(B, k_begin + (kt + 1) * BK, tid);
+  // Fragments of k-step s (32 bytes per row per step; lane half h reads the
+  // 16-byte chunk 2s+h of its row, the same k-positions for both operands).
+  __device__ __forceinline__ static void read_frags(u32x4_t (&fa)[C::kMI], u32x4_t (&fb)[C::kNI],
+                                                    const unsigned char* pa,
+                                                    const unsigned char* pb, int s) {
+#pragma unroll
+    for (int mi = 0; mi < C::kMI; ++mi) fa[mi] = lds_load16(pa + mi * 32 * kPitch + s * 32);
+#pragma unroll
+    for (int ni = 0; ni < C::kNI; ++ni) fb[ni] = lds_load16(pb + ni * 32 * kPitch + s * 32);
+  }
+
+  __device__ __forceinline__ static void mfmas(f32x16_t (&acc)[C::kMI][C::kNI],
+                                               const u32x4_t (&fa)[C::kMI],
+                                               const u32x4_t (&fb)[C::kNI]) {
+#pragma unroll
+    for (int mi = 0; mi < C::kMI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < C::kNI; ++ni) mfma_16B<P>(acc[mi][ni], fa[mi], fb[ni]);
+  }
+
+  // Issue counts per thread and stage, used to lay out the instruction schedule.
+  static constexpr int kMfmaPerStep = C::kMI * C::kNI * (P::kBytes == 2 ? 1 : 4);
+  static constexpr int kFragReads = C::kMI + C::kNI;
+  static constexpr int kStageWrites = (A_MC ? SA::kN * P::kVec : SA::kN) + (B_MC ? SB::kN * P::kVec : SB::kN);
+  static constexpr int kStageLoads = kStageWrites;
+
+  // Pins the order of one k-step: MFMAs evenly interleaved with the fragment
+  // reads of the next k-step and, when present, the stage's LDS writes or
+  // global loads. Without it the scheduler sinks the global loads to the end
+  // of the stage, where their latency is no longer hidden.
+  template <int NW, int NL, int NR>
+  __device__ __forceinline__ static void schedule_step() {
+#pragma unroll
+    for (int i = 0; i < kMfmaPerStep; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if ((i * NR) / kMfmaPerStep != ((i + 1) * NR) / kMfmaPerStep)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      if ((i * NW) / kMfmaPerStep != ((i + 1) * NW) / kMfmaPerStep)
+        __builtin_amdgcn_sched_group_barrier(0x200, (NW + kMfmaPerStep - 1) / kMfmaPerStep, 0);  // DS write
+      if ((i * NL) / kMfmaPerStep != ((i + 1) * NL) / kMfmaPerStep)
+        __builtin_amdgcn_sched_group_barrier(0x020, (NL + kMfmaPerStep - 1) / kMfmaPerStep, 0);  // VMEM read
     }
-    compute_stage<P>(acc, cur, cur + kBM * kPitch, wm, wn, lane);
-    if (more) {
-      unsigned char* nxt = lds + ((kt + 1) & 1) * kStageBytes;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // k-step S of a stage: read the fragments of step S+1, do the stage's LDS
+  // writes (S == 0) or global loads (S == 1), run the MFMAs of step S.
+  template <int S, bool STORE_NEXT, bool LOAD_NEXT>
+  __device__ __forceinline__ static void kstep(f32x16_t (&acc)[C::kMI][C::kNI],
+                                               u32x4_t (&fa)[2][C::kMI], u32x4_t (&fb)[2][C::kNI],
+                                               SA& sa, SB& sb, const Operand& A, const Operand& B,
+                                               const unsigned char* pa, const unsigned char* pb,
+                                               unsigned char* nxt, int k_next, int tid) {
+    constexpr int kSteps = kRowBytes / 32;
+    if constexpr (S + 1 < kSteps) read_frags(fa[(S + 1) & 1], fb[(S + 1) & 1], pa, pb, S + 1);
+    if constexpr (STORE_NEXT && S == 0) {
       sa.store(nxt, tid);
       sb.store(nxt + kBM * kPitch, tid);
     }
+    if constexpr (LOAD_NEXT && S == 1) {
+      sa.load(A, k_next);
+      sb.load(B, k_next);
+    }
+    mfmas(acc, fa[S & 1], fb[S & 1]);
+    constexpr int nr = (S + 1 < kSteps) ? kFragReads : 0;
+    constexpr int nw = (STORE_NEXT && S == 0) ? kStageWrites : 0;
+    constexpr int nl = (LOAD_NEXT && S == 1) ? kStageLoads : 0;
+    schedule_step<nw, nl, nr>();
+  }
+
+  // One stage: MFMAs on LDS buffer `cur`; optionally move the prefetched
+  // registers into `nxt` and refill them from global stage k_next.
+  template <bool STORE_NEXT, bool LOAD_NEXT>
+  __device__ __forceinline__ static void stage(f32x16_t (&acc)[C::kMI][C::kNI], SA& sa, SB& sb,
+                                               const Operand& A, const Operand& B,
+                                               const unsigned char* cur, unsigned char* nxt,
+                                               int k_next, int tid, int lane) {
+    static_assert(kRowBytes / 32 == 4, "four k-steps per stage");
+    const unsigned char* pa = cur + (C::wave_m() * C::kWM + (lane & 31)) * kPitch + (lane >> 5) * 16;
+    const unsigned char* pb =
+        cur + kBM * kPitch + (C::wave_n() * C::kWN + (lane & 31)) * kPitch + (lane >> 5) * 16;
+    u32x4_t fa[2][C::kMI], fb[2][C::kNI];
+    read_frags(fa[0], fb[0], pa, pb, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    kstep<0, STORE_NEXT, LOAD_NEXT>(acc, fa, fb, sa, sb, A, B, pa, pb, nxt, k_next, tid);
+    kstep<1, STORE_NEXT, LOAD_NEXT>(acc, fa, fb, sa, sb, A, B, pa, pb, nxt, k_next, tid);
+    kstep<2, STORE_NEXT, LOAD_NEXT>(acc, fa, fb, sa, sb, A, B, pa, pb, nxt, k_next, tid);
+    kstep<3, STORE_NEXT, LOAD_NEXT>(acc, fa, fb, sa, sb, A, B, pa, pb, nxt, k_next, tid);
     __syncthreads();
   }
+
+  // acc = A[tile, k_begin:k_end] . B[tile, k_begin:k_end]^T. k_begin is 0 or
+  // a multiple of the stage depth; the operands' k_lim zeroes anything past
+  // the true end of K.
+  __device__ __forceinline__ static void run(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
+                                             const Operand& B, int k_begin, int k_end,
+                                             unsigned char* lds) {
+    const int tid = threadIdx.x, lane = tid & 63;
+#pragma unroll
+    for (int mi = 0; mi < C::kMI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < C::kNI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+    const int nk = (k_end - k_begin + BK - 1) / BK;
+    if (nk <= 0) return;
+    SA sa;
+    SB sb;
+    sa.init(A, tid);
+    sb.init(B, tid);
+    sa.load(A, k_begin);
+    sb.load(B, k_begin);
+    sa.store(lds, tid);
+    sb.store(lds + kBM * kPitch, tid);
+    if (nk > 1) {
+      sa.load(A, k_begin + BK);
+      sb.load(B, k_begin + BK);
+    }
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt)
+      stage<true, true>(acc, sa, sb, A, B, lds + (kt & 1) * kStageBytes,
+                        lds + ((kt + 1) & 1) * kStageBytes, k_begin + (kt + 2) * BK, tid, lane);
+    if (kt + 1 < nk) {
+      stage<true, false>(acc, sa, sb, A, B, lds + (kt & 1) * kStageBytes,
+                         lds + ((kt + 1) & 1) * kStageBytes, 0, tid, lane);
+      ++kt;
+    }
+    stage<false, false>(acc, sa, sb, A, B, lds + (kt & 1) * kStageBytes, nullptr, 0, tid, lane);
+  }
+};
+
+template <class P, class C, bool A_MC, bool B_MC>
+__device__ __forceinline__ void gemm_tile(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
+                                          const Operand& B, int k_begin, int k_end,
+                                          unsigned char* lds) {
+  TileLoop<P, C, A_MC, B_MC>::run(acc, A, B, k_begin, k_end, lds);
 }
 
 // Row offset, inside the wave sub-tile, of accumulator element r of block mi.

@@ -26,6 +26,8 @@
 //   k_grad_w       MFMA product G^T . H accumulated into fp32 grad_W.
 #include <math.h>
 
+#include <cstdlib>
+
 #include "gemm_core.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
@@ -35,48 +37,47 @@ namespace fkl {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-#define FKL_GEMM_KERNEL __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ------------------------------------------------------------------ forward
 
-template <class P>
-FKL_GEMM_KERNEL void k_logits_lse(const unsigned char* __restrict__ W,
-                                  const unsigned char* __restrict__ H, int64_t d, int64_t V,
-                                  int64_t nrows, int64_t n_vt, int64_t n_tt, float c2,
-                                  float2* __restrict__ part, int64_t part_ld) {
+template <class P, class C>
+__global__ __launch_bounds__(C::kThreads) void k_logits_lse(
+    const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
+    int64_t nrows, int64_t n_vt, int64_t n_tt, float c2, float2* __restrict__ part,
+    int64_t part_ld) {
+  static_assert(C::kWM == kSliceVocab, "one LSE partial per wave row-slice");
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   const int64_t total = n_vt * n_tt;
   const int64_t t = xcd_tile_index(total);
   if (t >= total) return;
   const int64_t vt = t / n_tt, tt = t % n_tt;
-  const int64_t rb = d * P::kBytes;
+  const int64_t ld = d * P::kBytes;
   // MFMA rows = vocabulary entries (weight rows), columns = tokens, so each
   // lane's accumulators belong to one token and the reduction over the
   // vocabulary is mostly in-lane.
-  const Operand A{W, rb, vt * kBM, V, d};
-  const Operand B{H, rb, tt * kBN, nrows, d};
-  f32x16_t acc[kMI][kNI];
-  gemm_tile<P, false, false>(acc, A, B, 0, d, lds);
+  const Operand A = make_operand(W + vt * kBM * ld, ld, V - vt * kBM, d);
+  const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
+  f32x16_t acc[C::kMI][C::kNI];
+  gemm_tile<P, C, false, false>(acc, A, B, 0, static_cast<int>(d), lds);
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
-  const int64_t v0 = vt * kBM + wm * kWM;
+  const int lane = threadIdx.x & 63;
+  const int64_t v0 = vt * kBM + C::wave_m() * C::kWM;
   if (v0 >= V) return;
   const int64_t slot = v0 / kSliceVocab;
-  const bool full = v0 + kWM <= V;
-  const int vlim = full ? kWM : static_cast<int>(V - v0);
+  const bool full = v0 + C::kWM <= V;
+  const int vlim = full ? C::kWM : static_cast<int>(V - v0);
 #pragma unroll
-  for (int ni = 0; ni < kNI; ++ni) {
+  for (int ni = 0; ni < C::kNI; ++ni) {
     float m = -INFINITY;
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+    for (int mi = 0; mi < C::kMI; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (full || acc_row(mi, r, lane) < vlim) m = fmaxf(m, acc[mi][ni][r] * c2);
     float s = 0.f;
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+    for (int mi = 0; mi < C::kMI; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (full || acc_row(mi, r, lane) < vlim) s += fast_exp2(acc[mi][ni][r] * c2 - m);
@@ -85,7 +86,7 @@ FKL_GEMM_KERNEL void k_logits_lse(const unsigned char* __restrict__ W,
     const float so = __shfl_xor(s, 32);
     const float M = fmaxf(m, mo);
     const float S = (s > 0.f ? s * fast_exp2(m - M) : 0.f) + (so > 0.f ? so * fast_exp2(mo - M) : 0.f);
-    const int64_t tok = tt * kBN + wn * kWN + ni * 32 + (lane & 31);
+    const int64_t tok = tt * kBN + C::wave_n() * C::kWN + ni * 32 + (lane & 31);
     if (lane < 32 && tok < nrows) part[slot * part_ld + tok] = make_float2(M, S);
   }
 }
@@ -259,53 +260,57 @@ __device__ __forceinline__ void store4(unsigned char* p, const float (&v)[4]) {
   }
 }
 
-// Recompute the logit tile and write G_dense = acoef * 2^(z*c2 - lse2) into
-// G[row][v] (row pitch Vpad; columns in [V, Vpad) are written as zero).
-template <class P>
-FKL_GEMM_KERNEL void k_gprod(const unsigned char* __restrict__ W, const unsigned char* __restrict__ H,
-                             int64_t d, int64_t V, int64_t Vpad, int64_t nrows, int64_t n_vt,
-                             int64_t n_tt, float c2, const float* __restrict__ acoef,
-                             const float* __restrict__ lse2, unsigned char* __restrict__ G) {
+// Recompute the logit tile of rows [0, nrows) x vocabulary [v0, v0 + Vw) and
+// write G_dense = acoef * 2^(z*c2 - lse2) into the G block G[row][v - v0]
+// (row pitch gpitch elements; entries with v >= V are written as zero).
+template <class P, class C>
+__global__ __launch_bounds__(C::kThreads) void k_gprod(
+    const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
+    int64_t v0, int64_t Vw, int64_t gpitch, int64_t nrows, int64_t n_vt, int64_t n_tt, float c2,
+    const float* __restrict__ acoef, const float* __restrict__ lse2, unsigned char* __restrict__ G) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   const int64_t total = n_vt * n_tt;
   const int64_t t = xcd_tile_index(total);
   if (t >= total) return;
   const int64_t vt = t / n_tt, tt = t % n_tt;
-  const int64_t rb = d * P::kBytes;
-  const Operand A{W, rb, vt * kBM, V, d};
-  const Operand B{H, rb, tt * kBN, nrows, d};
-  f32x16_t acc[kMI][kNI];
-  gemm_tile<P, false, false>(acc, A, B, 0, d, lds);
+  const int64_t ld = d * P::kBytes;
+  const int64_t vbase = v0 + vt * kBM;  // first vocabulary entry of the tile
+  const Operand A = make_operand(W + vbase * ld, ld, V - vbase, d);
+  const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
+  f32x16_t acc[C::kMI][C::kNI];
+  gemm_tile<P, C, false, false>(acc, A, B, 0, static_cast<int>(d), lds);
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
-  const int64_t v0 = vt * kBM + wm * kWM;
-  if (v0 >= Vpad) return;
-  const int64_t gld = Vpad * P::kBytes;
+  const int lane = threadIdx.x & 63;
+  const int64_t w0 = vt * kBM + C::wave_m() * C::kWM;  // slice-relative column of the wave
+  if (w0 >= Vw) return;
+  const int64_t gld = gpitch * P::kBytes;
 #pragma unroll
-  for (int ni = 0; ni < kNI; ++ni) {
-    const int64_t tok = tt * kBN + wn * kWN + ni * 32 + (lane & 31);
+  for (int ni = 0; ni < C::kNI; ++ni) {
+    const int64_t tok = tt * kBN + C::wave_n() * C::kWN + ni * 32 + (lane & 31);
     if (tok >= nrows) continue;
     const float a = acoef[tok];
     const float l2 = lse2[tok];
     unsigned char* grow = G + tok * gld;
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+    for (int mi = 0; mi < C::kMI; ++mi)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int64_t v = v0 + mi * 32 + 8 * g4 + 4 * (lane >> 5);
-        if (v >= Vpad) continue;
+        const int64_t col = w0 + mi * 32 + 8 * g4 + 4 * (lane >> 5);
+        if (col >= Vw) continue;
         float vals[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          vals[j] = (v + j < V) ? a * fast_exp2(acc[mi][ni][4 * g4 + j] * c2 - l2) : 0.f;
-        store4<P>(grow + v * P::kBytes, vals);
+          vals[j] = (v0 + col + j < V) ? a * fast_exp2(acc[mi][ni][4 * g4 + j] * c2 - l2) : 0.f;
+        store4<P>(grow + col * P::kBytes, vals);
       }
   }
 }
 
-// One wave per row: G[row][idx_k] = acoef * 2^(z_k*c2 - lse2) - sum_{k': idx_k' = idx_k} pcoef_k'.
+// One wave per row: for the teacher ids inside the slice [v0, v0 + Vw),
+// G[row][idx_k - v0] = acoef * 2^(z_k*c2 - lse2) - sum_{k': idx_k' = idx_k} pcoef_k'.
 template <class P>
-__global__ __launch_bounds__(64) void k_fixup(unsigned char* __restrict__ G, int64_t Vpad,
+__global__ __launch_bounds__(64) void k_fixup(unsigned char* __restrict__ G, int64_t gpitch,
+                                              int64_t v0, int64_t Vw,
                                               const int32_t* __restrict__ idx,
                                               const float* __restrict__ zk,
                                               const float* __restrict__ pcoef,
@@ -322,50 +327,54 @@ __global__ __launch_bounds__(64) void k_fixup(unsigned char* __restrict__ G, int
   }
   __syncthreads();
   const float a = acoef[row], l2 = lse2[row];
-  unsigned char* grow = G + row * Vpad * P::kBytes;
+  unsigned char* grow = G + row * gpitch * P::kBytes;
   for (int k = lane; k < K; k += 64) {
     const int32_t v = sid[k];
+    if (v < v0 || v >= v0 + Vw) continue;
     float sum = 0.f;
     for (int k2 = 0; k2 < K; ++k2) sum += (sid[k2] == v) ? sp[k2] : 0.f;
     const float val = a * fast_exp2(zk[row * K + k] * c2 - l2) - sum;
     if constexpr (P::kBytes == 2)
-      reinterpret_cast<uint16_t*>(grow)[v] = f32_to_bf16_rne(val);
+      reinterpret_cast<uint16_t*>(grow)[v - v0] = f32_to_bf16_rne(val);
     else
-      reinterpret_cast<float*>(grow)[v] = val;
+      reinterpret_cast<float*>(grow)[v - v0] = val;
   }
 }
 
-// part[split][row][col] = sum over the split's vocabulary range of G[row][v] W[v][col].
-template <class P>
-FKL_GEMM_KERNEL void k_grad_hidden(const unsigned char* __restrict__ G, int64_t Vpad,
-                                   const unsigned char* __restrict__ W, int64_t d, int64_t V,
-                                   int64_t nrows, int64_t n_tt, int64_t n_dt, int64_t splits,
-                                   int64_t split_len, float* __restrict__ part) {
+// acc[row][col] (+)= sum over the slice of G[row][v - v0] W[v][col], for the rows
+// of one block; the slice is Vw entries wide (Vlim of them below V).
+template <class P, class C>
+__global__ __launch_bounds__(C::kThreads) void k_grad_hidden(
+    const unsigned char* __restrict__ G, int64_t gpitch, const unsigned char* __restrict__ W,
+    int64_t d, int64_t Vw, int64_t Vlim, int64_t nrows, int64_t n_tt, int64_t n_dt,
+    int accumulate, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  const int64_t total = splits * n_dt * n_tt;
+  const int64_t total = n_dt * n_tt;
   const int64_t t = xcd_tile_index(total);
   if (t >= total) return;
-  const int64_t tt = t % n_tt, rest = t / n_tt;
-  const int64_t dt = rest % n_dt, sp = rest / n_dt;
-  const Operand A{G, Vpad * P::kBytes, tt * kBM, nrows, Vpad};   // [row][v], k = v
-  const Operand B{W, d * P::kBytes, dt * kBN, d, V};             // [v][col], k = v
-  const int64_t k0 = sp * split_len;
-  const int64_t k1 = k0 + split_len < Vpad ? k0 + split_len : Vpad;
-  f32x16_t acc[kMI][kNI];
-  gemm_tile<P, false, true>(acc, A, B, k0, k1, lds);
+  const int64_t tt = t % n_tt, dt = t / n_tt;
+  const int64_t gld = gpitch * P::kBytes, wld = d * P::kBytes;
+  // A = G rows of this tile (k = slice column), B = W rows of the slice (k = v), columns of
+  // this tile
+  const Operand A = make_operand(G + tt * kBM * gld, gld, nrows - tt * kBM, Vw);
+  const Operand B = make_operand(W + dt * kBN * P::kBytes, wld, d - dt * kBN, Vlim);
+  f32x16_t acc[C::kMI][C::kNI];
+  gemm_tile<P, C, false, true>(acc, A, B, 0, static_cast<int>(Vw), lds);
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
-  float* out = part + sp * nrows * d;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int mi = 0; mi < kMI; ++mi)
+  for (int mi = 0; mi < C::kMI; ++mi)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t row = tt * kBM + wm * kWM + acc_row(mi, r, lane);
+      const int64_t row = tt * kBM + C::wave_m() * C::kWM + acc_row(mi, r, lane);
       if (row >= nrows) continue;
 #pragma unroll
-      for (int ni = 0; ni < kNI; ++ni) {
-        const int64_t col = dt * kBN + wn * kWN + ni * 32 + (lane & 31);
-        if (col < d) out[row * d + col] = acc[mi][ni][r];
+      for (int ni = 0; ni < C::kNI; ++ni) {
+        const int64_t col = dt * kBN + C::wave_n() * C::kWN + ni * 32 + (lane & 31);
+        if (col < d) {
+          float* p = out + row * d + col;
+          *p = accumulate ? *p + acc[mi][ni][r] : acc[mi][ni][r];
+        }
       }
     }
 }
@@ -391,32 +400,33 @@ __global__ __launch_bounds__(256) void k_reduce_gh(const float* __restrict__ par
   }
 }
 
-// grad_W[v][col] (+)= sum over the chunk's rows of G[row][v] H[row][col].
-template <class P>
-FKL_GEMM_KERNEL void k_grad_w(const unsigned char* __restrict__ G, int64_t Vpad,
-                              const unsigned char* __restrict__ H, int64_t d, int64_t V,
-                              int64_t nrows, int64_t n_vt, int64_t n_dt, int accumulate,
-                              float* __restrict__ grad_w) {
+// grad_W[v0 + v][col] (+)= sum over the block's rows of G[row][v] H[row][col].
+template <class P, class C>
+__global__ __launch_bounds__(C::kThreads) void k_grad_w(
+    const unsigned char* __restrict__ G, int64_t gpitch, const unsigned char* __restrict__ H,
+    int64_t d, int64_t Vw, int64_t Vlim, int64_t nrows, int64_t n_vt, int64_t n_dt, int accumulate,
+    float* __restrict__ grad_w) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   const int64_t total = n_vt * n_dt;
   const int64_t t = xcd_tile_index(total);
   if (t >= total) return;
   const int64_t vt = t / n_dt, dt = t % n_dt;
-  const Operand A{G, Vpad * P::kBytes, vt * kBM, Vpad, nrows};  // [row][v], k = row
-  const Operand B{H, d * P::kBytes, dt * kBN, d, nrows};        // [row][col], k = row
-  f32x16_t acc[kMI][kNI];
-  gemm_tile<P, true, true>(acc, A, B, 0, nrows, lds);
+  // A = G^T (stored [row][v], k = row), B = H (stored [row][col], k = row)
+  const Operand A = make_operand(G + vt * kBM * P::kBytes, gpitch * P::kBytes, Vw - vt * kBM, nrows);
+  const Operand B = make_operand(H + dt * kBN * P::kBytes, d * P::kBytes, d - dt * kBN, nrows);
+  f32x16_t acc[C::kMI][C::kNI];
+  gemm_tile<P, C, true, true>(acc, A, B, 0, static_cast<int>(nrows), lds);
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int mi = 0; mi < kMI; ++mi)
+  for (int mi = 0; mi < C::kMI; ++mi)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t v = vt * kBM + wm * kWM + acc_row(mi, r, lane);
-      if (v >= V) continue;
+      const int64_t v = vt * kBM + C::wave_m() * C::kWM + acc_row(mi, r, lane);
+      if (v >= Vlim) continue;
 #pragma unroll
-      for (int ni = 0; ni < kNI; ++ni) {
-        const int64_t col = dt * kBN + wn * kWN + ni * 32 + (lane & 31);
+      for (int ni = 0; ni < C::kNI; ++ni) {
+        const int64_t col = dt * kBN + C::wave_n() * C::kWN + ni * 32 + (lane & 31);
         if (col < d) {
           float* p = grad_w + v * d + col;
           *p = accumulate ? *p + acc[mi][ni][r] : acc[mi][ni][r];
@@ -451,26 +461,29 @@ static inline unsigned grid_for_tiles(int64_t total) {
   return static_cast<unsigned>(8 * ceil_div(total, 8));
 }
 
-#define FKL_DISPATCH(dtype, KERNEL, ...)      \
-  do {                                        \
-    if ((dtype) == 1)                         \
-      KERNEL<BF16><<<__VA_ARGS__>>>;          \
-    else                                      \
-      KERNEL<F32><<<__VA_ARGS__>>>;           \
-  } while (0)
+typedef TileCfg<2, 2> Cfg4;  // 4 waves, 128x128 per wave, one wave per SIMD
+typedef TileCfg<2, 4> Cfg8;  // 8 waves, 128x64 per wave, two waves per SIMD
 
-void grad_hidden_split(int64_t rows, int64_t d, int64_t Vpad, int dtype, int64_t* splits,
-                       int64_t* len) {
-  const int64_t bk = kRowBytes / (dtype == 1 ? 2 : 4);
-  const int64_t tiles = ceil_div(rows, kBM) * ceil_div(d, kBN);
-  const int64_t stages = ceil_div(Vpad, bk);
-  int64_t sp = ceil_div(512, tiles);
-  if (sp > stages) sp = stages;
-  if (sp < 1) sp = 1;
-  const int64_t l = ceil_div(stages, sp) * bk;
-  *len = l;
-  *splits = ceil_div(Vpad, l);
+// Wave grid of a bf16 MFMA kernel: its default unless FKL_TILE_WAVES (4 or 8) is set.
+static int tile_waves(int dflt) {
+  static const int w = [] {
+    const char* e = std::getenv("FKL_TILE_WAVES");
+    return e ? std::atoi(e) : 0;
+  }();
+  return (w == 4 || w == 8) ? w : dflt;
 }
+
+#define FKL_LAUNCH_GEMM(KERNEL, dtype, waves, grid, s, ...)                             \
+  do {                                                                                  \
+    if ((dtype) == 1) {                                                                 \
+      if (tile_waves(waves) == 4)                                                       \
+        KERNEL<BF16, Cfg4><<<(grid), Cfg4::kThreads, 0, (s)>>>(__VA_ARGS__);            \
+      else                                                                              \
+        KERNEL<BF16, Cfg8><<<(grid), Cfg8::kThreads, 0, (s)>>>(__VA_ARGS__);            \
+    } else {                                                                            \
+      KERNEL<F32, Cfg4><<<(grid), Cfg4::kThreads, 0, (s)>>>(__VA_ARGS__);               \
+    }                                                                                   \
+  } while (0)
 
 void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64_t V,
                        int64_t row0, int64_t nrows, float c2, float2* part, int64_t part_ld,
@@ -479,12 +492,9 @@ void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(V, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
-  if (dtype == 1)
-    k_logits_lse<BF16><<<grid_for_tiles(n_vt * n_tt), kThreads, 0, s>>>(
-        static_cast<const unsigned char*>(W), Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld);
-  else
-    k_logits_lse<F32><<<grid_for_tiles(n_vt * n_tt), kThreads, 0, s>>>(
-        static_cast<const unsigned char*>(W), Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld);
+  FKL_LAUNCH_GEMM(k_logits_lse, dtype, 8, grid_for_tiles(n_vt * n_tt), s,
+                  static_cast<const unsigned char*>(W), Hc, d, V, nrows, n_vt, n_tt, c2, part,
+                  part_ld);
 }
 
 void launch_gather_dot(int dtype, const void* W, const void* H, const int32_t* idx, int64_t d,
@@ -525,51 +535,44 @@ void launch_bwd_prep(const float* logit, const float* lse, const float* grad_los
                                     acoef, lse2);
 }
 
-void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t Vpad,
-                  int64_t row0, int64_t nrows, float c2, const float* acoef, const float* lse2,
-                  void* G, hipStream_t s) {
+void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t v0,
+                  int64_t Vw, int64_t gpitch, int64_t row0, int64_t nrows, float c2,
+                  const float* acoef, const float* lse2, void* G, hipStream_t s) {
   ScopedTimer timer_(KID_GPROD, s);
   const int64_t eb = dtype == 1 ? 2 : 4;
-  const int64_t n_vt = ceil_div(Vpad, kBM), n_tt = ceil_div(nrows, kBN);
+  const int64_t n_vt = ceil_div(Vw, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
-  if (dtype == 1)
-    k_gprod<BF16><<<grid_for_tiles(n_vt * n_tt), kThreads, 0, s>>>(
-        static_cast<const unsigned char*>(W), Hc, d, V, Vpad, nrows, n_vt, n_tt, c2, acoef, lse2,
-        static_cast<unsigned char*>(G));
-  else
-    k_gprod<F32><<<grid_for_tiles(n_vt * n_tt), kThreads, 0, s>>>(
-        static_cast<const unsigned char*>(W), Hc, d, V, Vpad, nrows, n_vt, n_tt, c2, acoef, lse2,
-        static_cast<unsigned char*>(G));
+  FKL_LAUNCH_GEMM(k_gprod, dtype, 8, grid_for_tiles(n_vt * n_tt), s,
+                  static_cast<const unsigned char*>(W), Hc, d, V, v0, Vw, gpitch, nrows, n_vt,
+                  n_tt, c2, acoef, lse2, static_cast<unsigned char*>(G));
 }
 
-void launch_fixup(int dtype, void* G, int64_t Vpad, const int32_t* idx, const float* zk,
-                  const float* pcoef, const float* acoef, const float* lse2, int64_t row0,
-                  int64_t nrows, int K, float c2, hipStream_t s) {
+void launch_fixup(int dtype, void* G, int64_t gpitch, int64_t v0, int64_t Vw, const int32_t* idx,
+                  const float* zk, const float* pcoef, const float* acoef, const float* lse2,
+                  int64_t row0, int64_t nrows, int K, float c2, hipStream_t s) {
   if (nrows <= 0) return;
   ScopedTimer timer_(KID_FIXUP, s);
   const size_t shm = static_cast<size_t>(K) * 8;
   if (dtype == 1)
     k_fixup<BF16><<<static_cast<unsigned>(nrows), 64, shm, s>>>(
-        static_cast<unsigned char*>(G), Vpad, idx + row0 * K, zk, pcoef, acoef, lse2, K, c2);
+        static_cast<unsigned char*>(G), gpitch, v0, Vw, idx + row0 * K, zk, pcoef, acoef, lse2, K,
+        c2);
   else
     k_fixup<F32><<<static_cast<unsigned>(nrows), 64, shm, s>>>(
-        static_cast<unsigned char*>(G), Vpad, idx + row0 * K, zk, pcoef, acoef, lse2, K, c2);
+        static_cast<unsigned char*>(G), gpitch, v0, Vw, idx + row0 * K, zk, pcoef, acoef, lse2, K,
+        c2);
 }
 
-void launch_grad_hidden(int dtype, const void* G, int64_t Vpad, const void* W, int64_t d,
-                        int64_t V, int64_t nrows, int64_t splits, int64_t split_len,
-                        float* part, hipStream_t s) {
+void launch_grad_hidden(int dtype, const void* G, int64_t gpitch, const void* W, int64_t d,
+                        int64_t v0, int64_t Vw, int64_t Vlim, int64_t nrows, bool accumulate,
+                        float* acc, hipStream_t s) {
   ScopedTimer timer_(KID_GRAD_HIDDEN, s);
+  const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_tt = ceil_div(nrows, kBM), n_dt = ceil_div(d, kBN);
-  const unsigned grid = grid_for_tiles(splits * n_tt * n_dt);
-  if (dtype == 1)
-    k_grad_hidden<BF16><<<grid, kThreads, 0, s>>>(static_cast<const unsigned char*>(G), Vpad,
-                                                   static_cast<const unsigned char*>(W), d, V,
-                                                   nrows, n_tt, n_dt, splits, split_len, part);
-  else
-    k_grad_hidden<F32><<<grid, kThreads, 0, s>>>(static_cast<const unsigned char*>(G), Vpad,
-                                                  static_cast<const unsigned char*>(W), d, V,
-                                                  nrows, n_tt, n_dt, splits, split_len, part);
+  const unsigned char* Ws = static_cast<const unsigned char*>(W) + v0 * d * eb;
+  FKL_LAUNCH_GEMM(k_grad_hidden, dtype, 4, grid_for_tiles(n_tt * n_dt), s,
+                  static_cast<const unsigned char*>(G), gpitch, Ws, d, Vw, Vlim, nrows, n_tt, n_dt,
+                  accumulate ? 1 : 0, acc);
 }
 
 void launch_reduce_grad_hidden(int dtype, const float* part, int64_t splits, int64_t nrows,
@@ -587,19 +590,16 @@ void launch_reduce_grad_hidden(int dtype, const float* part, int64_t splits, int
     k_reduce_gh<F32><<<static_cast<unsigned>(blocks), 256, 0, s>>>(part, splits, nrows, d, out);
 }
 
-void launch_grad_w(int dtype, const void* G, int64_t Vpad, const void* H, int64_t d, int64_t V,
-                   int64_t row0, int64_t nrows, bool accumulate, float* grad_w, hipStream_t s) {
+void launch_grad_w(int dtype, const void* G, int64_t gpitch, const void* H, int64_t d,
+                   int64_t v0, int64_t Vw, int64_t Vlim, int64_t row0, int64_t nrows,
+                   bool accumulate, float* grad_w, hipStream_t s) {
   ScopedTimer timer_(KID_GRAD_W, s);
   const int64_t eb = dtype == 1 ? 2 : 4;
-  const int64_t n_vt = ceil_div(V, kBM), n_dt = ceil_div(d, kBN);
+  const int64_t n_vt = ceil_div(Vw, kBM), n_dt = ceil_div(d, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
-  const unsigned grid = grid_for_tiles(n_vt * n_dt);
-  if (dtype == 1)
-    k_grad_w<BF16><<<grid, kThreads, 0, s>>>(static_cast<const unsigned char*>(G), Vpad, Hc, d, V,
-                                              nrows, n_vt, n_dt, accumulate ? 1 : 0, grad_w);
-  else
-    k_grad_w<F32><<<grid, kThreads, 0, s>>>(static_cast<const unsigned char*>(G), Vpad, Hc, d, V,
-                                             nrows, n_vt, n_dt, accumulate ? 1 : 0, grad_w);
+  FKL_LAUNCH_GEMM(k_grad_w, dtype, 4, grid_for_tiles(n_vt * n_dt), s,
+                  static_cast<const unsigned char*>(G), gpitch, Hc, d, Vw, Vlim, nrows, n_vt, n_dt,
+                  accumulate ? 1 : 0, grad_w + v0 * d);
 }
 
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {

@@ -15,10 +15,6 @@ inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
 // Number of partial slots per token (one per 128-wide vocabulary slice).
 inline int64_t lse_slots(int64_t V) { return ceil_div(V, 256) * 2; }
 
-// Split of the vocabulary contraction of grad_hidden: (splits, split length).
-void grad_hidden_split(int64_t rows, int64_t d, int64_t Vpad, int dtype, int64_t* splits,
-                       int64_t* len);
-
 // Forward, per chunk: partial (max, sum) of 2^(z * c2) per (vocab slice, token).
 void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64_t V,
                        int64_t row0, int64_t nrows, float c2, float2* part, int64_t part_ld,
@@ -37,19 +33,25 @@ void launch_reduce_loss(const float* row_loss, int64_t N, float* loss, hipStream
 void launch_bwd_prep(const float* logit, const float* lse, const float* grad_loss, int64_t row0,
                      int64_t nrows, int K, float T, float* pcoef, float* acoef, float* lse2,
                      hipStream_t s);
-void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t Vpad,
-                  int64_t row0, int64_t nrows, float c2, const float* acoef, const float* lse2,
-                  void* G, hipStream_t s);
-void launch_fixup(int dtype, void* G, int64_t Vpad, const int32_t* idx, const float* zk,
-                  const float* pcoef, const float* acoef, const float* lse2, int64_t row0,
-                  int64_t nrows, int K, float c2, hipStream_t s);
-void launch_grad_hidden(int dtype, const void* G, int64_t Vpad, const void* W, int64_t d,
-                        int64_t V, int64_t nrows, int64_t splits, int64_t split_len,
-                        float* part, hipStream_t s);
+// Recompute the logit block rows [row0, row0 + nrows) x vocabulary [v0, v0 + Vw) into
+// the dense part of G (pitch gpitch elements).
+void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t v0,
+                  int64_t Vw, int64_t gpitch, int64_t row0, int64_t nrows, float c2,
+                  const float* acoef, const float* lse2, void* G, hipStream_t s);
+// Exact G entries at the teacher ids that fall inside the slice.
+void launch_fixup(int dtype, void* G, int64_t gpitch, int64_t v0, int64_t Vw, const int32_t* idx,
+                  const float* zk, const float* pcoef, const float* acoef, const float* lse2,
+                  int64_t row0, int64_t nrows, int K, float c2, hipStream_t s);
+// acc[nrows][d] (+)= G_block . W[v0 : v0 + Vw]  (Vlim entries of the slice lie below V).
+void launch_grad_hidden(int dtype, const void* G, int64_t gpitch, const void* W, int64_t d,
+                        int64_t v0, int64_t Vw, int64_t Vlim, int64_t nrows, bool accumulate,
+                        float* acc, hipStream_t s);
 void launch_reduce_grad_hidden(int dtype, const float* part, int64_t splits, int64_t nrows,
                                int64_t d, void* grad_hidden, int64_t row0, hipStream_t s);
-void launch_grad_w(int dtype, const void* G, int64_t Vpad, const void* H, int64_t d, int64_t V,
-                   int64_t row0, int64_t nrows, bool accumulate, float* grad_w, hipStream_t s);
+// grad_W[v0 : v0 + Vlim] (+)= G_block^T . H[row0 : row0 + nrows].
+void launch_grad_w(int dtype, const void* G, int64_t gpitch, const void* H, int64_t d,
+                   int64_t v0, int64_t Vw, int64_t Vlim, int64_t row0, int64_t nrows,
+                   bool accumulate, float* grad_w, hipStream_t s);
 
 // Utilities.
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);

@@ -42,20 +42,22 @@ def test_abi_version_and_status_strings():
     assert fkl.fkl_status_string(12345) == "unknown status"
 
 
-def test_workspace_is_linear_in_rows_and_never_rows_times_vocab():
+def test_workspace_is_bounded_by_chunk_times_vocab_and_never_rows_times_vocab():
     d, V, K, chunk = 3072, 128256, 100, 2048
-    f1, b1 = fkl.fkl_workspace_size(32768, d, V, K, chunk, fkl.FKL_BF16)
-    f2, b2 = fkl.fkl_workspace_size(65536, d, V, K, chunk, fkl.FKL_BF16)
-    per_row_f = (f2 - f1) / 32768
-    per_row_b = (b2 - b1) / 32768
-    assert per_row_f < 8 * K        # per-row scratch only (row loss, gathered logits)
-    assert per_row_b == 0           # the backward's scratch is chunk-sized
-    # the only chunk x V object is the bf16 logit-gradient buffer
-    assert b1 < chunk * V * 2 * 1.5
-    assert b1 < 32768 * V * 2 / 8
-    # it scales with the chunk
-    _, b3 = fkl.fkl_workspace_size(32768, d, V, K, 4096, fkl.FKL_BF16)
-    assert b3 > 1.5 * b1
+    Vpad = (V + 7) // 8 * 8
+    for N in (8192, 32768, 65536, 131072):
+        f, b = fkl.fkl_workspace_size(N, d, V, K, chunk, fkl.FKL_BF16)
+        # forward: per-chunk partials (one float2 per row and 128-wide slice) + per-row scratch
+        assert f <= chunk * ((V + 255) // 256) * 2 * 8 + N * (4 + 4 * K) + (1 << 16)
+        # backward: one logit-gradient block within the chunk x V budget, plus per-row
+        # scratch of a row block (fp32 grad_hidden accumulator, teacher coefficients)
+        assert b <= chunk * Vpad * 2 + min(N, 1 << 16) * (4 * d + 8 * K + 8) + (1 << 16)
+        if N >= 8 * chunk:
+            assert b < N * V * 2 / 4  # far below one dense bf16 N x V matrix
+    # a larger chunk buys a larger block
+    _, b1 = fkl.fkl_workspace_size(32768, d, V, K, 1024, fkl.FKL_BF16)
+    _, b2 = fkl.fkl_workspace_size(32768, d, V, K, 4096, fkl.FKL_BF16)
+    assert b2 > 1.5 * b1
 
 
 def test_workspace_size_rejects_bad_shapes():
