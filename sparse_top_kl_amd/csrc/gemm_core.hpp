@@ -94,6 +94,7 @@ __device__ __forceinline__ u32x4_t load16(const unsigned char* p) {
 // as zero.
 struct Operand {
   __amdgpu_buffer_rsrc_t rsrc;
+  u32x4_t words;  // the same descriptor as four scalar words (for the LDS DMA loads)
   uint32_t ld;
   int32_t mn_count;
   int32_t k_lim;
@@ -103,11 +104,20 @@ __device__ __forceinline__ int32_t clamp_i32(int64_t x) {
   return static_cast<int32_t>(x < 0 ? 0 : (x > 0x7fffffffLL ? 0x7fffffffLL : x));
 }
 
+// The arguments are wave-uniform (kernel arguments and block indices); the
+// base address is passed through readfirstlane so the descriptor lives in
+// scalar registers even where the compiler cannot prove uniformity (otherwise
+// each buffer load is wrapped in a loop over lanes).
 __device__ __forceinline__ Operand make_operand(const unsigned char* base, int64_t ld,
                                                 int64_t mn_count, int64_t k_lim) {
   Operand op;
-  op.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0,
-                                             0x7fffffff, 0x00020000);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  unsigned char* ub = reinterpret_cast<unsigned char*>((static_cast<uint64_t>(hi) << 32) | lo);
+  op.rsrc = __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, 0x7fffffff, 0x00020000);
+  // base[31:0], base[47:32] with stride 0, record count, format/flags word
+  op.words = u32x4_t{lo, hi & 0xffffu, 0x7fffffffu, 0x00020000u};
   op.ld = static_cast<uint32_t>(ld);
   op.mn_count = clamp_i32(mn_count);
   op.k_lim = clamp_i32(k_lim);
@@ -334,8 +344,8 @@ struct TileLoop {
   // a multiple of the stage depth; the operands' k_lim zeroes anything past
   // the true end of K.
   __device__ __forceinline__ static void run(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
-                                             const Operand& B, int k_begin, int k_end,
-                                             unsigned char* lds) {
+                                             const Operand& B, int k_begin, int k_end) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63;
 #pragma unroll
     for (int mi = 0; mi < C::kMI; ++mi)
@@ -371,12 +381,350 @@ struct TileLoop {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS pipeline for bf16 operands.
+//
+// Global data goes straight into LDS with buffer_load ... lds (16 bytes per
+// lane, one 1 KiB block per wave instruction), so no registers hold staged
+// data and kDStages stages of 32 KiB (64 bytes of K per tile row) are in
+// flight at once: the loads for stage t + kDStages - 1 are issued while stage
+// t is consumed. Every iteration issues one stage (stages past K read out of
+// range, which returns zeros into a slot nobody reads), so "stage t+1 has
+// landed" is always "at most kDStages - 3 stages still in flight". The barrier
+// that publishes stage t+1 sits between the two k-steps of stage t, after the
+// fragments of step 1 were read, so the MFMAs resume right after it. Waves
+// wait for their own loads with s_waitcnt before the barrier, which carries no
+// memory fence (a fence would drain every load in flight).
+//
+// Stage layout of one operand (16 KiB):
+//  * k-major (stored [mn][k]): 256 rows of 64 bytes; the four 16-byte chunks
+//    of row r are XOR-swizzled by (r / 4) % 4, so the 16 rows one 256-byte
+//    (64-bank) LDS cycle serves land on 16 distinct chunk positions.
+//    Fragments are one ds_read_b128.
+//  * mn-major (stored [k][mn]): 32 k-rows of 512 bytes; the 32 chunks of k-row
+//    k are XOR-swizzled by 4 * (k % 4). Fragments are two ds_read_b64_tr_b16:
+//    within a group of 16 lanes, source lane s reads k-row kb + s/4 at
+//    mn = base + 4*(s%4) and lane j receives the 4 k-values of mn = base + j,
+//    so two reads give each lane the same 8 consecutive k as the k-major path.
+// Both swizzles make the fragment reads bank-conflict free.
+constexpr int kDRowBytes = 64;
+#ifndef FKL_DIRECT_STAGES
+#define FKL_DIRECT_STAGES 4
+#endif
+constexpr int kDStages = FKL_DIRECT_STAGES;
+constexpr int kDOperandBytes = 256 * kDRowBytes;       // 16 KiB
+constexpr int kDStageBytes = 2 * kDOperandBytes;        // 32 KiB
+
+__device__ __forceinline__ void raw_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding; expcnt unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// One 1 KiB LDS DMA load: lane l's 16 bytes at byte offset voff of the buffer
+// go to LDS address lds + 16*l. Written as inline asm so that the compiler's
+// wait-count insertion does not see it: it would otherwise guard LDS reads it
+// cannot disambiguate from the DMA target with vmcnt(0), draining every stage
+// in flight. The pipeline places all vmcnt waits for these loads explicitly.
+// The load writes no registers; M0 is set (plus the required wait state) in
+// the same block.
+__device__ __forceinline__ void dma_load16(const u32x4_t& words, uint32_t voff, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)lds)));
+  __asm__ volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(words), "s"(m0)
+      : "memory", "m0");
+}
+
+// One operand of the direct pipeline: per-lane byte offsets of its 1 KiB
+// load blocks and the k index each lane's chunk starts at.
+template <bool MC, int NINST>
+struct DirectOperand {
+  uint32_t off[NINST];  // offset at stage k0 = 0 (kOOB if the lane's mn is invalid)
+  int kk[NINST];        // k of the lane's data within a stage
+
+  __device__ __forceinline__ void init(const Operand& op, int w, int lane) {
+#pragma unroll
+    for (int j = 0; j < NINST; ++j) {
+      const int blk = w * NINST + j;
+      if constexpr (!MC) {
+        const int row = blk * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        kk[j] = c * 8;
+        off[j] = row < op.mn_count ? static_cast<uint32_t>(row) * op.ld + c * 16 : kOOB;
+      } else {
+        const int krow = blk * 2 + (lane >> 5);
+        const int c = (lane & 31) ^ (4 * (krow & 3));
+        kk[j] = krow;
+        off[j] = c * 8 < op.mn_count ? static_cast<uint32_t>(krow) * op.ld + c * 16 : kOOB;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void issue(const Operand& op, int k0, unsigned char* dst, int w) const {
+#pragma unroll
+    for (int j = 0; j < NINST; ++j) {
+      uint32_t o;
+      if constexpr (!MC)
+        o = (k0 + kk[j] < op.k_lim) ? off[j] + k0 * 2 : kOOB;
+      else
+        o = (off[j] != kOOB && k0 + kk[j] < op.k_lim) ? off[j] + static_cast<uint32_t>(k0) * op.ld
+                                                       : kOOB;
+      dma_load16(op.words, o, dst + (w * NINST + j) * 1024);
+    }
+  }
+
+  // Fragment of 32 rows (mn0 .. mn0 + 31 of the tile) for k-step s of a stage.
+  __device__ __forceinline__ static u32x4_t frag(const unsigned char* src, int mn0, int s, int lane) {
+    if constexpr (!MC) {
+      const int row = mn0 + (lane & 31);
+      const int c = (2 * s + (lane >> 5)) ^ ((row >> 2) & 3);
+      return lds_load16(src + row * kDRowBytes + c * 16);
+    } else {
+      const int g = lane >> 4, sl = lane & 15;
+      const int mn = mn0 + 16 * (g & 1) + 4 * (sl & 3);
+      const int kb = 16 * s + 8 * (g >> 1) + (sl >> 2);
+      u32x4_t r;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = kb + 4 * h;
+        const int c = (mn >> 3) ^ (4 * (k & 3));
+        const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(src + k * 512 + c * 16 + (mn & 7) * 2));
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t u = __builtin_bit_cast(u32x2_t, v);
+        r[2 * h] = u[0];
+        r[2 * h + 1] = u[1];
+      }
+      return r;
+    }
+  }
+};
+
+template <class C, bool A_MC, bool B_MC>
+struct DirectLoop {
+  typedef BF16 P;
+  static constexpr int BK = kDRowBytes / 2;  // 32 bf16 per stage
+  static constexpr int kWaves = C::kThreads / 64;
+  static constexpr int kInst = kDOperandBytes / 1024 / kWaves;  // 1 KiB loads per wave and operand
+  static constexpr int kLoads = 2 * kInst;
+  static constexpr int kInFlight = (kDStages - 3) * kLoads;     // loads allowed in flight at the barrier
+
+  DirectOperand<A_MC, kInst> a;
+  DirectOperand<B_MC, kInst> b;
+
+  __device__ __forceinline__ void issue(const Operand& A, const Operand& B, int k0,
+                                        unsigned char* stage, int w) const {
+    a.issue(A, k0, stage, w);
+    b.issue(B, k0, stage + kDOperandBytes, w);
+  }
+
+  __device__ __forceinline__ static void frags(u32x4_t (&fa)[C::kMI], u32x4_t (&fb)[C::kNI],
+                                               const unsigned char* stage, int s, int lane) {
+#pragma unroll
+    for (int mi = 0; mi < C::kMI; ++mi)
+      fa[mi] = DirectOperand<A_MC, kInst>::frag(stage, C::wave_m() * C::kWM + mi * 32, s, lane);
+#pragma unroll
+    for (int ni = 0; ni < C::kNI; ++ni)
+      fb[ni] = DirectOperand<B_MC, kInst>::frag(stage + kDOperandBytes,
+                                                C::wave_n() * C::kWN + ni * 32, s, lane);
+  }
+
+  __device__ __forceinline__ static void mfmas(f32x16_t (&acc)[C::kMI][C::kNI],
+                                               const u32x4_t (&fa)[C::kMI],
+                                               const u32x4_t (&fb)[C::kNI]) {
+#pragma unroll
+    for (int mi = 0; mi < C::kMI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < C::kNI; ++ni) mfma_16B<P>(acc[mi][ni], fa[mi], fb[ni]);
+  }
+
+  // MFMAs evenly interleaved with NR LDS reads and NL global loads.
+  template <int NR, int NL>
+  __device__ __forceinline__ static void interleave() {
+    constexpr int kM = C::kMI * C::kNI;
+#pragma unroll
+    for (int i = 0; i < kM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if ((i * NR) / kM != ((i + 1) * NR) / kM)
+        __builtin_amdgcn_sched_group_barrier(0x100, (NR + kM - 1) / kM, 0);
+      if ((i * NL) / kM != ((i + 1) * NL) / kM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  static constexpr int kReads = (A_MC ? 2 : 1) * C::kMI + (B_MC ? 2 : 1) * C::kNI;
+
+  // Stage kt held in `cur`; `nxt` holds stage kt+1; `fill` receives stage kt + kDStages - 1.
+  __device__ __forceinline__ void iter(f32x16_t (&acc)[C::kMI][C::kNI], u32x4_t (&f0a)[C::kMI],
+                                       u32x4_t (&f0b)[C::kNI], const Operand& A, const Operand& B,
+                                       const unsigned char* cur, const unsigned char* nxt,
+                                       unsigned char* fill, int kt, int w, int lane) const {
+    u32x4_t f1a[C::kMI], f1b[C::kNI];
+    frags(f1a, f1b, cur, 1, lane);
+    mfmas(acc, f0a, f0b);
+    interleave<kReads, 0>();
+    wait_vmcnt_lgkm0<kInFlight>();
+    raw_barrier();
+    issue(A, B, (kt + kDStages - 1) * BK, fill, w);
+    frags(f0a, f0b, nxt, 0, lane);
+    mfmas(acc, f1a, f1b);
+    interleave<kReads, kLoads>();
+  }
+
+  // The stages live in distinct __shared__ arrays (selected at compile time
+  // through the unrolled slot index): with one array the compiler cannot tell
+  // which in-flight LDS DMA a transpose read may alias and drains them all
+  // (vmcnt(0)) before it.
+  struct Stages {
+    unsigned char* s[kDStages];
+  };
+  __device__ __forceinline__ static Stages stage_arrays() {
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[kDStageBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[kDStageBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[kDStageBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[kDStageBytes];
+    static_assert(kDStages == 4 || kDStages == 5, "4 or 5 stages");
+    Stages r;
+    r.s[0] = st0;
+    r.s[1] = st1;
+    r.s[2] = st2;
+    r.s[3] = st3;
+    if constexpr (kDStages == 5) {
+      __shared__ __attribute__((aligned(1024))) unsigned char st4[kDStageBytes];
+      r.s[kDStages - 1] = st4;
+    }
+    return r;
+  }
+
+  template <int I>
+  __device__ __forceinline__ static unsigned char* slot(const Stages& st) {
+    return st.s[I % kDStages];
+  }
+
+  template <int I>
+  __device__ __forceinline__ void iter_at(f32x16_t (&acc)[C::kMI][C::kNI], u32x4_t (&f0a)[C::kMI],
+                                          u32x4_t (&f0b)[C::kNI], const Operand& A,
+                                          const Operand& B, const Stages& base, int kt, int w,
+                                          int lane) const {
+    iter(acc, f0a, f0b, A, B, slot<I>(base), slot<I + 1>(base), slot<I + kDStages - 1>(base), kt, w,
+         lane);
+  }
+
+  template <int I>
+  __device__ __forceinline__ void unrolled(f32x16_t (&acc)[C::kMI][C::kNI], u32x4_t (&f0a)[C::kMI],
+                                           u32x4_t (&f0b)[C::kNI], const Operand& A,
+                                           const Operand& B, const Stages& base, int kt, int w,
+                                           int lane) const {
+    if constexpr (I < kDStages) {
+      iter_at<I>(acc, f0a, f0b, A, B, base, kt + I, w, lane);
+      unrolled<I + 1>(acc, f0a, f0b, A, B, base, kt, w, lane);
+    }
+  }
+
+  template <int I>
+  __device__ __forceinline__ void tail(f32x16_t (&acc)[C::kMI][C::kNI], u32x4_t (&f0a)[C::kMI],
+                                       u32x4_t (&f0b)[C::kNI], const Operand& A, const Operand& B,
+                                       const Stages& base, int kt, int nk, int w, int lane) const {
+    if constexpr (I + 1 < kDStages) {
+      if (kt + I < nk) {
+        iter_at<I>(acc, f0a, f0b, A, B, base, kt + I, w, lane);
+        tail<I + 1>(acc, f0a, f0b, A, B, base, kt, nk, w, lane);
+      }
+    }
+  }
+
+  template <int I>
+  __device__ __forceinline__ void prologue(const Operand& A, const Operand& B, const Stages& base,
+                                           int w) const {
+    if constexpr (I + 1 < kDStages) {
+      issue(A, B, I * BK, slot<I>(base), w);
+      prologue<I + 1>(A, B, base, w);
+    }
+  }
+
+  __device__ __forceinline__ static void run(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
+                                             const Operand& B, int K) {
+    const Stages stages = stage_arrays();
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int mi = 0; mi < C::kMI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < C::kNI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+    const int nk = (K + BK - 1) / BK;
+    if (nk <= 0) return;
+    DirectLoop L;
+    L.a.init(A, w, lane);
+    L.b.init(B, w, lane);
+    L.prologue<0>(A, B, stages, w);
+    // stage 0 landed: kDStages - 2 later stages may still be in flight
+    wait_vmcnt_lgkm0<(kDStages - 2) * kLoads>();
+    raw_barrier();
+    u32x4_t f0a[C::kMI], f0b[C::kNI];
+    frags(f0a, f0b, stages.s[0], 0, lane);
+    int kt = 0;
+    for (; kt + kDStages <= nk; kt += kDStages) L.unrolled<0>(acc, f0a, f0b, A, B, stages, kt, w, lane);
+    L.tail<0>(acc, f0a, f0b, A, B, stages, kt, nk, w, lane);
+    // drain the out-of-range loads before the LDS is reused
+    wait_vmcnt_lgkm0<0>();
+  }
+};
+
+#ifndef FKL_DIRECT_LDS
+#define FKL_DIRECT_LDS 1
+#endif
+
+// acc = A[tile, 0:K] . B[tile, 0:K]^T for one 256 x 256 tile.
 template <class P, class C, bool A_MC, bool B_MC>
 __device__ __forceinline__ void gemm_tile(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
-                                          const Operand& B, int k_begin, int k_end,
-                                          unsigned char* lds) {
-  TileLoop<P, C, A_MC, B_MC>::run(acc, A, B, k_begin, k_end, lds);
+                                          const Operand& B, int K) {
+  if constexpr (FKL_DIRECT_LDS && P::kBytes == 2)
+    DirectLoop<C, A_MC, B_MC>::run(acc, A, B, K);
+  else
+    TileLoop<P, C, A_MC, B_MC>::run(acc, A, B, 0, K);
 }
+
+// Grouped, XCD-aware tile order. Blocks are dealt round-robin over the 8 XCDs
+// (launch block b runs on XCD b % 8) and each XCD runs ~32 workgroups at a
+// time (one per CU). Output tiles are cut into groups of GA x GB = 32 tiles;
+// group q runs entirely on XCD q % 8, as 32 consecutive blocks of that XCD, so
+// the workgroups resident on an XCD share GA panels of one operand and GB of
+// the other in its L2 instead of each streaming its own. Launch with
+// grouped_grid() blocks; blocks whose tile falls outside the grid exit.
+template <int GA, int GB>
+struct TileGroups {
+  static_assert(GA * GB == 32, "one group per XCD wave of workgroups");
+  static int64_t grid(int64_t mt, int64_t nt) {
+    const int64_t ngroups = ((mt + GA - 1) / GA) * ((nt + GB - 1) / GB);
+    return 8 * ((ngroups + 7) / 8) * 32;
+  }
+  __device__ __forceinline__ static bool coords(int64_t mt, int64_t nt, int64_t* tm, int64_t* tn) {
+    const int64_t b = blockIdx.x;
+    const int64_t xcd = b & 7, local = b >> 3;
+    const int64_t q = (local >> 5) * 8 + xcd, j = local & 31;
+    const int64_t gn = (nt + GB - 1) / GB;
+    const int64_t gm_i = q / gn, gn_i = q % gn;
+    *tm = gm_i * GA + (j % GA);
+    *tn = gn_i * GB + (j / GA);
+    return *tm < mt && *tn < nt;
+  }
+};
 
 // Row offset, inside the wave sub-tile, of accumulator element r of block mi.
 __device__ __forceinline__ int acc_row(int mi, int r, int lane) {

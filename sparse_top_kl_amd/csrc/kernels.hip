@@ -39,6 +39,17 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// out (+)= v for an fp32 output element that receives exactly one
+// contribution per launch (launches on one stream are ordered), so the sum is
+// the same as a read-modify-write but the wave never waits for the old value:
+// the add is a fire-and-forget atomic performed in L2.
+__device__ __forceinline__ void accumulate_out(float* p, float v, int accumulate) {
+  if (accumulate)
+    (void)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
 // ------------------------------------------------------------------ forward
 
 template <class P, class C>
@@ -47,11 +58,8 @@ __global__ __launch_bounds__(C::kThreads) void k_logits_lse(
     int64_t nrows, int64_t n_vt, int64_t n_tt, float c2, float2* __restrict__ part,
     int64_t part_ld) {
   static_assert(C::kWM == kSliceVocab, "one LSE partial per wave row-slice");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  const int64_t total = n_vt * n_tt;
-  const int64_t t = xcd_tile_index(total);
-  if (t >= total) return;
-  const int64_t vt = t / n_tt, tt = t % n_tt;
+  int64_t vt, tt;
+  if (!TileGroups<4, 8>::coords(n_vt, n_tt, &vt, &tt)) return;
   const int64_t ld = d * P::kBytes;
   // MFMA rows = vocabulary entries (weight rows), columns = tokens, so each
   // lane's accumulators belong to one token and the reduction over the
@@ -59,7 +67,7 @@ __global__ __launch_bounds__(C::kThreads) void k_logits_lse(
   const Operand A = make_operand(W + vt * kBM * ld, ld, V - vt * kBM, d);
   const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, false, false>(acc, A, B, 0, static_cast<int>(d), lds);
+  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
 
   const int lane = threadIdx.x & 63;
   const int64_t v0 = vt * kBM + C::wave_m() * C::kWM;
@@ -268,17 +276,14 @@ __global__ __launch_bounds__(C::kThreads) void k_gprod(
     const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
     int64_t v0, int64_t Vw, int64_t gpitch, int64_t nrows, int64_t n_vt, int64_t n_tt, float c2,
     const float* __restrict__ acoef, const float* __restrict__ lse2, unsigned char* __restrict__ G) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  const int64_t total = n_vt * n_tt;
-  const int64_t t = xcd_tile_index(total);
-  if (t >= total) return;
-  const int64_t vt = t / n_tt, tt = t % n_tt;
+  int64_t vt, tt;
+  if (!TileGroups<4, 8>::coords(n_vt, n_tt, &vt, &tt)) return;
   const int64_t ld = d * P::kBytes;
   const int64_t vbase = v0 + vt * kBM;  // first vocabulary entry of the tile
   const Operand A = make_operand(W + vbase * ld, ld, V - vbase, d);
   const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, false, false>(acc, A, B, 0, static_cast<int>(d), lds);
+  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
 
   const int lane = threadIdx.x & 63;
   const int64_t w0 = vt * kBM + C::wave_m() * C::kWM;  // slice-relative column of the wave
@@ -348,18 +353,15 @@ __global__ __launch_bounds__(C::kThreads) void k_grad_hidden(
     const unsigned char* __restrict__ G, int64_t gpitch, const unsigned char* __restrict__ W,
     int64_t d, int64_t Vw, int64_t Vlim, int64_t nrows, int64_t n_tt, int64_t n_dt,
     int accumulate, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  const int64_t total = n_dt * n_tt;
-  const int64_t t = xcd_tile_index(total);
-  if (t >= total) return;
-  const int64_t tt = t % n_tt, dt = t / n_tt;
+  int64_t tt, dt;
+  if (!TileGroups<8, 4>::coords(n_tt, n_dt, &tt, &dt)) return;
   const int64_t gld = gpitch * P::kBytes, wld = d * P::kBytes;
   // A = G rows of this tile (k = slice column), B = W rows of the slice (k = v), columns of
   // this tile
   const Operand A = make_operand(G + tt * kBM * gld, gld, nrows - tt * kBM, Vw);
   const Operand B = make_operand(W + dt * kBN * P::kBytes, wld, d - dt * kBN, Vlim);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, false, true>(acc, A, B, 0, static_cast<int>(Vw), lds);
+  gemm_tile<P, C, false, true>(acc, A, B, static_cast<int>(Vw));
 
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -371,10 +373,7 @@ __global__ __launch_bounds__(C::kThreads) void k_grad_hidden(
 #pragma unroll
       for (int ni = 0; ni < C::kNI; ++ni) {
         const int64_t col = dt * kBN + C::wave_n() * C::kWN + ni * 32 + (lane & 31);
-        if (col < d) {
-          float* p = out + row * d + col;
-          *p = accumulate ? *p + acc[mi][ni][r] : acc[mi][ni][r];
-        }
+        if (col < d) accumulate_out(out + row * d + col, acc[mi][ni][r], accumulate);
       }
     }
 }
@@ -406,16 +405,13 @@ __global__ __launch_bounds__(C::kThreads) void k_grad_w(
     const unsigned char* __restrict__ G, int64_t gpitch, const unsigned char* __restrict__ H,
     int64_t d, int64_t Vw, int64_t Vlim, int64_t nrows, int64_t n_vt, int64_t n_dt, int accumulate,
     float* __restrict__ grad_w) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  const int64_t total = n_vt * n_dt;
-  const int64_t t = xcd_tile_index(total);
-  if (t >= total) return;
-  const int64_t vt = t / n_dt, dt = t % n_dt;
+  int64_t vt, dt;
+  if (!TileGroups<8, 4>::coords(n_vt, n_dt, &vt, &dt)) return;
   // A = G^T (stored [row][v], k = row), B = H (stored [row][col], k = row)
   const Operand A = make_operand(G + vt * kBM * P::kBytes, gpitch * P::kBytes, Vw - vt * kBM, nrows);
   const Operand B = make_operand(H + dt * kBN * P::kBytes, d * P::kBytes, d - dt * kBN, nrows);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, true, true>(acc, A, B, 0, static_cast<int>(nrows), lds);
+  gemm_tile<P, C, true, true>(acc, A, B, static_cast<int>(nrows));
 
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -427,10 +423,7 @@ __global__ __launch_bounds__(C::kThreads) void k_grad_w(
 #pragma unroll
       for (int ni = 0; ni < C::kNI; ++ni) {
         const int64_t col = dt * kBN + C::wave_n() * C::kWN + ni * 32 + (lane & 31);
-        if (col < d) {
-          float* p = grad_w + v * d + col;
-          *p = accumulate ? *p + acc[mi][ni][r] : acc[mi][ni][r];
-        }
+        if (col < d) accumulate_out(grad_w + v * d + col, acc[mi][ni][r], accumulate);
       }
     }
 }
@@ -457,8 +450,9 @@ __global__ __launch_bounds__(256) void k_validate_idx(const int32_t* __restrict_
 
 // ------------------------------------------------------------------ launchers
 
-static inline unsigned grid_for_tiles(int64_t total) {
-  return static_cast<unsigned>(8 * ceil_div(total, 8));
+template <int GA, int GB>
+static inline unsigned grouped_grid(int64_t mt, int64_t nt) {
+  return static_cast<unsigned>(TileGroups<GA, GB>::grid(mt, nt));
 }
 
 typedef TileCfg<2, 2> Cfg4;  // 4 waves, 128x128 per wave, one wave per SIMD
@@ -492,7 +486,8 @@ void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(V, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
-  FKL_LAUNCH_GEMM(k_logits_lse, dtype, 8, grid_for_tiles(n_vt * n_tt), s,
+  const unsigned grid = grouped_grid<4, 8>(n_vt, n_tt);
+  FKL_LAUNCH_GEMM(k_logits_lse, dtype, 8, grid, s,
                   static_cast<const unsigned char*>(W), Hc, d, V, nrows, n_vt, n_tt, c2, part,
                   part_ld);
 }
@@ -542,7 +537,8 @@ void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V,
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(Vw, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
-  FKL_LAUNCH_GEMM(k_gprod, dtype, 8, grid_for_tiles(n_vt * n_tt), s,
+  const unsigned grid = grouped_grid<4, 8>(n_vt, n_tt);
+  FKL_LAUNCH_GEMM(k_gprod, dtype, 8, grid, s,
                   static_cast<const unsigned char*>(W), Hc, d, V, v0, Vw, gpitch, nrows, n_vt,
                   n_tt, c2, acoef, lse2, static_cast<unsigned char*>(G));
 }
@@ -570,7 +566,8 @@ void launch_grad_hidden(int dtype, const void* G, int64_t gpitch, const void* W,
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_tt = ceil_div(nrows, kBM), n_dt = ceil_div(d, kBN);
   const unsigned char* Ws = static_cast<const unsigned char*>(W) + v0 * d * eb;
-  FKL_LAUNCH_GEMM(k_grad_hidden, dtype, 4, grid_for_tiles(n_tt * n_dt), s,
+  const unsigned grid = grouped_grid<8, 4>(n_tt, n_dt);
+  FKL_LAUNCH_GEMM(k_grad_hidden, dtype, 8, grid, s,
                   static_cast<const unsigned char*>(G), gpitch, Ws, d, Vw, Vlim, nrows, n_tt, n_dt,
                   accumulate ? 1 : 0, acc);
 }
@@ -597,7 +594,8 @@ void launch_grad_w(int dtype, const void* G, int64_t gpitch, const void* H, int6
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(Vw, kBM), n_dt = ceil_div(d, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
-  FKL_LAUNCH_GEMM(k_grad_w, dtype, 4, grid_for_tiles(n_vt * n_dt), s,
+  const unsigned grid = grouped_grid<8, 4>(n_vt, n_dt);
+  FKL_LAUNCH_GEMM(k_grad_w, dtype, 8, grid, s,
                   static_cast<const unsigned char*>(G), gpitch, Hc, d, Vw, Vlim, nrows, n_vt, n_dt,
                   accumulate ? 1 : 0, grad_w + v0 * d);
 }

@@ -19,7 +19,7 @@ from dataclasses import dataclass
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libfkl.so")
+LIB_PATH = os.environ.get("FKL_LIBRARY") or os.path.join(HERE, "libfkl.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "fkl.h")
 
 
