@@ -37,6 +37,10 @@ namespace fkl {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Register budget of the MFMA kernels: one workgroup per CU (LDS-bound), so
+// kThreads / 256 waves per SIMD.
+#define FKL_WAVES_PER_EU(C) __attribute__((amdgpu_waves_per_eu(C::kThreads / 256, C::kThreads / 256)))
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // out (+)= v for an fp32 output element that receives exactly one
@@ -53,7 +57,7 @@ __device__ __forceinline__ void accumulate_out(float* p, float v, int accumulate
 // ------------------------------------------------------------------ forward
 
 template <class P, class C>
-__global__ __launch_bounds__(C::kThreads) void k_logits_lse(
+__global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_logits_lse(
     const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
     int64_t nrows, int64_t n_vt, int64_t n_tt, float c2, float2* __restrict__ part,
     int64_t part_ld) {
@@ -272,7 +276,7 @@ __device__ __forceinline__ void store4(unsigned char* p, const float (&v)[4]) {
 // write G_dense = acoef * 2^(z*c2 - lse2) into the G block G[row][v - v0]
 // (row pitch gpitch elements; entries with v >= V are written as zero).
 template <class P, class C>
-__global__ __launch_bounds__(C::kThreads) void k_gprod(
+__global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_gprod(
     const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
     int64_t v0, int64_t Vw, int64_t gpitch, int64_t nrows, int64_t n_vt, int64_t n_tt, float c2,
     const float* __restrict__ acoef, const float* __restrict__ lse2, unsigned char* __restrict__ G) {
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(64) void k_fixup(unsigned char* __restrict__ G, int
 // acc[row][col] (+)= sum over the slice of G[row][v - v0] W[v][col], for the rows
 // of one block; the slice is Vw entries wide (Vlim of them below V).
 template <class P, class C>
-__global__ __launch_bounds__(C::kThreads) void k_grad_hidden(
+__global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_grad_hidden(
     const unsigned char* __restrict__ G, int64_t gpitch, const unsigned char* __restrict__ W,
     int64_t d, int64_t Vw, int64_t Vlim, int64_t nrows, int64_t n_tt, int64_t n_dt,
     int accumulate, float* __restrict__ out) {
@@ -401,7 +405,7 @@ __global__ __launch_bounds__(256) void k_reduce_gh(const float* __restrict__ par
 
 // grad_W[v0 + v][col] (+)= sum over the block's rows of G[row][v] H[row][col].
 template <class P, class C>
-__global__ __launch_bounds__(C::kThreads) void k_grad_w(
+__global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_grad_w(
     const unsigned char* __restrict__ G, int64_t gpitch, const unsigned char* __restrict__ H,
     int64_t d, int64_t Vw, int64_t Vlim, int64_t nrows, int64_t n_vt, int64_t n_dt, int accumulate,
     float* __restrict__ grad_w) {
