@@ -386,34 +386,47 @@ struct TileLoop {
 //
 // Global data goes straight into LDS with buffer_load ... lds (16 bytes per
 // lane, one 1 KiB block per wave instruction), so no registers hold staged
-// data and kDStages stages of 32 KiB (64 bytes of K per tile row) are in
-// flight at once: the loads for stage t + kDStages - 1 are issued while stage
-// t is consumed. Every iteration issues one stage (stages past K read out of
-// range, which returns zeros into a slot nobody reads), so "stage t+1 has
-// landed" is always "at most kDStages - 3 stages still in flight". The barrier
-// that publishes stage t+1 sits between the two k-steps of stage t, after the
-// fragments of step 1 were read, so the MFMAs resume right after it. Waves
-// wait for their own loads with s_waitcnt before the barrier, which carries no
-// memory fence (a fence would drain every load in flight).
+// data. A stage holds 64 values of K for all 256 rows of both operands
+// (64 KiB); kDStages = 2 stages fill 128 KiB of LDS. A stage is consumed in
+// four k-steps of 16; the fragments of step s+1 are read while the MFMAs of
+// step s run. After the fragments of the stage's last step are in registers,
+// one barrier per stage both releases the slot (every wave has read it) and
+// publishes the next stage (every wave waited for its own loads of it with
+// s_waitcnt first; the barrier carries no memory fence, which would drain
+// every load in flight). The released slot is refilled at once with the stage
+// kDStages ahead, whose loads run behind the MFMAs of the last step and the
+// whole next stage. Stages past K read out of range, which returns zeros
+// into a slot nobody reads, so the loop has no branches around the loads.
 //
-// Stage layout of one operand (16 KiB):
-//  * k-major (stored [mn][k]): 256 rows of 64 bytes; the four 16-byte chunks
-//    of row r are XOR-swizzled by (r / 4) % 4, so the 16 rows one 256-byte
-//    (64-bank) LDS cycle serves land on 16 distinct chunk positions.
+// Each DMA instruction moves whole 128-byte lines: on this chip the L1 path
+// into LDS serves one cache line per clock, so a row segment of 64 bytes per
+// line would halve its throughput.
+//
+// Stage layout of one operand (32 KiB):
+//  * k-major (stored [mn][k]): 256 rows of 128 bytes; the eight 16-byte
+//    chunks of row r are XOR-swizzled by (r / 2) % 8, so the 16 rows one
+//    256-byte (64-bank) LDS cycle serves land on 16 distinct chunk positions.
 //    Fragments are one ds_read_b128.
-//  * mn-major (stored [k][mn]): 32 k-rows of 512 bytes; the 32 chunks of k-row
+//  * mn-major (stored [k][mn]): 64 k-rows of 512 bytes; the 32 chunks of k-row
 //    k are XOR-swizzled by 4 * (k % 4). Fragments are two ds_read_b64_tr_b16:
 //    within a group of 16 lanes, source lane s reads k-row kb + s/4 at
 //    mn = base + 4*(s%4) and lane j receives the 4 k-values of mn = base + j,
 //    so two reads give each lane the same 8 consecutive k as the k-major path.
 // Both swizzles make the fragment reads bank-conflict free.
-constexpr int kDRowBytes = 64;
-#ifndef FKL_DIRECT_STAGES
-#define FKL_DIRECT_STAGES 4
-#endif
-constexpr int kDStages = FKL_DIRECT_STAGES;
-constexpr int kDOperandBytes = 256 * kDRowBytes;       // 16 KiB
-constexpr int kDStageBytes = 2 * kDOperandBytes;        // 32 KiB
+// Lines [first, first + count) of an operand's 256-line stage that one
+// workgroup touches ahead of time; the workgroups sharing an operand tile
+// split its lines between them.
+struct PrefetchShare {
+  int first;
+  int count;
+};
+
+constexpr int kDRowBytes = 128;
+constexpr int kDStages = 2;
+constexpr int kDPrefetch = 4;  // a stage's lines are touched this many stages before use
+constexpr int kDSteps = kDRowBytes / 32;                // k-steps of 16 per stage
+constexpr int kDOperandBytes = 256 * kDRowBytes;       // 32 KiB
+constexpr int kDStageBytes = 2 * kDOperandBytes;        // 64 KiB
 
 __device__ __forceinline__ void raw_barrier() {
   __asm__ volatile("" ::: "memory");
@@ -430,6 +443,13 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// The DMA loads below set M0 themselves. The compiler treats M0 as reserved
+// and warns that clobbering it is not preserved; that is intended: it only
+// writes M0 immediately before an instruction that reads it, and on gfx950
+// no instruction these kernels compile to reads M0 except these loads.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 
 // One 1 KiB LDS DMA load: lane l's 16 bytes at byte offset voff of the buffer
 // go to LDS address lds + 16*l. Written as inline asm so that the compiler's
@@ -450,6 +470,23 @@ __device__ __forceinline__ void dma_load16(const u32x4_t& words, uint32_t voff, 
       : "memory", "m0");
 }
 
+// L2 prefetch: one dword per lane (64 distinct 128-byte lines per wave
+// instruction) is loaded into a scratch LDS area nobody reads, so lines that
+// miss in L2 are requested stages before the real loads need them.
+__device__ __forceinline__ void dma_touch4(const u32x4_t& words, uint32_t voff, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)lds)));
+  __asm__ volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(words), "s"(m0)
+      : "memory", "m0");
+}
+
+#pragma clang diagnostic pop
+
 // One operand of the direct pipeline: per-lane byte offsets of its 1 KiB
 // load blocks and the k index each lane's chunk starts at.
 template <bool MC, int NINST>
@@ -462,8 +499,8 @@ struct DirectOperand {
     for (int j = 0; j < NINST; ++j) {
       const int blk = w * NINST + j;
       if constexpr (!MC) {
-        const int row = blk * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        const int row = blk * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
         kk[j] = c * 8;
         off[j] = row < op.mn_count ? static_cast<uint32_t>(row) * op.ld + c * 16 : kOOB;
       } else {
@@ -488,11 +525,25 @@ struct DirectOperand {
     }
   }
 
+  // Byte offset of line `line` (0..255) of the stage starting at k0, or kOOB.
+  __device__ __forceinline__ static uint32_t line_offset(const Operand& op, int k0, int line) {
+    if constexpr (!MC) {
+      return (line < op.mn_count && k0 < op.k_lim)
+                 ? static_cast<uint32_t>(line) * op.ld + static_cast<uint32_t>(k0) * 2
+                 : kOOB;
+    } else {
+      const int krow = line >> 2, seg = line & 3;
+      return (seg * 64 < op.mn_count && k0 + krow < op.k_lim)
+                 ? static_cast<uint32_t>(k0 + krow) * op.ld + seg * 128
+                 : kOOB;
+    }
+  }
+
   // Fragment of 32 rows (mn0 .. mn0 + 31 of the tile) for k-step s of a stage.
   __device__ __forceinline__ static u32x4_t frag(const unsigned char* src, int mn0, int s, int lane) {
     if constexpr (!MC) {
       const int row = mn0 + (lane & 31);
-      const int c = (2 * s + (lane >> 5)) ^ ((row >> 2) & 3);
+      const int c = (2 * s + (lane >> 5)) ^ ((row >> 1) & 7);
       return lds_load16(src + row * kDRowBytes + c * 16);
     } else {
       const int g = lane >> 4, sl = lane & 15;
@@ -518,19 +569,43 @@ struct DirectOperand {
 template <class C, bool A_MC, bool B_MC>
 struct DirectLoop {
   typedef BF16 P;
-  static constexpr int BK = kDRowBytes / 2;  // 32 bf16 per stage
+  static constexpr int BK = kDRowBytes / 2;  // 64 bf16 per stage
   static constexpr int kWaves = C::kThreads / 64;
   static constexpr int kInst = kDOperandBytes / 1024 / kWaves;  // 1 KiB loads per wave and operand
   static constexpr int kLoads = 2 * kInst;
-  static constexpr int kInFlight = (kDStages - 3) * kLoads;     // loads allowed in flight at the barrier
+  // Every wave issues one L2 touch per iteration, after its stage loads, so at
+  // the barrier only the previous iteration's touch may still be in flight.
+  static constexpr int kInFlight = 1;
+  static_assert(kDStages == 2 && kDPrefetch >= kDStages, "pipeline accounting");
+  static constexpr int kTouchLanes = 128 / kWaves;  // lanes per wave; half the waves per operand
 
   DirectOperand<A_MC, kInst> a;
   DirectOperand<B_MC, kInst> b;
+  PrefetchShare pa, pb;
 
   __device__ __forceinline__ void issue(const Operand& A, const Operand& B, int k0,
                                         unsigned char* stage, int w) const {
     a.issue(A, k0, stage, w);
     b.issue(B, k0, stage + kDOperandBytes, w);
+  }
+
+  // Touch this workgroup's share of the lines of the stage starting at k0:
+  // the first half of the waves covers the A share, the second half the B
+  // share (up to 64 lines each). Waves with nothing to touch issue the load
+  // out of range, so every wave issues exactly one per iteration.
+  __device__ __forceinline__ void touch(const Operand& A, const Operand& B, int k0, int w,
+                                        int lane) const {
+    const bool is_a = w < kWaves / 2;  // wave-uniform
+    const int idx = (w % (kWaves / 2)) * kTouchLanes + lane;
+    const PrefetchShare sh = is_a ? pa : pb;
+    const bool valid = lane < kTouchLanes && idx < sh.count;
+    unsigned char* scratch = scratch_lds();
+    if (is_a)
+      dma_touch4(A.words, valid ? DirectOperand<A_MC, kInst>::line_offset(A, k0, sh.first + idx) : kOOB,
+                 scratch);
+    else
+      dma_touch4(B.words, valid ? DirectOperand<B_MC, kInst>::line_offset(B, k0, sh.first + idx) : kOOB,
+                 scratch);
   }
 
   __device__ __forceinline__ static void frags(u32x4_t (&fa)[C::kMI], u32x4_t (&fb)[C::kNI],
@@ -569,21 +644,42 @@ struct DirectLoop {
 
   static constexpr int kReads = (A_MC ? 2 : 1) * C::kMI + (B_MC ? 2 : 1) * C::kNI;
 
-  // Stage kt held in `cur`; `nxt` holds stage kt+1; `fill` receives stage kt + kDStages - 1.
+  // Steps s .. kDSteps - 2 of the stage in `cur`: read the fragments of step
+  // s + 1 while the MFMAs of step s run (even steps use set 0, odd steps set 1).
+  template <int S>
+  __device__ __forceinline__ static void steps(f32x16_t (&acc)[C::kMI][C::kNI],
+                                               u32x4_t (&f0a)[C::kMI], u32x4_t (&f0b)[C::kNI],
+                                               u32x4_t (&f1a)[C::kMI], u32x4_t (&f1b)[C::kNI],
+                                               const unsigned char* cur, int lane) {
+    if constexpr (S + 1 < kDSteps) {
+      if constexpr (S % 2 == 0) {
+        frags(f1a, f1b, cur, S + 1, lane);
+        mfmas(acc, f0a, f0b);
+      } else {
+        frags(f0a, f0b, cur, S + 1, lane);
+        mfmas(acc, f1a, f1b);
+      }
+      interleave<kReads, 0>();
+      steps<S + 1>(acc, f0a, f0b, f1a, f1b, cur, lane);
+    }
+  }
+
+  // Stage kt in slot `cur`, stage kt+1 in `nxt`; `cur` is refilled with stage
+  // kt + kDStages once every wave has read it.
   __device__ __forceinline__ void iter(f32x16_t (&acc)[C::kMI][C::kNI], u32x4_t (&f0a)[C::kMI],
                                        u32x4_t (&f0b)[C::kNI], const Operand& A, const Operand& B,
-                                       const unsigned char* cur, const unsigned char* nxt,
-                                       unsigned char* fill, int kt, int w, int lane) const {
+                                       unsigned char* cur, const unsigned char* nxt, int kt, int w,
+                                       int lane) const {
+    static_assert(kDSteps % 2 == 0, "the last step of a stage uses fragment set 1");
     u32x4_t f1a[C::kMI], f1b[C::kNI];
-    frags(f1a, f1b, cur, 1, lane);
-    mfmas(acc, f0a, f0b);
-    interleave<kReads, 0>();
+    steps<0>(acc, f0a, f0b, f1a, f1b, cur, lane);
     wait_vmcnt_lgkm0<kInFlight>();
     raw_barrier();
-    issue(A, B, (kt + kDStages - 1) * BK, fill, w);
+    issue(A, B, (kt + kDStages) * BK, cur, w);
+    touch(A, B, (kt + kDPrefetch) * BK, w, lane);
     frags(f0a, f0b, nxt, 0, lane);
     mfmas(acc, f1a, f1b);
-    interleave<kReads, kLoads>();
+    interleave<kReads, kLoads + 1>();
   }
 
   // The stages live in distinct __shared__ arrays (selected at compile time
@@ -596,19 +692,16 @@ struct DirectLoop {
   __device__ __forceinline__ static Stages stage_arrays() {
     __shared__ __attribute__((aligned(1024))) unsigned char st0[kDStageBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char st1[kDStageBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char st2[kDStageBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char st3[kDStageBytes];
-    static_assert(kDStages == 4 || kDStages == 5, "4 or 5 stages");
+    static_assert(kDStages == 2, "two stages");
     Stages r;
     r.s[0] = st0;
     r.s[1] = st1;
-    r.s[2] = st2;
-    r.s[3] = st3;
-    if constexpr (kDStages == 5) {
-      __shared__ __attribute__((aligned(1024))) unsigned char st4[kDStageBytes];
-      r.s[kDStages - 1] = st4;
-    }
     return r;
+  }
+
+  __device__ __forceinline__ static unsigned char* scratch_lds() {
+    __shared__ __attribute__((aligned(256))) unsigned char pf_scratch[256];
+    return pf_scratch;
   }
 
   template <int I>
@@ -617,21 +710,12 @@ struct DirectLoop {
   }
 
   template <int I>
-  __device__ __forceinline__ void iter_at(f32x16_t (&acc)[C::kMI][C::kNI], u32x4_t (&f0a)[C::kMI],
-                                          u32x4_t (&f0b)[C::kNI], const Operand& A,
-                                          const Operand& B, const Stages& base, int kt, int w,
-                                          int lane) const {
-    iter(acc, f0a, f0b, A, B, slot<I>(base), slot<I + 1>(base), slot<I + kDStages - 1>(base), kt, w,
-         lane);
-  }
-
-  template <int I>
   __device__ __forceinline__ void unrolled(f32x16_t (&acc)[C::kMI][C::kNI], u32x4_t (&f0a)[C::kMI],
                                            u32x4_t (&f0b)[C::kNI], const Operand& A,
                                            const Operand& B, const Stages& base, int kt, int w,
                                            int lane) const {
     if constexpr (I < kDStages) {
-      iter_at<I>(acc, f0a, f0b, A, B, base, kt + I, w, lane);
+      iter(acc, f0a, f0b, A, B, slot<I>(base), slot<I + 1>(base), kt + I, w, lane);
       unrolled<I + 1>(acc, f0a, f0b, A, B, base, kt, w, lane);
     }
   }
@@ -642,7 +726,7 @@ struct DirectLoop {
                                        const Stages& base, int kt, int nk, int w, int lane) const {
     if constexpr (I + 1 < kDStages) {
       if (kt + I < nk) {
-        iter_at<I>(acc, f0a, f0b, A, B, base, kt + I, w, lane);
+        iter(acc, f0a, f0b, A, B, slot<I>(base), slot<I + 1>(base), kt + I, w, lane);
         tail<I + 1>(acc, f0a, f0b, A, B, base, kt, nk, w, lane);
       }
     }
@@ -650,17 +734,22 @@ struct DirectLoop {
 
   template <int I>
   __device__ __forceinline__ void prologue(const Operand& A, const Operand& B, const Stages& base,
-                                           int w) const {
-    if constexpr (I + 1 < kDStages) {
+                                           int w, int lane) const {
+    if constexpr (I < kDStages) {
       issue(A, B, I * BK, slot<I>(base), w);
-      prologue<I + 1>(A, B, base, w);
+      prologue<I + 1>(A, B, base, w, lane);
+    } else if constexpr (I < kDPrefetch) {
+      touch(A, B, I * BK, w, lane);
+      prologue<I + 1>(A, B, base, w, lane);
     }
   }
 
   __device__ __forceinline__ static void run(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
-                                             const Operand& B, int K) {
+                                             const Operand& B, int K, PrefetchShare pa,
+                                             PrefetchShare pb) {
     const Stages stages = stage_arrays();
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 #pragma unroll
     for (int mi = 0; mi < C::kMI; ++mi)
 #pragma unroll
@@ -672,9 +761,11 @@ struct DirectLoop {
     DirectLoop L;
     L.a.init(A, w, lane);
     L.b.init(B, w, lane);
-    L.prologue<0>(A, B, stages, w);
-    // stage 0 landed: kDStages - 2 later stages may still be in flight
-    wait_vmcnt_lgkm0<(kDStages - 2) * kLoads>();
+    L.pa = pa;
+    L.pb = pb;
+    L.prologue<0>(A, B, stages, w, lane);
+    // stage 0 landed: the later stages and the prologue's touches may still be in flight
+    wait_vmcnt_lgkm0<(kDStages - 1) * kLoads + (kDPrefetch - kDStages)>();
     raw_barrier();
     u32x4_t f0a[C::kMI], f0b[C::kNI];
     frags(f0a, f0b, stages.s[0], 0, lane);
@@ -693,9 +784,10 @@ struct DirectLoop {
 // acc = A[tile, 0:K] . B[tile, 0:K]^T for one 256 x 256 tile.
 template <class P, class C, bool A_MC, bool B_MC>
 __device__ __forceinline__ void gemm_tile(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
-                                          const Operand& B, int K) {
+                                          const Operand& B, int K, PrefetchShare pa,
+                                          PrefetchShare pb) {
   if constexpr (FKL_DIRECT_LDS && P::kBytes == 2)
-    DirectLoop<C, A_MC, B_MC>::run(acc, A, B, K);
+    DirectLoop<C, A_MC, B_MC>::run(acc, A, B, K, pa, pb);
   else
     TileLoop<P, C, A_MC, B_MC>::run(acc, A, B, 0, K);
 }
@@ -723,6 +815,17 @@ struct TileGroups {
     *tm = gm_i * GA + (j % GA);
     *tn = gn_i * GB + (j / GA);
     return *tm < mt && *tn < nt;
+  }
+  // The GB workgroups of a group that read one A tile split its lines by
+  // their position along B, and the GA that read one B tile split by their
+  // position along A, so each line of the group is touched once.
+  __device__ __forceinline__ static PrefetchShare share_a() {
+    const int j = static_cast<int>((blockIdx.x >> 3) & 31);
+    return PrefetchShare{(j / GA) * (256 / GB), 256 / GB};
+  }
+  __device__ __forceinline__ static PrefetchShare share_b() {
+    const int j = static_cast<int>((blockIdx.x >> 3) & 31);
+    return PrefetchShare{(j % GA) * (256 / GA), 256 / GA};
   }
 };
 

@@ -71,7 +71,8 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_logits_lse(
   const Operand A = make_operand(W + vt * kBM * ld, ld, V - vt * kBM, d);
   const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
+  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d),
+                             TileGroups<4, 8>::share_a(), TileGroups<4, 8>::share_b());
 
   const int lane = threadIdx.x & 63;
   const int64_t v0 = vt * kBM + C::wave_m() * C::kWM;
@@ -287,7 +288,8 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_gprod(
   const Operand A = make_operand(W + vbase * ld, ld, V - vbase, d);
   const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
+  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d),
+                             TileGroups<4, 8>::share_a(), TileGroups<4, 8>::share_b());
 
   const int lane = threadIdx.x & 63;
   const int64_t w0 = vt * kBM + C::wave_m() * C::kWM;  // slice-relative column of the wave
@@ -365,7 +367,8 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_grad_hidden
   const Operand A = make_operand(G + tt * kBM * gld, gld, nrows - tt * kBM, Vw);
   const Operand B = make_operand(W + dt * kBN * P::kBytes, wld, d - dt * kBN, Vlim);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, false, true>(acc, A, B, static_cast<int>(Vw));
+  gemm_tile<P, C, false, true>(acc, A, B, static_cast<int>(Vw),
+                             TileGroups<8, 4>::share_a(), TileGroups<8, 4>::share_b());
 
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -415,7 +418,8 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_grad_w(
   const Operand A = make_operand(G + vt * kBM * P::kBytes, gpitch * P::kBytes, Vw - vt * kBM, nrows);
   const Operand B = make_operand(H + dt * kBN * P::kBytes, d * P::kBytes, d - dt * kBN, nrows);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, true, true>(acc, A, B, static_cast<int>(nrows));
+  gemm_tile<P, C, true, true>(acc, A, B, static_cast<int>(nrows),
+                             TileGroups<8, 4>::share_a(), TileGroups<8, 4>::share_b());
 
   const int lane = threadIdx.x & 63;
 #pragma unroll
