@@ -407,11 +407,13 @@ struct TileLoop {
 //    chunks of row r are XOR-swizzled by (r / 2) % 8, so the 16 rows one
 //    256-byte (64-bank) LDS cycle serves land on 16 distinct chunk positions.
 //    Fragments are one ds_read_b128.
-//  * mn-major (stored [k][mn]): 64 k-rows of 512 bytes; the 32 chunks of k-row
-//    k are XOR-swizzled by 4 * (k % 4). Fragments are two ds_read_b64_tr_b16:
-//    within a group of 16 lanes, source lane s reads k-row kb + s/4 at
-//    mn = base + 4*(s%4) and lane j receives the 4 k-values of mn = base + j,
-//    so two reads give each lane the same 8 consecutive k as the k-major path.
+//  * mn-major (stored [k][mn]): two halves of 128 mn values, each 64 k-rows of
+//    256 bytes (so one 1 KiB load holds four k-rows of one half); the 16
+//    chunks of k-row k are XOR-swizzled by 4 * (k % 4). Fragments are two
+//    ds_read_b64_tr_b16: within a group of 16 lanes, source lane s reads k-row
+//    kb + s/4 at mn = base + 4*(s%4) and lane j receives the 4 k-values of
+//    mn = base + j, so two reads give each lane the same 8 consecutive k as
+//    the k-major path.
 // Both swizzles make the fragment reads bank-conflict free.
 // Lines [first, first + count) of an operand's 256-line stage that one
 // workgroup touches ahead of time; the workgroups sharing an operand tile
@@ -489,30 +491,38 @@ __device__ __forceinline__ void dma_touch4(const u32x4_t& words, uint32_t voff, 
 
 // One operand of the direct pipeline: per-lane byte offsets of its 1 KiB
 // load blocks and the k index each lane's chunk starts at.
+// The 32 blocks of 1 KiB of an operand's stage: k-major, block b holds rows
+// 8b .. 8b+7; mn-major, block b holds k-rows 4(b%16) .. 4(b%16)+3 of half b/16.
+// A wave moves NINST consecutive blocks starting at `base`.
 template <bool MC, int NINST>
 struct DirectOperand {
   uint32_t off[NINST];  // offset at stage k0 = 0 (kOOB if the lane's mn is invalid)
   int kk[NINST];        // k of the lane's data within a stage
+  int base;             // first block (wave-uniform)
 
-  __device__ __forceinline__ void init(const Operand& op, int w, int lane) {
+  __device__ __forceinline__ void init(const Operand& op, int w, int lane, int blk0 = 0) {
+    base = blk0 + w * NINST;
 #pragma unroll
     for (int j = 0; j < NINST; ++j) {
-      const int blk = w * NINST + j;
+      const int blk = base + j;
       if constexpr (!MC) {
         const int row = blk * 8 + (lane >> 3);
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         kk[j] = c * 8;
         off[j] = row < op.mn_count ? static_cast<uint32_t>(row) * op.ld + c * 16 : kOOB;
       } else {
-        const int krow = blk * 2 + (lane >> 5);
-        const int c = (lane & 31) ^ (4 * (krow & 3));
+        const int half = blk >> 4;
+        const int krow = 4 * (blk & 15) + (lane >> 4);
+        const int c = (lane & 15) ^ (4 * (krow & 3));
         kk[j] = krow;
-        off[j] = c * 8 < op.mn_count ? static_cast<uint32_t>(krow) * op.ld + c * 16 : kOOB;
+        off[j] = half * 128 + c * 8 < op.mn_count
+                     ? static_cast<uint32_t>(krow) * op.ld + half * 256 + c * 16
+                     : kOOB;
       }
     }
   }
 
-  __device__ __forceinline__ void issue(const Operand& op, int k0, unsigned char* dst, int w) const {
+  __device__ __forceinline__ void issue(const Operand& op, int k0, unsigned char* dst) const {
 #pragma unroll
     for (int j = 0; j < NINST; ++j) {
       uint32_t o;
@@ -521,7 +531,7 @@ struct DirectOperand {
       else
         o = (off[j] != kOOB && k0 + kk[j] < op.k_lim) ? off[j] + static_cast<uint32_t>(k0) * op.ld
                                                        : kOOB;
-      dma_load16(op.words, o, dst + (w * NINST + j) * 1024);
+      dma_load16(op.words, o, dst + (base + j) * 1024);
     }
   }
 
@@ -548,14 +558,16 @@ struct DirectOperand {
     } else {
       const int g = lane >> 4, sl = lane & 15;
       const int mn = mn0 + 16 * (g & 1) + 4 * (sl & 3);
+      const unsigned char* hsrc = src + (mn >> 7) * (kDOperandBytes / 2);
+      const int mh = mn & 127;
       const int kb = 16 * s + 8 * (g >> 1) + (sl >> 2);
       u32x4_t r;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int k = kb + 4 * h;
-        const int c = (mn >> 3) ^ (4 * (k & 3));
+        const int c = (mh >> 3) ^ (4 * (k & 3));
         const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16_t*)(src + k * 512 + c * 16 + (mn & 7) * 2));
+            (__attribute__((address_space(3))) v4i16_t*)(hsrc + k * 256 + c * 16 + (mh & 7) * 2));
         typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
         const u32x2_t u = __builtin_bit_cast(u32x2_t, v);
         r[2 * h] = u[0];
@@ -585,8 +597,9 @@ struct DirectLoop {
 
   __device__ __forceinline__ void issue(const Operand& A, const Operand& B, int k0,
                                         unsigned char* stage, int w) const {
-    a.issue(A, k0, stage, w);
-    b.issue(B, k0, stage + kDOperandBytes, w);
+    (void)w;
+    a.issue(A, k0, stage);
+    b.issue(B, k0, stage + kDOperandBytes);
   }
 
   // Touch this workgroup's share of the lines of the stage starting at k0:
@@ -628,15 +641,20 @@ struct DirectLoop {
       for (int ni = 0; ni < C::kNI; ++ni) mfma_16B<P>(acc[mi][ni], fa[mi], fb[ni]);
   }
 
-  // MFMAs evenly interleaved with NR LDS reads and NL global loads.
+  // MFMAs interleaved with NR LDS reads and NL global loads. With two waves
+  // per SIMD the reads are spread evenly (the other wave covers their
+  // latency); with one wave per SIMD they all go behind the first two MFMAs,
+  // so they land while the rest of the step runs.
+  static constexpr int kReadSpread = kWaves == 4 ? 2 : C::kMI * C::kNI;
   template <int NR, int NL>
   __device__ __forceinline__ static void interleave() {
     constexpr int kM = C::kMI * C::kNI;
+    constexpr int kR = kReadSpread;
 #pragma unroll
     for (int i = 0; i < kM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if ((i * NR) / kM != ((i + 1) * NR) / kM)
-        __builtin_amdgcn_sched_group_barrier(0x100, (NR + kM - 1) / kM, 0);
+      if (i < kR && (i * NR) / kR != ((i + 1) * NR) / kR)
+        __builtin_amdgcn_sched_group_barrier(0x100, (NR + kR - 1) / kR, 0);
       if ((i * NL) / kM != ((i + 1) * NL) / kM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -777,6 +795,180 @@ struct DirectLoop {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Ping-pong schedule for eight waves. The two waves that share a SIMD (w and
+// w + 4) sit in different groups, G0 = waves 0-3 and G1 = waves 4-7, which run
+// the same program one phase apart. A wave alternates LOAD (the fragments of
+// a k-block of two k-steps, LDS to registers, plus a quarter of a stage's DMA
+// traffic) and COMPUTE (that k-block's MFMAs at raised issue priority), with a
+// workgroup barrier between phases. While one wave of a SIMD computes, the
+// other loads, so the matrix pipe is fed in back-to-back bursts.
+//
+// Only loading waves issue DMA: a wave issues in order, and a DMA load stalls
+// at issue while the address unit is busy with earlier ones, so a computing
+// wave that issued DMA would starve its MFMAs. Each LOAD phase moves 16 KiB
+// (four 1 KiB loads per wave, after the fragment reads), about as long at the
+// address unit as the other group's MFMA burst.
+//
+// The LDS stages are those of DirectLoop (two 64 KiB slots of 64 values of K,
+// i.e. two k-blocks each). G0 loads k-block j in phase 2j and computes it in
+// 2j+1; G1 loads it in 2j+1 and computes it in 2j+2. G0 reads rows 0-127 of A
+// ("A-lo") and all of B, G1 rows 128-255 ("A-hi") and all of B. For stage s
+// the regions of its slot are last read in phase 4s+2 (A-lo) and 4s+3 (A-hi,
+// B), and stage s+2 is moved into them in four parts:
+//   phase 4s+3, G1: A-lo          phase 4s+4, G0: B rows 0-127 (+ G0's touch)
+//   phase 4s+5, G1: B rows 128-255 (+ G1's touch)   phase 4s+6, G0: A-hi
+// Stage s+2 is first read by G0 in phase 4s+8 and by G1 in 4s+9; each wave
+// waits for the parts it moved before the barrier that opens that phase (the
+// A-lo and B parts at the end of phase 4s+7, the A-hi part at the end of
+// 4s+8), counting the loads it issued after them.
+template <class C, bool A_MC, bool B_MC>
+struct PingPongLoop {
+  static_assert(C::kThreads == 512, "two groups of four waves");
+  typedef DirectLoop<C, A_MC, B_MC> D;
+  static constexpr int BK = D::BK;
+  static constexpr int kTouchLanes = 16;  // four waves x 16 lanes = 64 lines
+
+  __device__ __forceinline__ static void fence() { __builtin_amdgcn_sched_barrier(0); }
+  __device__ __forceinline__ static void phase_barrier() {
+    fence();
+    raw_barrier();
+    fence();
+  }
+
+  // What one group moves: G0 B rows 0-127 (p) and A rows 128-255 (q), G1 A
+  // rows 0-127 (p) and B rows 128-255 (q); G0 touches its share of B's lines,
+  // G1 its share of A's.
+  template <int G>
+  struct Stream {
+    static constexpr bool kPMC = G == 0 ? B_MC : A_MC;
+    static constexpr bool kQMC = G == 0 ? A_MC : B_MC;
+    DirectOperand<kPMC, 4> p;
+    DirectOperand<kQMC, 4> q;
+    PrefetchShare share;
+
+    __device__ __forceinline__ void init(const Operand& P, const Operand& Q, int wg, int lane) {
+      p.init(P, wg, lane, 0);
+      q.init(Q, wg, lane, 16);
+    }
+    __device__ __forceinline__ void touch(const Operand& P, int k0, int wg, int lane) const {
+      const int idx = wg * kTouchLanes + lane;
+      const bool valid = lane < kTouchLanes && idx < share.count;
+      dma_touch4(P.words,
+                 valid ? DirectOperand<kPMC, 4>::line_offset(P, k0, share.first + idx) : kOOB,
+                 D::scratch_lds());
+    }
+  };
+
+  // One k-block: R = j % 4 fixes the slot (stage parity) and the half.
+  // P and Q are the operands of the group's p and q parts.
+  template <int G, int R>
+  __device__ __forceinline__ static void block(f32x16_t (&acc)[C::kMI][C::kNI],
+                                               u32x4_t (&fa)[2][C::kMI], u32x4_t (&fb)[2][C::kNI],
+                                               const Stream<G>& str, const Operand& P,
+                                               const Operand& Q, const typename D::Stages& st,
+                                               int j, int wg, int lane) {
+    constexpr int h = R & 1, sp = R >> 1;
+    constexpr int kP = G == 0 ? kDOperandBytes : 0;  // slot offset of p's operand
+    constexpr int kQ = kDOperandBytes - kP;
+    const int s = j >> 1;
+    unsigned char* cur = st.s[sp];
+    unsigned char* other = st.s[1 - sp];
+    // LOAD(j)
+    D::frags(fa[0], fb[0], cur, 2 * h, lane);
+    D::frags(fa[1], fb[1], cur, 2 * h + 1, lane);
+    if constexpr (G == 0 && h == 0) {
+      if (j >= 2) {  // B rows 0-127 of stage s+1 (phase 4s'+4 for s' = s-1)
+        str.p.issue(P, (s + 1) * BK, other + kP);
+        str.touch(P, (s + 3) * BK, wg, lane);
+      }
+      wait_vmcnt_lgkm0<5>();  // A rows 128-255 of stage s landed
+    } else if constexpr (G == 0 && h == 1) {
+      str.q.issue(Q, (s + 1) * BK, other + kQ);  // A rows 128-255 of stage s+1
+      wait_vmcnt_lgkm0<63>();
+    } else if constexpr (G == 1 && h == 1) {
+      str.p.issue(P, (s + 2) * BK, cur + kP);  // A rows 0-127 of stage s+2
+      wait_vmcnt_lgkm0<5>();  // A rows 0-127 and B rows 128-255 of stage s+1 landed
+    } else {
+      if (j >= 2) {  // B rows 128-255 of stage s+1
+        str.q.issue(Q, (s + 1) * BK, other + kQ);
+        str.touch(P, (s + 3) * BK, wg, lane);
+      }
+      wait_vmcnt_lgkm0<63>();
+    }
+    phase_barrier();
+    // COMPUTE(j)
+    __builtin_amdgcn_s_setprio(1);
+    D::mfmas(acc, fa[0], fb[0]);
+    D::mfmas(acc, fa[1], fb[1]);
+    fence();
+    __builtin_amdgcn_s_setprio(0);
+    if constexpr (G == 0 && h == 1) wait_vmcnt_lgkm0<5>();  // B rows 0-127 of stage s+1 landed
+    phase_barrier();
+  }
+
+  template <int G>
+  __device__ __forceinline__ static void program(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& P,
+                                                 const Operand& Q, PrefetchShare share,
+                                                 const typename D::Stages& st, int nk, int wg,
+                                                 int lane) {
+    constexpr int kP = G == 0 ? kDOperandBytes : 0;
+    constexpr int kQ = kDOperandBytes - kP;
+    Stream<G> str;
+    str.init(P, Q, wg, lane);
+    str.share = share;
+    // prologue: stages 0 and 1, touches of stages 2 and 3
+    static_assert(kDPrefetch == 4, "the waits count two prologue touches");
+#pragma unroll
+    for (int t = 0; t < kDStages; ++t) {
+      str.p.issue(P, t * BK, st.s[t] + kP);
+      str.q.issue(Q, t * BK, st.s[t] + kQ);
+    }
+    str.touch(P, 2 * BK, wg, lane);
+    str.touch(P, 3 * BK, wg, lane);
+    // stage 0 landed: stage 1 (8 loads per wave) and the touches may still be in flight
+    wait_vmcnt_lgkm0<10>();
+    phase_barrier();
+    u32x4_t fa[2][C::kMI], fb[2][C::kNI];
+    if constexpr (G == 1) phase_barrier();  // G1 runs one phase behind
+    const int J = 2 * nk;
+    int j = 0;
+    for (; j + 4 <= J; j += 4) {
+      block<G, 0>(acc, fa, fb, str, P, Q, st, j, wg, lane);
+      block<G, 1>(acc, fa, fb, str, P, Q, st, j + 1, wg, lane);
+      block<G, 2>(acc, fa, fb, str, P, Q, st, j + 2, wg, lane);
+      block<G, 3>(acc, fa, fb, str, P, Q, st, j + 3, wg, lane);
+    }
+    if (j < J) {  // odd number of stages: one more in slot 0
+      block<G, 0>(acc, fa, fb, str, P, Q, st, j, wg, lane);
+      block<G, 1>(acc, fa, fb, str, P, Q, st, j + 1, wg, lane);
+    }
+    if constexpr (G == 0) phase_barrier();  // pairs with G1's last one
+  }
+
+  __device__ __forceinline__ static void run(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
+                                             const Operand& B, int K, PrefetchShare pa,
+                                             PrefetchShare pb) {
+    const typename D::Stages st = D::stage_arrays();
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+#pragma unroll
+    for (int mi = 0; mi < C::kMI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < C::kNI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+    const int nk = (K + BK - 1) / BK;
+    if (nk <= 0) return;
+    if (w < 4)
+      program<0>(acc, B, A, pb, st, nk, w, lane);  // G0: p = B rows 0-127, q = A rows 128-255
+    else
+      program<1>(acc, A, B, pa, st, nk, w - 4, lane);  // G1: p = A rows 0-127, q = B rows 128-255
+    // drain the out-of-range loads before the LDS is reused
+    wait_vmcnt_lgkm0<0>();
+  }
+};
+
 #ifndef FKL_DIRECT_LDS
 #define FKL_DIRECT_LDS 1
 #endif
@@ -786,7 +978,9 @@ template <class P, class C, bool A_MC, bool B_MC>
 __device__ __forceinline__ void gemm_tile(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
                                           const Operand& B, int K, PrefetchShare pa,
                                           PrefetchShare pb) {
-  if constexpr (FKL_DIRECT_LDS && P::kBytes == 2)
+  if constexpr (FKL_DIRECT_LDS && P::kBytes == 2 && C::kThreads == 512)
+    PingPongLoop<C, A_MC, B_MC>::run(acc, A, B, K, pa, pb);
+  else if constexpr (FKL_DIRECT_LDS && P::kBytes == 2)
     DirectLoop<C, A_MC, B_MC>::run(acc, A, B, K, pa, pb);
   else
     TileLoop<P, C, A_MC, B_MC>::run(acc, A, B, 0, K);
