@@ -387,48 +387,29 @@ struct TileLoop {
 // Global data goes straight into LDS with buffer_load ... lds (16 bytes per
 // lane, one 1 KiB block per wave instruction), so no registers hold staged
 // data. A stage holds 64 values of K for all 256 rows of both operands
-// (64 KiB); kDStages = 2 stages fill 128 KiB of LDS. A stage is consumed in
-// four k-steps of 16; the fragments of step s+1 are read while the MFMAs of
-// step s run. After the fragments of the stage's last step are in registers,
-// one barrier per stage both releases the slot (every wave has read it) and
-// publishes the next stage (every wave waited for its own loads of it with
-// s_waitcnt first; the barrier carries no memory fence, which would drain
-// every load in flight). The released slot is refilled at once with the stage
-// kDStages ahead, whose loads run behind the MFMAs of the last step and the
-// whole next stage. Stages past K read out of range, which returns zeros
-// into a slot nobody reads, so the loop has no branches around the loads.
+// (64 KiB); two stages fill 128 KiB of LDS. Each DMA instruction moves whole
+// 128-byte lines: the L1 path into LDS serves one cache line per clock, so a
+// row segment of 64 bytes per line would halve its throughput. Loads past K
+// or past the operand read out of range, which returns zeros, so tails need
+// no branches.
 //
-// Each DMA instruction moves whole 128-byte lines: on this chip the L1 path
-// into LDS serves one cache line per clock, so a row segment of 64 bytes per
-// line would halve its throughput.
-//
-// Stage layout of one operand (32 KiB):
-//  * k-major (stored [mn][k]): 256 rows of 128 bytes; the eight 16-byte
-//    chunks of row r are XOR-swizzled by (r / 2) % 8, so the 16 rows one
-//    256-byte (64-bank) LDS cycle serves land on 16 distinct chunk positions.
-//    Fragments are one ds_read_b128.
+// Stage layout of one operand (32 KiB, 32 blocks of 1 KiB):
+//  * k-major (stored [mn][k]): 256 rows of 128 bytes, block b = rows 8b..8b+7;
+//    the eight 16-byte chunks of row r are XOR-swizzled by (r / 2) % 8, so the
+//    16 rows one 256-byte (64-bank) LDS cycle serves land on 16 distinct chunk
+//    positions. Fragments are one ds_read_b128.
 //  * mn-major (stored [k][mn]): two halves of 128 mn values, each 64 k-rows of
-//    256 bytes (so one 1 KiB load holds four k-rows of one half); the 16
+//    256 bytes, block b = k-rows 4(b%16)..4(b%16)+3 of half b/16; the 16
 //    chunks of k-row k are XOR-swizzled by 4 * (k % 4). Fragments are two
 //    ds_read_b64_tr_b16: within a group of 16 lanes, source lane s reads k-row
 //    kb + s/4 at mn = base + 4*(s%4) and lane j receives the 4 k-values of
 //    mn = base + j, so two reads give each lane the same 8 consecutive k as
 //    the k-major path.
 // Both swizzles make the fragment reads bank-conflict free.
-// Lines [first, first + count) of an operand's 256-line stage that one
-// workgroup touches ahead of time; the workgroups sharing an operand tile
-// split its lines between them.
-struct PrefetchShare {
-  int first;
-  int count;
-};
-
 constexpr int kDRowBytes = 128;
 constexpr int kDStages = 2;
-constexpr int kDPrefetch = 4;  // a stage's lines are touched this many stages before use
-constexpr int kDSteps = kDRowBytes / 32;                // k-steps of 16 per stage
-constexpr int kDOperandBytes = 256 * kDRowBytes;       // 32 KiB
-constexpr int kDStageBytes = 2 * kDOperandBytes;        // 64 KiB
+constexpr int kDOperandBytes = 256 * kDRowBytes;  // 32 KiB
+constexpr int kDStageBytes = 2 * kDOperandBytes;   // 64 KiB
 
 __device__ __forceinline__ void raw_barrier() {
   __asm__ volatile("" ::: "memory");
@@ -446,17 +427,17 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
-// The DMA loads below set M0 themselves. The compiler treats M0 as reserved
-// and warns that clobbering it is not preserved; that is intended: it only
-// writes M0 immediately before an instruction that reads it, and on gfx950
-// no instruction these kernels compile to reads M0 except these loads.
+// The DMA load below sets M0 itself. The compiler treats M0 as reserved and
+// warns that clobbering it is not preserved; that is intended: it only writes
+// M0 immediately before an instruction that reads it, and on gfx950 no
+// instruction these kernels compile to reads M0 except these loads.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 
 // One 1 KiB LDS DMA load: lane l's 16 bytes at byte offset voff of the buffer
 // go to LDS address lds + 16*l. Written as inline asm so that the compiler's
 // wait-count insertion does not see it: it would otherwise guard LDS reads it
-// cannot disambiguate from the DMA target with vmcnt(0), draining every stage
+// cannot disambiguate from the DMA target with vmcnt(0), draining every load
 // in flight. The pipeline places all vmcnt waits for these loads explicitly.
 // The load writes no registers; M0 is set (plus the required wait state) in
 // the same block.
@@ -472,35 +453,18 @@ __device__ __forceinline__ void dma_load16(const u32x4_t& words, uint32_t voff, 
       : "memory", "m0");
 }
 
-// L2 prefetch: one dword per lane (64 distinct 128-byte lines per wave
-// instruction) is loaded into a scratch LDS area nobody reads, so lines that
-// miss in L2 are requested stages before the real loads need them.
-__device__ __forceinline__ void dma_touch4(const u32x4_t& words, uint32_t voff, const void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)lds)));
-  __asm__ volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %0, %1, 0 offen lds"
-      :
-      : "v"(voff), "s"(words), "s"(m0)
-      : "memory", "m0");
-}
-
 #pragma clang diagnostic pop
 
-// One operand of the direct pipeline: per-lane byte offsets of its 1 KiB
-// load blocks and the k index each lane's chunk starts at.
-// The 32 blocks of 1 KiB of an operand's stage: k-major, block b holds rows
-// 8b .. 8b+7; mn-major, block b holds k-rows 4(b%16) .. 4(b%16)+3 of half b/16.
-// A wave moves NINST consecutive blocks starting at `base`.
+// NINST consecutive blocks of one operand's stage, starting at block `base`,
+// moved by one wave: per-lane byte offsets (at k0 = 0) and the k each lane's
+// chunk starts at.
 template <bool MC, int NINST>
 struct DirectOperand {
   uint32_t off[NINST];  // offset at stage k0 = 0 (kOOB if the lane's mn is invalid)
   int kk[NINST];        // k of the lane's data within a stage
   int base;             // first block (wave-uniform)
 
-  __device__ __forceinline__ void init(const Operand& op, int w, int lane, int blk0 = 0) {
+  __device__ __forceinline__ void init(const Operand& op, int w, int lane, int blk0) {
     base = blk0 + w * NINST;
 #pragma unroll
     for (int j = 0; j < NINST; ++j) {
@@ -522,6 +486,7 @@ struct DirectOperand {
     }
   }
 
+  // Loads of the stage starting at k0 into the operand region at dst.
   __device__ __forceinline__ void issue(const Operand& op, int k0, unsigned char* dst) const {
 #pragma unroll
     for (int j = 0; j < NINST; ++j) {
@@ -532,20 +497,6 @@ struct DirectOperand {
         o = (off[j] != kOOB && k0 + kk[j] < op.k_lim) ? off[j] + static_cast<uint32_t>(k0) * op.ld
                                                        : kOOB;
       dma_load16(op.words, o, dst + (base + j) * 1024);
-    }
-  }
-
-  // Byte offset of line `line` (0..255) of the stage starting at k0, or kOOB.
-  __device__ __forceinline__ static uint32_t line_offset(const Operand& op, int k0, int line) {
-    if constexpr (!MC) {
-      return (line < op.mn_count && k0 < op.k_lim)
-                 ? static_cast<uint32_t>(line) * op.ld + static_cast<uint32_t>(k0) * 2
-                 : kOOB;
-    } else {
-      const int krow = line >> 2, seg = line & 3;
-      return (seg * 64 < op.mn_count && k0 + krow < op.k_lim)
-                 ? static_cast<uint32_t>(k0 + krow) * op.ld + seg * 128
-                 : kOOB;
     }
   }
 
@@ -578,132 +529,48 @@ struct DirectOperand {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Ping-pong k-loop (eight waves, 128 x 64 outputs each). The two waves that
+// share a SIMD (w and w + 4) sit in different groups, G0 = waves 0-3 and
+// G1 = waves 4-7, which run the same program one phase apart. A wave
+// alternates LOAD (the fragments of a k-block of two k-steps, LDS to
+// registers, plus a quarter of a stage's DMA traffic) and COMPUTE (that
+// k-block's 16 MFMAs at raised issue priority), with a workgroup barrier
+// between phases. While one wave of a SIMD computes, the other loads, so the
+// matrix pipe is fed in back-to-back bursts.
+//
+// Only loading waves issue DMA: a wave issues in order, and a DMA load stalls
+// at issue while the address unit is busy with earlier ones, so a computing
+// wave that issued DMA would starve its MFMAs. Each LOAD phase moves 16 KiB
+// (four 1 KiB loads per wave, after the fragment reads), about as long at the
+// address unit as the other group's MFMA burst.
+//
+// G0 loads k-block j in phase 2j and computes it in 2j+1; G1 loads it in 2j+1
+// and computes it in 2j+2; stage s holds k-blocks 2s and 2s+1 in slot s % 2.
+// G0 reads rows 0-127 of A ("A-lo") and all of B, G1 rows 128-255 ("A-hi")
+// and all of B, so for stage s the slot's A-lo is last read in phase 4s+2 and
+// the rest in 4s+3. Stage s+2 is moved into the slot in four parts:
+//   phase 4s+3, G1: A-lo            phase 4s+4, G0: B rows 0-127
+//   phase 4s+5, G1: B rows 128-255  phase 4s+6, G0: A-hi
+// Stage s+2 is first read by G0 in phase 4s+8 and by G1 in 4s+9; each wave
+// waits for the parts it moved before the barrier that opens that phase (A-lo
+// and B at the end of phase 4s+7, A-hi at the end of 4s+8), counting the four
+// loads it issued after them (the hardware returns loads in order). The
+// barriers carry no memory fence, which would drain every load in flight.
 template <class C, bool A_MC, bool B_MC>
-struct DirectLoop {
-  typedef BF16 P;
-  static constexpr int BK = kDRowBytes / 2;  // 64 bf16 per stage
-  static constexpr int kWaves = C::kThreads / 64;
-  static constexpr int kInst = kDOperandBytes / 1024 / kWaves;  // 1 KiB loads per wave and operand
-  static constexpr int kLoads = 2 * kInst;
-  // Every wave issues one L2 touch per iteration, after its stage loads, so at
-  // the barrier only the previous iteration's touch may still be in flight.
-  static constexpr int kInFlight = 1;
-  static_assert(kDStages == 2 && kDPrefetch >= kDStages, "pipeline accounting");
-  static constexpr int kTouchLanes = 128 / kWaves;  // lanes per wave; half the waves per operand
+struct PingPongLoop {
+  static_assert(C::kThreads == 512 && C::kWavesM == 2, "two groups of four waves");
+  static constexpr int BK = kDRowBytes / 2;  // 64 bf16 of K per stage
 
-  DirectOperand<A_MC, kInst> a;
-  DirectOperand<B_MC, kInst> b;
-  PrefetchShare pa, pb;
-
-  __device__ __forceinline__ void issue(const Operand& A, const Operand& B, int k0,
-                                        unsigned char* stage, int w) const {
-    (void)w;
-    a.issue(A, k0, stage);
-    b.issue(B, k0, stage + kDOperandBytes);
-  }
-
-  // Touch this workgroup's share of the lines of the stage starting at k0:
-  // the first half of the waves covers the A share, the second half the B
-  // share (up to 64 lines each). Waves with nothing to touch issue the load
-  // out of range, so every wave issues exactly one per iteration.
-  __device__ __forceinline__ void touch(const Operand& A, const Operand& B, int k0, int w,
-                                        int lane) const {
-    const bool is_a = w < kWaves / 2;  // wave-uniform
-    const int idx = (w % (kWaves / 2)) * kTouchLanes + lane;
-    const PrefetchShare sh = is_a ? pa : pb;
-    const bool valid = lane < kTouchLanes && idx < sh.count;
-    unsigned char* scratch = scratch_lds();
-    if (is_a)
-      dma_touch4(A.words, valid ? DirectOperand<A_MC, kInst>::line_offset(A, k0, sh.first + idx) : kOOB,
-                 scratch);
-    else
-      dma_touch4(B.words, valid ? DirectOperand<B_MC, kInst>::line_offset(B, k0, sh.first + idx) : kOOB,
-                 scratch);
-  }
-
-  __device__ __forceinline__ static void frags(u32x4_t (&fa)[C::kMI], u32x4_t (&fb)[C::kNI],
-                                               const unsigned char* stage, int s, int lane) {
-#pragma unroll
-    for (int mi = 0; mi < C::kMI; ++mi)
-      fa[mi] = DirectOperand<A_MC, kInst>::frag(stage, C::wave_m() * C::kWM + mi * 32, s, lane);
-#pragma unroll
-    for (int ni = 0; ni < C::kNI; ++ni)
-      fb[ni] = DirectOperand<B_MC, kInst>::frag(stage + kDOperandBytes,
-                                                C::wave_n() * C::kWN + ni * 32, s, lane);
-  }
-
-  __device__ __forceinline__ static void mfmas(f32x16_t (&acc)[C::kMI][C::kNI],
-                                               const u32x4_t (&fa)[C::kMI],
-                                               const u32x4_t (&fb)[C::kNI]) {
-#pragma unroll
-    for (int mi = 0; mi < C::kMI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < C::kNI; ++ni) mfma_16B<P>(acc[mi][ni], fa[mi], fb[ni]);
-  }
-
-  // MFMAs interleaved with NR LDS reads and NL global loads. With two waves
-  // per SIMD the reads are spread evenly (the other wave covers their
-  // latency); with one wave per SIMD they all go behind the first two MFMAs,
-  // so they land while the rest of the step runs.
-  static constexpr int kReadSpread = kWaves == 4 ? 2 : C::kMI * C::kNI;
-  template <int NR, int NL>
-  __device__ __forceinline__ static void interleave() {
-    constexpr int kM = C::kMI * C::kNI;
-    constexpr int kR = kReadSpread;
-#pragma unroll
-    for (int i = 0; i < kM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < kR && (i * NR) / kR != ((i + 1) * NR) / kR)
-        __builtin_amdgcn_sched_group_barrier(0x100, (NR + kR - 1) / kR, 0);
-      if ((i * NL) / kM != ((i + 1) * NL) / kM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  static constexpr int kReads = (A_MC ? 2 : 1) * C::kMI + (B_MC ? 2 : 1) * C::kNI;
-
-  // Steps s .. kDSteps - 2 of the stage in `cur`: read the fragments of step
-  // s + 1 while the MFMAs of step s run (even steps use set 0, odd steps set 1).
-  template <int S>
-  __device__ __forceinline__ static void steps(f32x16_t (&acc)[C::kMI][C::kNI],
-                                               u32x4_t (&f0a)[C::kMI], u32x4_t (&f0b)[C::kNI],
-                                               u32x4_t (&f1a)[C::kMI], u32x4_t (&f1b)[C::kNI],
-                                               const unsigned char* cur, int lane) {
-    if constexpr (S + 1 < kDSteps) {
-      if constexpr (S % 2 == 0) {
-        frags(f1a, f1b, cur, S + 1, lane);
-        mfmas(acc, f0a, f0b);
-      } else {
-        frags(f0a, f0b, cur, S + 1, lane);
-        mfmas(acc, f1a, f1b);
-      }
-      interleave<kReads, 0>();
-      steps<S + 1>(acc, f0a, f0b, f1a, f1b, cur, lane);
-    }
-  }
-
-  // Stage kt in slot `cur`, stage kt+1 in `nxt`; `cur` is refilled with stage
-  // kt + kDStages once every wave has read it.
-  __device__ __forceinline__ void iter(f32x16_t (&acc)[C::kMI][C::kNI], u32x4_t (&f0a)[C::kMI],
-                                       u32x4_t (&f0b)[C::kNI], const Operand& A, const Operand& B,
-                                       unsigned char* cur, const unsigned char* nxt, int kt, int w,
-                                       int lane) const {
-    static_assert(kDSteps % 2 == 0, "the last step of a stage uses fragment set 1");
-    u32x4_t f1a[C::kMI], f1b[C::kNI];
-    steps<0>(acc, f0a, f0b, f1a, f1b, cur, lane);
-    wait_vmcnt_lgkm0<kInFlight>();
+  __device__ __forceinline__ static void fence() { __builtin_amdgcn_sched_barrier(0); }
+  __device__ __forceinline__ static void phase_barrier() {
+    fence();
     raw_barrier();
-    issue(A, B, (kt + kDStages) * BK, cur, w);
-    touch(A, B, (kt + kDPrefetch) * BK, w, lane);
-    frags(f0a, f0b, nxt, 0, lane);
-    mfmas(acc, f1a, f1b);
-    interleave<kReads, kLoads + 1>();
+    fence();
   }
 
-  // The stages live in distinct __shared__ arrays (selected at compile time
-  // through the unrolled slot index): with one array the compiler cannot tell
-  // which in-flight LDS DMA a transpose read may alias and drains them all
-  // (vmcnt(0)) before it.
+  // The stages live in distinct __shared__ arrays (the slot is a compile-time
+  // index of the unrolled loop).
   struct Stages {
     unsigned char* s[kDStages];
   };
@@ -717,147 +584,34 @@ struct DirectLoop {
     return r;
   }
 
-  __device__ __forceinline__ static unsigned char* scratch_lds() {
-    __shared__ __attribute__((aligned(256))) unsigned char pf_scratch[256];
-    return pf_scratch;
+  __device__ __forceinline__ static void frags(u32x4_t (&fa)[C::kMI], u32x4_t (&fb)[C::kNI],
+                                               const unsigned char* stage, int s, int lane) {
+#pragma unroll
+    for (int mi = 0; mi < C::kMI; ++mi)
+      fa[mi] = DirectOperand<A_MC, 1>::frag(stage, C::wave_m() * C::kWM + mi * 32, s, lane);
+#pragma unroll
+    for (int ni = 0; ni < C::kNI; ++ni)
+      fb[ni] = DirectOperand<B_MC, 1>::frag(stage + kDOperandBytes,
+                                            C::wave_n() * C::kWN + ni * 32, s, lane);
   }
 
-  template <int I>
-  __device__ __forceinline__ static unsigned char* slot(const Stages& st) {
-    return st.s[I % kDStages];
-  }
-
-  template <int I>
-  __device__ __forceinline__ void unrolled(f32x16_t (&acc)[C::kMI][C::kNI], u32x4_t (&f0a)[C::kMI],
-                                           u32x4_t (&f0b)[C::kNI], const Operand& A,
-                                           const Operand& B, const Stages& base, int kt, int w,
-                                           int lane) const {
-    if constexpr (I < kDStages) {
-      iter(acc, f0a, f0b, A, B, slot<I>(base), slot<I + 1>(base), kt + I, w, lane);
-      unrolled<I + 1>(acc, f0a, f0b, A, B, base, kt, w, lane);
-    }
-  }
-
-  template <int I>
-  __device__ __forceinline__ void tail(f32x16_t (&acc)[C::kMI][C::kNI], u32x4_t (&f0a)[C::kMI],
-                                       u32x4_t (&f0b)[C::kNI], const Operand& A, const Operand& B,
-                                       const Stages& base, int kt, int nk, int w, int lane) const {
-    if constexpr (I + 1 < kDStages) {
-      if (kt + I < nk) {
-        iter(acc, f0a, f0b, A, B, slot<I>(base), slot<I + 1>(base), kt + I, w, lane);
-        tail<I + 1>(acc, f0a, f0b, A, B, base, kt, nk, w, lane);
-      }
-    }
-  }
-
-  template <int I>
-  __device__ __forceinline__ void prologue(const Operand& A, const Operand& B, const Stages& base,
-                                           int w, int lane) const {
-    if constexpr (I < kDStages) {
-      issue(A, B, I * BK, slot<I>(base), w);
-      prologue<I + 1>(A, B, base, w, lane);
-    } else if constexpr (I < kDPrefetch) {
-      touch(A, B, I * BK, w, lane);
-      prologue<I + 1>(A, B, base, w, lane);
-    }
-  }
-
-  __device__ __forceinline__ static void run(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
-                                             const Operand& B, int K, PrefetchShare pa,
-                                             PrefetchShare pb) {
-    const Stages stages = stage_arrays();
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  __device__ __forceinline__ static void mfmas(f32x16_t (&acc)[C::kMI][C::kNI],
+                                               const u32x4_t (&fa)[C::kMI],
+                                               const u32x4_t (&fb)[C::kNI]) {
 #pragma unroll
     for (int mi = 0; mi < C::kMI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < C::kNI; ++ni)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-    const int nk = (K + BK - 1) / BK;
-    if (nk <= 0) return;
-    DirectLoop L;
-    L.a.init(A, w, lane);
-    L.b.init(B, w, lane);
-    L.pa = pa;
-    L.pb = pb;
-    L.prologue<0>(A, B, stages, w, lane);
-    // stage 0 landed: the later stages and the prologue's touches may still be in flight
-    wait_vmcnt_lgkm0<(kDStages - 1) * kLoads + (kDPrefetch - kDStages)>();
-    raw_barrier();
-    u32x4_t f0a[C::kMI], f0b[C::kNI];
-    frags(f0a, f0b, stages.s[0], 0, lane);
-    int kt = 0;
-    for (; kt + kDStages <= nk; kt += kDStages) L.unrolled<0>(acc, f0a, f0b, A, B, stages, kt, w, lane);
-    L.tail<0>(acc, f0a, f0b, A, B, stages, kt, nk, w, lane);
-    // drain the out-of-range loads before the LDS is reused
-    wait_vmcnt_lgkm0<0>();
-  }
-};
-
-// ---------------------------------------------------------------------------
-// Ping-pong schedule for eight waves. The two waves that share a SIMD (w and
-// w + 4) sit in different groups, G0 = waves 0-3 and G1 = waves 4-7, which run
-// the same program one phase apart. A wave alternates LOAD (the fragments of
-// a k-block of two k-steps, LDS to registers, plus a quarter of a stage's DMA
-// traffic) and COMPUTE (that k-block's MFMAs at raised issue priority), with a
-// workgroup barrier between phases. While one wave of a SIMD computes, the
-// other loads, so the matrix pipe is fed in back-to-back bursts.
-//
-// Only loading waves issue DMA: a wave issues in order, and a DMA load stalls
-// at issue while the address unit is busy with earlier ones, so a computing
-// wave that issued DMA would starve its MFMAs. Each LOAD phase moves 16 KiB
-// (four 1 KiB loads per wave, after the fragment reads), about as long at the
-// address unit as the other group's MFMA burst.
-//
-// The LDS stages are those of DirectLoop (two 64 KiB slots of 64 values of K,
-// i.e. two k-blocks each). G0 loads k-block j in phase 2j and computes it in
-// 2j+1; G1 loads it in 2j+1 and computes it in 2j+2. G0 reads rows 0-127 of A
-// ("A-lo") and all of B, G1 rows 128-255 ("A-hi") and all of B. For stage s
-// the regions of its slot are last read in phase 4s+2 (A-lo) and 4s+3 (A-hi,
-// B), and stage s+2 is moved into them in four parts:
-//   phase 4s+3, G1: A-lo          phase 4s+4, G0: B rows 0-127 (+ G0's touch)
-//   phase 4s+5, G1: B rows 128-255 (+ G1's touch)   phase 4s+6, G0: A-hi
-// Stage s+2 is first read by G0 in phase 4s+8 and by G1 in 4s+9; each wave
-// waits for the parts it moved before the barrier that opens that phase (the
-// A-lo and B parts at the end of phase 4s+7, the A-hi part at the end of
-// 4s+8), counting the loads it issued after them.
-template <class C, bool A_MC, bool B_MC>
-struct PingPongLoop {
-  static_assert(C::kThreads == 512, "two groups of four waves");
-  typedef DirectLoop<C, A_MC, B_MC> D;
-  static constexpr int BK = D::BK;
-  static constexpr int kTouchLanes = 16;  // four waves x 16 lanes = 64 lines
-
-  __device__ __forceinline__ static void fence() { __builtin_amdgcn_sched_barrier(0); }
-  __device__ __forceinline__ static void phase_barrier() {
-    fence();
-    raw_barrier();
-    fence();
+      for (int ni = 0; ni < C::kNI; ++ni) mfma_16B<BF16>(acc[mi][ni], fa[mi], fb[ni]);
   }
 
-  // What one group moves: G0 B rows 0-127 (p) and A rows 128-255 (q), G1 A
-  // rows 0-127 (p) and B rows 128-255 (q); G0 touches its share of B's lines,
-  // G1 its share of A's.
+  // What one group moves, four blocks per wave each: G0 B rows 0-127 (p) and
+  // A rows 128-255 (q), G1 A rows 0-127 (p) and B rows 128-255 (q).
   template <int G>
   struct Stream {
-    static constexpr bool kPMC = G == 0 ? B_MC : A_MC;
-    static constexpr bool kQMC = G == 0 ? A_MC : B_MC;
-    DirectOperand<kPMC, 4> p;
-    DirectOperand<kQMC, 4> q;
-    PrefetchShare share;
-
-    __device__ __forceinline__ void init(const Operand& P, const Operand& Q, int wg, int lane) {
-      p.init(P, wg, lane, 0);
-      q.init(Q, wg, lane, 16);
-    }
-    __device__ __forceinline__ void touch(const Operand& P, int k0, int wg, int lane) const {
-      const int idx = wg * kTouchLanes + lane;
-      const bool valid = lane < kTouchLanes && idx < share.count;
-      dma_touch4(P.words,
-                 valid ? DirectOperand<kPMC, 4>::line_offset(P, k0, share.first + idx) : kOOB,
-                 D::scratch_lds());
-    }
+    DirectOperand<G == 0 ? B_MC : A_MC, 4> p;
+    DirectOperand<G == 0 ? A_MC : B_MC, 4> q;
+    static constexpr int kP = G == 0 ? kDOperandBytes : 0;  // slot offset of p's operand
+    static constexpr int kQ = kDOperandBytes - kP;
   };
 
   // One k-block: R = j % 4 fixes the slot (stage parity) and the half.
@@ -866,90 +620,74 @@ struct PingPongLoop {
   __device__ __forceinline__ static void block(f32x16_t (&acc)[C::kMI][C::kNI],
                                                u32x4_t (&fa)[2][C::kMI], u32x4_t (&fb)[2][C::kNI],
                                                const Stream<G>& str, const Operand& P,
-                                               const Operand& Q, const typename D::Stages& st,
-                                               int j, int wg, int lane) {
+                                               const Operand& Q, const Stages& st, int j,
+                                               int lane) {
     constexpr int h = R & 1, sp = R >> 1;
-    constexpr int kP = G == 0 ? kDOperandBytes : 0;  // slot offset of p's operand
-    constexpr int kQ = kDOperandBytes - kP;
     const int s = j >> 1;
     unsigned char* cur = st.s[sp];
     unsigned char* other = st.s[1 - sp];
     // LOAD(j)
-    D::frags(fa[0], fb[0], cur, 2 * h, lane);
-    D::frags(fa[1], fb[1], cur, 2 * h + 1, lane);
+    frags(fa[0], fb[0], cur, 2 * h, lane);
+    frags(fa[1], fb[1], cur, 2 * h + 1, lane);
     if constexpr (G == 0 && h == 0) {
-      if (j >= 2) {  // B rows 0-127 of stage s+1 (phase 4s'+4 for s' = s-1)
-        str.p.issue(P, (s + 1) * BK, other + kP);
-        str.touch(P, (s + 3) * BK, wg, lane);
-      }
-      wait_vmcnt_lgkm0<5>();  // A rows 128-255 of stage s landed
+      if (j >= 2) str.p.issue(P, (s + 1) * BK, other + Stream<G>::kP);  // B rows 0-127, stage s+1
+      wait_vmcnt_lgkm0<4>();  // A rows 128-255 of stage s landed
     } else if constexpr (G == 0 && h == 1) {
-      str.q.issue(Q, (s + 1) * BK, other + kQ);  // A rows 128-255 of stage s+1
+      str.q.issue(Q, (s + 1) * BK, other + Stream<G>::kQ);  // A rows 128-255, stage s+1
       wait_vmcnt_lgkm0<63>();
     } else if constexpr (G == 1 && h == 1) {
-      str.p.issue(P, (s + 2) * BK, cur + kP);  // A rows 0-127 of stage s+2
-      wait_vmcnt_lgkm0<5>();  // A rows 0-127 and B rows 128-255 of stage s+1 landed
+      str.p.issue(P, (s + 2) * BK, cur + Stream<G>::kP);  // A rows 0-127, stage s+2
+      wait_vmcnt_lgkm0<4>();  // A rows 0-127 and B rows 128-255 of stage s+1 landed
     } else {
-      if (j >= 2) {  // B rows 128-255 of stage s+1
-        str.q.issue(Q, (s + 1) * BK, other + kQ);
-        str.touch(P, (s + 3) * BK, wg, lane);
-      }
+      if (j >= 2) str.q.issue(Q, (s + 1) * BK, other + Stream<G>::kQ);  // B rows 128-255, stage s+1
       wait_vmcnt_lgkm0<63>();
     }
     phase_barrier();
     // COMPUTE(j)
     __builtin_amdgcn_s_setprio(1);
-    D::mfmas(acc, fa[0], fb[0]);
-    D::mfmas(acc, fa[1], fb[1]);
+    mfmas(acc, fa[0], fb[0]);
+    mfmas(acc, fa[1], fb[1]);
     fence();
     __builtin_amdgcn_s_setprio(0);
-    if constexpr (G == 0 && h == 1) wait_vmcnt_lgkm0<5>();  // B rows 0-127 of stage s+1 landed
+    if constexpr (G == 0 && h == 1) wait_vmcnt_lgkm0<4>();  // B rows 0-127 of stage s+1 landed
     phase_barrier();
   }
 
   template <int G>
   __device__ __forceinline__ static void program(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& P,
-                                                 const Operand& Q, PrefetchShare share,
-                                                 const typename D::Stages& st, int nk, int wg,
-                                                 int lane) {
-    constexpr int kP = G == 0 ? kDOperandBytes : 0;
-    constexpr int kQ = kDOperandBytes - kP;
+                                                 const Operand& Q, const Stages& st, int nk,
+                                                 int wg, int lane) {
     Stream<G> str;
-    str.init(P, Q, wg, lane);
-    str.share = share;
-    // prologue: stages 0 and 1, touches of stages 2 and 3
-    static_assert(kDPrefetch == 4, "the waits count two prologue touches");
+    str.p.init(P, wg, lane, 0);
+    str.q.init(Q, wg, lane, 16);
+    // prologue: stages 0 and 1; stage 0 landed, stage 1 (8 loads) may still be in flight
 #pragma unroll
     for (int t = 0; t < kDStages; ++t) {
-      str.p.issue(P, t * BK, st.s[t] + kP);
-      str.q.issue(Q, t * BK, st.s[t] + kQ);
+      str.p.issue(P, t * BK, st.s[t] + Stream<G>::kP);
+      str.q.issue(Q, t * BK, st.s[t] + Stream<G>::kQ);
     }
-    str.touch(P, 2 * BK, wg, lane);
-    str.touch(P, 3 * BK, wg, lane);
-    // stage 0 landed: stage 1 (8 loads per wave) and the touches may still be in flight
-    wait_vmcnt_lgkm0<10>();
+    wait_vmcnt_lgkm0<8>();
     phase_barrier();
     u32x4_t fa[2][C::kMI], fb[2][C::kNI];
     if constexpr (G == 1) phase_barrier();  // G1 runs one phase behind
     const int J = 2 * nk;
     int j = 0;
     for (; j + 4 <= J; j += 4) {
-      block<G, 0>(acc, fa, fb, str, P, Q, st, j, wg, lane);
-      block<G, 1>(acc, fa, fb, str, P, Q, st, j + 1, wg, lane);
-      block<G, 2>(acc, fa, fb, str, P, Q, st, j + 2, wg, lane);
-      block<G, 3>(acc, fa, fb, str, P, Q, st, j + 3, wg, lane);
+      block<G, 0>(acc, fa, fb, str, P, Q, st, j, lane);
+      block<G, 1>(acc, fa, fb, str, P, Q, st, j + 1, lane);
+      block<G, 2>(acc, fa, fb, str, P, Q, st, j + 2, lane);
+      block<G, 3>(acc, fa, fb, str, P, Q, st, j + 3, lane);
     }
     if (j < J) {  // odd number of stages: one more in slot 0
-      block<G, 0>(acc, fa, fb, str, P, Q, st, j, wg, lane);
-      block<G, 1>(acc, fa, fb, str, P, Q, st, j + 1, wg, lane);
+      block<G, 0>(acc, fa, fb, str, P, Q, st, j, lane);
+      block<G, 1>(acc, fa, fb, str, P, Q, st, j + 1, lane);
     }
     if constexpr (G == 0) phase_barrier();  // pairs with G1's last one
   }
 
   __device__ __forceinline__ static void run(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
-                                             const Operand& B, int K, PrefetchShare pa,
-                                             PrefetchShare pb) {
-    const typename D::Stages st = D::stage_arrays();
+                                             const Operand& B, int K) {
+    const Stages st = stage_arrays();
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 #pragma unroll
@@ -961,27 +699,22 @@ struct PingPongLoop {
     const int nk = (K + BK - 1) / BK;
     if (nk <= 0) return;
     if (w < 4)
-      program<0>(acc, B, A, pb, st, nk, w, lane);  // G0: p = B rows 0-127, q = A rows 128-255
+      program<0>(acc, B, A, st, nk, w, lane);
     else
-      program<1>(acc, A, B, pa, st, nk, w - 4, lane);  // G1: p = A rows 0-127, q = B rows 128-255
+      program<1>(acc, A, B, st, nk, w - 4, lane);
     // drain the out-of-range loads before the LDS is reused
     wait_vmcnt_lgkm0<0>();
   }
 };
 
-#ifndef FKL_DIRECT_LDS
-#define FKL_DIRECT_LDS 1
-#endif
-
-// acc = A[tile, 0:K] . B[tile, 0:K]^T for one 256 x 256 tile.
+// acc = A[tile, 0:K] . B[tile, 0:K]^T for one 256 x 256 tile: bf16 through the
+// direct-to-LDS ping-pong loop (eight waves), fp32 through the register-staged
+// loop.
 template <class P, class C, bool A_MC, bool B_MC>
 __device__ __forceinline__ void gemm_tile(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
-                                          const Operand& B, int K, PrefetchShare pa,
-                                          PrefetchShare pb) {
-  if constexpr (FKL_DIRECT_LDS && P::kBytes == 2 && C::kThreads == 512)
-    PingPongLoop<C, A_MC, B_MC>::run(acc, A, B, K, pa, pb);
-  else if constexpr (FKL_DIRECT_LDS && P::kBytes == 2)
-    DirectLoop<C, A_MC, B_MC>::run(acc, A, B, K, pa, pb);
+                                          const Operand& B, int K) {
+  if constexpr (P::kBytes == 2)
+    PingPongLoop<C, A_MC, B_MC>::run(acc, A, B, K);
   else
     TileLoop<P, C, A_MC, B_MC>::run(acc, A, B, 0, K);
 }
@@ -1009,17 +742,6 @@ struct TileGroups {
     *tm = gm_i * GA + (j % GA);
     *tn = gn_i * GB + (j / GA);
     return *tm < mt && *tn < nt;
-  }
-  // The GB workgroups of a group that read one A tile split its lines by
-  // their position along B, and the GA that read one B tile split by their
-  // position along A, so each line of the group is touched once.
-  __device__ __forceinline__ static PrefetchShare share_a() {
-    const int j = static_cast<int>((blockIdx.x >> 3) & 31);
-    return PrefetchShare{(j / GA) * (256 / GB), 256 / GB};
-  }
-  __device__ __forceinline__ static PrefetchShare share_b() {
-    const int j = static_cast<int>((blockIdx.x >> 3) & 31);
-    return PrefetchShare{(j % GA) * (256 / GA), 256 / GA};
   }
 };
 

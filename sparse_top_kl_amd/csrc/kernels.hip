@@ -71,8 +71,7 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_logits_lse(
   const Operand A = make_operand(W + vt * kBM * ld, ld, V - vt * kBM, d);
   const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d),
-                             TileGroups<4, 8>::share_a(), TileGroups<4, 8>::share_b());
+  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
 
   const int lane = threadIdx.x & 63;
   const int64_t v0 = vt * kBM + C::wave_m() * C::kWM;
@@ -288,8 +287,7 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_gprod(
   const Operand A = make_operand(W + vbase * ld, ld, V - vbase, d);
   const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d),
-                             TileGroups<4, 8>::share_a(), TileGroups<4, 8>::share_b());
+  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
 
   const int lane = threadIdx.x & 63;
   const int64_t w0 = vt * kBM + C::wave_m() * C::kWM;  // slice-relative column of the wave
@@ -367,8 +365,7 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_grad_hidden
   const Operand A = make_operand(G + tt * kBM * gld, gld, nrows - tt * kBM, Vw);
   const Operand B = make_operand(W + dt * kBN * P::kBytes, wld, d - dt * kBN, Vlim);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, false, true>(acc, A, B, static_cast<int>(Vw),
-                             TileGroups<8, 4>::share_a(), TileGroups<8, 4>::share_b());
+  gemm_tile<P, C, false, true>(acc, A, B, static_cast<int>(Vw));
 
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -418,8 +415,7 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_grad_w(
   const Operand A = make_operand(G + vt * kBM * P::kBytes, gpitch * P::kBytes, Vw - vt * kBM, nrows);
   const Operand B = make_operand(H + dt * kBN * P::kBytes, d * P::kBytes, d - dt * kBN, nrows);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, true, true>(acc, A, B, static_cast<int>(nrows),
-                             TileGroups<8, 4>::share_a(), TileGroups<8, 4>::share_b());
+  gemm_tile<P, C, true, true>(acc, A, B, static_cast<int>(nrows));
 
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -463,28 +459,15 @@ static inline unsigned grouped_grid(int64_t mt, int64_t nt) {
   return static_cast<unsigned>(TileGroups<GA, GB>::grid(mt, nt));
 }
 
-typedef TileCfg<2, 2> Cfg4;  // 4 waves, 128x128 per wave, one wave per SIMD
-typedef TileCfg<2, 4> Cfg8;  // 8 waves, 128x64 per wave, two waves per SIMD
+typedef TileCfg<2, 2> Cfg4;  // 4 waves, 128x128 per wave (fp32, register-staged loop)
+typedef TileCfg<2, 4> Cfg8;  // 8 waves, 128x64 per wave (bf16, ping-pong loop)
 
-// Wave grid of a bf16 MFMA kernel: its default unless FKL_TILE_WAVES (4 or 8) is set.
-static int tile_waves(int dflt) {
-  static const int w = [] {
-    const char* e = std::getenv("FKL_TILE_WAVES");
-    return e ? std::atoi(e) : 0;
-  }();
-  return (w == 4 || w == 8) ? w : dflt;
-}
-
-#define FKL_LAUNCH_GEMM(KERNEL, dtype, waves, grid, s, ...)                             \
+#define FKL_LAUNCH_GEMM(KERNEL, dtype, grid, s, ...)                                    \
   do {                                                                                  \
-    if ((dtype) == 1) {                                                                 \
-      if (tile_waves(waves) == 4)                                                       \
-        KERNEL<BF16, Cfg4><<<(grid), Cfg4::kThreads, 0, (s)>>>(__VA_ARGS__);            \
-      else                                                                              \
-        KERNEL<BF16, Cfg8><<<(grid), Cfg8::kThreads, 0, (s)>>>(__VA_ARGS__);            \
-    } else {                                                                            \
+    if ((dtype) == 1)                                                                   \
+      KERNEL<BF16, Cfg8><<<(grid), Cfg8::kThreads, 0, (s)>>>(__VA_ARGS__);              \
+    else                                                                                \
       KERNEL<F32, Cfg4><<<(grid), Cfg4::kThreads, 0, (s)>>>(__VA_ARGS__);               \
-    }                                                                                   \
   } while (0)
 
 void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64_t V,
@@ -495,7 +478,7 @@ void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64
   const int64_t n_vt = ceil_div(V, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
   const unsigned grid = grouped_grid<4, 8>(n_vt, n_tt);
-  FKL_LAUNCH_GEMM(k_logits_lse, dtype, 8, grid, s,
+  FKL_LAUNCH_GEMM(k_logits_lse, dtype, grid, s,
                   static_cast<const unsigned char*>(W), Hc, d, V, nrows, n_vt, n_tt, c2, part,
                   part_ld);
 }
@@ -546,7 +529,7 @@ void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V,
   const int64_t n_vt = ceil_div(Vw, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
   const unsigned grid = grouped_grid<4, 8>(n_vt, n_tt);
-  FKL_LAUNCH_GEMM(k_gprod, dtype, 8, grid, s,
+  FKL_LAUNCH_GEMM(k_gprod, dtype, grid, s,
                   static_cast<const unsigned char*>(W), Hc, d, V, v0, Vw, gpitch, nrows, n_vt,
                   n_tt, c2, acoef, lse2, static_cast<unsigned char*>(G));
 }
@@ -575,7 +558,7 @@ void launch_grad_hidden(int dtype, const void* G, int64_t gpitch, const void* W,
   const int64_t n_tt = ceil_div(nrows, kBM), n_dt = ceil_div(d, kBN);
   const unsigned char* Ws = static_cast<const unsigned char*>(W) + v0 * d * eb;
   const unsigned grid = grouped_grid<8, 4>(n_tt, n_dt);
-  FKL_LAUNCH_GEMM(k_grad_hidden, dtype, 8, grid, s,
+  FKL_LAUNCH_GEMM(k_grad_hidden, dtype, grid, s,
                   static_cast<const unsigned char*>(G), gpitch, Ws, d, Vw, Vlim, nrows, n_tt, n_dt,
                   accumulate ? 1 : 0, acc);
 }
@@ -603,7 +586,7 @@ void launch_grad_w(int dtype, const void* G, int64_t gpitch, const void* H, int6
   const int64_t n_vt = ceil_div(Vw, kBM), n_dt = ceil_div(d, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
   const unsigned grid = grouped_grid<8, 4>(n_vt, n_dt);
-  FKL_LAUNCH_GEMM(k_grad_w, dtype, 8, grid, s,
+  FKL_LAUNCH_GEMM(k_grad_w, dtype, grid, s,
                   static_cast<const unsigned char*>(G), gpitch, Hc, d, Vw, Vlim, nrows, n_vt, n_dt,
                   accumulate ? 1 : 0, grad_w + v0 * d);
 }
