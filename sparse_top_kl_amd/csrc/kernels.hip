@@ -291,8 +291,54 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_gprod(
 
   const int lane = threadIdx.x & 63;
   const int64_t w0 = vt * kBM + C::wave_m() * C::kWM;  // slice-relative column of the wave
-  if (w0 >= Vw) return;
   const int64_t gld = gpitch * P::kBytes;
+  if constexpr (P::kBytes == 2) {
+    // A lane holds 4 consecutive vocabulary entries of one token, so direct
+    // stores would put 16 bytes into each of 32 rows of G per instruction.
+    // Each wave instead transposes its 128 x 64 sub-tile through 16 KiB of the
+    // (now idle) stage LDS, laid out [token][vocabulary] in 256-byte rows, and
+    // writes 16 bytes per lane, 16 lanes per contiguous row segment. The
+    // 16-byte unit u of row t sits at unit u ^ (t % 16), its 8-byte halves
+    // swapped when bit 4 of t is set, so the 32 rows one write instruction
+    // touches hit 32 distinct 8-byte bank positions.
+    __syncthreads();  // every wave has drained its loads: the stage LDS is free
+    const int w = static_cast<int>(threadIdx.x >> 6);
+    unsigned char* tp =
+        PingPongLoop<C, false, false>::stage_arrays().s[w >> 2] + (w & 3) * (kDStageBytes / 4);
+    const int64_t t0 = tt * kBN + C::wave_n() * C::kWN;  // first token of the wave
+#pragma unroll
+    for (int ni = 0; ni < C::kNI; ++ni) {
+      const int tl = ni * 32 + (lane & 31);
+      const int64_t tok = t0 + tl;
+      const float a = tok < nrows ? acoef[tok] : 0.f;
+      const float l2 = tok < nrows ? lse2[tok] : 0.f;
+      const int half = (lane >> 5) ^ ((tl >> 4) & 1);
+#pragma unroll
+      for (int mi = 0; mi < C::kMI; ++mi)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int64_t col = w0 + mi * 32 + 8 * g4 + 4 * (lane >> 5);
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            v[j] = (v0 + col + j < V) ? a * fast_exp2(acc[mi][ni][4 * g4 + j] * c2 - l2) : 0.f;
+          const int unit = (mi * 4 + g4) ^ (tl & 15);
+          store4<P>(tp + tl * 256 + unit * 16 + half * 8, v);
+        }
+    }
+    if (w0 >= Vw) return;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int tl = it * 4 + (lane >> 4), u = lane & 15;
+      u32x4_t x = lds_load16(tp + tl * 256 + (u ^ (tl & 15)) * 16);
+      if ((tl >> 4) & 1) x = u32x4_t{x[2], x[3], x[0], x[1]};
+      const int64_t tok = t0 + tl, col = w0 + u * 8;
+      if (tok < nrows && col < Vw)
+        *reinterpret_cast<u32x4_t*>(G + tok * gld + col * P::kBytes) = x;
+    }
+    return;
+  }
+  if (w0 >= Vw) return;
 #pragma unroll
   for (int ni = 0; ni < C::kNI; ++ni) {
     const int64_t tok = tt * kBN + C::wave_n() * C::kWN + ni * 32 + (lane & 31);
