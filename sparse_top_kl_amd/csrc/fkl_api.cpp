@@ -33,62 +33,86 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Largest offset a buffer load may reach: 2 GiB less a margin.
 constexpr int64_t kMaxBlockBytes = (int64_t(1) << 31) - (int64_t(1) << 20);
 
-// The backward keeps one block of the logit gradient G, bw_rows x bw_pitch,
-// with bw_rows * bw_pitch <= chunk * Vpad (the memory the chunk size allows).
-// grad_W is read-modified-written once per extra row block and the fp32
-// grad_hidden accumulator once per extra vocabulary slice, so the shape
-// minimising (row blocks - 1) * V + (slices - 1) * N is chosen.
+// The backward keeps one block of the logit gradient G: bw_rows rows of a
+// vocabulary slice bw_width wide, with bw_rows * bw_width <= chunk * Vpad (the
+// memory the chunk size allows); rows are padded to bw_pitch, a multiple of 64
+// elements, so every row starts on a 128-byte line.
 struct Plan {
   int64_t chunk_cap;  // forward rows per pass (<= N, >= 1)
   int64_t Vpad;       // vocabulary rounded up to 8
   int64_t nslots;     // vocabulary slices holding a partial (valid ones)
   int64_t slot_cap;   // partial slots allocated per row
-  // backward blocking: row blocks of bw_rows x vocabulary slices of bw_pitch
-  int64_t bw_rows, bw_pitch;
+  // backward blocking: row blocks of bw_rows x vocabulary slices of bw_width
+  int64_t bw_rows, bw_width, bw_pitch;
   // forward workspace offsets
   size_t f_part, f_rowloss, f_topkz, f_flag, f_total;
   // backward workspace offsets
   size_t b_G, b_ghacc, b_pcoef, b_acoef, b_lse2, b_zk, b_flag, b_total;
 };
 
-void plan_backward_blocks(int64_t N, int64_t V, int64_t Vpad, int64_t chunk_cap, int64_t eb,
-                          int64_t* rows, int64_t* pitch) {
+// Predicted cost of the backward contractions for row blocks of rc rows and
+// vocabulary slices of width vs, in units of one value of the contraction
+// length on a full round of 256 x 256 tiles: a launch runs ceil(tiles / CUs)
+// rounds whose contraction length is d (logit tiles), the slice width
+// (grad_hidden) or the block's rows (grad_W); each slice adds a fixed cost for
+// its launches. The sizes are those of the loops in fkl_backward.
+double backward_cost(int64_t N, int64_t Vpad, int64_t d, int64_t rc, int64_t vs) {
+  constexpr int64_t kCUs = 256;  // MI355X compute units
+  constexpr double kSliceCost = 1000.0;
+  const int64_t dt = fkl::ceil_div(d, 256);
+  double c = 0.0;
+  for (int64_t r0 = 0; r0 < N; r0 += rc) {
+    const int64_t nr = N - r0 < rc ? N - r0 : rc;
+    const int64_t rt = fkl::ceil_div(nr, 256);
+    for (int64_t v0 = 0; v0 < Vpad; v0 += vs) {
+      const int64_t vw = Vpad - v0 < vs ? Vpad - v0 : vs;
+      const int64_t vt = fkl::ceil_div(vw, 256);
+      c += double(fkl::ceil_div(rt * vt, kCUs)) * d + double(fkl::ceil_div(rt * dt, kCUs)) * vw +
+           double(fkl::ceil_div(vt * dt, kCUs)) * nr + kSliceCost;
+    }
+  }
+  return c;
+}
+
+// Row blocks are multiples of 256 rows (or all N), slice widths multiples of
+// 32 elements; among the shapes within the budget the one with the least
+// predicted cost is chosen.
+void plan_backward_blocks(int64_t N, int64_t Vpad, int64_t d, int64_t chunk_cap, int64_t eb,
+                          int64_t* rows, int64_t* width) {
+  constexpr int64_t kGran = 32;
   int64_t budget = chunk_cap * Vpad;
-  if (budget > kMaxBlockBytes / eb) budget = kMaxBlockBytes / eb;
+  // rows * pitch * eb must stay below kMaxBlockBytes with up to 63 pad elements per row
+  if (budget > kMaxBlockBytes / eb - 64 * N) budget = kMaxBlockBytes / eb - 64 * N;
   if (budget >= N * Vpad) {  // one block covers everything
     *rows = N;
-    *pitch = Vpad;
+    *width = Vpad;
     return;
   }
   double best = 1e300;
   *rows = 1;
-  *pitch = Vpad;
+  *width = Vpad;
   const int64_t max_blocks = fkl::ceil_div(N, 256);
   for (int64_t nb = 1; nb <= max_blocks; ++nb) {
     const int64_t rc = nb == 1 ? N : fkl::round_up(fkl::ceil_div(N, nb), 256);
-    if (rc > N || rc * 256 > budget) continue;
+    if (rc > N || rc * kGran > budget) continue;
+    if (nb > 1 && fkl::ceil_div(N, rc) != nb) continue;  // same blocking as a smaller nb
     const int64_t vs_max = budget / rc;
-    int64_t ns, vs;
-    if (vs_max >= Vpad) {
-      ns = 1;
-      vs = Vpad;
-    } else {
-      const int64_t vm = vs_max / 256 * 256;
-      ns = fkl::ceil_div(Vpad, vm);
-      vs = fkl::round_up(fkl::ceil_div(Vpad, ns), 256);
+    const int64_t vm = vs_max >= Vpad ? Vpad : vs_max / kGran * kGran;
+    const int64_t ns0 = fkl::ceil_div(Vpad, vm);
+    for (int64_t ns = ns0; ns < ns0 + 3; ++ns) {
+      const int64_t vs = fkl::round_up(fkl::ceil_div(Vpad, ns), kGran);
       if (vs > vm) continue;
-    }
-    const int64_t nblk = fkl::ceil_div(N, rc);
-    const double cost = double(nblk - 1) * V + double(ns - 1) * N + 1024.0 * nblk * ns;
-    if (cost < best) {
-      best = cost;
-      *rows = rc;
-      *pitch = vs;
+      const double cost = backward_cost(N, Vpad, d, rc, vs);
+      if (cost < best) {
+        best = cost;
+        *rows = rc;
+        *width = vs;
+      }
     }
   }
   if (best == 1e300) {  // tiny budget: one row per block, whole vocabulary
     *rows = budget / Vpad > 0 ? (budget / Vpad < N ? budget / Vpad : N) : 1;
-    *pitch = Vpad;
+    *width = Vpad;
   }
 }
 
@@ -117,7 +141,8 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_
   p.Vpad = round_up(V, 8);
   p.nslots = ceil_div(V, kSliceVocab);
   p.slot_cap = lse_slots(V);
-  plan_backward_blocks(N > 0 ? N : 1, V, p.Vpad, p.chunk_cap, eb, &p.bw_rows, &p.bw_pitch);
+  plan_backward_blocks(N > 0 ? N : 1, p.Vpad, d, p.chunk_cap, eb, &p.bw_rows, &p.bw_width);
+  p.bw_pitch = fkl::round_up(p.bw_width, 64);
 
   size_t off = 0;
   p.f_part = off;
@@ -310,8 +335,8 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
       zk = zk_ws;
     }
     fkl::launch_bwd_prep(topk_logit, lse, grad_loss, row0, nrows, K, T, pcoef, acoef, lse2, s);
-    for (int64_t v0 = 0; v0 < p.Vpad; v0 += p.bw_pitch) {
-      const int64_t Vw = (p.Vpad - v0) < p.bw_pitch ? (p.Vpad - v0) : p.bw_pitch;
+    for (int64_t v0 = 0; v0 < p.Vpad; v0 += p.bw_width) {
+      const int64_t Vw = (p.Vpad - v0) < p.bw_width ? (p.Vpad - v0) : p.bw_width;
       const int64_t Vlim = (V - v0) < Vw ? (V - v0) : Vw;
       fkl::launch_gprod(dtype, weight, hidden, d, V, v0, Vw, p.bw_pitch, row0, nrows, c2, acoef,
                         lse2, G, s);

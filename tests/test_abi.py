@@ -49,9 +49,10 @@ def test_workspace_is_bounded_by_chunk_times_vocab_and_never_rows_times_vocab():
         f, b = fkl.fkl_workspace_size(N, d, V, K, chunk, fkl.FKL_BF16)
         # forward: per-chunk partials (one float2 per row and 128-wide slice) + per-row scratch
         assert f <= chunk * ((V + 255) // 256) * 2 * 8 + N * (4 + 4 * K) + (1 << 16)
-        # backward: one logit-gradient block within the chunk x V budget, plus per-row
-        # scratch of a row block (fp32 grad_hidden accumulator, teacher coefficients)
-        assert b <= chunk * Vpad * 2 + min(N, 1 << 16) * (4 * d + 8 * K + 8) + (1 << 16)
+        # backward: one logit-gradient block within the chunk x V budget (its rows padded
+        # by fewer than 64 elements to whole 128-byte lines), plus per-row scratch of a
+        # row block (fp32 grad_hidden accumulator, teacher coefficients)
+        assert b <= chunk * Vpad * 2 + min(N, 1 << 16) * (4 * d + 8 * K + 8 + 128) + (1 << 16)
         if N >= 8 * chunk:
             assert b < N * V * 2 / 4  # far below one dense bf16 N x V matrix
     # a larger chunk buys a larger block
