@@ -80,12 +80,15 @@ def cpu_baseline(inp, gpu_rows: dict, budget_s: float):
                                       inp["topk_logit"][:n], w.T)
         return out, time.perf_counter() - t0
 
-    # calibrate on two sizes (the fixed per-call cost is large), then fill the budget
-    _, t1 = run(16)
-    _, t2 = run(64)
-    per_row = max((t2 - t1) / 48, 1e-6)
-    n = int(max(64, min(w.N, (budget_s - max(t1 - 16 * per_row, 0.0)) / per_row)))
-    n = max(16, (n // 16) * 16)
+    # The oracle works in blocks of 128 rows, each costing three fp64 products
+    # over the whole vocabulary, plus a fixed cost per call (the fp64 copy of
+    # W); calibrate on one and two blocks, then size the sample to the budget.
+    _, t1 = run(128)
+    _, t2 = run(256)
+    per_row = max((t2 - t1) / 128, 1e-6)
+    fixed = max(t1 - 128 * per_row, 0.0)
+    n = int((budget_s - fixed) / per_row) // 128 * 128
+    n = max(128, min(w.N, n))
     out, t = run(n)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     tol = 1e-3 if w.dtype == "bf16" else 1e-5
@@ -121,6 +124,9 @@ def main():
     ap.add_argument("--workload", default="long32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, copy this many MiB once on the device (a plain "
+                         "copy of known size for calibrating rocprofv3 byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -159,6 +165,16 @@ def main():
         gh, _ = fkl.fkl_backward(h, W, idx, lg, out.lse, w.T, w.chunk, topk_z=out.topk_z,
                                  grad_weight=gw, workspace=ws_b)
         return out, gh
+
+    if args.copy_calibration_mib > 0:
+        nb = args.copy_calibration_mib << 20
+        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
