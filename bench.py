@@ -18,6 +18,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -44,11 +45,16 @@ def log(msg):
 
 
 def source_hash() -> str:
+    """Hash of the kernel and library sources without comments or blank lines,
+    so that counters stay attached to the code they were measured on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_top_kl_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+        h.update(name.encode() + "\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 

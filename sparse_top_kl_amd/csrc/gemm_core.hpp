@@ -2,23 +2,23 @@
 //
 // Every contraction of the loss (the logit tile z = W_tile . H_tile^T, its
 // recompute in the backward, grad_hidden = G . W and grad_W = G^T . H) runs
-// through gemm_tile(). Operands are staged through LDS in a k-contiguous
-// layout with a padded row pitch; an operand stored contiguous along its m/n
-// index ("MN-major", e.g. W read as [v][d] when v is the contraction index) is
-// transposed in registers on its way into LDS, so every fragment read is one
-// 16-byte ds_read per lane.
+// through gemm_tile(). bf16 operands go through the direct-to-LDS ping-pong
+// loop further down (eight waves, 128 x 64 outputs each); fp32 operands
+// through the register-staged loop below (four waves, 128 x 128 each).
 //
 // Global reads are raw buffer loads: the buffer's record count makes reads
 // past the end of the operand return zero, and lanes whose element lies
 // outside the operand use an offset beyond the record count, so tails need no
 // branches.
 //
-// Pipeline (one workgroup, two LDS stages of 128 bytes of K per row):
-//   the registers of each thread hold the global data of stage t+1 while the
-//   waves run the MFMAs of stage t; early in stage t those registers are
-//   written to the other LDS buffer and refilled with stage t+2. Inside a
-//   stage the fragments of k-step s+1 are read from LDS while the MFMAs of
-//   k-step s run. One barrier per stage.
+// Register-staged loop (fp32): two LDS stages of 128 bytes of K per row with a
+// padded pitch; an operand stored contiguous along its m/n index ("MN-major",
+// e.g. W read as [v][d] when v is the contraction index) is transposed in
+// registers on its way into LDS, so every fragment read is one 16-byte
+// ds_read. The registers of each thread hold the global data of stage t+1
+// while the waves run the MFMAs of stage t; early in stage t those registers
+// are written to the other LDS buffer and refilled with stage t+2. One
+// barrier per stage.
 //
 // Accumulator layout (32x32 MFMA result): element r of block (mi, ni) in lane
 // l is row  mi*32 + 8*(r/4) + 4*(l/32) + (r%4)  and column  ni*32 + (l%32)

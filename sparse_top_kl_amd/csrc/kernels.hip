@@ -14,16 +14,21 @@
 //   k_merge_loss   merge the slices into lse, teacher softmax over the K cached
 //                  logits, per-row KL.
 // once: k_gather_dot (z at the teacher ids), k_reduce_loss (fixed-order sum).
-// Backward, per chunk:
-//   k_bwd_prep     teacher probabilities scaled by s*T, lse in base 2.
-//   k_gprod        recompute z tile (same tile code as the forward) and write
-//                  the dense part of the logit gradient, s*T*sum(p)*softmax, as
-//                  one rounding into the chunk-sized G buffer.
-//   k_fixup        subtract s*T*p at the teacher ids (recomputing the same
-//                  value from z at the id, so each entry is rounded once).
-//   k_grad_hidden  split-K MFMA product G . W into fp32 partials;
-//   k_reduce_gh    fixed-order sum of the partials -> grad_hidden rows.
-//   k_grad_w       MFMA product G^T . H accumulated into fp32 grad_W.
+// Backward, per block of rows (as many as the chunk x V budget allows) and,
+// inside it, per vocabulary slice:
+//   k_bwd_prep     (per row block) teacher probabilities scaled by s*T, lse in
+//                  base 2.
+//   k_gprod        recompute the z tile (same tile code as the forward) and
+//                  write the dense part of the logit gradient,
+//                  s*T*sum(p)*softmax, rounded once into the G block.
+//   k_fixup        subtract s*T*p at the teacher ids inside the slice
+//                  (recomputing the same value from z at the id, so each entry
+//                  is rounded once).
+//   k_grad_hidden  MFMA product G . W_slice, accumulated over the slices into
+//                  an fp32 accumulator of the row block;
+//   k_reduce_gh    (per row block) accumulator -> grad_hidden rows.
+//   k_grad_w       MFMA product G^T . H_block into the fp32 grad_W rows of the
+//                  slice, accumulated over the row blocks.
 #include <math.h>
 
 #include <cstdlib>
