@@ -124,23 +124,34 @@ __device__ __forceinline__ float dot16(u32x4_t a, u32x4_t b, float acc) {
   return acc;
 }
 
-// One wave per row; four 16-lane groups take every fourth teacher id.
-template <class P>
+// One wave per row; four 16-lane groups take every fourth teacher id and
+// stream that weight row. With STAGE the block's four hidden rows are first
+// copied to LDS (each is read once per id), otherwise read from memory.
+template <class P, bool STAGE>
 __global__ __launch_bounds__(256) void k_gather_dot(const unsigned char* __restrict__ W,
                                                     const unsigned char* __restrict__ H,
                                                     const int32_t* __restrict__ idx, int64_t d,
                                                     int64_t nrows, int K, float* __restrict__ zk) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char sh_rows[];
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= nrows) return;
   const int64_t rb = d * P::kBytes;
-  const unsigned char* h = H + row * rb;
   const int64_t nvec = rb / 16;
+  const unsigned char* h = H + row * rb;
+  if constexpr (STAGE) {
+    unsigned char* hs = sh_rows + (threadIdx.x >> 6) * rb;  // this wave's row
+    for (int64_t j = lane; j < nvec; j += 64) lds_store16(hs + j * 16, load16(h + j * 16));
+    h = hs;  // each wave reads back only what it wrote: no barrier needed
+  }
   for (int k = g; k < K; k += 4) {
     const int64_t v = idx[row * K + k];
     const unsigned char* wr = W + v * rb;
     float acc = 0.f;
-    for (int64_t j = li; j < nvec; j += 16) acc = dot16<P>(load16(h + j * 16), load16(wr + j * 16), acc);
+    for (int64_t j = li; j < nvec; j += 16) {
+      const u32x4_t hv = STAGE ? lds_load16(h + j * 16) : load16(h + j * 16);
+      acc = dot16<P>(hv, load16(wr + j * 16), acc);
+    }
     acc += __shfl_xor(acc, 8);
     acc += __shfl_xor(acc, 4);
     acc += __shfl_xor(acc, 2);
@@ -541,12 +552,24 @@ void launch_gather_dot(int dtype, const void* W, const void* H, const int32_t* i
   const int64_t eb = dtype == 1 ? 2 : 4;
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
   const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, 4));
-  if (dtype == 1)
-    k_gather_dot<BF16><<<blocks, 256, 0, s>>>(static_cast<const unsigned char*>(W), Hc,
-                                               idx + row0 * K, d, nrows, K, zk + row0 * K);
-  else
-    k_gather_dot<F32><<<blocks, 256, 0, s>>>(static_cast<const unsigned char*>(W), Hc,
-                                              idx + row0 * K, d, nrows, K, zk + row0 * K);
+  const unsigned char* Wc = static_cast<const unsigned char*>(W);
+  const size_t lds = static_cast<size_t>(4 * d * eb);  // four hidden rows
+  const bool stage = lds <= 64 * 1024;
+  if (dtype == 1) {
+    if (stage)
+      k_gather_dot<BF16, true><<<blocks, 256, lds, s>>>(Wc, Hc, idx + row0 * K, d, nrows, K,
+                                                        zk + row0 * K);
+    else
+      k_gather_dot<BF16, false><<<blocks, 256, 0, s>>>(Wc, Hc, idx + row0 * K, d, nrows, K,
+                                                       zk + row0 * K);
+  } else {
+    if (stage)
+      k_gather_dot<F32, true><<<blocks, 256, lds, s>>>(Wc, Hc, idx + row0 * K, d, nrows, K,
+                                                       zk + row0 * K);
+    else
+      k_gather_dot<F32, false><<<blocks, 256, 0, s>>>(Wc, Hc, idx + row0 * K, d, nrows, K,
+                                                      zk + row0 * K);
+  }
 }
 
 void launch_merge_loss(const float2* part, int64_t part_ld, int64_t nslots, const float* zk,
