@@ -8,7 +8,11 @@ JSON line: throughput in tokens/s, the MFMA roofline of the dominant kernel
 peak HBM of one step, a sampled parity check against the fp64 oracle and the
 oracle's own host throughput on a bounded sample of the same rows.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+With --keep-logits the step is the forward-chunked variant instead
+(fkl_forward_keep + fkl_backward_keep: the logits are kept in an N x V buffer
+and not recomputed, 6 N d V flops per step).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--keep-logits]
 """
 
 from __future__ import annotations
@@ -130,6 +134,8 @@ def main():
     ap.add_argument("--workload", default="long32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--keep-logits", action="store_true",
+                    help="time the forward-chunked variant (kept logits, no recompute)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy this many MiB once on the device (a plain "
                          "copy of known size for calibrating rocprofv3 byte counters)")
@@ -161,12 +167,22 @@ def main():
     torch.cuda.synchronize()
     input_bytes = sum(t.numel() * t.element_size() for t in (h, W, idx, lg))
 
+    keep = args.keep_logits
     fw, bw = fkl.fkl_workspace_size(w.N, w.d, w.V, w.K, w.chunk, dt)
+    zbytes = 0
+    if keep:
+        zbytes, bw = fkl.fkl_keep_sizes(w.N, w.d, w.V, w.K, dt)
     ws_f = torch.empty(fw, dtype=torch.uint8, device=dev)
     ws_b = torch.empty(bw, dtype=torch.uint8, device=dev)
     gw = torch.empty(w.V, w.d, dtype=torch.float32, device=dev)
+    zbuf = torch.empty(w.N, fkl.keep_pitch(w.V), dtype=dt, device=dev) if keep else None
 
     def step():
+        if keep:
+            out, z = fkl.fkl_forward_keep(h, W, idx, lg, w.T, w.chunk, logits=zbuf, workspace=ws_f)
+            gh, _ = fkl.fkl_backward_keep(h, W, idx, lg, out.lse, w.T, z, topk_z=out.topk_z,
+                                          grad_weight=gw, workspace=ws_b)
+            return out, gh
         out = fkl.fkl_forward(h, W, idx, lg, w.T, w.chunk, workspace=ws_f)
         gh, _ = fkl.fkl_backward(h, W, idx, lg, out.lse, w.T, w.chunk, topk_z=out.topk_z,
                                  grad_weight=gw, workspace=ws_b)
@@ -187,12 +203,13 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # peak HBM of one step (inputs, outputs, workspaces, grad_W)
-    del ws_f, ws_b
+    # peak HBM of one step (inputs, outputs, workspaces, grad_W, kept logits)
+    del ws_f, ws_b, zbuf
     torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats(dev)
     ws_f = torch.empty(fw, dtype=torch.uint8, device=dev)
     ws_b = torch.empty(bw, dtype=torch.uint8, device=dev)
+    zbuf = torch.empty(w.N, fkl.keep_pitch(w.V), dtype=dt, device=dev) if keep else None
     out, gh = step()
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated(dev)
@@ -218,7 +235,9 @@ def main():
     ktimes = fkl.kernel_times()
     log(f"[bench] {elapsed / args.steps * 1e3:.2f} ms/step")
 
-    flops_step = 8.0 * w.N * w.d * w.V
+    # four contractions of 2 N d V each (logits, their recompute, grad_hidden,
+    # grad_W); the kept-logits variant skips the recompute
+    flops_step = (6.0 if keep else 8.0) * w.N * w.d * w.V
     ms_step = elapsed / args.steps * 1e3
     kernels = {k: {"launches_per_step": n / args.steps, "avg_ms": ms / n,
                    "ms_per_step": ms / args.steps} for k, (n, ms) in ktimes.items()}
@@ -226,17 +245,18 @@ def main():
     n_launch, dom_ms = ktimes[dom]
     avg_ms = dom_ms / n_launch
     peak_tf = PEAK_TFLOPS[w.dtype]
+    traffic_key = w.name + ("/keep" if keep else "")  # stored counters per workload and variant
     if dom in GEMM_KERNELS:
-        # each of the four contractions covers all N x V logits once per step
+        # each contraction covers all N x V logits once per step
         flops_launch = 2.0 * w.N * w.d * w.V / (n_launch / args.steps)
         achieved = flops_launch / (avg_ms * 1e-3) / 1e12
-        traffic = load_traffic(dom, w.name)
+        traffic = load_traffic(dom, traffic_key)
         roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak_tf,
                     "unit": "TFLOP/s", "frac": achieved / peak_tf, "traffic": traffic,
                     "flops_per_launch": flops_launch, "avg_launch_ms": avg_ms}
     else:
         roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": None, "traffic": load_traffic(dom, w.name),
+                    "unit": "GB/s", "frac": None, "traffic": load_traffic(dom, traffic_key),
                     "avg_launch_ms": avg_ms}
 
     if args.no_cpu_baseline:
@@ -260,7 +280,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "S": w.S, "N": w.N, "d": w.d, "V": w.V,
-                   "K": w.K, "T": w.T, "chunk": w.chunk, "teacher_ids": w.ids},
+                   "K": w.K, "T": w.T, "chunk": w.chunk, "teacher_ids": w.ids,
+                   "variant": "forward-chunked, kept logits" if keep else "fused chunked"},
         "mfma_frac_step": flops_step / (ms_step * 1e-3) / (peak_tf * 1e12),
         "flops_per_step": flops_step,
         "roofline": roofline,
@@ -269,6 +290,7 @@ def main():
         "peak_hbm_gib": peak / 2**30,
         "peak_hbm_path_gib": (peak - input_bytes) / 2**30,
         "largest_workspace_gib": largest_ws / 2**30,
+        "kept_logits_gib": zbytes / 2**30,
         "dense_nxv_fp32_gib": w.N * w.V * 4 / 2**30,
         "loss": loss_val,
         "kernels": kernels,

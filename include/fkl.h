@@ -134,6 +134,61 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
                      int64_t V, int32_t K, int32_t dtype, uint32_t flags, void* grad_hidden,
                      float* grad_weight, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward-chunked variant ("keep the logits")
+ * ------------------------------------------
+ * The pages name a less aggressive alternative to the fused method: the loss
+ * is still computed chunk by chunk, but the student logits of every chunk are
+ * kept for the backward pass, which then needs no recompute. It is faster and
+ * needs an N x V buffer ("Wissensdestillation mit deutlich weniger
+ * GPU-Speicher", section "KL-Verlust wird in Blöcken berechnet"; the method
+ * table of the malakhovai.ru article lists it as the fast variant). These
+ * entry points implement it for callers whose memory allows the buffer; the
+ * results are those of fkl_forward / fkl_backward up to rounding (the forward
+ * outputs are identical; the backward starts from logits rounded to dtype
+ * instead of recomputed ones).
+ *
+ * Kept-logits buffer: N rows of keep_pitch = round_up(V, 64) elements of dtype,
+ * row-major; element (r, v) holds z_rv rounded to dtype (bf16: round to
+ * nearest even) for v < V and zero for V <= v < keep_pitch. The caller owns it.
+ *
+ * fkl_keep_sizes: bytes of the kept-logits buffer (N * keep_pitch * element
+ * size) and of the fkl_backward_keep workspace (O(N * (K + d)), per-row
+ * coefficients and an fp32 grad_hidden accumulator). Host-only. Returns
+ * FKL_E_UNSUPPORTED when 256 kept rows exceed 2 GiB (V above about 4 million
+ * in bf16). Either output pointer may be NULL. */
+int32_t fkl_keep_sizes(int64_t N, int64_t d, int64_t V, int32_t K, int32_t dtype,
+                       size_t* logits_bytes, size_t* bwd_bytes);
+
+/* fkl_forward plus the kept logits: arguments and outputs as fkl_forward
+ * (workspace sized by fkl_workspace_size's fwd_bytes), and
+ *   logits [N, keep_pitch] (dtype) written as described above (may be NULL
+ *                       only when N = 0)
+ *   logits_bytes        its size; FKL_E_WORKSPACE if below fkl_keep_sizes */
+int32_t fkl_forward_keep(const void* hidden, const void* weight, const int32_t* topk_idx,
+                         const float* topk_logit, float T, int64_t chunk, int64_t N, int64_t d,
+                         int64_t V, int32_t K, int32_t dtype, uint32_t flags, float* loss,
+                         float* lse, float* row_loss, float* topk_z, void* logits,
+                         size_t logits_bytes, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Backward pass from kept logits: arguments and outputs as fkl_backward
+ * (there is no chunk: nothing is recomputed), and
+ *   logits [N, keep_pitch] as written by fkl_forward_keep with the same
+ *                      inputs. It is CONSUMED: the call overwrites it with
+ *                      the logit gradient G (dtype), so it serves one
+ *                      backward pass only (may be NULL only when N = 0).
+ *   workspace          at least fkl_keep_sizes's bwd_bytes
+ * G = s T (softmax_T(z) sum_k p_k - scatter(p)) is formed in place row by row
+ * (teacher-id entries from topk_z, recomputed when topk_z is NULL), then
+ * grad_hidden = G . W in one MFMA product over the whole vocabulary and
+ * grad_W = G^T . H in fp32 over row blocks. */
+int32_t fkl_backward_keep(const void* hidden, const void* weight, const int32_t* topk_idx,
+                          const float* topk_logit, const float* lse, const float* topk_z,
+                          const float* grad_loss, float T, int64_t N, int64_t d, int64_t V,
+                          int32_t K, int32_t dtype, uint32_t flags, void* logits,
+                          size_t logits_bytes, void* grad_hidden, float* grad_weight,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Per-kernel timing, a profiling aid (off by default). While enabled, every
  * kernel launch the library makes is bracketed by two HIP events recorded on
  * the launch stream; the events cost a few microseconds of GPU time each.

@@ -196,6 +196,108 @@ int32_t validate_ids(const int32_t* idx, int64_t N, int32_t K, int64_t V, int32_
   return FKL_OK;
 }
 
+// Kept logits: each row padded to a multiple of 64 elements (128-byte lines in bf16).
+int64_t keep_pitch(int64_t V) { return fkl::round_up(V, 64); }
+size_t keep_bytes(int64_t N, int64_t V, int32_t dtype) {
+  return static_cast<size_t>(N) * static_cast<size_t>(keep_pitch(V)) * (dtype == FKL_BF16 ? 2 : 4);
+}
+
+// The gradient products read 256-row tiles of the kept rows through 32-bit
+// buffer offsets.
+int32_t check_keep(int64_t V, int32_t dtype) {
+  const int64_t eb = dtype == FKL_BF16 ? 2 : 4;
+  if (256 * keep_pitch(V) * eb > kMaxBlockBytes)
+    return fail(FKL_E_UNSUPPORTED, "vocabulary too large to keep the logits (V = %lld)",
+                (long long)V);
+  return FKL_OK;
+}
+
+// Workspace of fkl_backward_keep: per-row teacher coefficients, z at the ids
+// and the fp32 grad_hidden accumulator, for all N rows.
+struct KeepPlan {
+  size_t pcoef, acoef, lse2, zk, ghacc, flag, total;
+};
+KeepPlan make_keep_plan(int64_t N, int64_t d, int32_t K) {
+  KeepPlan q{};
+  const size_t n = static_cast<size_t>(N);
+  size_t off = 0;
+  q.pcoef = off;
+  off = align_up(off + n * K * 4);
+  q.acoef = off;
+  off = align_up(off + n * 4);
+  q.lse2 = off;
+  off = align_up(off + n * 4);
+  q.zk = off;
+  off = align_up(off + n * K * 4);
+  q.ghacc = off;
+  off = align_up(off + n * d * 4);
+  q.flag = off;
+  off = align_up(off + 4);
+  q.total = off;
+  return q;
+}
+
+// fkl_forward and fkl_forward_keep: the chunk loop, with the logits kept in
+// `logits` (N rows of keep_pitch(V) elements) when it is non-null.
+int32_t forward_impl(const void* hidden, const void* weight, const int32_t* topk_idx,
+                     const float* topk_logit, float T, int64_t chunk, int64_t N, int64_t d,
+                     int64_t V, int32_t K, int32_t dtype, uint32_t flags, float* loss, float* lse,
+                     float* row_loss, float* topk_z, void* logits, size_t logits_bytes,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t r = check_shapes(N, d, V, K, chunk, dtype);
+  if (r) return r;
+  if (!std::isfinite(T) || !(T > 0.0f)) return fail(FKL_E_ARG, "T must be finite and > 0");
+  if ((flags & ~FKL_FLAG_VALIDATE_IDX) != 0) return fail(FKL_E_ARG, "unknown forward flag bits");
+  if (!loss || !weight || !workspace) return fail(FKL_E_ARG, "null pointer argument");
+  if (N > 0 && (!hidden || !topk_idx || !topk_logit || !lse))
+    return fail(FKL_E_ARG, "null pointer argument");
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 16))
+    return fail(FKL_E_ARG, "hidden, weight and workspace must be 16-byte aligned");
+  if (!aligned(topk_idx, 4) || !aligned(topk_logit, 4) || !aligned(loss, 4) || !aligned(lse, 4) ||
+      !aligned(row_loss, 4) || !aligned(topk_z, 4))
+    return fail(FKL_E_ARG, "fp32/int32 arrays must be 4-byte aligned");
+  const int64_t zpitch = keep_pitch(V);
+  if (logits) {
+    r = check_keep(V, dtype);
+    if (r) return r;
+    if (!aligned(logits, 16)) return fail(FKL_E_ARG, "logits must be 16-byte aligned");
+    const size_t need = keep_bytes(N, V, dtype);
+    if (logits_bytes < need)
+      return fail(FKL_E_WORKSPACE, "kept logits need %zu bytes, got %zu", need, logits_bytes);
+  }
+  const Plan p = make_plan(N, d, V, K, chunk, dtype);
+  if (workspace_bytes < p.f_total)
+    return fail(FKL_E_WORKSPACE, "forward workspace needs %zu bytes, got %zu", p.f_total,
+                workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  (void)hipGetLastError();
+
+  if (N == 0) {
+    fkl::launch_fill_f32(loss, 1, 0.0f, s);
+    return hip_check("forward (empty batch)");
+  }
+  if (flags & FKL_FLAG_VALIDATE_IDX) {
+    r = validate_ids(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + p.f_flag), s);
+    if (r) return r;
+  }
+  float2* part = reinterpret_cast<float2*>(ws + p.f_part);
+  float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + p.f_rowloss);
+  float* zk = topk_z ? topk_z : reinterpret_cast<float*>(ws + p.f_topkz);
+  const float c2 = 1.4426950408889634f / T;
+
+  fkl::launch_gather_dot(dtype, weight, hidden, topk_idx, d, 0, N, K, zk, s);
+  for (int64_t row0 = 0; row0 < N; row0 += p.chunk_cap) {
+    const int64_t nrows = (N - row0) < p.chunk_cap ? (N - row0) : p.chunk_cap;
+    fkl::launch_logits_lse(dtype, weight, hidden, d, V, row0, nrows, c2, part, p.chunk_cap, logits,
+                           zpitch, s);
+    fkl::launch_merge_loss(part, p.chunk_cap, p.nslots, zk, topk_logit, row0, nrows, K, T, lse, rl,
+                           s);
+  }
+  fkl::launch_reduce_loss(rl, N, loss, s);
+  return hip_check("forward launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -233,48 +335,21 @@ int32_t fkl_forward(const void* hidden, const void* weight, const int32_t* topk_
                     float* row_loss, float* topk_z, void* workspace, size_t workspace_bytes,
                     void* stream) {
   g_last_error[0] = 0;
-  int32_t r = check_shapes(N, d, V, K, chunk, dtype);
-  if (r) return r;
-  if (!std::isfinite(T) || !(T > 0.0f)) return fail(FKL_E_ARG, "T must be finite and > 0");
-  if ((flags & ~FKL_FLAG_VALIDATE_IDX) != 0) return fail(FKL_E_ARG, "unknown forward flag bits");
-  if (!loss || !weight || !workspace) return fail(FKL_E_ARG, "null pointer argument");
-  if (N > 0 && (!hidden || !topk_idx || !topk_logit || !lse))
-    return fail(FKL_E_ARG, "null pointer argument");
-  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 16))
-    return fail(FKL_E_ARG, "hidden, weight and workspace must be 16-byte aligned");
-  if (!aligned(topk_idx, 4) || !aligned(topk_logit, 4) || !aligned(loss, 4) || !aligned(lse, 4) ||
-      !aligned(row_loss, 4) || !aligned(topk_z, 4))
-    return fail(FKL_E_ARG, "fp32/int32 arrays must be 4-byte aligned");
-  const Plan p = make_plan(N, d, V, K, chunk, dtype);
-  if (workspace_bytes < p.f_total)
-    return fail(FKL_E_WORKSPACE, "forward workspace needs %zu bytes, got %zu", p.f_total,
-                workspace_bytes);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  (void)hipGetLastError();
+  return forward_impl(hidden, weight, topk_idx, topk_logit, T, chunk, N, d, V, K, dtype, flags,
+                      loss, lse, row_loss, topk_z, nullptr, 0, workspace, workspace_bytes, stream);
+}
 
-  if (N == 0) {
-    fkl::launch_fill_f32(loss, 1, 0.0f, s);
-    return hip_check("forward (empty batch)");
-  }
-  if (flags & FKL_FLAG_VALIDATE_IDX) {
-    r = validate_ids(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + p.f_flag), s);
-    if (r) return r;
-  }
-  float2* part = reinterpret_cast<float2*>(ws + p.f_part);
-  float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + p.f_rowloss);
-  float* zk = topk_z ? topk_z : reinterpret_cast<float*>(ws + p.f_topkz);
-  const float c2 = 1.4426950408889634f / T;
-
-  fkl::launch_gather_dot(dtype, weight, hidden, topk_idx, d, 0, N, K, zk, s);
-  for (int64_t row0 = 0; row0 < N; row0 += p.chunk_cap) {
-    const int64_t nrows = (N - row0) < p.chunk_cap ? (N - row0) : p.chunk_cap;
-    fkl::launch_logits_lse(dtype, weight, hidden, d, V, row0, nrows, c2, part, p.chunk_cap, s);
-    fkl::launch_merge_loss(part, p.chunk_cap, p.nslots, zk, topk_logit, row0, nrows, K, T, lse, rl,
-                           s);
-  }
-  fkl::launch_reduce_loss(rl, N, loss, s);
-  return hip_check("forward launch");
+int32_t fkl_forward_keep(const void* hidden, const void* weight, const int32_t* topk_idx,
+                         const float* topk_logit, float T, int64_t chunk, int64_t N, int64_t d,
+                         int64_t V, int32_t K, int32_t dtype, uint32_t flags, float* loss,
+                         float* lse, float* row_loss, float* topk_z, void* logits,
+                         size_t logits_bytes, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_last_error[0] = 0;
+  if (!logits && N > 0) return fail(FKL_E_ARG, "null pointer argument (logits)");
+  return forward_impl(hidden, weight, topk_idx, topk_logit, T, chunk, N, d, V, K, dtype, flags,
+                      loss, lse, row_loss, topk_z, logits, logits_bytes, workspace,
+                      workspace_bytes, stream);
 }
 
 int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk_idx,
@@ -348,6 +423,96 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
                          accumulate || row0 > 0, grad_weight, s);
     }
     fkl::launch_reduce_grad_hidden(dtype, ghacc, 1, nrows, d, grad_hidden, row0, s);
+  }
+  return hip_check("backward launch");
+}
+
+int32_t fkl_keep_sizes(int64_t N, int64_t d, int64_t V, int32_t K, int32_t dtype,
+                       size_t* logits_bytes, size_t* bwd_bytes) {
+  g_last_error[0] = 0;
+  int32_t r = check_shapes(N, d, V, K, 1, dtype);
+  if (r) return r;
+  r = check_keep(V, dtype);
+  if (r) return r;
+  if (logits_bytes) *logits_bytes = keep_bytes(N, V, dtype);
+  if (bwd_bytes) *bwd_bytes = make_keep_plan(N, d, K).total;
+  return FKL_OK;
+}
+
+int32_t fkl_backward_keep(const void* hidden, const void* weight, const int32_t* topk_idx,
+                          const float* topk_logit, const float* lse, const float* topk_z,
+                          const float* grad_loss, float T, int64_t N, int64_t d, int64_t V,
+                          int32_t K, int32_t dtype, uint32_t flags, void* logits,
+                          size_t logits_bytes, void* grad_hidden, float* grad_weight,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  int32_t r = check_shapes(N, d, V, K, 1, dtype);
+  if (r) return r;
+  r = check_keep(V, dtype);
+  if (r) return r;
+  if (!std::isfinite(T) || !(T > 0.0f)) return fail(FKL_E_ARG, "T must be finite and > 0");
+  if ((flags & ~(FKL_FLAG_VALIDATE_IDX | FKL_FLAG_ACCUMULATE_GRAD_W)) != 0)
+    return fail(FKL_E_ARG, "unknown backward flag bits");
+  if (!weight || !grad_weight || !workspace) return fail(FKL_E_ARG, "null pointer argument");
+  if (N > 0 && (!hidden || !topk_idx || !topk_logit || !lse || !grad_hidden || !logits))
+    return fail(FKL_E_ARG, "null pointer argument");
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 16) ||
+      !aligned(grad_hidden, 16) || !aligned(grad_weight, 16) || !aligned(logits, 16))
+    return fail(FKL_E_ARG,
+                "hidden, weight, logits, gradients and workspace must be 16-byte aligned");
+  if (!aligned(topk_idx, 4) || !aligned(topk_logit, 4) || !aligned(lse, 4) || !aligned(topk_z, 4) ||
+      !aligned(grad_loss, 4))
+    return fail(FKL_E_ARG, "fp32/int32 arrays must be 4-byte aligned");
+  const size_t need = keep_bytes(N, V, dtype);
+  if (logits_bytes < need)
+    return fail(FKL_E_WORKSPACE, "kept logits need %zu bytes, got %zu", need, logits_bytes);
+  const KeepPlan q = make_keep_plan(N, d, K);
+  if (workspace_bytes < q.total)
+    return fail(FKL_E_WORKSPACE, "backward workspace needs %zu bytes, got %zu", q.total,
+                workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  const bool accumulate = (flags & FKL_FLAG_ACCUMULATE_GRAD_W) != 0;
+  (void)hipGetLastError();
+
+  if (N == 0) {
+    if (!accumulate) fkl::launch_fill_f32(grad_weight, V * d, 0.0f, s);
+    return hip_check("backward (empty batch)");
+  }
+  if (flags & FKL_FLAG_VALIDATE_IDX) {
+    r = validate_ids(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + q.flag), s);
+    if (r) return r;
+  }
+  float* pcoef = reinterpret_cast<float*>(ws + q.pcoef);
+  float* acoef = reinterpret_cast<float*>(ws + q.acoef);
+  float* lse2 = reinterpret_cast<float*>(ws + q.lse2);
+  float* ghacc = reinterpret_cast<float*>(ws + q.ghacc);
+  const float c2 = 1.4426950408889634f / T;
+  const int64_t eb = dtype == FKL_BF16 ? 2 : 4;
+  const int64_t zpitch = keep_pitch(V);
+  const int64_t zld = zpitch * eb;
+
+  const float* zk = topk_z;
+  if (!zk) {
+    float* zk_ws = reinterpret_cast<float*>(ws + q.zk);
+    fkl::launch_gather_dot(dtype, weight, hidden, topk_idx, d, 0, N, K, zk_ws, s);
+    zk = zk_ws;
+  }
+  fkl::launch_bwd_prep(topk_logit, lse, grad_loss, 0, N, K, T, pcoef, acoef, lse2, s);
+  fkl::launch_g_from_z(dtype, logits, zpitch, V, topk_idx, zk, pcoef, acoef, lse2, N, K, c2, s);
+  // grad_hidden over all rows in one launch (tiles of 256 rows reach 256 * zld bytes)
+  fkl::launch_grad_hidden(dtype, logits, zpitch, weight, d, 0, zpitch, V, N, false, ghacc, s);
+  fkl::launch_reduce_grad_hidden(dtype, ghacc, 1, N, d, grad_hidden, 0, s);
+  // grad_W over row blocks whose rows stay within the 32-bit offsets of one operand
+  const int64_t rmax = kMaxBlockBytes / zld;
+  const int64_t nb = fkl::ceil_div(N, rmax);
+  int64_t rb = fkl::round_up(fkl::ceil_div(N, nb), 64);
+  if (rb > rmax) rb = fkl::ceil_div(N, nb);
+  const unsigned char* zb = static_cast<const unsigned char*>(logits);
+  for (int64_t row0 = 0; row0 < N; row0 += rb) {
+    const int64_t nrows = (N - row0) < rb ? (N - row0) : rb;
+    fkl::launch_grad_w(dtype, zb + row0 * zld, zpitch, hidden, d, 0, zpitch, V, row0, nrows,
+                       accumulate || row0 > 0, grad_weight, s);
   }
   return hip_check("backward launch");
 }

@@ -61,26 +61,135 @@ __device__ __forceinline__ void accumulate_out(float* p, float v, int accumulate
 
 // ------------------------------------------------------------------ forward
 
-template <class P, class C>
-__global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_logits_lse(
-    const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
-    int64_t nrows, int64_t n_vt, int64_t n_tt, float c2, float2* __restrict__ part,
-    int64_t part_ld) {
-  static_assert(C::kWM == kSliceVocab, "one LSE partial per wave row-slice");
-  int64_t vt, tt;
-  if (!TileGroups<4, 8>::coords(n_vt, n_tt, &vt, &tt)) return;
-  const int64_t ld = d * P::kBytes;
-  // MFMA rows = vocabulary entries (weight rows), columns = tokens, so each
-  // lane's accumulators belong to one token and the reduction over the
-  // vocabulary is mostly in-lane.
-  const Operand A = make_operand(W + vt * kBM * ld, ld, V - vt * kBM, d);
-  const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
-  f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
+template <class P>
+__device__ __forceinline__ void store4(unsigned char* p, const float (&v)[4]) {
+  if constexpr (P::kBytes == 2) {
+    const uint32_t lo = f32_to_bf16_rne(v[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
+    const uint32_t hi = f32_to_bf16_rne(v[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{lo, hi};
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
 
+// Values the logit-tile kernels write per accumulator element (a raw logit z
+// of token `tok` at output column `col`): row() loads what a token row needs,
+// the call operator gives the value.
+struct LogitValue {  // z itself, zero in the padding columns >= vlim
+  int64_t vlim;
+  struct Row {};
+  __device__ __forceinline__ Row row(int64_t) const { return Row{}; }
+  __device__ __forceinline__ float operator()(const Row&, float z, int64_t col) const {
+    return col < vlim ? z : 0.f;
+  }
+};
+struct GradValue {  // dense part of the logit gradient, acoef * 2^(z*c2 - lse2)
+  const float* acoef;
+  const float* lse2;
+  float c2;
+  int64_t vlim;   // columns >= vlim lie past the vocabulary (written as zero)
+  int64_t nrows;  // tokens of the block
+  struct Row {
+    float a, l2;
+  };
+  __device__ __forceinline__ Row row(int64_t tok) const {
+    return tok < nrows ? Row{acoef[tok], lse2[tok]} : Row{0.f, 0.f};
+  }
+  __device__ __forceinline__ float operator()(const Row& r, float z, int64_t col) const {
+    return col < vlim ? r.a * fast_exp2(z * c2 - r.l2) : 0.f;
+  }
+};
+
+// Writes f(z) for the wave's sub-tile of a logit tile (accumulator rows =
+// output columns w0.., accumulator columns = tokens t0..) into Out[token][column]
+// (row pitch out_ld bytes), for tokens < nrows and columns < ncols. Called by
+// every thread of the workgroup after the k-loop. NT marks the stores
+// nontemporal (data not read again soon).
+template <class P, class C, bool NT = false, class F>
+__device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::kMI][C::kNI], const F& f,
+                                                 int64_t w0, int64_t t0, int64_t nrows,
+                                                 int64_t ncols, unsigned char* __restrict__ out,
+                                                 int64_t out_ld) {
   const int lane = threadIdx.x & 63;
-  const int64_t v0 = vt * kBM + C::wave_m() * C::kWM;
-  if (v0 >= V) return;
+  if constexpr (P::kBytes == 2) {
+    // A lane holds 4 consecutive columns of one token, so direct stores would
+    // put 16 bytes into each of 32 output rows per instruction. Each wave
+    // instead transposes its 128 x 64 sub-tile through 16 KiB of the (now
+    // idle) stage LDS, laid out [token][column] in 256-byte rows, and writes 16
+    // bytes per lane, 16 lanes per contiguous row segment. The 16-byte unit u
+    // of row t sits at unit u ^ (t % 16), its 8-byte halves swapped when bit 4
+    // of t is set, so the 32 rows one write instruction touches hit 32
+    // distinct 8-byte bank positions.
+    static_assert(C::kWM == 128 && C::kWN == 64, "transpose layout of the eight-wave tile");
+    __syncthreads();  // every wave has drained its loads: the stage LDS is free
+    const int w = static_cast<int>(threadIdx.x >> 6);
+    unsigned char* tp =
+        PingPongLoop<C, false, false>::stage_arrays().s[w >> 2] + (w & 3) * (kDStageBytes / 4);
+#pragma unroll
+    for (int ni = 0; ni < C::kNI; ++ni) {
+      const int tl = ni * 32 + (lane & 31);
+      const typename F::Row rw = f.row(t0 + tl);
+      const int half = (lane >> 5) ^ ((tl >> 4) & 1);
+#pragma unroll
+      for (int mi = 0; mi < C::kMI; ++mi)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int64_t col = w0 + mi * 32 + 8 * g4 + 4 * (lane >> 5);
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = f(rw, acc[mi][ni][4 * g4 + j], col + j);
+          const int unit = (mi * 4 + g4) ^ (tl & 15);
+          store4<P>(tp + tl * 256 + unit * 16 + half * 8, v);
+        }
+    }
+    if (w0 >= ncols) return;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int tl = it * 4 + (lane >> 4), u = lane & 15;
+      u32x4_t x = lds_load16(tp + tl * 256 + (u ^ (tl & 15)) * 16);
+      if ((tl >> 4) & 1) x = u32x4_t{x[2], x[3], x[0], x[1]};
+      const int64_t tok = t0 + tl, col = w0 + u * 8;
+      if (tok < nrows && col < ncols) {
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + tok * out_ld + col * P::kBytes);
+        if constexpr (NT)
+          __builtin_nontemporal_store(x, dst);
+        else
+          *dst = x;
+      }
+    }
+    return;
+  }
+  if (w0 >= ncols) return;
+#pragma unroll
+  for (int ni = 0; ni < C::kNI; ++ni) {
+    const int64_t tok = t0 + ni * 32 + (lane & 31);
+    if (tok >= nrows) continue;
+    const typename F::Row rw = f.row(tok);
+    unsigned char* orow = out + tok * out_ld;
+#pragma unroll
+    for (int mi = 0; mi < C::kMI; ++mi)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int64_t col = w0 + mi * 32 + 8 * g4 + 4 * (lane >> 5);
+        if (col >= ncols) continue;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = f(rw, acc[mi][ni][4 * g4 + j], col + j);
+        store4<P>(orow + col * P::kBytes, v);
+      }
+  }
+}
+
+
+// Per token of the wave's sub-tile: running max and sum of 2^(z * c2) over its
+// 128 vocabulary rows v0.. (those below V), stored as the partial of slot
+// v0 / 128.
+template <class C>
+__device__ __forceinline__ void lse_partials(const f32x16_t (&acc)[C::kMI][C::kNI], int64_t v0,
+                                             int64_t V, int64_t t0, int64_t nrows, float c2,
+                                             float2* __restrict__ part, int64_t part_ld) {
+  const int lane = threadIdx.x & 63;
   const int64_t slot = v0 / kSliceVocab;
   const bool full = v0 + C::kWM <= V;
   const int vlim = full ? C::kWM : static_cast<int>(V - v0);
@@ -103,9 +212,36 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_logits_lse(
     const float so = __shfl_xor(s, 32);
     const float M = fmaxf(m, mo);
     const float S = (s > 0.f ? s * fast_exp2(m - M) : 0.f) + (so > 0.f ? so * fast_exp2(mo - M) : 0.f);
-    const int64_t tok = tt * kBN + C::wave_n() * C::kWN + ni * 32 + (lane & 31);
+    const int64_t tok = t0 + ni * 32 + (lane & 31);
     if (lane < 32 && tok < nrows) part[slot * part_ld + tok] = make_float2(M, S);
   }
+}
+
+// With KEEP the tile's logits are also written, rounded to the element type,
+// into Z[token][v] (row pitch zld bytes) for v < zcols, as zero for v >= V
+// (streaming stores: the backward reads them much later).
+template <class P, class C, bool KEEP>
+__global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_logits_lse(
+    const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
+    int64_t nrows, int64_t n_vt, int64_t n_tt, float c2, float2* __restrict__ part,
+    int64_t part_ld, unsigned char* __restrict__ Z, int64_t zld, int64_t zcols) {
+  static_assert(C::kWM == kSliceVocab, "one LSE partial per wave row-slice");
+  int64_t vt, tt;
+  if (!TileGroups<4, 8>::coords(n_vt, n_tt, &vt, &tt)) return;
+  const int64_t ld = d * P::kBytes;
+  // MFMA rows = vocabulary entries (weight rows), columns = tokens, so each
+  // lane's accumulators belong to one token and the reduction over the
+  // vocabulary is mostly in-lane.
+  const Operand A = make_operand(W + vt * kBM * ld, ld, V - vt * kBM, d);
+  const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
+  f32x16_t acc[C::kMI][C::kNI];
+  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
+
+  const int64_t v0 = vt * kBM + C::wave_m() * C::kWM;
+  if (v0 < V) lse_partials<C>(acc, v0, V, tt * kBN + C::wave_n() * C::kWN, nrows, c2, part, part_ld);
+  if constexpr (KEEP)
+    store_token_rows<P, C, true>(acc, LogitValue{V}, v0, tt * kBN + C::wave_n() * C::kWN, nrows, zcols,
+                           Z, zld);
 }
 
 template <class P>
@@ -276,18 +412,6 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const float* __restrict__ logi
   }
 }
 
-template <class P>
-__device__ __forceinline__ void store4(unsigned char* p, const float (&v)[4]) {
-  if constexpr (P::kBytes == 2) {
-    const uint32_t lo = f32_to_bf16_rne(v[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
-    const uint32_t hi = f32_to_bf16_rne(v[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{lo, hi};
-  } else {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  }
-}
-
 // Recompute the logit tile of rows [0, nrows) x vocabulary [v0, v0 + Vw) and
 // write G_dense = acoef * 2^(z*c2 - lse2) into the G block G[row][v - v0]
 // (row pitch gpitch elements; entries with v >= V are written as zero).
@@ -305,76 +429,10 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_gprod(
   f32x16_t acc[C::kMI][C::kNI];
   gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
 
-  const int lane = threadIdx.x & 63;
   const int64_t w0 = vt * kBM + C::wave_m() * C::kWM;  // slice-relative column of the wave
-  const int64_t gld = gpitch * P::kBytes;
-  if constexpr (P::kBytes == 2) {
-    // A lane holds 4 consecutive vocabulary entries of one token, so direct
-    // stores would put 16 bytes into each of 32 rows of G per instruction.
-    // Each wave instead transposes its 128 x 64 sub-tile through 16 KiB of the
-    // (now idle) stage LDS, laid out [token][vocabulary] in 256-byte rows, and
-    // writes 16 bytes per lane, 16 lanes per contiguous row segment. The
-    // 16-byte unit u of row t sits at unit u ^ (t % 16), its 8-byte halves
-    // swapped when bit 4 of t is set, so the 32 rows one write instruction
-    // touches hit 32 distinct 8-byte bank positions.
-    __syncthreads();  // every wave has drained its loads: the stage LDS is free
-    const int w = static_cast<int>(threadIdx.x >> 6);
-    unsigned char* tp =
-        PingPongLoop<C, false, false>::stage_arrays().s[w >> 2] + (w & 3) * (kDStageBytes / 4);
-    const int64_t t0 = tt * kBN + C::wave_n() * C::kWN;  // first token of the wave
-#pragma unroll
-    for (int ni = 0; ni < C::kNI; ++ni) {
-      const int tl = ni * 32 + (lane & 31);
-      const int64_t tok = t0 + tl;
-      const float a = tok < nrows ? acoef[tok] : 0.f;
-      const float l2 = tok < nrows ? lse2[tok] : 0.f;
-      const int half = (lane >> 5) ^ ((tl >> 4) & 1);
-#pragma unroll
-      for (int mi = 0; mi < C::kMI; ++mi)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int64_t col = w0 + mi * 32 + 8 * g4 + 4 * (lane >> 5);
-          float v[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            v[j] = (v0 + col + j < V) ? a * fast_exp2(acc[mi][ni][4 * g4 + j] * c2 - l2) : 0.f;
-          const int unit = (mi * 4 + g4) ^ (tl & 15);
-          store4<P>(tp + tl * 256 + unit * 16 + half * 8, v);
-        }
-    }
-    if (w0 >= Vw) return;
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int tl = it * 4 + (lane >> 4), u = lane & 15;
-      u32x4_t x = lds_load16(tp + tl * 256 + (u ^ (tl & 15)) * 16);
-      if ((tl >> 4) & 1) x = u32x4_t{x[2], x[3], x[0], x[1]};
-      const int64_t tok = t0 + tl, col = w0 + u * 8;
-      if (tok < nrows && col < Vw)
-        *reinterpret_cast<u32x4_t*>(G + tok * gld + col * P::kBytes) = x;
-    }
-    return;
-  }
-  if (w0 >= Vw) return;
-#pragma unroll
-  for (int ni = 0; ni < C::kNI; ++ni) {
-    const int64_t tok = tt * kBN + C::wave_n() * C::kWN + ni * 32 + (lane & 31);
-    if (tok >= nrows) continue;
-    const float a = acoef[tok];
-    const float l2 = lse2[tok];
-    unsigned char* grow = G + tok * gld;
-#pragma unroll
-    for (int mi = 0; mi < C::kMI; ++mi)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int64_t col = w0 + mi * 32 + 8 * g4 + 4 * (lane >> 5);
-        if (col >= Vw) continue;
-        float vals[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vals[j] = (v0 + col + j < V) ? a * fast_exp2(acc[mi][ni][4 * g4 + j] * c2 - l2) : 0.f;
-        store4<P>(grow + col * P::kBytes, vals);
-      }
-  }
+  const int64_t t0 = tt * kBN + C::wave_n() * C::kWN;  // first token of the wave
+  const GradValue f{acoef, lse2, c2, V - v0, nrows};
+  store_token_rows<P, C>(acc, f, w0, t0, nrows, Vw, G, gpitch * P::kBytes);
 }
 
 // One wave per row: for the teacher ids inside the slice [v0, v0 + Vw),
@@ -409,6 +467,81 @@ __global__ __launch_bounds__(64) void k_fixup(unsigned char* __restrict__ G, int
       reinterpret_cast<uint16_t*>(grow)[v - v0] = f32_to_bf16_rne(val);
     else
       reinterpret_cast<float*>(grow)[v - v0] = val;
+  }
+}
+
+// Kept-logits backward, one workgroup per row: turns the row's kept logits
+// z (element type P, zcols entries, the ones at v >= V zero) into its logit
+// gradient in place, G = acoef * 2^(z*c2 - lse2) below V and zero above, then
+// gives the teacher ids the exact value acoef * 2^(zk*c2 - lse2) - (sum of
+// pcoef over the equal ids), computed from the fp32 logit at the id (as
+// k_fixup does for a slice).
+constexpr int kGzThreads = 256;
+
+template <class P>
+__global__ __launch_bounds__(kGzThreads) void k_g_from_z(unsigned char* __restrict__ Z, int64_t zld,
+                                                  int64_t V, int64_t zcols,
+                                                  const int32_t* __restrict__ idx,
+                                                  const float* __restrict__ zk,
+                                                  const float* __restrict__ pcoef,
+                                                  const float* __restrict__ acoef,
+                                                  const float* __restrict__ lse2, int K, float c2) {
+  extern __shared__ int32_t sh_gz[];
+  int32_t* sid = sh_gz;
+  float* sp = reinterpret_cast<float*>(sh_gz + K);
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  unsigned char* zr = Z + row * zld;
+  const float a = acoef[row], l2 = lse2[row];
+  // Each element is read and written once: streaming (nontemporal) accesses
+  // keep the row out of the caches' reuse sets.
+  constexpr int kPer = 16 / P::kBytes;  // elements per 16-byte vector
+  constexpr int kU = 4;                 // vectors in flight per thread
+  const int64_t nvec = zcols / kPer;    // zcols is a multiple of the vector width
+  for (int64_t i0 = 0; i0 < nvec; i0 += kGzThreads * kU) {
+    u32x4_t x[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = i0 + u * kGzThreads + t;
+      if (i < nvec) x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(zr + i * 16));
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = i0 + u * kGzThreads + t;
+      if (i >= nvec) continue;
+      const int64_t v = i * kPer;
+      u32x4_t y;
+      if constexpr (P::kBytes == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float z0 = as_f32(x[u][e] << 16), z1 = as_f32(x[u][e] & 0xffff0000u);
+          const float g0 = v + 2 * e < V ? a * fast_exp2(z0 * c2 - l2) : 0.f;
+          const float g1 = v + 2 * e + 1 < V ? a * fast_exp2(z1 * c2 - l2) : 0.f;
+          y[e] = f32_to_bf16_rne(g0) | (static_cast<uint32_t>(f32_to_bf16_rne(g1)) << 16);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          y[e] = __builtin_bit_cast(uint32_t, v + e < V ? a * fast_exp2(as_f32(x[u][e]) * c2 - l2)
+                                                        : 0.f);
+      }
+      __builtin_nontemporal_store(y, reinterpret_cast<u32x4_t*>(zr + i * 16));
+    }
+  }
+  for (int k = t; k < K; k += kGzThreads) {
+    sid[k] = idx[row * K + k];
+    sp[k] = pcoef[row * K + k];
+  }
+  __syncthreads();  // the dense stores of the row are done before the id entries are rewritten
+  for (int k = t; k < K; k += kGzThreads) {
+    const int32_t v = sid[k];
+    float sum = 0.f;
+    for (int k2 = 0; k2 < K; ++k2) sum += (sid[k2] == v) ? sp[k2] : 0.f;
+    const float val = a * fast_exp2(zk[row * K + k] * c2 - l2) - sum;
+    if constexpr (P::kBytes == 2)
+      reinterpret_cast<uint16_t*>(zr)[v] = f32_to_bf16_rne(val);
+    else
+      reinterpret_cast<float*>(zr)[v] = val;
   }
 }
 
@@ -534,15 +667,29 @@ typedef TileCfg<2, 4> Cfg8;  // 8 waves, 128x64 per wave (bf16, ping-pong loop)
 
 void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64_t V,
                        int64_t row0, int64_t nrows, float c2, float2* part, int64_t part_ld,
-                       hipStream_t s) {
+                       void* Z, int64_t zpitch, hipStream_t s) {
   ScopedTimer timer_(KID_LOGITS_LSE, s);
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(V, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
+  const unsigned char* Wc = static_cast<const unsigned char*>(W);
   const unsigned grid = grouped_grid<4, 8>(n_vt, n_tt);
-  FKL_LAUNCH_GEMM(k_logits_lse, dtype, grid, s,
-                  static_cast<const unsigned char*>(W), Hc, d, V, nrows, n_vt, n_tt, c2, part,
-                  part_ld);
+  if (Z) {
+    unsigned char* Zc = static_cast<unsigned char*>(Z) + row0 * zpitch * eb;
+    if (dtype == 1)
+      k_logits_lse<BF16, Cfg8, true><<<grid, Cfg8::kThreads, 0, s>>>(
+          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, Zc, zpitch * eb, zpitch);
+    else
+      k_logits_lse<F32, Cfg4, true><<<grid, Cfg4::kThreads, 0, s>>>(
+          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, Zc, zpitch * eb, zpitch);
+  } else {
+    if (dtype == 1)
+      k_logits_lse<BF16, Cfg8, false><<<grid, Cfg8::kThreads, 0, s>>>(
+          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, nullptr, 0, 0);
+    else
+      k_logits_lse<F32, Cfg4, false><<<grid, Cfg4::kThreads, 0, s>>>(
+          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, nullptr, 0, 0);
+  }
 }
 
 void launch_gather_dot(int dtype, const void* W, const void* H, const int32_t* idx, int64_t d,
@@ -622,6 +769,22 @@ void launch_fixup(int dtype, void* G, int64_t gpitch, int64_t v0, int64_t Vw, co
     k_fixup<F32><<<static_cast<unsigned>(nrows), 64, shm, s>>>(
         static_cast<unsigned char*>(G), gpitch, v0, Vw, idx + row0 * K, zk, pcoef, acoef, lse2, K,
         c2);
+}
+
+void launch_g_from_z(int dtype, void* Z, int64_t zpitch, int64_t V, const int32_t* idx,
+                     const float* zk, const float* pcoef, const float* acoef, const float* lse2,
+                     int64_t nrows, int K, float c2, hipStream_t s) {
+  if (nrows <= 0) return;
+  ScopedTimer timer_(KID_G_FROM_Z, s);
+  const size_t shm = static_cast<size_t>(K) * 8;
+  const unsigned blocks = static_cast<unsigned>(nrows);
+  unsigned char* Zc = static_cast<unsigned char*>(Z);
+  if (dtype == 1)
+    k_g_from_z<BF16><<<blocks, kGzThreads, shm, s>>>(Zc, zpitch * 2, V, zpitch, idx, zk, pcoef, acoef,
+                                              lse2, K, c2);
+  else
+    k_g_from_z<F32><<<blocks, kGzThreads, shm, s>>>(Zc, zpitch * 4, V, zpitch, idx, zk, pcoef, acoef,
+                                             lse2, K, c2);
 }
 
 void launch_grad_hidden(int dtype, const void* G, int64_t gpitch, const void* W, int64_t d,

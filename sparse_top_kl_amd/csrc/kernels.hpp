@@ -16,9 +16,11 @@ inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
 inline int64_t lse_slots(int64_t V) { return ceil_div(V, 256) * 2; }
 
 // Forward, per chunk: partial (max, sum) of 2^(z * c2) per (vocab slice, token).
+// With Z non-null the chunk's logits are also kept: Z[row0 + r][v] (pitch zpitch
+// elements of the dtype) = z rounded to the dtype for v < V, zero for V <= v < zpitch.
 void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64_t V,
                        int64_t row0, int64_t nrows, float c2, float2* part, int64_t part_ld,
-                       hipStream_t s);
+                       void* Z, int64_t zpitch, hipStream_t s);
 // z at the teacher ids for rows [row0, row0 + nrows).
 void launch_gather_dot(int dtype, const void* W, const void* H, const int32_t* idx, int64_t d,
                        int64_t row0, int64_t nrows, int K, float* zk, hipStream_t s);
@@ -42,6 +44,11 @@ void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V,
 void launch_fixup(int dtype, void* G, int64_t gpitch, int64_t v0, int64_t Vw, const int32_t* idx,
                   const float* zk, const float* pcoef, const float* acoef, const float* lse2,
                   int64_t row0, int64_t nrows, int K, float c2, hipStream_t s);
+// Kept logits -> logit gradient in place, rows [0, nrows) of Z (pitch zpitch elements),
+// teacher-id entries included; idx, zk, pcoef, acoef and lse2 start at row 0 of Z.
+void launch_g_from_z(int dtype, void* Z, int64_t zpitch, int64_t V, const int32_t* idx,
+                     const float* zk, const float* pcoef, const float* acoef, const float* lse2,
+                     int64_t nrows, int K, float c2, hipStream_t s);
 // acc[nrows][d] (+)= G_block . W[v0 : v0 + Vw]  (Vlim entries of the slice lie below V).
 void launch_grad_hidden(int dtype, const void* G, int64_t gpitch, const void* W, int64_t d,
                         int64_t v0, int64_t Vw, int64_t Vlim, int64_t nrows, bool accumulate,

@@ -53,7 +53,8 @@ const char* kernel_name(int32_t kid) {
   static const char* names[KID_COUNT] = {
       "k_logits_lse", "k_gather_dot", "k_merge_loss", "k_reduce_loss",
       "k_bwd_prep",   "k_gprod",      "k_fixup",      "k_grad_hidden",
-      "k_reduce_gh",  "k_grad_w",     "k_fill_f32",   "k_validate_idx"};
+      "k_reduce_gh",  "k_grad_w",     "k_fill_f32",   "k_validate_idx",
+      "k_g_from_z"};
   return (kid >= 0 && kid < KID_COUNT) ? names[kid] : nullptr;
 }
 

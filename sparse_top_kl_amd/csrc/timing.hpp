@@ -20,6 +20,7 @@ enum KernelId : int32_t {
   KID_GRAD_W,
   KID_FILL,
   KID_VALIDATE,
+  KID_G_FROM_Z,
   KID_COUNT
 };
 

@@ -69,6 +69,12 @@ _SIGNATURES = {
                            _p, _p, _p, _p, _p, _sz, _p]),
     "fkl_backward": (_i32, [_p, _p, _p, _p, _p, _p, _p, _f32, _i64, _i64, _i64, _i64, _i32,
                             _i32, _u32, _p, _p, _p, _sz, _p]),
+    "fkl_keep_sizes": (_i32, [_i64, _i64, _i64, _i32, _i32,
+                              ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "fkl_forward_keep": (_i32, [_p, _p, _p, _p, _f32, _i64, _i64, _i64, _i64, _i32, _i32, _u32,
+                                _p, _p, _p, _p, _p, _sz, _p, _sz, _p]),
+    "fkl_backward_keep": (_i32, [_p, _p, _p, _p, _p, _p, _p, _f32, _i64, _i64, _i64, _i32,
+                                 _i32, _u32, _p, _sz, _p, _p, _p, _sz, _p]),
     "fkl_timing_enable": (_i32, [_i32]),
     "fkl_timing_reset": (_i32, []),
     "fkl_timing_read": (_i32, [_i32, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]),
@@ -212,6 +218,88 @@ def fkl_backward(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Ten
     return grad_hidden, grad_weight
 
 
+def keep_pitch(V: int) -> int:
+    """Row pitch (elements) of the kept-logits buffer: V rounded up to 64."""
+    return (V + 63) // 64 * 64
+
+
+def fkl_keep_sizes(N, d, V, K, dtype) -> tuple[int, int]:
+    """(kept-logits bytes, fkl_backward_keep workspace bytes)."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    z, b = _sz(0), _sz(0)
+    _check(lib().fkl_keep_sizes(N, d, V, K, code, ctypes.byref(z), ctypes.byref(b)))
+    return z.value, b.value
+
+
+def fkl_forward_keep(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Tensor,
+                     topk_logit: torch.Tensor, T: float, chunk: int, *,
+                     logits: torch.Tensor | None = None, validate: bool = False,
+                     workspace: torch.Tensor | None = None):
+    """Forward pass that also keeps the logits; returns (ForwardResult, logits
+    [N, keep_pitch(V)] in hidden's dtype). The logits serve one fkl_backward_keep."""
+    N, d = hidden.shape
+    V, K = weight.shape[0], topk_idx.shape[1]
+    code = dtype_code(hidden.dtype)
+    for t, n, dt in ((hidden, "hidden", None), (weight, "weight", hidden.dtype),
+                     (topk_idx, "topk_idx", torch.int32), (topk_logit, "topk_logit", torch.float32)):
+        _require(t, n, dt)
+    dev = hidden.device
+    fw, _ = fkl_workspace_size(N, d, V, K, chunk, code)
+    ws = workspace if workspace is not None else _workspace(fw, dev)
+    if logits is None:
+        logits = torch.empty(N, keep_pitch(V), dtype=hidden.dtype, device=dev)
+    else:
+        _require(logits, "logits", hidden.dtype)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    row_loss = torch.empty(N, dtype=torch.float32, device=dev)
+    topk_z = torch.empty(N, K, dtype=torch.float32, device=dev)
+    flags = FKL_FLAG_VALIDATE_IDX if validate else 0
+    _check(lib().fkl_forward_keep(_ptr(hidden), _ptr(weight), _ptr(topk_idx), _ptr(topk_logit),
+                                  float(T), chunk, N, d, V, K, code, flags, _ptr(loss), _ptr(lse),
+                                  _ptr(row_loss), _ptr(topk_z), _ptr(logits),
+                                  logits.numel() * logits.element_size(), _ptr(ws), ws.numel(),
+                                  _stream(dev)))
+    return ForwardResult(loss, lse, row_loss, topk_z), logits
+
+
+def fkl_backward_keep(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Tensor,
+                      topk_logit: torch.Tensor, lse: torch.Tensor, T: float,
+                      logits: torch.Tensor, *, topk_z: torch.Tensor | None = None,
+                      grad_loss: torch.Tensor | None = None,
+                      grad_weight: torch.Tensor | None = None, accumulate: bool = False,
+                      validate: bool = False, workspace: torch.Tensor | None = None):
+    """Backward from kept logits (which it overwrites with the logit gradient);
+    returns (grad_hidden, grad_weight fp32) as fkl_backward."""
+    N, d = hidden.shape
+    V, K = weight.shape[0], topk_idx.shape[1]
+    code = dtype_code(hidden.dtype)
+    for t, n, dt in ((hidden, "hidden", None), (weight, "weight", hidden.dtype),
+                     (topk_idx, "topk_idx", torch.int32), (topk_logit, "topk_logit", torch.float32),
+                     (lse, "lse", torch.float32), (logits, "logits", hidden.dtype)):
+        _require(t, n, dt)
+    if topk_z is not None:
+        _require(topk_z, "topk_z", torch.float32)
+    if grad_loss is not None:
+        _require(grad_loss, "grad_loss", torch.float32)
+    dev = hidden.device
+    _, bw = fkl_keep_sizes(N, d, V, K, code)
+    ws = workspace if workspace is not None else _workspace(bw, dev)
+    grad_hidden = torch.empty_like(hidden)
+    if grad_weight is None:
+        grad_weight = torch.empty(V, d, dtype=torch.float32, device=dev)
+    else:
+        _require(grad_weight, "grad_weight", torch.float32)
+    flags = (FKL_FLAG_ACCUMULATE_GRAD_W if accumulate else 0) | \
+        (FKL_FLAG_VALIDATE_IDX if validate else 0)
+    _check(lib().fkl_backward_keep(_ptr(hidden), _ptr(weight), _ptr(topk_idx), _ptr(topk_logit),
+                                   _ptr(lse), _ptr(topk_z), _ptr(grad_loss), float(T), N, d, V, K,
+                                   code, flags, _ptr(logits),
+                                   logits.numel() * logits.element_size(), _ptr(grad_hidden),
+                                   _ptr(grad_weight), _ptr(ws), ws.numel(), _stream(dev)))
+    return grad_hidden, grad_weight
+
+
 def fkl_timing_enable(on: bool) -> bool:
     """Turns per-kernel event timing on or off; returns the previous state."""
     return bool(lib().fkl_timing_enable(1 if on else 0))
@@ -248,34 +336,74 @@ def kernel_times() -> dict:
 
 
 class FusedChunkedKL(torch.autograd.Function):
-    """Autograd wrapper: saves lse and the gathered logits, not the N x V logits."""
+    """Autograd wrapper. The fused method saves lse and the gathered logits, not
+    the N x V logits; with keep=True the forward-chunked variant saves the
+    logits instead and its backward skips the recompute."""
 
     @staticmethod
-    def forward(ctx, hidden, weight, topk_idx, topk_logit, T, chunk):
+    def forward(ctx, hidden, weight, topk_idx, topk_logit, T, chunk, keep):
         shape = hidden.shape
         h2 = hidden.reshape(-1, shape[-1]).contiguous()
         idx = topk_idx.reshape(h2.shape[0], -1).to(torch.int32).contiguous()
         lg = topk_logit.reshape(h2.shape[0], -1).to(torch.float32).contiguous()
         w = weight.contiguous()
-        out = fkl_forward(h2, w, idx, lg, T, chunk)
-        ctx.save_for_backward(h2, w, idx, lg, out.lse, out.topk_z)
-        ctx.T, ctx.chunk, ctx.shape = T, chunk, shape
+        if keep:
+            out, z = fkl_forward_keep(h2, w, idx, lg, T, chunk)
+            ctx.save_for_backward(h2, w, idx, lg, out.lse, out.topk_z, z)
+        else:
+            out = fkl_forward(h2, w, idx, lg, T, chunk)
+            ctx.save_for_backward(h2, w, idx, lg, out.lse, out.topk_z)
+        ctx.T, ctx.chunk, ctx.shape, ctx.keep = T, chunk, shape, keep
         return out.loss
 
     @staticmethod
+    @torch.autograd.function.once_differentiable
     def backward(ctx, grad_loss):
-        h2, w, idx, lg, lse, zk = ctx.saved_tensors
         g = grad_loss.to(torch.float32).reshape(()).contiguous()
-        gh, gw = fkl_backward(h2, w, idx, lg, lse, ctx.T, ctx.chunk, topk_z=zk, grad_loss=g)
-        return gh.reshape(ctx.shape), gw.to(w.dtype), None, None, None, None
+        if ctx.keep:
+            h2, w, idx, lg, lse, zk, z = ctx.saved_tensors
+            gh, gw = fkl_backward_keep(h2, w, idx, lg, lse, ctx.T, z, topk_z=zk, grad_loss=g)
+        else:
+            h2, w, idx, lg, lse, zk = ctx.saved_tensors
+            gh, gw = fkl_backward(h2, w, idx, lg, lse, ctx.T, ctx.chunk, topk_z=zk, grad_loss=g)
+        return gh.reshape(ctx.shape), gw.to(w.dtype), None, None, None, None, None
+
+
+def choose_keep(N: int, d: int, V: int, K: int, dtype: torch.dtype, budget: int | None,
+                device=None) -> bool:
+    """Memory-budget rule of keep="auto": keep the logits when the kept logits
+    plus the keep-mode backward workspace fit in `budget` bytes (default: half
+    of the device memory free now)."""
+    zb, wb = fkl_keep_sizes(N, d, V, K, dtype)
+    if budget is None:
+        free, _ = torch.cuda.mem_get_info(device)
+        budget = free // 2
+    return zb + wb <= budget
 
 
 def fused_chunked_kl(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Tensor,
-                     topk_logit: torch.Tensor, T: float = 1.0, chunk: int = 2048) -> torch.Tensor:
+                     topk_logit: torch.Tensor, T: float = 1.0, chunk: int = 2048, *,
+                     keep_logits: bool | str = False,
+                     memory_budget: int | None = None) -> torch.Tensor:
     """Sum over tokens of T^2 KL(teacher top-K softmax || student softmax) at temperature T.
 
     hidden [..., d] (bf16 or fp32), weight [V, d] (LM head, nn.Linear layout),
     topk_idx / topk_logit [..., K]. Returns a 0-d fp32 tensor; gradients flow to
     hidden and weight.
+
+    keep_logits=False is the fused chunked method (memory linear in the tokens,
+    logits recomputed in the backward); True keeps the N x V logits for the
+    backward (the forward-chunked variant: no recompute, N * V elements more
+    memory); "auto" keeps them when they fit in memory_budget bytes (default:
+    half of the free device memory).
     """
-    return FusedChunkedKL.apply(hidden, weight, topk_idx, topk_logit, float(T), int(chunk))
+    keep = keep_logits
+    if keep == "auto":
+        V, d = weight.shape
+        N = hidden.numel() // hidden.shape[-1]
+        keep = choose_keep(N, d, V, topk_idx.shape[-1], hidden.dtype, memory_budget,
+                           hidden.device)
+    elif not isinstance(keep, bool):
+        raise ValueError(f"keep_logits must be True, False or 'auto' (got {keep_logits!r})")
+    return FusedChunkedKL.apply(hidden, weight, topk_idx, topk_logit, float(T), int(chunk),
+                                bool(keep))

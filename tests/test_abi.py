@@ -140,3 +140,78 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(fkl, "LIB_PATH", "/nonexistent/libfkl.so")
     with pytest.raises(RuntimeError, match="missing"):
         fkl.lib()
+
+
+# ----------------------------------------------------------- kept-logits variant
+
+def test_keep_sizes_are_rows_times_padded_vocab():
+    for N, d, V, K, dt, eb in ((32768, 3072, 128256, 100, fkl.FKL_BF16, 2),
+                               (131072, 2880, 201088, 100, fkl.FKL_BF16, 2),
+                               (512, 512, 8192, 100, fkl.FKL_F32, 4),
+                               (7, 16, 1001, 5, fkl.FKL_BF16, 2)):
+        z, b = fkl.fkl_keep_sizes(N, d, V, K, dt)
+        assert z == N * fkl.keep_pitch(V) * eb
+        assert fkl.keep_pitch(V) % 64 == 0 and 0 <= fkl.keep_pitch(V) - V < 64
+        # per-row coefficients (p, z at the ids, two scalars) and the fp32 grad_hidden rows
+        assert N * (8 * K + 8 + 4 * d) <= b <= N * (8 * K + 8 + 4 * d) + 6 * 256
+
+
+def test_keep_sizes_reject_a_vocabulary_too_large_to_keep():
+    # 256 kept rows must fit in 2 GiB: V * 2 bytes * 256 > 2^31 from V ~ 4.19M on
+    with pytest.raises(fkl.FklError) as e:
+        fkl.fkl_keep_sizes(16, 8, 5_000_000, 5, fkl.FKL_BF16)
+    assert e.value.status == fkl.FKL_E_UNSUPPORTED
+    fkl.fkl_keep_sizes(16, 8, 4_000_000, 5, fkl.FKL_BF16)
+
+
+def _fwd_keep(**over):
+    args = dict(hidden=A, weight=A, idx=A, logit=A, T=1.0, chunk=4, N=10, d=16, V=100, K=5,
+                dtype=fkl.FKL_BF16, flags=0, loss=A, lse=A, row_loss=None, topk_z=None,
+                logits=A, logits_bytes=1 << 40, ws=A, ws_bytes=1 << 40, stream=None)
+    args.update(over)
+    return fkl.lib().fkl_forward_keep(*args.values())
+
+
+def _bwd_keep(**over):
+    args = dict(hidden=A, weight=A, idx=A, logit=A, lse=A, topk_z=None, grad_loss=None, T=1.0,
+                N=10, d=16, V=100, K=5, dtype=fkl.FKL_BF16, flags=0, logits=A,
+                logits_bytes=1 << 40, gh=A, gw=A, ws=A, ws_bytes=1 << 40, stream=None)
+    args.update(over)
+    return fkl.lib().fkl_backward_keep(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(logits=None), fkl.FKL_E_ARG),
+    (dict(logits=A + 8), fkl.FKL_E_ARG),
+    (dict(logits_bytes=10 * 128 * 2 - 2), fkl.FKL_E_WORKSPACE),
+    (dict(hidden=None), fkl.FKL_E_ARG),
+    (dict(T=0.0), fkl.FKL_E_ARG),
+    (dict(flags=1), fkl.FKL_E_ARG),
+    (dict(ws_bytes=16), fkl.FKL_E_WORKSPACE),
+    (dict(V=5_000_000, d=8), fkl.FKL_E_UNSUPPORTED),
+])
+def test_forward_keep_validation(over, code):
+    assert _fwd_keep(**over) == code
+    assert fkl.fkl_last_error() != ""
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(logits=None), fkl.FKL_E_ARG),
+    (dict(logits=A + 4), fkl.FKL_E_ARG),
+    (dict(logits_bytes=10 * 128 * 2 - 2), fkl.FKL_E_WORKSPACE),
+    (dict(gh=None), fkl.FKL_E_ARG),
+    (dict(lse=None), fkl.FKL_E_ARG),
+    (dict(grad_loss=A + 1), fkl.FKL_E_ARG),
+    (dict(flags=4), fkl.FKL_E_ARG),
+    (dict(ws_bytes=1024), fkl.FKL_E_WORKSPACE),
+])
+def test_backward_keep_validation(over, code):
+    assert _bwd_keep(**over) == code
+    assert fkl.fkl_last_error() != ""
+
+
+def test_keep_buffers_one_byte_short_are_rejected():
+    """One byte less than fkl_keep_sizes reports, for either buffer, is an error."""
+    z, b = fkl.fkl_keep_sizes(10, 16, 100, 5, fkl.FKL_BF16)
+    assert _bwd_keep(logits_bytes=z - 1) == fkl.FKL_E_WORKSPACE
+    assert _bwd_keep(ws_bytes=b - 1) == fkl.FKL_E_WORKSPACE

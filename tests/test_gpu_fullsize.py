@@ -13,6 +13,9 @@ The fp64 oracle cannot afford the whole N x V problem, so these tests check
   * grad_W rows of sampled vocabulary ids against an independent PyTorch
     fp32 computation that builds its own log-sum-exp over the whole
     vocabulary (no value of the HIP path enters it).
+The forward-chunked variant (kept logits) runs on two of the workloads: its
+forward outputs must equal the fused forward's bitwise, and its gradients
+pass the same checks.
 Tolerances are those of the small-shape parity tests (bf16: 1e-3 relative on
 loss-like values, 2e-2 of the largest reference magnitude on gradients); the
 two summation properties use bounds derived in the test from bf16 rounding of
@@ -64,13 +67,18 @@ def _torch_grad_w_rows(h32, w32, idx, lg, T, vocab, chunk=2048):
     return (G.t().contiguous() @ h32).double().cpu().numpy()          # [S, d]
 
 
+# (workload, keep): keep=True runs the forward-chunked variant (kept logits)
+CASES = [(n, False) for n in FULL_WORKLOADS] + [("long32k", True), ("stress_b4_32k", True)]
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", FULL_WORKLOADS)
-def test_full_size_parity(name, gpu_device):
+@pytest.mark.parametrize("name,keep", CASES,
+                         ids=[n + ("-keep" if k else "") for n, k in CASES])
+def test_full_size_parity(name, keep, gpu_device):
     w = synth.WORKLOADS[name]
     tol = TOL[w.dtype]
-    announce(f"full size {name}: N={w.N} d={w.d} V={w.V} K={w.K} T={w.T} chunk={w.chunk} "
-             f"{w.dtype} ids={w.ids} (generating inputs)")
+    announce(f"full size {name}{' (kept logits)' if keep else ''}: N={w.N} d={w.d} V={w.V} "
+             f"K={w.K} T={w.T} chunk={w.chunk} {w.dtype} ids={w.ids} (generating inputs)")
     inp = synth.make_inputs(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     h = torch.from_numpy(inp["hidden"]).to(gpu_device).to(dt).contiguous()
@@ -79,8 +87,18 @@ def test_full_size_parity(name, gpu_device):
     lg = torch.from_numpy(inp["topk_logit"]).to(gpu_device)
 
     announce(f"full size {name}: HIP forward + backward")
-    out = fkl.fkl_forward(h, W, idx, lg, w.T, w.chunk)
-    gh, gw = fkl.fkl_backward(h, W, idx, lg, out.lse, w.T, w.chunk, topk_z=out.topk_z)
+    if keep:
+        out, z = fkl.fkl_forward_keep(h, W, idx, lg, w.T, w.chunk)
+        ref_out = fkl.fkl_forward(h, W, idx, lg, w.T, w.chunk)
+        for field in ("loss", "lse", "row_loss", "topk_z"):
+            assert torch.equal(getattr(out, field), getattr(ref_out, field)), field
+        del ref_out
+        gh, gw = fkl.fkl_backward_keep(h, W, idx, lg, out.lse, w.T, z, topk_z=out.topk_z)
+        torch.cuda.synchronize()
+        del z
+    else:
+        out = fkl.fkl_forward(h, W, idx, lg, w.T, w.chunk)
+        gh, gw = fkl.fkl_backward(h, W, idx, lg, out.lse, w.T, w.chunk, topk_z=out.topk_z)
     torch.cuda.synchronize()
     loss = out.loss.item()
     row_loss = out.row_loss.double().cpu().numpy()
