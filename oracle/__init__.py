@@ -9,7 +9,8 @@ method's arithmetic.
 
 Every function in ``kl_oracle`` is pinned by a CPU test against something
 other than itself (library routines, closed forms, brute force, finite
-differences); see ``tests/test_oracle.py``.
+differences); see ``tests/test_oracle.py``. ``topk_oracle`` (the teacher
+top-K cache) is pinned the same way in ``tests/test_oracle_topk.py``.
 """
 
 from .kl_oracle import (  # noqa: F401
@@ -19,3 +20,4 @@ from .kl_oracle import (  # noqa: F401
     student_logits,
     teacher_log_probs,
 )
+from .topk_oracle import teacher_logits, teacher_topk, topk_rows  # noqa: F401,E402

@@ -21,6 +21,21 @@ Stand-ins (no model weights, training data or evaluation suite is used):
                         65536-token run (the dense loss no longer runs at 64K,
                         iitak.ru fifth paragraph)
 
+Teacher side (inputs of the top-K cache producer; ``TEACHER_WORKLOADS``):
+  * ``teacher_tiny``    512 tokens, d=256, V=4096, fp32 (oracle-sized case)
+  * ``teacher_llama8b_32k``
+                        32768 tokens through a Llama-3.1-8B-shaped teacher
+                        head (d=4096, V=128256): the teacher of the student
+                        experiment on the iitak.ru page, fourth paragraph
+  * ``teacher_gptoss120b_b4_32k``
+                        batch 4 x 32K through a gpt-oss-120b-shaped head
+                        (d=2880, V=201088): the malakhovai.ru page's
+                        teacher-tensor example
+  Streams t = 4 (teacher hidden) and 5 (teacher weight); "normal" values as
+  for the student (N(0, 1) and N(0, 1/d)), or "integer" values drawn
+  uniformly from {-2, ..., 2} for both, so every logit is an exact small
+  integer in fp32 and in fp64 (and many logits tie).
+
 Recipe (fixed; tests depend on it):
   * streams ``numpy.random.default_rng([seed, t])`` with t = 0 hidden,
     1 weight, 2 ids, 3 teacher logits;
@@ -191,3 +206,55 @@ def small_workload(name="small", n=300, d=64, V=1000, K=100, T=1.0, dtype="fp32"
                    chunk=128, ids="uniform", seed=7) -> Workload:
     """A custom (usually tiny) workload with the same recipe."""
     return Workload(name, 1, n, d, V, K, T, dtype, chunk, ids, seed)
+
+
+@dataclasses.dataclass(frozen=True)
+class TeacherWorkload:
+    name: str
+    B: int
+    S: int
+    d: int
+    V: int
+    K: int
+    dtype: str          # "fp32" or "bf16"
+    chunk: int
+    seed: int
+    values: str = "normal"   # "normal" or "integer"
+
+    @property
+    def N(self) -> int:
+        return self.B * self.S
+
+
+TEACHER_WORKLOADS = {
+    w.name: w
+    for w in [
+        TeacherWorkload("teacher_tiny", 1, 512, 256, 4096, 100, "fp32", 128, 2001),
+        TeacherWorkload("teacher_llama8b_32k", 1, 32768, 4096, 128256, 100, "bf16", 2048, 2002),
+        TeacherWorkload("teacher_gptoss120b_b4_32k", 4, 32768, 2880, 201088, 100, "bf16", 4096,
+                        2003),
+    ]
+}
+
+
+def make_teacher_inputs(w: TeacherWorkload, n_rows: int | None = None) -> dict:
+    """Teacher hidden states [N, d] and teacher LM head [V, d] (fp32 arrays;
+    bf16 workloads hold bf16-representable values)."""
+    n = w.N if n_rows is None else n_rows
+    if w.values == "integer":
+        h = _rng(w.seed, 4).integers(-2, 3, size=(n, w.d)).astype(np.float32)
+        W = _rng(w.seed, 5).integers(-2, 3, size=(w.V, w.d)).astype(np.float32)
+    else:
+        h = _rng(w.seed, 4).standard_normal((n, w.d), dtype=np.float32)
+        W = _rng(w.seed, 5).standard_normal((w.V, w.d), dtype=np.float32)
+        W *= np.float32(1.0 / np.sqrt(w.d))
+        if w.dtype == "bf16":
+            h, W = round_to_bf16(h), round_to_bf16(W)
+    return {"workload": w, "hidden": h, "weight": W, "K": w.K, "chunk": w.chunk,
+            "dtype": w.dtype}
+
+
+def small_teacher_workload(name="teacher_small", n=300, d=64, V=1000, K=100, dtype="fp32",
+                           chunk=128, seed=9, values="normal") -> TeacherWorkload:
+    """A custom (usually tiny) teacher workload with the same recipe."""
+    return TeacherWorkload(name, 1, n, d, V, K, dtype, chunk, seed, values)

@@ -68,3 +68,20 @@ def test_workloads_have_the_stated_shapes():
     assert W["long32k"].T == 2.0 and W["long32k"].ids == "zipf"
     assert (W["gptoss20b_32k"].d, W["gptoss20b_32k"].V) == (2880, 201088)
     assert W["stress_b4_32k"].N == 131072 and W["stress_b1_64k"].N == 65536
+
+
+def test_teacher_workloads_and_recipe():
+    w = synth.TEACHER_WORKLOADS["teacher_llama8b_32k"]
+    assert (w.N, w.d, w.V, w.K, w.dtype) == (32768, 4096, 128256, 100, "bf16")
+    w = synth.TEACHER_WORKLOADS["teacher_gptoss120b_b4_32k"]
+    assert (w.N, w.d, w.V) == (131072, 2880, 201088)
+    small = synth.small_teacher_workload(n=40, d=32, V=300, dtype="bf16")
+    a = synth.make_teacher_inputs(small)
+    b = synth.make_teacher_inputs(small)
+    assert a["hidden"].shape == (40, 32) and a["weight"].shape == (300, 32)
+    np.testing.assert_array_equal(a["weight"], b["weight"])          # seeded
+    np.testing.assert_array_equal(synth.round_to_bf16(a["hidden"]), a["hidden"])
+    ints = synth.make_teacher_inputs(synth.small_teacher_workload(n=40, d=32, V=300,
+                                                                  values="integer"))
+    assert set(np.unique(ints["hidden"])) <= {-2.0, -1.0, 0.0, 1.0, 2.0}
+    assert set(np.unique(ints["weight"])) <= {-2.0, -1.0, 0.0, 1.0, 2.0}
