@@ -189,6 +189,35 @@ int32_t fkl_backward_keep(const void* hidden, const void* weight, const int32_t*
                           size_t logits_bytes, void* grad_hidden, float* grad_weight,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Teacher top-K cache
+ * -------------------
+ * The step before the loss: the pages run the teacher once and keep, for
+ * every position, its 100 most probable tokens ("Эффективная дистилляция
+ * знаний ..." (malakhovai.ru), second paragraph; "Multiverse Computing ...
+ * (iitak.ru)", third paragraph; "Wissensdestillation mit deutlich weniger
+ * GPU-Speicher", section "Teacher-Ausgaben einmalig zwischenspeichern").
+ * With l = hidden . weight^T (teacher final hidden states [N, d], teacher LM
+ * head [V, d] in nn.Linear layout, fp32 accumulation), per row r:
+ *   topk_idx[r]   the K ids with the largest l_rv, by value descending, ties
+ *                 to the lower id (the most probable tokens of the teacher
+ *                 softmax at any temperature, in order)
+ *   topk_logit[r] l_rv at those ids (fp32, exactly the accumulated values)
+ * These are the topk_idx / topk_logit inputs of fkl_forward. Logits must be
+ * finite. 1 <= K <= min(V, 1024); other shapes and dtypes as for the loss.
+ *
+ * fkl_topk_workspace_size: host-only; bytes of one chunk's fp32 logits
+ * (V * round_up(min(chunk, N), 64) * 4) plus per-row scratch.
+ * fkl_teacher_topk: flags must be 0. Rows are processed `chunk` at a time; the
+ * result does not depend on chunk. Rows whose candidate list overflows (more
+ * than 2048 logits at or above the K-th largest 128-vocab slice maximum,
+ * e.g. massive ties) take an exact but slower path. */
+int32_t fkl_topk_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
+                                int32_t dtype, size_t* bytes);
+int32_t fkl_teacher_topk(const void* hidden, const void* weight, int64_t N, int64_t d, int64_t V,
+                         int32_t K, int64_t chunk, int32_t dtype, uint32_t flags,
+                         int32_t* topk_idx, float* topk_logit, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Per-kernel timing, a profiling aid (off by default). While enabled, every
  * kernel launch the library makes is bracketed by two HIP events recorded on
  * the launch stream; the events cost a few microseconds of GPU time each.

@@ -60,6 +60,20 @@ void launch_grad_w(int dtype, const void* G, int64_t gpitch, const void* H, int6
                    int64_t v0, int64_t Vw, int64_t Vlim, int64_t row0, int64_t nrows,
                    bool accumulate, float* grad_w, hipStream_t s);
 
+// Teacher top-K cache, per chunk of rows [row0, row0 + nrows): the chunk's
+// fp32 logits LT[v][r] (pitch lt_ld floats) and per (row, 128-vocab slice)
+// maxima smax[r][slot] (pitch sm_ld) ...
+void launch_teacher_logits(int dtype, const void* W, const void* H, int64_t d, int64_t V,
+                           int64_t row0, int64_t nrows, float* LT, int64_t lt_ld,
+                           uint32_t* smax, int64_t sm_ld, hipStream_t s);
+// ... then per row the K largest (ids, values) sorted, ties to the lower id;
+// theta [nrows], cand [nrows][topk_capacity()] and count [nrows] are scratch.
+void launch_topk_select(const float* LT, int64_t lt_ld, int64_t V, const uint32_t* smax,
+                        int64_t sm_ld, int64_t nslots, int64_t nrows, int K, uint32_t* theta,
+                        uint64_t* cand, uint32_t* count, int32_t* out_idx, float* out_val,
+                        hipStream_t s);
+int topk_capacity();
+
 // Utilities.
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 void launch_validate_idx(const int32_t* idx, int64_t N, int K, int64_t V, int32_t* flag,

@@ -54,7 +54,8 @@ const char* kernel_name(int32_t kid) {
       "k_logits_lse", "k_gather_dot", "k_merge_loss", "k_reduce_loss",
       "k_bwd_prep",   "k_gprod",      "k_fixup",      "k_grad_hidden",
       "k_reduce_gh",  "k_grad_w",     "k_fill_f32",   "k_validate_idx",
-      "k_g_from_z"};
+      "k_g_from_z",   "k_teacher_logits", "k_topk_threshold", "k_topk_collect",
+      "k_topk_final"};
   return (kid >= 0 && kid < KID_COUNT) ? names[kid] : nullptr;
 }
 

@@ -21,6 +21,10 @@ enum KernelId : int32_t {
   KID_FILL,
   KID_VALIDATE,
   KID_G_FROM_Z,
+  KID_TEACHER_LOGITS,
+  KID_TOPK_THRESHOLD,
+  KID_TOPK_COLLECT,
+  KID_TOPK_FINAL,
   KID_COUNT
 };
 

@@ -75,6 +75,10 @@ _SIGNATURES = {
                                 _p, _p, _p, _p, _p, _sz, _p, _sz, _p]),
     "fkl_backward_keep": (_i32, [_p, _p, _p, _p, _p, _p, _p, _f32, _i64, _i64, _i64, _i32,
                                  _i32, _u32, _p, _sz, _p, _p, _p, _sz, _p]),
+    "fkl_topk_workspace_size": (_i32, [_i64, _i64, _i64, _i32, _i64, _i32,
+                                       ctypes.POINTER(_sz)]),
+    "fkl_teacher_topk": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _i64, _i32, _u32, _p, _p, _p,
+                                _sz, _p]),
     "fkl_timing_enable": (_i32, [_i32]),
     "fkl_timing_reset": (_i32, []),
     "fkl_timing_read": (_i32, [_i32, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]),
@@ -298,6 +302,33 @@ def fkl_backward_keep(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torc
                                    logits.numel() * logits.element_size(), _ptr(grad_hidden),
                                    _ptr(grad_weight), _ptr(ws), ws.numel(), _stream(dev)))
     return grad_hidden, grad_weight
+
+
+def fkl_topk_workspace_size(N, d, V, K, chunk, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    b = _sz(0)
+    _check(lib().fkl_topk_workspace_size(N, d, V, K, chunk, code, ctypes.byref(b)))
+    return b.value
+
+
+def fkl_teacher_topk(hidden: torch.Tensor, weight: torch.Tensor, K: int, chunk: int = 2048, *,
+                     workspace: torch.Tensor | None = None):
+    """Teacher top-K cache: per row of hidden [N, d] the K largest logits of
+    hidden . weight^T (weight [V, d]), ordered by value with ties to the lower
+    id. Returns (ids int32 [N, K], logits fp32 [N, K])."""
+    N, d = hidden.shape
+    V = weight.shape[0]
+    code = dtype_code(hidden.dtype)
+    _require(hidden, "hidden")
+    _require(weight, "weight", hidden.dtype)
+    dev = hidden.device
+    nb = fkl_topk_workspace_size(N, d, V, K, chunk, code)
+    ws = workspace if workspace is not None else _workspace(nb, dev)
+    idx = torch.empty(N, K, dtype=torch.int32, device=dev)
+    val = torch.empty(N, K, dtype=torch.float32, device=dev)
+    _check(lib().fkl_teacher_topk(_ptr(hidden), _ptr(weight), N, d, V, K, chunk, code, 0,
+                                  _ptr(idx), _ptr(val), _ptr(ws), ws.numel(), _stream(dev)))
+    return idx, val
 
 
 def fkl_timing_enable(on: bool) -> bool:

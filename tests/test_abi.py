@@ -215,3 +215,38 @@ def test_keep_buffers_one_byte_short_are_rejected():
     z, b = fkl.fkl_keep_sizes(10, 16, 100, 5, fkl.FKL_BF16)
     assert _bwd_keep(logits_bytes=z - 1) == fkl.FKL_E_WORKSPACE
     assert _bwd_keep(ws_bytes=b - 1) == fkl.FKL_E_WORKSPACE
+
+
+# ------------------------------------------------------------- teacher top-K
+
+def test_topk_workspace_holds_one_chunk_of_fp32_logits():
+    for N, d, V, K, chunk in ((32768, 4096, 128256, 100, 2048), (100, 64, 1000, 10, 4096)):
+        b = fkl.fkl_topk_workspace_size(N, d, V, K, chunk, fkl.FKL_BF16)
+        rows = min(N, chunk)
+        lt = V * ((rows + 63) // 64 * 64) * 4
+        assert lt <= b <= lt + rows * (4 * ((V + 127) // 128 + 4) + 8 + 2048 * 8) + 6 * 256
+
+
+def _topk(**over):
+    args = dict(hidden=A, weight=A, N=10, d=16, V=100, K=5, chunk=4, dtype=fkl.FKL_BF16,
+                flags=0, idx=A, val=A, ws=A, ws_bytes=1 << 40, stream=None)
+    args.update(over)
+    return fkl.lib().fkl_teacher_topk(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(hidden=None), fkl.FKL_E_ARG),
+    (dict(idx=None), fkl.FKL_E_ARG),
+    (dict(val=A + 2), fkl.FKL_E_ARG),
+    (dict(weight=A + 8), fkl.FKL_E_ARG),
+    (dict(K=0), fkl.FKL_E_ARG),
+    (dict(K=101), fkl.FKL_E_ARG),
+    (dict(K=1025, V=5000), fkl.FKL_E_UNSUPPORTED),
+    (dict(d=12), fkl.FKL_E_UNSUPPORTED),
+    (dict(chunk=0), fkl.FKL_E_ARG),
+    (dict(flags=1), fkl.FKL_E_ARG),
+    (dict(ws_bytes=64), fkl.FKL_E_WORKSPACE),
+])
+def test_teacher_topk_validation(over, code):
+    assert _topk(**over) == code
+    assert fkl.fkl_last_error() != ""
