@@ -8,6 +8,8 @@ JSON line: throughput in tokens/s, the MFMA roofline of the dominant kernel
 peak HBM of one step, a sampled parity check against the fp64 oracle and the
 oracle's own host throughput on a bounded sample of the same rows.
 
+With --teacher-topk it times the teacher top-K cache producer
+(fkl_teacher_topk over a teacher workload) and prints that line instead.
 With --keep-logits the step is the forward-chunked variant instead
 (fkl_forward_keep + fkl_backward_keep: the logits are kept in an N x V buffer
 and not recomputed, 6 N d V flops per step).
@@ -126,6 +128,141 @@ def cpu_baseline(inp, gpu_rows: dict, budget_s: float):
     return base, parity
 
 
+def cpu_baseline_topk(inp, gpu_idx, gpu_val, budget_s: float):
+    """Time the fp64 teacher top-K oracle on a bounded prefix of the rows and
+    compare those rows with the GPU's."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    w = inp["workload"]
+
+    def run(n):
+        t0 = time.perf_counter()
+        logits = oracle.teacher_logits(inp["hidden"][:n], inp["weight"])
+        ids, vals = oracle.topk_rows(logits, w.K)
+        return logits, ids, vals, time.perf_counter() - t0
+
+    _, _, _, t1 = run(32)
+    _, _, _, t2 = run(64)
+    per_row = max((t2 - t1) / 32, 1e-6)
+    fixed = max(t1 - 32 * per_row, 0.0)
+    n = int((budget_s - fixed) / per_row) // 32 * 32
+    n = max(32, min(w.N, n))
+    logits, ids, vals, t = run(n)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    tol = 1e-5  # fp32 accumulation against fp64 (relative, absolute floor 1)
+    val_err = float(np.max(np.abs(gpu_val[:n] - vals) / np.maximum(np.abs(vals), 1.0)))
+    # ids may order near-equal logits differently from fp64; what is unique is
+    # the k-th largest value, so the GPU's k-th id must carry it (in fp64)
+    at = np.take_along_axis(logits, gpu_idx[:n].astype(np.int64), axis=1)
+    rank_err = float(np.max(np.abs(at - vals) / np.maximum(np.abs(vals), 1.0)))
+    distinct = all(len(set(r.tolist())) == w.K for r in gpu_idx[:n])
+    rows_differ = int((gpu_idx[:n] != ids).any(axis=1).sum())
+    parity = {"rows": n, "value_rel_err": val_err, "kth_id_value_rel_err": rank_err,
+              "rows_ordering_near_ties_differently": rows_differ,
+              "ok": bool(val_err <= tol and rank_err <= 2 * tol and distinct)}
+    base = {"value": n / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {w.N} rows of {w.name}: fp64 logits (NumPy BLAS) and "
+                      f"exact per-row selection, {t:.1f} s"}
+    return base, parity
+
+
+def run_teacher_topk(args, torch, fkl, synth, dev):
+    """Benchmark of the teacher top-K cache producer (fkl_teacher_topk)."""
+    name = args.workload if args.workload in synth.TEACHER_WORKLOADS else "teacher_llama8b_32k"
+    w = synth.TEACHER_WORKLOADS[name]
+    log(f"[bench] generating {w.name}: N={w.N} d={w.d} V={w.V} K={w.K} chunk={w.chunk} {w.dtype}")
+    inp = synth.make_teacher_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    h = torch.from_numpy(inp["hidden"]).to(dev).to(dt).contiguous()
+    W = torch.from_numpy(inp["weight"]).to(dev).to(dt).contiguous()
+    torch.cuda.synchronize()
+    input_bytes = sum(t.numel() * t.element_size() for t in (h, W))
+    nb = fkl.fkl_topk_workspace_size(w.N, w.d, w.V, w.K, w.chunk, dt)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+    def step():
+        return fkl.fkl_teacher_topk(h, W, w.K, w.chunk, workspace=ws)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    del ws
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    idx, val = step()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev)
+    gpu_idx, gpu_val = idx.cpu().numpy(), val.double().cpu().numpy()
+    del idx, val
+
+    log(f"[bench] timing {args.steps} steps")
+    fkl.fkl_timing_reset()
+    fkl.fkl_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fkl.fkl_timing_enable(False)
+    ktimes = fkl.kernel_times()
+    ms_step = elapsed / args.steps * 1e3
+    log(f"[bench] {ms_step:.2f} ms/step")
+    kernels = {k: {"launches_per_step": n / args.steps, "avg_ms": ms / n,
+                   "ms_per_step": ms / args.steps} for k, (n, ms) in ktimes.items()}
+    dom = max(ktimes, key=lambda k: ktimes[k][1])
+    n_launch, dom_ms = ktimes[dom]
+    avg_ms = dom_ms / n_launch
+    peak_tf = PEAK_TFLOPS[w.dtype]
+    flops_step = 2.0 * w.N * w.d * w.V
+    if dom == "k_teacher_logits":
+        flops_launch = flops_step / (n_launch / args.steps)
+        achieved = flops_launch / (avg_ms * 1e-3) / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak_tf,
+                    "unit": "TFLOP/s", "frac": achieved / peak_tf,
+                    "traffic": load_traffic(dom, w.name), "flops_per_launch": flops_launch,
+                    "avg_launch_ms": avg_ms}
+    else:
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": None, "traffic": load_traffic(dom, w.name),
+                    "avg_launch_ms": avg_ms}
+    if args.no_cpu_baseline:
+        base, parity = None, None
+    else:
+        log("[bench] oracle on the host (cpu_baseline and sampled parity)")
+        base, parity = cpu_baseline_topk(inp, gpu_idx, gpu_val, args.cpu_seconds)
+    result = {
+        "metric": "teacher top-K cache tokens/s + % bf16 MFMA peak",
+        "value": w.N * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "N": w.N, "d": w.d, "V": w.V,
+                   "K": w.K, "chunk": w.chunk},
+        "mfma_frac_step": flops_step / (ms_step * 1e-3) / (peak_tf * 1e12),
+        "flops_per_step": flops_step,
+        "roofline": roofline,
+        "cpu_baseline": base,
+        "parity_sampled": parity,
+        "peak_hbm_gib": peak / 2**30,
+        "peak_hbm_path_gib": (peak - input_bytes) / 2**30,
+        "workspace_gib": nb / 2**30,
+        "kernels": kernels,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +273,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--keep-logits", action="store_true",
                     help="time the forward-chunked variant (kept logits, no recompute)")
+    ap.add_argument("--teacher-topk", action="store_true",
+                    help="time the teacher top-K cache producer instead of the loss "
+                         "(workload teacher_llama8b_32k unless --workload names a teacher one)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy this many MiB once on the device (a plain "
                          "copy of known size for calibrating rocprofv3 byte counters)")
@@ -155,6 +295,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.teacher_topk:
+        run_teacher_topk(args, torch, fkl, synth, dev)
+        return
     w = synth.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name}: N={w.N} d={w.d} V={w.V} K={w.K} T={w.T} "
         f"chunk={w.chunk} {w.dtype}")

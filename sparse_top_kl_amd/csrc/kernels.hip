@@ -694,7 +694,7 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_teacher_log
         const int vr = acc_row(mi, r, lane);
         if (full || vr < vlim) {
           const float x = acc[mi][ni][r];
-          if (tok_ok) LT[(v0 + vr) * lt_ld + tok] = x;
+          if (tok_ok) __builtin_nontemporal_store(x, LT + (v0 + vr) * lt_ld + tok);
           best = max(best, ord_f32(x));
         }
       }
@@ -775,37 +775,48 @@ __global__ __launch_bounds__(64) void k_topk_threshold(const uint32_t* __restric
   if (lane == 0) theta[tok] = prefix;
 }
 
-// Grid (token blocks of 64, vocabulary ranges): wave w of a workgroup reads
-// vocabulary rows v = begin + w, begin + w + 4, ... of its range, lane = token,
-// so each load is one 256-byte row segment of the stored logits. Keys at or
-// above the token's threshold are appended to its list (count may exceed the
-// capacity: the final kernel then takes the exact path).
+// Grid (token blocks of 256, vocabulary ranges): lane l of wave w reads
+// tokens t0 + 4l .. t0 + 4l + 3 of vocabulary rows begin + w, begin + w + 4,
+// ..., so each wave load is one 1 KiB row segment of the stored logits
+// (streaming loads: every value is read once). Keys at or above the token's
+// threshold are appended to its list (the count may pass the capacity: the
+// final kernel then takes the exact path).
+constexpr int kCollectTokens = 256;
 __global__ __launch_bounds__(256) void k_topk_collect(const float* __restrict__ LT, int64_t lt_ld,
                                                       int64_t V, int64_t nrows, int64_t vrange,
                                                       const uint32_t* __restrict__ theta,
                                                       uint64_t* __restrict__ cand, int cap,
                                                       uint32_t* __restrict__ count) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t tok = static_cast<int64_t>(blockIdx.x) * 64 + lane;
-  if (tok >= nrows) return;
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * kCollectTokens + 4 * lane;
+  if (tok0 >= nrows) return;
   const int64_t vb = static_cast<int64_t>(blockIdx.y) * vrange;
   const int64_t ve = vb + vrange < V ? vb + vrange : V;
-  const uint32_t th = theta[tok];
-  constexpr int kU = 8;  // loads in flight per thread
+  uint32_t th[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) th[j] = tok0 + j < nrows ? theta[tok0 + j] : 0xffffffffu;
+  constexpr int kU = 2;  // 16-byte loads in flight per thread (2, 4, 8 measured alike)
   for (int64_t v = vb + w; v < ve; v += 4 * kU) {
-    float x[kU];
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    f32x4_t x[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int64_t vv = v + 4 * u;
-      x[u] = vv < ve ? LT[vv * lt_ld + tok] : -INFINITY;
+      x[u] = vv < ve ? __builtin_nontemporal_load(
+                           reinterpret_cast<const f32x4_t*>(LT + vv * lt_ld + tok0))
+                     : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int64_t vv = v + 4 * u;
-      const uint32_t o = ord_f32(x[u]);
-      if (vv < ve && o >= th) {
-        const uint32_t pos = atomicAdd(&count[tok], 1u);
-        if (pos < static_cast<uint32_t>(cap)) cand[tok * cap + pos] = topk_key(o, vv);
+      const float xs[4] = {x[u][0], x[u][1], x[u][2], x[u][3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t o = ord_f32(xs[j]);
+        if (vv < ve && o >= th[j] && th[j] != 0xffffffffu) {
+          const uint32_t pos = atomicAdd(&count[tok0 + j], 1u);
+          if (pos < static_cast<uint32_t>(cap)) cand[(tok0 + j) * cap + pos] = topk_key(o, vv);
+        }
       }
     }
   }
@@ -1124,7 +1135,7 @@ void launch_topk_select(const float* LT, int64_t lt_ld, int64_t V, const uint32_
     // counts start at zero (a fill kernel, not a memset node, so graph capture stays safe)
     launch_fill_f32(reinterpret_cast<float*>(count), nrows, 0.0f, s);
     ScopedTimer timer_(KID_TOPK_COLLECT, s);
-    const int64_t tb = ceil_div(nrows, 64);
+    const int64_t tb = ceil_div(nrows, kCollectTokens);
     int64_t ranges = ceil_div(2048, tb);  // about 2048 workgroups
     if (ranges < 1) ranges = 1;
     if (ranges > ceil_div(V, 64)) ranges = ceil_div(V, 64);
