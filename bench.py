@@ -128,6 +128,20 @@ def cpu_baseline(inp, gpu_rows: dict, budget_s: float):
     return base, parity
 
 
+def calibration_copy(args, torch, dev):
+    """A plain device copy of known size (for calibrating byte counters)."""
+    if args.copy_calibration_mib <= 0:
+        return
+    nb = args.copy_calibration_mib << 20
+    src = torch.ones(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
+
+
 def cpu_baseline_topk(inp, gpu_idx, gpu_val, budget_s: float):
     """Time the fp64 teacher top-K oracle on a bounded prefix of the rows and
     compare those rows with the GPU's."""
@@ -183,6 +197,8 @@ def run_teacher_topk(args, torch, fkl, synth, dev):
 
     def step():
         return fkl.fkl_teacher_topk(h, W, w.K, w.chunk, workspace=ws)
+
+    calibration_copy(args, torch, dev)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -331,15 +347,7 @@ def main():
                                  grad_weight=gw, workspace=ws_b)
         return out, gh
 
-    if args.copy_calibration_mib > 0:
-        nb = args.copy_calibration_mib << 20
-        src = torch.ones(nb, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
+    calibration_copy(args, torch, dev)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
