@@ -23,6 +23,21 @@ chunked method reorganises exactly:
   the softmax, the KL divergence is taken between the two softened
   distributions, and the KL term is multiplied by T squared.
 
+Extensions (options of the loss): the same page, same section, says the
+student's total loss mixes the KL term with the ordinary cross-entropy on the
+true labels. With hard labels y_r (a label < 0 marks a row without one) and a
+mixing weight alpha, and per-row weights w_r (padding masks, mean
+reductions), the loss becomes
+
+    loss = sum_r w_r * (a_kl * T^2 * KL_r + a_ce * CE_r),
+    CE_r = lse1_r - z_r,y_r,   lse1_r = log sum_v exp(z_rv)   (temperature 1)
+
+with a_kl = alpha, a_ce = 1 - alpha when labels are given and a_kl = 1,
+a_ce = 0 otherwise (readings: the formula itself was stripped from the page;
+the cross-entropy is taken at temperature 1, as in the classic recipe the
+page describes, and the mixture is convex). Rows with w_r = 0 contribute
+nothing, whatever their teacher logits.
+
 Readings taken where the pages are silent (each listed in the design notes):
 forward KL(p_t || p_s); the teacher softmax is renormalised over its K cached
 entries; the student is normalised over the full vocabulary; tokens are summed
@@ -94,7 +109,8 @@ def teacher_log_probs(topk_logit, T: float):
 
 def forward_backward(hidden, w_store, topk_idx, topk_logit, T: float,
                      grad_scale: float = 1.0, want_grads: bool = True,
-                     block_rows: int = 128) -> dict:
+                     block_rows: int = 128, row_weight=None, labels=None,
+                     alpha: float = 1.0) -> dict:
     """Loss, per-row pieces and gradients of the top-K KL loss, in fp64.
 
     hidden [N, d], w_store [V, d] (any float dtype; upcast exactly),
@@ -104,8 +120,10 @@ def forward_backward(hidden, w_store, topk_idx, topk_logit, T: float,
 
     Returns a dict with ``loss`` (float, math.fsum of rows), ``row_loss`` [N],
     ``lse`` [N] (natural log of sum exp(z/T)), ``topk_z`` [N, K] (raw z at
-    the ids), and when ``want_grads``: ``grad_hidden`` [N, d] and
-    ``grad_w`` [V, d] (stored layout).
+    the ids), ``lse1`` [N] (log sum exp(z), temperature 1), and when
+    ``want_grads``: ``grad_hidden`` [N, d] and ``grad_w`` [V, d] (stored
+    layout). ``row_weight`` [N], ``labels`` [N] and ``alpha`` as in the module
+    docstring.
     """
     h = _f64(hidden)
     w = _f64(w_store)
@@ -117,10 +135,22 @@ def forward_backward(hidden, w_store, topk_idx, topk_logit, T: float,
     if idx.size and (idx.min() < 0 or idx.max() >= v):
         raise ValueError("token id out of range")
     T = float(T)
-    log_p, p = teacher_log_probs(topk_logit, T)
+    wr = np.ones(n) if row_weight is None else _f64(row_weight).reshape(n)
+    if labels is None:
+        a_kl, a_ce, y = 1.0, 0.0, np.full(n, -1)
+    else:
+        a_kl, a_ce, y = float(alpha), 1.0 - float(alpha), np.asarray(labels).reshape(n)
+        if np.any(y >= v):
+            raise ValueError("label out of range")
+    # rows with weight 0 contribute nothing: give them finite placeholder
+    # teacher logits so that a padding row of -inf entries stays harmless
+    tl = np.array(topk_logit, dtype=np.float64)
+    tl[wr == 0] = 0.0
+    log_p, p = teacher_log_probs(tl, T)
 
     row_loss = np.zeros(n)
     lse = np.zeros(n)
+    lse1 = np.zeros(n)
     topk_z = np.zeros(idx.shape)
     grad_h = np.zeros((n, d)) if want_grads else None
     grad_w = np.zeros((v, d)) if want_grads else None
@@ -135,15 +165,29 @@ def forward_backward(hidden, w_store, topk_idx, topk_logit, T: float,
         pb, lpb = p[r0:r1], log_p[r0:r1]
         # p * (log p - log p_s), with the 0 * log 0 = 0 convention
         term = np.where(pb > 0, pb * (np.where(pb > 0, lpb, 0.0) - log_ps), 0.0)
-        row_loss[r0:r1] = T * T * term.sum(axis=1)
+        kl = T * T * term.sum(axis=1)
+        lse1_b = logsumexp_rows(z)
+        yb = y[r0:r1]
+        has = yb >= 0
+        zy = np.where(has, np.take_along_axis(z, np.where(has, yb, 0)[:, None], axis=1)[:, 0], 0.0)
+        ce = np.where(has, lse1_b - zy, 0.0)
+        wb = wr[r0:r1]
+        row_loss[r0:r1] = np.where(wb != 0, wb * (a_kl * kl + a_ce * ce), 0.0)
         lse[r0:r1] = lse_b
+        lse1[r0:r1] = lse1_b
         topk_z[r0:r1] = zk
         if want_grads:
             q = np.exp(u - lse_b[:, None])
             P = np.zeros_like(q)
             rows = np.repeat(np.arange(r1 - r0), idx.shape[1])
             np.add.at(P, (rows, idx[r0:r1].ravel()), pb.ravel())
-            G = grad_scale * T * (q * pb.sum(axis=1, keepdims=True) - P)
+            G = a_kl * T * (q * pb.sum(axis=1, keepdims=True) - P)
+            if a_ce != 0.0:
+                q1 = np.exp(z - lse1_b[:, None])
+                E = np.zeros_like(q1)
+                E[np.arange(r1 - r0)[has], yb[has]] = 1.0
+                G = G + a_ce * (q1 * has[:, None] - E)
+            G = grad_scale * wb[:, None] * G
             grad_h[r0:r1] = G @ w
             grad_w += G.T @ h[r0:r1]
 
@@ -151,6 +195,7 @@ def forward_backward(hidden, w_store, topk_idx, topk_logit, T: float,
         "loss": math.fsum(row_loss.tolist()),
         "row_loss": row_loss,
         "lse": lse,
+        "lse1": lse1,
         "topk_z": topk_z,
     }
     if want_grads:
@@ -160,7 +205,8 @@ def forward_backward(hidden, w_store, topk_idx, topk_logit, T: float,
 
 
 def brute_force(hidden, w_store, topk_idx, topk_logit, T: float,
-                grad_scale: float = 1.0) -> dict:
+                grad_scale: float = 1.0, row_weight=None, labels=None,
+                alpha: float = 1.0) -> dict:
     """The same quantities written as scalar Python loops (tiny inputs only).
 
     No NumPy arithmetic: every sum is ``math.fsum`` over Python floats, so a
@@ -173,6 +219,9 @@ def brute_force(hidden, w_store, topk_idx, topk_logit, T: float,
     L = [[float(x) for x in row] for row in np.asarray(topk_logit, dtype=np.float64)]
     n, d, v = len(H), len(H[0]), len(W)
     T = float(T)
+    Wr = [1.0] * n if row_weight is None else [float(x) for x in row_weight]
+    Y = [-1] * n if labels is None else [int(x) for x in labels]
+    a_kl, a_ce = (1.0, 0.0) if labels is None else (float(alpha), 1.0 - float(alpha))
     row_loss, lse_all, grad_h = [], [], []
     grad_w = [[0.0] * d for _ in range(v)]
     contrib_w = [[[] for _ in range(d)] for _ in range(v)]
@@ -180,6 +229,12 @@ def brute_force(hidden, w_store, topk_idx, topk_logit, T: float,
         z = [math.fsum(H[r][j] * W[c][j] for j in range(d)) for c in range(v)]
         mz = max(z)
         lse = mz / T + math.log(math.fsum(math.exp((zc - mz) / T) for zc in z))
+        lse1 = mz + math.log(math.fsum(math.exp(zc - mz) for zc in z))
+        if Wr[r] == 0.0:
+            row_loss.append(0.0)
+            lse_all.append(lse)
+            grad_h.append([0.0] * d)
+            continue
         a = [x / T for x in L[r]]
         ma = max(a)
         ln = ma + math.log(math.fsum(math.exp(x - ma) for x in a if x != -math.inf))
@@ -188,14 +243,18 @@ def brute_force(hidden, w_store, topk_idx, topk_logit, T: float,
         for k, c in enumerate(I[r]):
             if pt[k] > 0.0:
                 terms.append(pt[k] * ((a[k] - ln) - (z[c] / T - lse)))
-        row_loss.append(T * T * math.fsum(terms))
+        ce = (lse1 - z[Y[r]]) if Y[r] >= 0 else 0.0
+        row_loss.append(Wr[r] * (a_kl * T * T * math.fsum(terms) + a_ce * ce))
         lse_all.append(lse)
         sp = math.fsum(pt)
         G = []
         for c in range(v):
             q = math.exp(z[c] / T - lse)
             Pc = math.fsum(pt[k] for k, cc in enumerate(I[r]) if cc == c)
-            G.append(grad_scale * T * (q * sp - Pc))
+            g = a_kl * T * (q * sp - Pc)
+            if Y[r] >= 0:
+                g += a_ce * (math.exp(z[c] - lse1) - (1.0 if c == Y[r] else 0.0))
+            G.append(grad_scale * Wr[r] * g)
         grad_h.append([math.fsum(G[c] * W[c][j] for c in range(v)) for j in range(d)])
         for c in range(v):
             for j in range(d):

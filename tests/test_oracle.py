@@ -378,3 +378,139 @@ def test_pins_accept_the_oracle():
 @pytest.mark.parametrize("mutant", _mutants(), ids=lambda f: f.__name__)
 def test_planted_mistakes_are_caught(mutant):
     assert not all(_pin_suite(mutant))
+
+
+# ------------------------------------------- options: row weights, hard labels
+
+def _labels(seed, n, v, ignore=()):
+    y = np.random.default_rng(seed).integers(0, v, size=n).astype(np.int32)
+    for r in ignore:
+        y[r] = -1
+    return y
+
+
+@pytest.mark.parametrize("T", [1.0, 2.5])
+def test_pure_hard_label_term_equals_torch_cross_entropy(T):
+    """alpha = 0: only the cross-entropy at temperature 1 remains, whatever T."""
+    h, w, idx, logit = _rand_problem(21, n=6, d=5, v=17, k=4)
+    y = _labels(3, 6, 17)
+    out = _run(h, w, idx, logit, T, labels=y, alpha=0.0)
+    ht = torch.tensor(h, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    ref = torch.nn.functional.cross_entropy(ht @ wt.T, torch.tensor(y, dtype=torch.long),
+                                            reduction="sum")
+    ref.backward()
+    assert out["loss"] == pytest.approx(ref.item(), rel=1e-12)
+    np.testing.assert_allclose(out["grad_hidden"], ht.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(out["grad_w"], wt.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(out["lse1"], torch.logsumexp(ht @ wt.T, 1).detach().numpy(),
+                               rtol=1e-13)
+
+
+@pytest.mark.parametrize("T", [1.0, 2.0])
+def test_options_match_brute_force(T):
+    h, w, idx, logit = _rand_problem(22, n=5, d=4, v=11, k=4, dup=True)
+    wr = np.array([1.0, 0.0, 0.25, 2.0, 1.0])
+    y = _labels(4, 5, 11, ignore=(3,))
+    kw = dict(row_weight=wr, labels=y, alpha=0.3, grad_scale=-0.7)
+    out = _run(h, w, idx, logit, T, **kw)
+    bf = kl_oracle.brute_force(h, w, idx, logit, T, **kw)
+    assert out["loss"] == pytest.approx(bf["loss"], rel=1e-12)
+    for key in ("row_loss", "grad_hidden", "grad_w"):
+        np.testing.assert_allclose(out[key], bf[key], rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("T", [1.0, 3.0])
+def test_option_gradients_match_finite_differences(T):
+    h, w, idx, logit = _rand_problem(23, n=3, d=4, v=9, k=5)
+    kw = dict(row_weight=np.array([0.5, 1.5, 1.0]), labels=_labels(5, 3, 9), alpha=0.6)
+    out = _run(h, w, idx, logit, T, **kw)
+
+    def f():
+        return _run(h, w, idx, logit, T, want_grads=False, **kw)["loss"]
+
+    np.testing.assert_allclose(out["grad_hidden"], _fd_grad(f, h), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(out["grad_w"], _fd_grad(f, w), rtol=1e-6, atol=1e-8)
+
+
+def test_zero_weight_rows_contribute_nothing_even_if_padding():
+    h, w, idx, logit = _rand_problem(24, n=4, d=5, v=12, k=3)
+    logit = logit.copy()
+    logit[2, :] = -np.inf                      # a padding row: no teacher entry at all
+    wr = np.array([1.0, 1.0, 0.0, 1.0])
+    out = _run(h, w, idx, logit, 1.5, row_weight=wr, labels=np.array([1, 2, -1, 3]), alpha=0.5)
+    assert out["row_loss"][2] == 0.0 and np.all(out["grad_hidden"][2] == 0.0)
+    keep = [0, 1, 3]
+    sub = _run(h[keep], w, idx[keep], logit[keep], 1.5, labels=np.array([1, 2, 3]), alpha=0.5)
+    assert out["loss"] == pytest.approx(sub["loss"], rel=1e-13)
+    np.testing.assert_allclose(out["grad_w"], sub["grad_w"], rtol=1e-12, atol=1e-15)
+
+
+def test_weights_one_over_n_give_the_mean_and_neutral_options_change_nothing():
+    h, w, idx, logit = _rand_problem(25, n=6, d=5, v=14, k=4)
+    base = _run(h, w, idx, logit, 2.0)
+    mean = _run(h, w, idx, logit, 2.0, row_weight=np.full(6, 1 / 6))
+    assert mean["loss"] == pytest.approx(base["loss"] / 6, rel=1e-13)
+    np.testing.assert_allclose(mean["grad_w"], base["grad_w"] / 6, rtol=1e-12)
+    alpha_one = _run(h, w, idx, logit, 2.0, labels=_labels(6, 6, 14), alpha=1.0)
+    no_labels = _run(h, w, idx, logit, 2.0, alpha=0.2)     # alpha ignored without labels
+    for o in (alpha_one, no_labels):
+        assert o["loss"] == pytest.approx(base["loss"], rel=1e-13)
+        np.testing.assert_allclose(o["grad_hidden"], base["grad_hidden"], rtol=1e-12, atol=1e-15)
+
+
+def _option_mutants():
+    """Plausible slips in the options, each a wrapper around the oracle."""
+    base = kl_oracle.forward_backward
+
+    def swapped_mixture(h, w, idx, logit, T, labels=None, alpha=1.0, **k):
+        return base(h, w, idx, logit, T, labels=labels,
+                    alpha=(1.0 - alpha) if labels is not None else alpha, **k)
+
+    def weights_on_loss_only(h, w, idx, logit, T, row_weight=None, **k):
+        out = dict(base(h, w, idx, logit, T, row_weight=row_weight, **k))
+        if k.get("want_grads", True):
+            plain = base(h, w, idx, logit, T, **k)
+            out["grad_hidden"], out["grad_w"] = plain["grad_hidden"], plain["grad_w"]
+        return out
+
+    def ce_at_temperature_t(h, w, idx, logit, T, labels=None, alpha=1.0, **k):
+        out = dict(base(h, w, idx, logit, T, labels=labels, alpha=alpha, **k))
+        if labels is not None:
+            kl = base(h, w, idx, logit, T, want_grads=False)["loss"]
+            ce_t = base(np.asarray(h) / T, w, idx, logit, 1.0, labels=labels, alpha=0.0,
+                        want_grads=False)["loss"]
+            out["loss"] = alpha * kl + (1.0 - alpha) * ce_t
+        return out
+
+    return [swapped_mixture, weights_on_loss_only, ce_at_temperature_t]
+
+
+def _option_pin_suite(fb):
+    ok = []
+    h, w, idx, logit = _rand_problem(21, n=6, d=5, v=17, k=4)
+    y = _labels(3, 6, 17)
+    out = fb(h, w, idx, logit, 2.5, labels=y, alpha=0.0)
+    ref = torch.nn.functional.cross_entropy(torch.tensor(h) @ torch.tensor(w).T,
+                                            torch.tensor(y, dtype=torch.long), reduction="sum")
+    ok.append(math.isclose(out["loss"], ref.item(), rel_tol=1e-10))
+    h, w, idx, logit = _rand_problem(23, n=3, d=4, v=9, k=5)
+    kw = dict(row_weight=np.array([0.5, 1.5, 1.0]), labels=_labels(5, 3, 9), alpha=0.6)
+    out = fb(h, w, idx, logit, 3.0, **kw)
+
+    def f():
+        return fb(h, w, idx, logit, 3.0, want_grads=False, **kw)["loss"]
+
+    ok.append(np.allclose(out["grad_hidden"], _fd_grad(f, h), rtol=1e-5, atol=1e-7))
+    bf = oracle.brute_force(h, w, idx, logit, 3.0, **kw)
+    ok.append(math.isclose(out["loss"], bf["loss"], rel_tol=1e-10))
+    return ok
+
+
+def test_option_pins_accept_the_oracle():
+    assert all(_option_pin_suite(kl_oracle.forward_backward))
+
+
+@pytest.mark.parametrize("mutant", _option_mutants(), ids=lambda f: f.__name__)
+def test_planted_option_mistakes_are_caught(mutant):
+    assert not all(_option_pin_suite(mutant))
