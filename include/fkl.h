@@ -134,6 +134,49 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
                      int64_t V, int32_t K, int32_t dtype, uint32_t flags, void* grad_hidden,
                      float* grad_weight, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Loss options
+ * ------------
+ * The ml-book page ("Дистилляция и сжатие моделей", section "Как это
+ * работает: мягкие метки и температура") describes the student's total loss
+ * as the KL term plus the ordinary cross-entropy on the true labels; training
+ * also needs padding rows masked out and mean reductions. The *_ex entry
+ * points take these through a struct (NULL = the plain loss above):
+ *
+ *   loss = sum_r w_r (a_kl T^2 KL_r + a_ce CE_r),  CE_r = lse1_r - z_r,y_r,
+ *   lse1_r = ln sum_v exp(z_rv)   (temperature 1),
+ *   a_kl = alpha, a_ce = 1 - alpha with labels; a_kl = 1, a_ce = 0 without.
+ *
+ * Rows with w_r = 0 contribute nothing (their teacher logits may then all
+ * be -inf, e.g. padding). A mean over the valid rows is row_weight = mask /
+ * mask.sum(). The gradients follow: G_r = s w_r (a_kl T (softmax_T(z_r) sum_k
+ * p_rk - scatter(p_r)) + a_ce (softmax_1(z_r) - onehot(y_r))). */
+typedef struct fkl_loss_options {
+  const float* row_weight; /* [N] fp32 per-row weights, or NULL (all 1) */
+  const int32_t* labels;   /* [N] hard labels in [0, V), a value < 0 for a row
+                              without one; or NULL (no cross-entropy term) */
+  float alpha;             /* with labels: weight of the KL term (the
+                              cross-entropy gets 1 - alpha); finite */
+  float* lse1;             /* [N] fp32 ln sum_v exp(z_rv) at temperature 1:
+                              written by the forward when non-NULL; read by
+                              the backward, which requires it when labels are
+                              given and T != 1 (else it may be NULL) */
+} fkl_loss_options;
+
+/* fkl_forward, fkl_backward, fkl_forward_keep and fkl_backward_keep with loss
+ * options (the opts pointer may be NULL). Under FKL_FLAG_VALIDATE_IDX labels
+ * >= V are rejected too. row_loss holds the weighted per-row loss. */
+int32_t fkl_forward_ex(const void* hidden, const void* weight, const int32_t* topk_idx,
+                       const float* topk_logit, float T, int64_t chunk, int64_t N, int64_t d,
+                       int64_t V, int32_t K, int32_t dtype, uint32_t flags,
+                       const fkl_loss_options* opts, float* loss, float* lse, float* row_loss,
+                       float* topk_z, void* workspace, size_t workspace_bytes, void* stream);
+int32_t fkl_backward_ex(const void* hidden, const void* weight, const int32_t* topk_idx,
+                        const float* topk_logit, const float* lse, const float* topk_z,
+                        const float* grad_loss, float T, int64_t chunk, int64_t N, int64_t d,
+                        int64_t V, int32_t K, int32_t dtype, uint32_t flags,
+                        const fkl_loss_options* opts, void* grad_hidden, float* grad_weight,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Forward-chunked variant ("keep the logits")
  * ------------------------------------------
  * The pages name a less aggressive alternative to the fused method: the loss
@@ -188,6 +231,20 @@ int32_t fkl_backward_keep(const void* hidden, const void* weight, const int32_t*
                           int32_t K, int32_t dtype, uint32_t flags, void* logits,
                           size_t logits_bytes, void* grad_hidden, float* grad_weight,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+int32_t fkl_forward_keep_ex(const void* hidden, const void* weight, const int32_t* topk_idx,
+                            const float* topk_logit, float T, int64_t chunk, int64_t N,
+                            int64_t d, int64_t V, int32_t K, int32_t dtype, uint32_t flags,
+                            const fkl_loss_options* opts, float* loss, float* lse,
+                            float* row_loss, float* topk_z, void* logits, size_t logits_bytes,
+                            void* workspace, size_t workspace_bytes, void* stream);
+int32_t fkl_backward_keep_ex(const void* hidden, const void* weight, const int32_t* topk_idx,
+                             const float* topk_logit, const float* lse, const float* topk_z,
+                             const float* grad_loss, float T, int64_t N, int64_t d, int64_t V,
+                             int32_t K, int32_t dtype, uint32_t flags,
+                             const fkl_loss_options* opts, void* logits, size_t logits_bytes,
+                             void* grad_hidden, float* grad_weight, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* Teacher top-K cache
  * -------------------

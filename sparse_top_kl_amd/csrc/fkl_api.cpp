@@ -45,9 +45,10 @@ struct Plan {
   // backward blocking: row blocks of bw_rows x vocabulary slices of bw_width
   int64_t bw_rows, bw_width, bw_pitch;
   // forward workspace offsets
-  size_t f_part, f_rowloss, f_topkz, f_flag, f_total;
+  size_t f_part, f_part_ce, f_rowloss, f_topkz, f_zy, f_flag, f_total;
   // backward workspace offsets
-  size_t b_G, b_ghacc, b_pcoef, b_acoef, b_lse2, b_zk, b_flag, b_total;
+  size_t b_G, b_ghacc, b_pcoef, b_acoef, b_lse2, b_zk, b_bcoef, b_lse12, b_ycoef, b_zy, b_flag,
+      b_total;
 };
 
 // Predicted cost of the backward contractions for row blocks of rc rows and
@@ -147,10 +148,14 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_
   size_t off = 0;
   p.f_part = off;
   off = align_up(off + static_cast<size_t>(p.slot_cap) * p.chunk_cap * 8);
+  p.f_part_ce = off;  // temperature-1 partials (cross-entropy term at T != 1)
+  off = align_up(off + static_cast<size_t>(p.slot_cap) * p.chunk_cap * 8);
   p.f_rowloss = off;
   off = align_up(off + static_cast<size_t>(N) * 4);
   p.f_topkz = off;
   off = align_up(off + static_cast<size_t>(N) * K * 4);
+  p.f_zy = off;  // z at the labels
+  off = align_up(off + static_cast<size_t>(N) * 4);
   p.f_flag = off;
   off = align_up(off + 4);
   p.f_total = off;
@@ -169,6 +174,14 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_
   off = align_up(off + rows * 4);
   p.b_zk = off;
   off = align_up(off + rows * K * 4);
+  p.b_bcoef = off;
+  off = align_up(off + rows * 4);
+  p.b_lse12 = off;
+  off = align_up(off + rows * 4);
+  p.b_ycoef = off;
+  off = align_up(off + rows * 4);
+  p.b_zy = off;
+  off = align_up(off + rows * 4);
   p.b_flag = off;
   off = align_up(off + 4);
   p.b_total = off;
@@ -181,18 +194,20 @@ int32_t hip_check(const char* where) {
   return FKL_OK;
 }
 
-// Runs the device-side id check and waits for its verdict.
+// Runs the device-side id check (teacher ids in [0, V), labels below V) and
+// waits for its verdict.
 int32_t validate_ids(const int32_t* idx, int64_t N, int32_t K, int64_t V, int32_t* dflag,
-                     hipStream_t s) {
+                     hipStream_t s, const int32_t* labels = nullptr) {
   fkl::launch_fill_f32(reinterpret_cast<float*>(dflag), 1, 0.0f, s);
-  fkl::launch_validate_idx(idx, N, K, V, dflag, s);
+  fkl::launch_validate_idx(idx, N, K, V, false, dflag, s);
+  if (labels) fkl::launch_validate_idx(labels, N, 1, V, true, dflag, s);
   int32_t r = hip_check("id validation launch");
   if (r) return r;
   int32_t host = 0;
   hipError_t e = hipMemcpyAsync(&host, dflag, 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(FKL_E_HIP, "id validation: %s", hipGetErrorString(e));
-  if (host != 0) return fail(FKL_E_INDEX, "a teacher id is outside [0, V)");
+  if (host != 0) return fail(FKL_E_INDEX, "a teacher id is outside [0, V) or a label >= V");
   return FKL_OK;
 }
 
@@ -215,7 +230,7 @@ int32_t check_keep(int64_t V, int32_t dtype) {
 // Workspace of fkl_backward_keep: per-row teacher coefficients, z at the ids
 // and the fp32 grad_hidden accumulator, for all N rows.
 struct KeepPlan {
-  size_t pcoef, acoef, lse2, zk, ghacc, flag, total;
+  size_t pcoef, acoef, lse2, zk, ghacc, bcoef, lse12, ycoef, zy, flag, total;
 };
 KeepPlan make_keep_plan(int64_t N, int64_t d, int32_t K) {
   KeepPlan q{};
@@ -231,19 +246,40 @@ KeepPlan make_keep_plan(int64_t N, int64_t d, int32_t K) {
   off = align_up(off + n * K * 4);
   q.ghacc = off;
   off = align_up(off + n * d * 4);
+  q.bcoef = off;
+  off = align_up(off + n * 4);
+  q.lse12 = off;
+  off = align_up(off + n * 4);
+  q.ycoef = off;
+  off = align_up(off + n * 4);
+  q.zy = off;
+  off = align_up(off + n * 4);
   q.flag = off;
   off = align_up(off + 4);
   q.total = off;
   return q;
 }
 
+// Loss options: their pointers' alignment, alpha, and (backward) lse1 when
+// the cross-entropy term has its own softmax.
+int32_t check_options(const fkl_loss_options* o, float T, bool backward) {
+  if (!o) return FKL_OK;
+  if (!std::isfinite(o->alpha)) return fail(FKL_E_ARG, "alpha must be finite");
+  if (!aligned(o->row_weight, 4) || !aligned(o->labels, 4) || !aligned(o->lse1, 4))
+    return fail(FKL_E_ARG, "row_weight, labels and lse1 must be 4-byte aligned");
+  if (backward && o->labels && T != 1.0f && !o->lse1)
+    return fail(FKL_E_ARG, "lse1 (from the forward) is required with labels when T != 1");
+  return FKL_OK;
+}
+
 // fkl_forward and fkl_forward_keep: the chunk loop, with the logits kept in
 // `logits` (N rows of keep_pitch(V) elements) when it is non-null.
 int32_t forward_impl(const void* hidden, const void* weight, const int32_t* topk_idx,
                      const float* topk_logit, float T, int64_t chunk, int64_t N, int64_t d,
-                     int64_t V, int32_t K, int32_t dtype, uint32_t flags, float* loss, float* lse,
-                     float* row_loss, float* topk_z, void* logits, size_t logits_bytes,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     int64_t V, int32_t K, int32_t dtype, uint32_t flags,
+                     const fkl_loss_options* o, float* loss, float* lse, float* row_loss,
+                     float* topk_z, void* logits, size_t logits_bytes, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   int32_t r = check_shapes(N, d, V, K, chunk, dtype);
   if (r) return r;
   if (!std::isfinite(T) || !(T > 0.0f)) return fail(FKL_E_ARG, "T must be finite and > 0");
@@ -256,6 +292,8 @@ int32_t forward_impl(const void* hidden, const void* weight, const int32_t* topk
   if (!aligned(topk_idx, 4) || !aligned(topk_logit, 4) || !aligned(loss, 4) || !aligned(lse, 4) ||
       !aligned(row_loss, 4) || !aligned(topk_z, 4))
     return fail(FKL_E_ARG, "fp32/int32 arrays must be 4-byte aligned");
+  r = check_options(o, T, false);
+  if (r) return r;
   const int64_t zpitch = keep_pitch(V);
   if (logits) {
     r = check_keep(V, dtype);
@@ -277,22 +315,36 @@ int32_t forward_impl(const void* hidden, const void* weight, const int32_t* topk
     fkl::launch_fill_f32(loss, 1, 0.0f, s);
     return hip_check("forward (empty batch)");
   }
+  const int32_t* labels = o ? o->labels : nullptr;
   if (flags & FKL_FLAG_VALIDATE_IDX) {
-    r = validate_ids(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + p.f_flag), s);
+    r = validate_ids(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + p.f_flag), s, labels);
     if (r) return r;
   }
   float2* part = reinterpret_cast<float2*>(ws + p.f_part);
   float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + p.f_rowloss);
   float* zk = topk_z ? topk_z : reinterpret_cast<float*>(ws + p.f_topkz);
   const float c2 = 1.4426950408889634f / T;
+  const bool two_sm = labels && T != 1.0f;  // the cross-entropy needs its own softmax
+  fkl::MergeOpts mo{};
+  mo.part_ce = two_sm ? reinterpret_cast<float2*>(ws + p.f_part_ce) : nullptr;
+  mo.labels = labels;
+  mo.row_weight = o ? o->row_weight : nullptr;
+  mo.a_kl = labels ? o->alpha : 1.0f;
+  mo.a_ce = labels ? 1.0f - o->alpha : 0.0f;
+  mo.lse1 = o ? o->lse1 : nullptr;
 
   fkl::launch_gather_dot(dtype, weight, hidden, topk_idx, d, 0, N, K, zk, s);
+  if (labels) {
+    float* zy = reinterpret_cast<float*>(ws + p.f_zy);
+    fkl::launch_gather_dot(dtype, weight, hidden, labels, d, 0, N, 1, zy, s);
+    mo.zy = zy;
+  }
   for (int64_t row0 = 0; row0 < N; row0 += p.chunk_cap) {
     const int64_t nrows = (N - row0) < p.chunk_cap ? (N - row0) : p.chunk_cap;
-    fkl::launch_logits_lse(dtype, weight, hidden, d, V, row0, nrows, c2, part, p.chunk_cap, logits,
-                           zpitch, s);
+    fkl::launch_logits_lse(dtype, weight, hidden, d, V, row0, nrows, c2, part, p.chunk_cap,
+                           const_cast<float2*>(mo.part_ce), logits, zpitch, s);
     fkl::launch_merge_loss(part, p.chunk_cap, p.nslots, zk, topk_logit, row0, nrows, K, T, lse, rl,
-                           s);
+                           mo, s);
   }
   fkl::launch_reduce_loss(rl, N, loss, s);
   return hip_check("forward launch");
@@ -336,7 +388,19 @@ int32_t fkl_forward(const void* hidden, const void* weight, const int32_t* topk_
                     void* stream) {
   g_last_error[0] = 0;
   return forward_impl(hidden, weight, topk_idx, topk_logit, T, chunk, N, d, V, K, dtype, flags,
-                      loss, lse, row_loss, topk_z, nullptr, 0, workspace, workspace_bytes, stream);
+                      nullptr, loss, lse, row_loss, topk_z, nullptr, 0, workspace,
+                      workspace_bytes, stream);
+}
+
+int32_t fkl_forward_ex(const void* hidden, const void* weight, const int32_t* topk_idx,
+                       const float* topk_logit, float T, int64_t chunk, int64_t N, int64_t d,
+                       int64_t V, int32_t K, int32_t dtype, uint32_t flags,
+                       const fkl_loss_options* opts, float* loss, float* lse, float* row_loss,
+                       float* topk_z, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  return forward_impl(hidden, weight, topk_idx, topk_logit, T, chunk, N, d, V, K, dtype, flags,
+                      opts, loss, lse, row_loss, topk_z, nullptr, 0, workspace, workspace_bytes,
+                      stream);
 }
 
 int32_t fkl_forward_keep(const void* hidden, const void* weight, const int32_t* topk_idx,
@@ -348,16 +412,29 @@ int32_t fkl_forward_keep(const void* hidden, const void* weight, const int32_t* 
   g_last_error[0] = 0;
   if (!logits && N > 0) return fail(FKL_E_ARG, "null pointer argument (logits)");
   return forward_impl(hidden, weight, topk_idx, topk_logit, T, chunk, N, d, V, K, dtype, flags,
-                      loss, lse, row_loss, topk_z, logits, logits_bytes, workspace,
+                      nullptr, loss, lse, row_loss, topk_z, logits, logits_bytes, workspace,
                       workspace_bytes, stream);
 }
 
-int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk_idx,
-                     const float* topk_logit, const float* lse, const float* topk_z,
-                     const float* grad_loss, float T, int64_t chunk, int64_t N, int64_t d,
-                     int64_t V, int32_t K, int32_t dtype, uint32_t flags, void* grad_hidden,
-                     float* grad_weight, void* workspace, size_t workspace_bytes, void* stream) {
+int32_t fkl_forward_keep_ex(const void* hidden, const void* weight, const int32_t* topk_idx,
+                            const float* topk_logit, float T, int64_t chunk, int64_t N,
+                            int64_t d, int64_t V, int32_t K, int32_t dtype, uint32_t flags,
+                            const fkl_loss_options* opts, float* loss, float* lse,
+                            float* row_loss, float* topk_z, void* logits, size_t logits_bytes,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
+  if (!logits && N > 0) return fail(FKL_E_ARG, "null pointer argument (logits)");
+  return forward_impl(hidden, weight, topk_idx, topk_logit, T, chunk, N, d, V, K, dtype, flags,
+                      opts, loss, lse, row_loss, topk_z, logits, logits_bytes, workspace,
+                      workspace_bytes, stream);
+}
+
+static int32_t backward_impl(const void* hidden, const void* weight, const int32_t* topk_idx,
+                             const float* topk_logit, const float* lse, const float* topk_z,
+                             const float* grad_loss, float T, int64_t chunk, int64_t N,
+                             int64_t d, int64_t V, int32_t K, int32_t dtype, uint32_t flags,
+                             const fkl_loss_options* o, void* grad_hidden, float* grad_weight,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   int32_t r = check_shapes(N, d, V, K, chunk, dtype);
   if (r) return r;
   if (!std::isfinite(T) || !(T > 0.0f)) return fail(FKL_E_ARG, "T must be finite and > 0");
@@ -372,6 +449,8 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
   if (!aligned(topk_idx, 4) || !aligned(topk_logit, 4) || !aligned(lse, 4) || !aligned(topk_z, 4) ||
       !aligned(grad_loss, 4))
     return fail(FKL_E_ARG, "fp32/int32 arrays must be 4-byte aligned");
+  r = check_options(o, T, true);
+  if (r) return r;
   const Plan p = make_plan(N, d, V, K, chunk, dtype);
   if (workspace_bytes < p.b_total)
     return fail(FKL_E_WORKSPACE, "backward workspace needs %zu bytes, got %zu", p.b_total,
@@ -385,11 +464,19 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
     if (!accumulate) fkl::launch_fill_f32(grad_weight, V * d, 0.0f, s);
     return hip_check("backward (empty batch)");
   }
+  const int32_t* labels = o ? o->labels : nullptr;
+  const float* row_weight = o ? o->row_weight : nullptr;
+  const bool two_sm = labels && T != 1.0f;
+  const float a_kl = labels ? o->alpha : 1.0f, a_ce = labels ? 1.0f - o->alpha : 0.0f;
   if (flags & FKL_FLAG_VALIDATE_IDX) {
-    r = validate_ids(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + p.b_flag), s);
+    r = validate_ids(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + p.b_flag), s, labels);
     if (r) return r;
   }
   void* G = ws + p.b_G;
+  float* bcoef = reinterpret_cast<float*>(ws + p.b_bcoef);
+  float* lse12 = reinterpret_cast<float*>(ws + p.b_lse12);
+  float* ycoef = reinterpret_cast<float*>(ws + p.b_ycoef);
+  float* zy = reinterpret_cast<float*>(ws + p.b_zy);
   float* ghacc = reinterpret_cast<float*>(ws + p.b_ghacc);
   float* pcoef = reinterpret_cast<float*>(ws + p.b_pcoef);
   float* acoef = reinterpret_cast<float*>(ws + p.b_acoef);
@@ -409,14 +496,21 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
                              topk_idx + row0 * K, d, 0, nrows, K, zk_ws, s);
       zk = zk_ws;
     }
-    fkl::launch_bwd_prep(topk_logit, lse, grad_loss, row0, nrows, K, T, pcoef, acoef, lse2, s);
+    if (labels)  // z at the labels of this block (rows 0..nrows)
+      fkl::launch_gather_dot(dtype, weight, static_cast<const unsigned char*>(hidden) + row0 * d * eb,
+                             labels + row0, d, 0, nrows, 1, zy, s);
+    fkl::launch_bwd_prep(topk_logit, lse, grad_loss, row0, nrows, K, T, row_weight, labels, a_kl,
+                         a_ce, o ? o->lse1 : nullptr, two_sm, pcoef, acoef, lse2,
+                         two_sm ? bcoef : nullptr, two_sm ? lse12 : nullptr,
+                         labels ? ycoef : nullptr, s);
+    fkl::RowCoef rc{pcoef, acoef, lse2, two_sm ? bcoef : nullptr, two_sm ? lse12 : nullptr,
+                    labels ? ycoef : nullptr, labels ? labels + row0 : nullptr,
+                    labels ? zy : nullptr};
     for (int64_t v0 = 0; v0 < p.Vpad; v0 += p.bw_width) {
       const int64_t Vw = (p.Vpad - v0) < p.bw_width ? (p.Vpad - v0) : p.bw_width;
       const int64_t Vlim = (V - v0) < Vw ? (V - v0) : Vw;
-      fkl::launch_gprod(dtype, weight, hidden, d, V, v0, Vw, p.bw_pitch, row0, nrows, c2, acoef,
-                        lse2, G, s);
-      fkl::launch_fixup(dtype, G, p.bw_pitch, v0, Vw, topk_idx, zk, pcoef, acoef, lse2, row0, nrows,
-                        K, c2, s);
+      fkl::launch_gprod(dtype, weight, hidden, d, V, v0, Vw, p.bw_pitch, row0, nrows, c2, rc, G, s);
+      fkl::launch_fixup(dtype, G, p.bw_pitch, v0, Vw, topk_idx, zk, rc, row0, nrows, K, c2, s);
       fkl::launch_grad_hidden(dtype, G, p.bw_pitch, weight, d, v0, Vw, Vlim, nrows, v0 > 0, ghacc,
                               s);
       fkl::launch_grad_w(dtype, G, p.bw_pitch, hidden, d, v0, Vw, Vlim, row0, nrows,
@@ -425,6 +519,29 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
     fkl::launch_reduce_grad_hidden(dtype, ghacc, 1, nrows, d, grad_hidden, row0, s);
   }
   return hip_check("backward launch");
+}
+
+int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk_idx,
+                     const float* topk_logit, const float* lse, const float* topk_z,
+                     const float* grad_loss, float T, int64_t chunk, int64_t N, int64_t d,
+                     int64_t V, int32_t K, int32_t dtype, uint32_t flags, void* grad_hidden,
+                     float* grad_weight, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  return backward_impl(hidden, weight, topk_idx, topk_logit, lse, topk_z, grad_loss, T, chunk, N,
+                       d, V, K, dtype, flags, nullptr, grad_hidden, grad_weight, workspace,
+                       workspace_bytes, stream);
+}
+
+int32_t fkl_backward_ex(const void* hidden, const void* weight, const int32_t* topk_idx,
+                        const float* topk_logit, const float* lse, const float* topk_z,
+                        const float* grad_loss, float T, int64_t chunk, int64_t N, int64_t d,
+                        int64_t V, int32_t K, int32_t dtype, uint32_t flags,
+                        const fkl_loss_options* opts, void* grad_hidden, float* grad_weight,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  return backward_impl(hidden, weight, topk_idx, topk_logit, lse, topk_z, grad_loss, T, chunk, N,
+                       d, V, K, dtype, flags, opts, grad_hidden, grad_weight, workspace,
+                       workspace_bytes, stream);
 }
 
 int32_t fkl_keep_sizes(int64_t N, int64_t d, int64_t V, int32_t K, int32_t dtype,
@@ -439,13 +556,14 @@ int32_t fkl_keep_sizes(int64_t N, int64_t d, int64_t V, int32_t K, int32_t dtype
   return FKL_OK;
 }
 
-int32_t fkl_backward_keep(const void* hidden, const void* weight, const int32_t* topk_idx,
-                          const float* topk_logit, const float* lse, const float* topk_z,
-                          const float* grad_loss, float T, int64_t N, int64_t d, int64_t V,
-                          int32_t K, int32_t dtype, uint32_t flags, void* logits,
-                          size_t logits_bytes, void* grad_hidden, float* grad_weight,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error[0] = 0;
+static int32_t backward_keep_impl(const void* hidden, const void* weight,
+                                  const int32_t* topk_idx, const float* topk_logit,
+                                  const float* lse, const float* topk_z, const float* grad_loss,
+                                  float T, int64_t N, int64_t d, int64_t V, int32_t K,
+                                  int32_t dtype, uint32_t flags, const fkl_loss_options* o,
+                                  void* logits, size_t logits_bytes, void* grad_hidden,
+                                  float* grad_weight, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   int32_t r = check_shapes(N, d, V, K, 1, dtype);
   if (r) return r;
   r = check_keep(V, dtype);
@@ -463,6 +581,8 @@ int32_t fkl_backward_keep(const void* hidden, const void* weight, const int32_t*
   if (!aligned(topk_idx, 4) || !aligned(topk_logit, 4) || !aligned(lse, 4) || !aligned(topk_z, 4) ||
       !aligned(grad_loss, 4))
     return fail(FKL_E_ARG, "fp32/int32 arrays must be 4-byte aligned");
+  r = check_options(o, T, true);
+  if (r) return r;
   const size_t need = keep_bytes(N, V, dtype);
   if (logits_bytes < need)
     return fail(FKL_E_WORKSPACE, "kept logits need %zu bytes, got %zu", need, logits_bytes);
@@ -479,8 +599,11 @@ int32_t fkl_backward_keep(const void* hidden, const void* weight, const int32_t*
     if (!accumulate) fkl::launch_fill_f32(grad_weight, V * d, 0.0f, s);
     return hip_check("backward (empty batch)");
   }
+  const int32_t* labels = o ? o->labels : nullptr;
+  const bool two_sm = labels && T != 1.0f;
+  const float a_kl = labels ? o->alpha : 1.0f, a_ce = labels ? 1.0f - o->alpha : 0.0f;
   if (flags & FKL_FLAG_VALIDATE_IDX) {
-    r = validate_ids(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + q.flag), s);
+    r = validate_ids(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + q.flag), s, labels);
     if (r) return r;
   }
   float* pcoef = reinterpret_cast<float*>(ws + q.pcoef);
@@ -498,8 +621,18 @@ int32_t fkl_backward_keep(const void* hidden, const void* weight, const int32_t*
     fkl::launch_gather_dot(dtype, weight, hidden, topk_idx, d, 0, N, K, zk_ws, s);
     zk = zk_ws;
   }
-  fkl::launch_bwd_prep(topk_logit, lse, grad_loss, 0, N, K, T, pcoef, acoef, lse2, s);
-  fkl::launch_g_from_z(dtype, logits, zpitch, V, topk_idx, zk, pcoef, acoef, lse2, N, K, c2, s);
+  float* bcoef = reinterpret_cast<float*>(ws + q.bcoef);
+  float* lse12 = reinterpret_cast<float*>(ws + q.lse12);
+  float* ycoef = reinterpret_cast<float*>(ws + q.ycoef);
+  float* zy = reinterpret_cast<float*>(ws + q.zy);
+  if (labels) fkl::launch_gather_dot(dtype, weight, hidden, labels, d, 0, N, 1, zy, s);
+  fkl::launch_bwd_prep(topk_logit, lse, grad_loss, 0, N, K, T, o ? o->row_weight : nullptr, labels,
+                       a_kl, a_ce, o ? o->lse1 : nullptr, two_sm, pcoef, acoef, lse2,
+                       two_sm ? bcoef : nullptr, two_sm ? lse12 : nullptr,
+                       labels ? ycoef : nullptr, s);
+  const fkl::RowCoef rc{pcoef, acoef, lse2, two_sm ? bcoef : nullptr, two_sm ? lse12 : nullptr,
+                        labels ? ycoef : nullptr, labels, labels ? zy : nullptr};
+  fkl::launch_g_from_z(dtype, logits, zpitch, V, topk_idx, zk, rc, N, K, c2, s);
   // grad_hidden over all rows in one launch (tiles of 256 rows reach 256 * zld bytes)
   fkl::launch_grad_hidden(dtype, logits, zpitch, weight, d, 0, zpitch, V, N, false, ghacc, s);
   fkl::launch_reduce_grad_hidden(dtype, ghacc, 1, N, d, grad_hidden, 0, s);
@@ -515,6 +648,31 @@ int32_t fkl_backward_keep(const void* hidden, const void* weight, const int32_t*
                        accumulate || row0 > 0, grad_weight, s);
   }
   return hip_check("backward launch");
+}
+
+int32_t fkl_backward_keep(const void* hidden, const void* weight, const int32_t* topk_idx,
+                          const float* topk_logit, const float* lse, const float* topk_z,
+                          const float* grad_loss, float T, int64_t N, int64_t d, int64_t V,
+                          int32_t K, int32_t dtype, uint32_t flags, void* logits,
+                          size_t logits_bytes, void* grad_hidden, float* grad_weight,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  return backward_keep_impl(hidden, weight, topk_idx, topk_logit, lse, topk_z, grad_loss, T, N, d,
+                            V, K, dtype, flags, nullptr, logits, logits_bytes, grad_hidden,
+                            grad_weight, workspace, workspace_bytes, stream);
+}
+
+int32_t fkl_backward_keep_ex(const void* hidden, const void* weight, const int32_t* topk_idx,
+                             const float* topk_logit, const float* lse, const float* topk_z,
+                             const float* grad_loss, float T, int64_t N, int64_t d, int64_t V,
+                             int32_t K, int32_t dtype, uint32_t flags,
+                             const fkl_loss_options* opts, void* logits, size_t logits_bytes,
+                             void* grad_hidden, float* grad_weight, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  return backward_keep_impl(hidden, weight, topk_idx, topk_logit, lse, topk_z, grad_loss, T, N, d,
+                            V, K, dtype, flags, opts, logits, logits_bytes, grad_hidden,
+                            grad_weight, workspace, workspace_bytes, stream);
 }
 
 namespace {

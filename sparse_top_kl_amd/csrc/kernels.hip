@@ -84,20 +84,31 @@ struct LogitValue {  // z itself, zero in the padding columns >= vlim
     return col < vlim ? z : 0.f;
   }
 };
-struct GradValue {  // dense part of the logit gradient, acoef * 2^(z*c2 - lse2)
+// Dense part of the logit gradient, acoef * 2^(z*c2 - lse2), plus with CE2
+// the separate temperature-1 softmax of the cross-entropy term,
+// bcoef * 2^(z*log2(e) - lse1_2).
+template <bool CE2>
+struct GradValue {
   const float* acoef;
   const float* lse2;
+  const float* bcoef;
+  const float* lse1_2;
   float c2;
   int64_t vlim;   // columns >= vlim lie past the vocabulary (written as zero)
   int64_t nrows;  // tokens of the block
   struct Row {
-    float a, l2;
+    float a, l2, b, l1;
   };
   __device__ __forceinline__ Row row(int64_t tok) const {
-    return tok < nrows ? Row{acoef[tok], lse2[tok]} : Row{0.f, 0.f};
+    if (tok >= nrows) return Row{0.f, 0.f, 0.f, 0.f};
+    if constexpr (CE2) return Row{acoef[tok], lse2[tok], bcoef[tok], lse1_2[tok]};
+    return Row{acoef[tok], lse2[tok], 0.f, 0.f};
   }
   __device__ __forceinline__ float operator()(const Row& r, float z, int64_t col) const {
-    return col < vlim ? r.a * fast_exp2(z * c2 - r.l2) : 0.f;
+    if (col >= vlim) return 0.f;
+    float g = r.a * fast_exp2(z * c2 - r.l2);
+    if constexpr (CE2) g += r.b * fast_exp2(z * kLog2e - r.l1);
+    return g;
   }
 };
 
@@ -220,11 +231,13 @@ __device__ __forceinline__ void lse_partials(const f32x16_t (&acc)[C::kMI][C::kN
 // With KEEP the tile's logits are also written, rounded to the element type,
 // into Z[token][v] (row pitch zld bytes) for v < zcols, as zero for v >= V
 // (streaming stores: the backward reads them much later).
-template <class P, class C, bool KEEP>
+// With CE2 the partials at temperature 1 (c = log2(e)) go to part_ce as well.
+template <class P, class C, bool KEEP, bool CE2>
 __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_logits_lse(
     const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
     int64_t nrows, int64_t n_vt, int64_t n_tt, float c2, float2* __restrict__ part,
-    int64_t part_ld, unsigned char* __restrict__ Z, int64_t zld, int64_t zcols) {
+    int64_t part_ld, float2* __restrict__ part_ce, unsigned char* __restrict__ Z, int64_t zld,
+    int64_t zcols) {
   static_assert(C::kWM == kSliceVocab, "one LSE partial per wave row-slice");
   int64_t vt, tt;
   if (!TileGroups<4, 8>::coords(n_vt, n_tt, &vt, &tt)) return;
@@ -238,7 +251,12 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_logits_lse(
   gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
 
   const int64_t v0 = vt * kBM + C::wave_m() * C::kWM;
-  if (v0 < V) lse_partials<C>(acc, v0, V, tt * kBN + C::wave_n() * C::kWN, nrows, c2, part, part_ld);
+  if (v0 < V) {
+    lse_partials<C>(acc, v0, V, tt * kBN + C::wave_n() * C::kWN, nrows, c2, part, part_ld);
+    if constexpr (CE2)
+      lse_partials<C>(acc, v0, V, tt * kBN + C::wave_n() * C::kWN, nrows, kLog2e, part_ce,
+                      part_ld);
+  }
   if constexpr (KEEP)
     store_token_rows<P, C, true>(acc, LogitValue{V}, v0, tt * kBN + C::wave_n() * C::kWN, nrows, zcols,
                            Z, zld);
@@ -282,6 +300,10 @@ __global__ __launch_bounds__(256) void k_gather_dot(const unsigned char* __restr
   }
   for (int k = g; k < K; k += 4) {
     const int64_t v = idx[row * K + k];
+    if (v < 0) {  // no id (a row without a hard label)
+      if (li == 0) zk[row * K + k] = 0.f;
+      continue;
+    }
     const unsigned char* wr = W + v * rb;
     float acc = 0.f;
     for (int64_t j = li; j < nvec; j += 16) {
@@ -319,15 +341,11 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One wave per row of the chunk.
-__global__ __launch_bounds__(256) void k_merge_loss(const float2* __restrict__ part, int64_t part_ld,
-                                                    int64_t nslots, const float* __restrict__ zk,
-                                                    const float* __restrict__ logit, int64_t nrows,
-                                                    int K, float T, float* __restrict__ lse_out,
-                                                    float* __restrict__ row_loss) {
+// Merge of one row's partials (running max m, sum s of 2^(z*c - m)) into the
+// natural-log log-sum-exp, by one wave.
+__device__ __forceinline__ float merge_lse(const float2* __restrict__ part, int64_t part_ld,
+                                           int64_t nslots, int64_t row) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= nrows) return;
   float m = -INFINITY, s = 0.f;
   for (int64_t sl = lane; sl < nslots; sl += 64) {
     const float2 p = part[sl * part_ld + row];
@@ -338,28 +356,52 @@ __global__ __launch_bounds__(256) void k_merge_loss(const float2* __restrict__ p
     const float mo = __shfl_xor(m, o), so = __shfl_xor(s, o);
     merge_ms(m, s, mo, so);
   }
-  const float lse = (m + log2f(s)) * kLn2;  // ln sum_v exp(z_v / T)
+  return (m + log2f(s)) * kLn2;
+}
 
-  const float invT = 1.0f / T;
-  const float* lg = logit + row * K;
-  const float* z = zk + row * K;
-  float ma = -INFINITY;
-  for (int k = lane; k < K; k += 64) ma = fmaxf(ma, lg[k] * invT);
-  ma = wave_max(ma);
-  float zsum = 0.f;
-  for (int k = lane; k < K; k += 64) zsum += expf(lg[k] * invT - ma);
-  zsum = wave_sum(zsum);
-  const float logZ = logf(zsum);
+// One wave per row of the chunk: lse at T (and at temperature 1 with
+// partials there), the teacher softmax over the K entries, the row's KL term
+// and, with labels, its cross-entropy; row_loss = w (a_kl T^2 KL + a_ce CE).
+// zk, logit, lse_out and row_loss start at the chunk's first row; the
+// option arrays are indexed by absolute row (row0 + row).
+__global__ __launch_bounds__(256) void k_merge_loss(const float2* __restrict__ part, int64_t part_ld,
+                                                    int64_t nslots, const float* __restrict__ zk,
+                                                    const float* __restrict__ logit, int64_t row0,
+                                                    int64_t nrows, int K, float T,
+                                                    float* __restrict__ lse_out,
+                                                    float* __restrict__ row_loss, MergeOpts o) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  const int64_t ar = row0 + row;
+  const float lse = merge_lse(part, part_ld, nslots, row);
+  const float lse1 = o.part_ce ? merge_lse(o.part_ce, part_ld, nslots, row) : lse;
+  const float w = o.row_weight ? o.row_weight[ar] : 1.0f;
   float term = 0.f;
-  for (int k = lane; k < K; k += 64) {
-    const float a = lg[k] * invT - ma;
-    const float p = expf(a) / zsum;
-    if (p > 0.f) term += p * ((a - logZ) - (z[k] * invT - lse));
+  if (w != 0.f) {  // uniform per wave; a weight-0 (padding) row may lack teacher entries
+    const float invT = 1.0f / T;
+    const float* lg = logit + row * K;
+    const float* z = zk + row * K;
+    float ma = -INFINITY;
+    for (int k = lane; k < K; k += 64) ma = fmaxf(ma, lg[k] * invT);
+    ma = wave_max(ma);
+    float zsum = 0.f;
+    for (int k = lane; k < K; k += 64) zsum += expf(lg[k] * invT - ma);
+    zsum = wave_sum(zsum);
+    const float logZ = logf(zsum);
+    for (int k = lane; k < K; k += 64) {
+      const float a = lg[k] * invT - ma;
+      const float p = expf(a) / zsum;
+      if (p > 0.f) term += p * ((a - logZ) - (z[k] * invT - lse));
+    }
+    term = wave_sum(term);
   }
-  term = wave_sum(term);
   if (lane == 0) {
     lse_out[row] = lse;
-    if (row_loss) row_loss[row] = T * T * term;
+    if (o.lse1) o.lse1[ar] = lse1;
+    float ce = 0.f;
+    if (o.labels && o.labels[ar] >= 0) ce = lse1 - o.zy[ar];
+    if (row_loss) row_loss[row] = w != 0.f ? w * (o.a_kl * T * T * term + o.a_ce * ce) : 0.f;
   }
 }
 
@@ -379,47 +421,66 @@ __global__ __launch_bounds__(1024) void k_reduce_loss(const float* __restrict__ 
 
 // ------------------------------------------------------------------ backward
 
-// One wave per row: pcoef = s*T*p_k, acoef = s*T*sum_k p_k, lse2 = lse*log2(e).
-__global__ __launch_bounds__(256) void k_bwd_prep(const float* __restrict__ logit,
-                                                  const float* __restrict__ lse,
-                                                  const float* __restrict__ grad_loss,
-                                                  int64_t nrows, int K, float T,
-                                                  float* __restrict__ pcoef,
-                                                  float* __restrict__ acoef,
-                                                  float* __restrict__ lse2) {
+// One wave per row, coefficients of its logit gradient with s the upstream
+// scale, w the row weight and y the label:
+//   pcoef_k = s w a_kl T p_k,  ycoef = s w a_ce [y >= 0],
+//   acoef = s w a_kl T sum_k p_k (+ ycoef when the cross-entropy shares the
+//   softmax, i.e. T = 1), bcoef = ycoef when it has its own (two_sm),
+//   lse2 = lse log2(e), lse1_2 = lse1 log2(e).
+// logit, lse and the outputs start at the block's first row; row_weight,
+// labels and lse1 are indexed by absolute row (row0 + row).
+__global__ __launch_bounds__(256) void k_bwd_prep(
+    const float* __restrict__ logit, const float* __restrict__ lse,
+    const float* __restrict__ grad_loss, int64_t row0, int64_t nrows, int K, float T,
+    const float* __restrict__ row_weight, const int32_t* __restrict__ labels, float a_kl,
+    float a_ce, const float* __restrict__ lse1, bool two_sm, float* __restrict__ pcoef,
+    float* __restrict__ acoef, float* __restrict__ lse2, float* __restrict__ bcoef,
+    float* __restrict__ lse1_2, float* __restrict__ ycoef) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= nrows) return;
-  const float scale = (grad_loss ? *grad_loss : 1.0f) * T;
-  const float invT = 1.0f / T;
-  const float* lg = logit + row * K;
-  float ma = -INFINITY;
-  for (int k = lane; k < K; k += 64) ma = fmaxf(ma, lg[k] * invT);
-  ma = wave_max(ma);
-  float zsum = 0.f;
-  for (int k = lane; k < K; k += 64) zsum += expf(lg[k] * invT - ma);
-  zsum = wave_sum(zsum);
+  const int64_t ar = row0 + row;
+  const float s = grad_loss ? *grad_loss : 1.0f;
+  const float w = row_weight ? row_weight[ar] : 1.0f;
+  const bool has_y = labels && labels[ar] >= 0;
+  const float yc = has_y ? s * w * a_ce : 0.f;
+  const float scale = s * w * a_kl * T;
   float psum = 0.f;
-  for (int k = lane; k < K; k += 64) {
-    const float p = expf(lg[k] * invT - ma) / zsum;
-    psum += p;
-    pcoef[row * K + k] = scale * p;
+  if (w != 0.f) {  // uniform per wave
+    const float invT = 1.0f / T;
+    const float* lg = logit + row * K;
+    float ma = -INFINITY;
+    for (int k = lane; k < K; k += 64) ma = fmaxf(ma, lg[k] * invT);
+    ma = wave_max(ma);
+    float zsum = 0.f;
+    for (int k = lane; k < K; k += 64) zsum += expf(lg[k] * invT - ma);
+    zsum = wave_sum(zsum);
+    for (int k = lane; k < K; k += 64) {
+      const float p = expf(lg[k] * invT - ma) / zsum;
+      psum += p;
+      pcoef[row * K + k] = scale * p;
+    }
+    psum = wave_sum(psum);
+  } else {
+    for (int k = lane; k < K; k += 64) pcoef[row * K + k] = 0.f;
   }
-  psum = wave_sum(psum);
   if (lane == 0) {
-    acoef[row] = scale * psum;
+    acoef[row] = scale * psum + (two_sm ? 0.f : yc);
     lse2[row] = lse[row] * kLog2e;
+    if (bcoef) bcoef[row] = two_sm ? yc : 0.f;
+    if (lse1_2) lse1_2[row] = two_sm ? lse1[ar] * kLog2e : 0.f;
+    if (ycoef) ycoef[row] = yc;
   }
 }
 
 // Recompute the logit tile of rows [0, nrows) x vocabulary [v0, v0 + Vw) and
-// write G_dense = acoef * 2^(z*c2 - lse2) into the G block G[row][v - v0]
+// write the dense part of G (GradValue) into the G block G[row][v - v0]
 // (row pitch gpitch elements; entries with v >= V are written as zero).
-template <class P, class C>
+template <class P, class C, bool CE2>
 __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_gprod(
     const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
     int64_t v0, int64_t Vw, int64_t gpitch, int64_t nrows, int64_t n_vt, int64_t n_tt, float c2,
-    const float* __restrict__ acoef, const float* __restrict__ lse2, unsigned char* __restrict__ G) {
+    RowCoef rc, unsigned char* __restrict__ G) {
   int64_t vt, tt;
   if (!TileGroups<4, 8>::coords(n_vt, n_tt, &vt, &tt)) return;
   const int64_t ld = d * P::kBytes;
@@ -431,20 +492,66 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_gprod(
 
   const int64_t w0 = vt * kBM + C::wave_m() * C::kWM;  // slice-relative column of the wave
   const int64_t t0 = tt * kBN + C::wave_n() * C::kWN;  // first token of the wave
-  const GradValue f{acoef, lse2, c2, V - v0, nrows};
+  const GradValue<CE2> f{rc.acoef, rc.lse2, rc.bcoef, rc.lse1_2, c2, V - v0, nrows};
   store_token_rows<P, C>(acc, f, w0, t0, nrows, Vw, G, gpitch * P::kBytes);
 }
 
-// One wave per row: for the teacher ids inside the slice [v0, v0 + Vw),
-// G[row][idx_k - v0] = acoef * 2^(z_k*c2 - lse2) - sum_{k': idx_k' = idx_k} pcoef_k'.
+// Dense part of G at one logit for one row's coefficients.
+struct DenseCoef {
+  float a, l2, b, l1;
+};
+__device__ __forceinline__ DenseCoef row_dense(const RowCoef& rc, int64_t row) {
+  return DenseCoef{rc.acoef[row], rc.lse2[row], rc.bcoef ? rc.bcoef[row] : 0.f,
+                   rc.lse1_2 ? rc.lse1_2[row] : 0.f};
+}
+__device__ __forceinline__ float dense_g(const DenseCoef& c, float z, float c2) {
+  float g = c.a * fast_exp2(z * c2 - c.l2);
+  if (c.b != 0.f) g += c.b * fast_exp2(z * kLog2e - c.l1);
+  return g;
+}
+
+template <class P>
+__device__ __forceinline__ void store_one(unsigned char* grow, int64_t col, float val) {
+  if constexpr (P::kBytes == 2)
+    reinterpret_cast<uint16_t*>(grow)[col] = f32_to_bf16_rne(val);
+  else
+    reinterpret_cast<float*>(grow)[col] = val;
+}
+
+// The exact entries of one row of G inside columns [v0, v0 + Vw): at each
+// teacher id v, dense(z_v) - (sum of pcoef over the ids equal to v) - (ycoef
+// if v is the label); at a label that is no teacher id, dense(z_y) - ycoef.
+// z at an id or the label is the fp32 gathered logit, so every entry is
+// rounded once. sid / sp hold the row's ids and pcoef (LDS); threads
+// t = 0 .. nthreads - 1 of the workgroup share the work.
+template <class P>
+__device__ __forceinline__ void write_exact_entries(unsigned char* grow, int64_t v0, int64_t Vw,
+                                                    const int32_t* sid, const float* sp, int K,
+                                                    const float* zk_row, const DenseCoef& dc,
+                                                    float c2, int32_t y, float yc, float zy,
+                                                    int t, int nthreads) {
+  for (int k = t; k < K; k += nthreads) {
+    const int32_t v = sid[k];
+    if (v < v0 || v >= v0 + Vw) continue;
+    float sum = 0.f;
+    for (int k2 = 0; k2 < K; ++k2) sum += (sid[k2] == v) ? sp[k2] : 0.f;
+    store_one<P>(grow, v - v0, dense_g(dc, zk_row[k], c2) - sum - (v == y ? yc : 0.f));
+  }
+  if (t == 0 && y >= 0 && y >= v0 && y < v0 + Vw) {
+    bool found = false;
+    for (int k2 = 0; k2 < K; ++k2) found |= (sid[k2] == y);
+    if (!found) store_one<P>(grow, y - v0, dense_g(dc, zy, c2) - yc);
+  }
+}
+
+// One wave per row: the exact entries of the slice [v0, v0 + Vw) of its G
+// row (write_exact_entries). Arrays start at the block's first row.
 template <class P>
 __global__ __launch_bounds__(64) void k_fixup(unsigned char* __restrict__ G, int64_t gpitch,
                                               int64_t v0, int64_t Vw,
                                               const int32_t* __restrict__ idx,
-                                              const float* __restrict__ zk,
-                                              const float* __restrict__ pcoef,
-                                              const float* __restrict__ acoef,
-                                              const float* __restrict__ lse2, int K, float c2) {
+                                              const float* __restrict__ zk, RowCoef rc, int K,
+                                              float c2) {
   extern __shared__ int32_t sh_fix[];
   int32_t* sid = sh_fix;
   float* sp = reinterpret_cast<float*>(sh_fix + K);
@@ -452,47 +559,35 @@ __global__ __launch_bounds__(64) void k_fixup(unsigned char* __restrict__ G, int
   const int64_t row = blockIdx.x;
   for (int k = lane; k < K; k += 64) {
     sid[k] = idx[row * K + k];
-    sp[k] = pcoef[row * K + k];
+    sp[k] = rc.pcoef[row * K + k];
   }
   __syncthreads();
-  const float a = acoef[row], l2 = lse2[row];
-  unsigned char* grow = G + row * gpitch * P::kBytes;
-  for (int k = lane; k < K; k += 64) {
-    const int32_t v = sid[k];
-    if (v < v0 || v >= v0 + Vw) continue;
-    float sum = 0.f;
-    for (int k2 = 0; k2 < K; ++k2) sum += (sid[k2] == v) ? sp[k2] : 0.f;
-    const float val = a * fast_exp2(zk[row * K + k] * c2 - l2) - sum;
-    if constexpr (P::kBytes == 2)
-      reinterpret_cast<uint16_t*>(grow)[v - v0] = f32_to_bf16_rne(val);
-    else
-      reinterpret_cast<float*>(grow)[v - v0] = val;
-  }
+  const int32_t y = rc.labels ? rc.labels[row] : -1;
+  write_exact_entries<P>(G + row * gpitch * P::kBytes, v0, Vw, sid, sp, K, zk + row * K,
+                         row_dense(rc, row), c2, y, rc.ycoef ? rc.ycoef[row] : 0.f,
+                         y >= 0 ? rc.zy[row] : 0.f, lane, 64);
 }
 
 // Kept-logits backward, one workgroup per row: turns the row's kept logits
 // z (element type P, zcols entries, the ones at v >= V zero) into its logit
-// gradient in place, G = acoef * 2^(z*c2 - lse2) below V and zero above, then
-// gives the teacher ids the exact value acoef * 2^(zk*c2 - lse2) - (sum of
-// pcoef over the equal ids), computed from the fp32 logit at the id (as
-// k_fixup does for a slice).
+// gradient in place: the dense part below V, zero above, then the exact
+// teacher-id and label entries (write_exact_entries, as k_fixup does for a
+// slice). Arrays are indexed by row.
 constexpr int kGzThreads = 256;
 
 template <class P>
 __global__ __launch_bounds__(kGzThreads) void k_g_from_z(unsigned char* __restrict__ Z, int64_t zld,
                                                   int64_t V, int64_t zcols,
                                                   const int32_t* __restrict__ idx,
-                                                  const float* __restrict__ zk,
-                                                  const float* __restrict__ pcoef,
-                                                  const float* __restrict__ acoef,
-                                                  const float* __restrict__ lse2, int K, float c2) {
+                                                  const float* __restrict__ zk, RowCoef rc, int K,
+                                                  float c2) {
   extern __shared__ int32_t sh_gz[];
   int32_t* sid = sh_gz;
   float* sp = reinterpret_cast<float*>(sh_gz + K);
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
   unsigned char* zr = Z + row * zld;
-  const float a = acoef[row], l2 = lse2[row];
+  const DenseCoef dc = row_dense(rc, row);
   // Each element is read and written once: streaming (nontemporal) accesses
   // keep the row out of the caches' reuse sets.
   constexpr int kPer = 16 / P::kBytes;  // elements per 16-byte vector
@@ -515,34 +610,27 @@ __global__ __launch_bounds__(kGzThreads) void k_g_from_z(unsigned char* __restri
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float z0 = as_f32(x[u][e] << 16), z1 = as_f32(x[u][e] & 0xffff0000u);
-          const float g0 = v + 2 * e < V ? a * fast_exp2(z0 * c2 - l2) : 0.f;
-          const float g1 = v + 2 * e + 1 < V ? a * fast_exp2(z1 * c2 - l2) : 0.f;
+          const float g0 = v + 2 * e < V ? dense_g(dc, z0, c2) : 0.f;
+          const float g1 = v + 2 * e + 1 < V ? dense_g(dc, z1, c2) : 0.f;
           y[e] = f32_to_bf16_rne(g0) | (static_cast<uint32_t>(f32_to_bf16_rne(g1)) << 16);
         }
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          y[e] = __builtin_bit_cast(uint32_t, v + e < V ? a * fast_exp2(as_f32(x[u][e]) * c2 - l2)
-                                                        : 0.f);
+          y[e] = __builtin_bit_cast(uint32_t, v + e < V ? dense_g(dc, as_f32(x[u][e]), c2) : 0.f);
       }
       __builtin_nontemporal_store(y, reinterpret_cast<u32x4_t*>(zr + i * 16));
     }
   }
   for (int k = t; k < K; k += kGzThreads) {
     sid[k] = idx[row * K + k];
-    sp[k] = pcoef[row * K + k];
+    sp[k] = rc.pcoef[row * K + k];
   }
-  __syncthreads();  // the dense stores of the row are done before the id entries are rewritten
-  for (int k = t; k < K; k += kGzThreads) {
-    const int32_t v = sid[k];
-    float sum = 0.f;
-    for (int k2 = 0; k2 < K; ++k2) sum += (sid[k2] == v) ? sp[k2] : 0.f;
-    const float val = a * fast_exp2(zk[row * K + k] * c2 - l2) - sum;
-    if constexpr (P::kBytes == 2)
-      reinterpret_cast<uint16_t*>(zr)[v] = f32_to_bf16_rne(val);
-    else
-      reinterpret_cast<float*>(zr)[v] = val;
-  }
+  __syncthreads();  // the dense stores of the row are done before the exact entries are written
+  const int32_t y = rc.labels ? rc.labels[row] : -1;
+  write_exact_entries<P>(zr, 0, zcols, sid, sp, K, zk + row * K, dc, c2, y,
+                         rc.ycoef ? rc.ycoef[row] : 0.f, y >= 0 ? rc.zy[row] : 0.f, t,
+                         kGzThreads);
 }
 
 // acc[row][col] (+)= sum over the slice of G[row][v - v0] W[v][col], for the rows
@@ -917,14 +1005,15 @@ __global__ void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
     p[i] = v;
 }
 
-// Every id in [0, V).
+// Every id in [0, V) (with allow_negative: every id below V).
 __global__ __launch_bounds__(256) void k_validate_idx(const int32_t* __restrict__ idx, int64_t n,
-                                                      int64_t V, int32_t* __restrict__ flag) {
+                                                      int64_t V, int allow_negative,
+                                                      int32_t* __restrict__ flag) {
   int bad = 0;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * 256) {
     const int32_t v = idx[i];
-    bad |= (v < 0 || v >= V);
+    bad |= ((v < 0 && !allow_negative) || v >= V);
   }
   if (bad) atomicOr(flag, 1);
 }
@@ -949,29 +1038,33 @@ typedef TileCfg<2, 4> Cfg8;  // 8 waves, 128x64 per wave (bf16, ping-pong loop)
 
 void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64_t V,
                        int64_t row0, int64_t nrows, float c2, float2* part, int64_t part_ld,
-                       void* Z, int64_t zpitch, hipStream_t s) {
+                       float2* part_ce, void* Z, int64_t zpitch, hipStream_t s) {
   ScopedTimer timer_(KID_LOGITS_LSE, s);
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(V, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
   const unsigned char* Wc = static_cast<const unsigned char*>(W);
   const unsigned grid = grouped_grid<4, 8>(n_vt, n_tt);
-  if (Z) {
-    unsigned char* Zc = static_cast<unsigned char*>(Z) + row0 * zpitch * eb;
-    if (dtype == 1)
-      k_logits_lse<BF16, Cfg8, true><<<grid, Cfg8::kThreads, 0, s>>>(
-          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, Zc, zpitch * eb, zpitch);
-    else
-      k_logits_lse<F32, Cfg4, true><<<grid, Cfg4::kThreads, 0, s>>>(
-          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, Zc, zpitch * eb, zpitch);
-  } else {
-    if (dtype == 1)
-      k_logits_lse<BF16, Cfg8, false><<<grid, Cfg8::kThreads, 0, s>>>(
-          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, nullptr, 0, 0);
-    else
-      k_logits_lse<F32, Cfg4, false><<<grid, Cfg4::kThreads, 0, s>>>(
-          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, nullptr, 0, 0);
-  }
+  unsigned char* Zc = Z ? static_cast<unsigned char*>(Z) + row0 * zpitch * eb : nullptr;
+  const int64_t zld = zpitch * eb;
+#define FKL_LOGITS(KEEP, CE2)                                                                     \
+  do {                                                                                            \
+    if (dtype == 1)                                                                               \
+      k_logits_lse<BF16, Cfg8, KEEP, CE2><<<grid, Cfg8::kThreads, 0, s>>>(                        \
+          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, part_ce, Zc, zld, zpitch);          \
+    else                                                                                          \
+      k_logits_lse<F32, Cfg4, KEEP, CE2><<<grid, Cfg4::kThreads, 0, s>>>(                         \
+          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, part_ce, Zc, zld, zpitch);          \
+  } while (0)
+  if (Z && part_ce)
+    FKL_LOGITS(true, true);
+  else if (Z)
+    FKL_LOGITS(true, false);
+  else if (part_ce)
+    FKL_LOGITS(false, true);
+  else
+    FKL_LOGITS(false, false);
+#undef FKL_LOGITS
 }
 
 void launch_gather_dot(int dtype, const void* W, const void* H, const int32_t* idx, int64_t d,
@@ -1003,11 +1096,12 @@ void launch_gather_dot(int dtype, const void* W, const void* H, const int32_t* i
 
 void launch_merge_loss(const float2* part, int64_t part_ld, int64_t nslots, const float* zk,
                        const float* logit, int64_t row0, int64_t nrows, int K, float T,
-                       float* lse, float* row_loss, hipStream_t s) {
+                       float* lse, float* row_loss, const MergeOpts& opts, hipStream_t s) {
   ScopedTimer timer_(KID_MERGE_LOSS, s);
   const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, 4));
   k_merge_loss<<<blocks, 256, 0, s>>>(part, part_ld, nslots, zk + row0 * K, logit + row0 * K,
-                                      nrows, K, T, lse + row0, row_loss ? row_loss + row0 : nullptr);
+                                      row0, nrows, K, T, lse + row0,
+                                      row_loss ? row_loss + row0 : nullptr, opts);
 }
 
 void launch_reduce_loss(const float* row_loss, int64_t N, float* loss, hipStream_t s) {
@@ -1016,57 +1110,69 @@ void launch_reduce_loss(const float* row_loss, int64_t N, float* loss, hipStream
 }
 
 void launch_bwd_prep(const float* logit, const float* lse, const float* grad_loss, int64_t row0,
-                     int64_t nrows, int K, float T, float* pcoef, float* acoef, float* lse2,
-                     hipStream_t s) {
+                     int64_t nrows, int K, float T, const float* row_weight,
+                     const int32_t* labels, float a_kl, float a_ce, const float* lse1,
+                     bool two_sm, float* pcoef, float* acoef, float* lse2, float* bcoef,
+                     float* lse1_2, float* ycoef, hipStream_t s) {
   ScopedTimer timer_(KID_BWD_PREP, s);
   const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, 4));
-  k_bwd_prep<<<blocks, 256, 0, s>>>(logit + row0 * K, lse + row0, grad_loss, nrows, K, T, pcoef,
-                                    acoef, lse2);
+  k_bwd_prep<<<blocks, 256, 0, s>>>(logit + row0 * K, lse + row0, grad_loss, row0, nrows, K, T,
+                                    row_weight, labels, a_kl, a_ce, lse1, two_sm, pcoef, acoef,
+                                    lse2, bcoef, lse1_2, ycoef);
 }
 
 void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t v0,
                   int64_t Vw, int64_t gpitch, int64_t row0, int64_t nrows, float c2,
-                  const float* acoef, const float* lse2, void* G, hipStream_t s) {
+                  const RowCoef& rc, void* G, hipStream_t s) {
   ScopedTimer timer_(KID_GPROD, s);
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(Vw, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
+  const unsigned char* Wc = static_cast<const unsigned char*>(W);
   const unsigned grid = grouped_grid<4, 8>(n_vt, n_tt);
-  FKL_LAUNCH_GEMM(k_gprod, dtype, grid, s,
-                  static_cast<const unsigned char*>(W), Hc, d, V, v0, Vw, gpitch, nrows, n_vt,
-                  n_tt, c2, acoef, lse2, static_cast<unsigned char*>(G));
+  unsigned char* Gc = static_cast<unsigned char*>(G);
+#define FKL_GPROD(CE2)                                                                            \
+  do {                                                                                            \
+    if (dtype == 1)                                                                               \
+      k_gprod<BF16, Cfg8, CE2><<<grid, Cfg8::kThreads, 0, s>>>(Wc, Hc, d, V, v0, Vw, gpitch,       \
+                                                               nrows, n_vt, n_tt, c2, rc, Gc);    \
+    else                                                                                          \
+      k_gprod<F32, Cfg4, CE2><<<grid, Cfg4::kThreads, 0, s>>>(Wc, Hc, d, V, v0, Vw, gpitch, nrows, \
+                                                              n_vt, n_tt, c2, rc, Gc);            \
+  } while (0)
+  if (rc.bcoef)
+    FKL_GPROD(true);
+  else
+    FKL_GPROD(false);
+#undef FKL_GPROD
 }
 
 void launch_fixup(int dtype, void* G, int64_t gpitch, int64_t v0, int64_t Vw, const int32_t* idx,
-                  const float* zk, const float* pcoef, const float* acoef, const float* lse2,
-                  int64_t row0, int64_t nrows, int K, float c2, hipStream_t s) {
+                  const float* zk, const RowCoef& rc, int64_t row0, int64_t nrows, int K,
+                  float c2, hipStream_t s) {
   if (nrows <= 0) return;
   ScopedTimer timer_(KID_FIXUP, s);
   const size_t shm = static_cast<size_t>(K) * 8;
   if (dtype == 1)
     k_fixup<BF16><<<static_cast<unsigned>(nrows), 64, shm, s>>>(
-        static_cast<unsigned char*>(G), gpitch, v0, Vw, idx + row0 * K, zk, pcoef, acoef, lse2, K,
-        c2);
+        static_cast<unsigned char*>(G), gpitch, v0, Vw, idx + row0 * K, zk, rc, K, c2);
   else
     k_fixup<F32><<<static_cast<unsigned>(nrows), 64, shm, s>>>(
-        static_cast<unsigned char*>(G), gpitch, v0, Vw, idx + row0 * K, zk, pcoef, acoef, lse2, K,
-        c2);
+        static_cast<unsigned char*>(G), gpitch, v0, Vw, idx + row0 * K, zk, rc, K, c2);
 }
 
 void launch_g_from_z(int dtype, void* Z, int64_t zpitch, int64_t V, const int32_t* idx,
-                     const float* zk, const float* pcoef, const float* acoef, const float* lse2,
-                     int64_t nrows, int K, float c2, hipStream_t s) {
+                     const float* zk, const RowCoef& rc, int64_t nrows, int K, float c2,
+                     hipStream_t s) {
   if (nrows <= 0) return;
   ScopedTimer timer_(KID_G_FROM_Z, s);
   const size_t shm = static_cast<size_t>(K) * 8;
   const unsigned blocks = static_cast<unsigned>(nrows);
   unsigned char* Zc = static_cast<unsigned char*>(Z);
   if (dtype == 1)
-    k_g_from_z<BF16><<<blocks, kGzThreads, shm, s>>>(Zc, zpitch * 2, V, zpitch, idx, zk, pcoef, acoef,
-                                              lse2, K, c2);
+    k_g_from_z<BF16><<<blocks, kGzThreads, shm, s>>>(Zc, zpitch * 2, V, zpitch, idx, zk, rc, K, c2);
   else
-    k_g_from_z<F32><<<blocks, kGzThreads, shm, s>>>(Zc, zpitch * 4, V, zpitch, idx, zk, pcoef, acoef,
-                                             lse2, K, c2);
+    k_g_from_z<F32><<<blocks, kGzThreads, shm, s>>>(Zc, zpitch * 4, V, zpitch, idx, zk, rc, K, c2);
 }
 
 void launch_grad_hidden(int dtype, const void* G, int64_t gpitch, const void* W, int64_t d,
@@ -1160,14 +1266,15 @@ void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
   k_fill_f32<<<static_cast<unsigned>(blocks), 256, 0, s>>>(p, n, v);
 }
 
-void launch_validate_idx(const int32_t* idx, int64_t N, int K, int64_t V, int32_t* flag,
-                         hipStream_t s) {
+void launch_validate_idx(const int32_t* idx, int64_t N, int K, int64_t V, bool allow_negative,
+                         int32_t* flag, hipStream_t s) {
   const int64_t n = N * K;
   if (n <= 0) return;
   ScopedTimer timer_(KID_VALIDATE, s);
   int64_t blocks = ceil_div(n, 256);
   if (blocks > 4096) blocks = 4096;
-  k_validate_idx<<<static_cast<unsigned>(blocks), 256, 0, s>>>(idx, n, V, flag);
+  k_validate_idx<<<static_cast<unsigned>(blocks), 256, 0, s>>>(idx, n, V, allow_negative ? 1 : 0,
+                                                               flag);
 }
 
 }  // namespace fkl

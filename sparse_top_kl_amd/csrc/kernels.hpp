@@ -6,6 +6,33 @@
 
 namespace fkl {
 
+// Options of the loss beyond the plain KL (forward side), per chunk of rows:
+// per-row weights, hard labels (< 0: none) with z at the label, the mixing
+// weights of the KL and cross-entropy terms, and the temperature-1 partials
+// (present when labels are given and T != 1, else lse1 = lse).
+struct MergeOpts {
+  const float2* part_ce;     // [slot][row] partials at temperature 1, or null
+  const float* zy;           // [rows] z at the label, or null (no labels)
+  const int32_t* labels;     // [rows] or null
+  const float* row_weight;   // [rows] or null (weight 1)
+  float a_kl, a_ce;          // weights of the KL and cross-entropy terms
+  float* lse1;               // [rows] out: ln sum exp(z) at temperature 1, or null
+};
+
+// Per-row coefficients of the logit gradient (backward), rows of one block:
+//   dense G = acoef * 2^(z*c2 - lse2) [+ bcoef * 2^(z*log2(e) - lse1_2)]
+//   at the teacher ids minus pcoef_k, at the label minus ycoef.
+struct RowCoef {
+  const float* pcoef;      // [rows][K]
+  const float* acoef;      // [rows]
+  const float* lse2;       // [rows]
+  const float* bcoef;      // [rows] or null (one softmax)
+  const float* lse1_2;     // [rows] or null
+  const float* ycoef;      // [rows] or null (no labels)
+  const int32_t* labels;   // [rows] or null
+  const float* zy;         // [rows] z at the label, or null
+};
+
 // Rows of a (vocab-slice, token) partial: running max and sum of 2^(z*c2).
 constexpr int kSliceVocab = 128;  // vocabulary entries per partial slot
 
@@ -18,37 +45,45 @@ inline int64_t lse_slots(int64_t V) { return ceil_div(V, 256) * 2; }
 // Forward, per chunk: partial (max, sum) of 2^(z * c2) per (vocab slice, token).
 // With Z non-null the chunk's logits are also kept: Z[row0 + r][v] (pitch zpitch
 // elements of the dtype) = z rounded to the dtype for v < V, zero for V <= v < zpitch.
+// With part_ce non-null, partials at temperature 1 are written there too.
 void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64_t V,
                        int64_t row0, int64_t nrows, float c2, float2* part, int64_t part_ld,
-                       void* Z, int64_t zpitch, hipStream_t s);
-// z at the teacher ids for rows [row0, row0 + nrows).
+                       float2* part_ce, void* Z, int64_t zpitch, hipStream_t s);
+// z at the teacher ids for rows [row0, row0 + nrows) (an id < 0 gives 0).
 void launch_gather_dot(int dtype, const void* W, const void* H, const int32_t* idx, int64_t d,
                        int64_t row0, int64_t nrows, int K, float* zk, hipStream_t s);
 // Merge partials into lse, teacher softmax and per-row loss for one chunk.
+// (opts pointers are indexed by absolute row.)
 void launch_merge_loss(const float2* part, int64_t part_ld, int64_t nslots, const float* zk,
                        const float* logit, int64_t row0, int64_t nrows, int K, float T,
-                       float* lse, float* row_loss, hipStream_t s);
+                       float* lse, float* row_loss, const MergeOpts& opts, hipStream_t s);
 // loss = sum of row_loss in a fixed order (fp64 accumulation).
 void launch_reduce_loss(const float* row_loss, int64_t N, float* loss, hipStream_t s);
 
 // Backward, per chunk.
+// Coefficients of rows [row0, row0 + nrows) into the block arrays (row 0 =
+// row0): row_weight, labels and lse1 are indexed by absolute row; bcoef,
+// lse1_2 and ycoef may be null (not needed); two_sm selects the separate
+// temperature-1 softmax of the cross-entropy term.
 void launch_bwd_prep(const float* logit, const float* lse, const float* grad_loss, int64_t row0,
-                     int64_t nrows, int K, float T, float* pcoef, float* acoef, float* lse2,
-                     hipStream_t s);
+                     int64_t nrows, int K, float T, const float* row_weight,
+                     const int32_t* labels, float a_kl, float a_ce, const float* lse1,
+                     bool two_sm, float* pcoef, float* acoef, float* lse2, float* bcoef,
+                     float* lse1_2, float* ycoef, hipStream_t s);
 // Recompute the logit block rows [row0, row0 + nrows) x vocabulary [v0, v0 + Vw) into
 // the dense part of G (pitch gpitch elements).
 void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t v0,
                   int64_t Vw, int64_t gpitch, int64_t row0, int64_t nrows, float c2,
-                  const float* acoef, const float* lse2, void* G, hipStream_t s);
-// Exact G entries at the teacher ids that fall inside the slice.
+                  const RowCoef& rc, void* G, hipStream_t s);
+// Exact G entries at the teacher ids and the label that fall inside the slice.
 void launch_fixup(int dtype, void* G, int64_t gpitch, int64_t v0, int64_t Vw, const int32_t* idx,
-                  const float* zk, const float* pcoef, const float* acoef, const float* lse2,
-                  int64_t row0, int64_t nrows, int K, float c2, hipStream_t s);
+                  const float* zk, const RowCoef& rc, int64_t row0, int64_t nrows, int K,
+                  float c2, hipStream_t s);
 // Kept logits -> logit gradient in place, rows [0, nrows) of Z (pitch zpitch elements),
 // teacher-id entries included; idx, zk, pcoef, acoef and lse2 start at row 0 of Z.
 void launch_g_from_z(int dtype, void* Z, int64_t zpitch, int64_t V, const int32_t* idx,
-                     const float* zk, const float* pcoef, const float* acoef, const float* lse2,
-                     int64_t nrows, int K, float c2, hipStream_t s);
+                     const float* zk, const RowCoef& rc, int64_t nrows, int K, float c2,
+                     hipStream_t s);
 // acc[nrows][d] (+)= G_block . W[v0 : v0 + Vw]  (Vlim entries of the slice lie below V).
 void launch_grad_hidden(int dtype, const void* G, int64_t gpitch, const void* W, int64_t d,
                         int64_t v0, int64_t Vw, int64_t Vlim, int64_t nrows, bool accumulate,
@@ -76,7 +111,7 @@ int topk_capacity();
 
 // Utilities.
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
-void launch_validate_idx(const int32_t* idx, int64_t N, int K, int64_t V, int32_t* flag,
-                         hipStream_t s);
+void launch_validate_idx(const int32_t* idx, int64_t N, int K, int64_t V, bool allow_negative,
+                         int32_t* flag, hipStream_t s);
 
 }  // namespace fkl

@@ -59,6 +59,14 @@ _u32 = ctypes.c_uint32
 _f32 = ctypes.c_float
 _sz = ctypes.c_size_t
 
+class LossOptions(ctypes.Structure):
+    """Mirror of fkl_loss_options (include/fkl.h)."""
+    _fields_ = [("row_weight", ctypes.c_void_p), ("labels", ctypes.c_void_p),
+                ("alpha", ctypes.c_float), ("lse1", ctypes.c_void_p)]
+
+
+_opt = ctypes.POINTER(LossOptions)
+
 _SIGNATURES = {
     "fkl_abi_version": (_i32, []),
     "fkl_status_string": (ctypes.c_char_p, [_i32]),
@@ -79,6 +87,14 @@ _SIGNATURES = {
                                        ctypes.POINTER(_sz)]),
     "fkl_teacher_topk": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _i64, _i32, _u32, _p, _p, _p,
                                 _sz, _p]),
+    "fkl_forward_ex": (_i32, [_p, _p, _p, _p, _f32, _i64, _i64, _i64, _i64, _i32, _i32, _u32,
+                              _opt, _p, _p, _p, _p, _p, _sz, _p]),
+    "fkl_backward_ex": (_i32, [_p, _p, _p, _p, _p, _p, _p, _f32, _i64, _i64, _i64, _i64, _i32,
+                               _i32, _u32, _opt, _p, _p, _p, _sz, _p]),
+    "fkl_forward_keep_ex": (_i32, [_p, _p, _p, _p, _f32, _i64, _i64, _i64, _i64, _i32, _i32,
+                                   _u32, _opt, _p, _p, _p, _p, _p, _sz, _p, _sz, _p]),
+    "fkl_backward_keep_ex": (_i32, [_p, _p, _p, _p, _p, _p, _p, _f32, _i64, _i64, _i64, _i32,
+                                    _i32, _u32, _opt, _p, _sz, _p, _p, _p, _sz, _p]),
     "fkl_timing_enable": (_i32, [_i32]),
     "fkl_timing_reset": (_i32, []),
     "fkl_timing_read": (_i32, [_i32, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]),
@@ -162,6 +178,29 @@ class ForwardResult:
     lse: torch.Tensor        # [N] fp32
     row_loss: torch.Tensor   # [N] fp32
     topk_z: torch.Tensor     # [N, K] fp32
+    lse1: torch.Tensor | None = None   # [N] fp32, temperature-1 lse (with labels)
+
+
+def _loss_options(N, row_weight, labels, alpha, lse1):
+    """(LossOptions, keep-alive tensors) for the *_ex entry points."""
+    keep = []
+    if row_weight is not None:
+        row_weight = row_weight.reshape(-1).to(torch.float32).contiguous()
+        _require(row_weight, "row_weight", torch.float32)
+        if row_weight.numel() != N:
+            raise FklError(FKL_E_ARG, "row_weight must have N entries")
+        keep.append(row_weight)
+    if labels is not None:
+        labels = labels.reshape(-1).to(torch.int32).contiguous()
+        _require(labels, "labels", torch.int32)
+        if labels.numel() != N:
+            raise FklError(FKL_E_ARG, "labels must have N entries")
+        keep.append(labels)
+    if lse1 is not None:
+        _require(lse1, "lse1", torch.float32)
+        keep.append(lse1)
+    o = LossOptions(_ptr(row_weight), _ptr(labels), float(alpha), _ptr(lse1))
+    return o, keep
 
 
 def fkl_forward(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Tensor,
@@ -331,6 +370,97 @@ def fkl_teacher_topk(hidden: torch.Tensor, weight: torch.Tensor, K: int, chunk: 
     return idx, val
 
 
+def fkl_forward_ex(hidden, weight, topk_idx, topk_logit, T: float, chunk: int, *,
+                   row_weight=None, labels=None, alpha: float = 1.0, keep_logits=None,
+                   validate: bool = False, workspace=None):
+    """fkl_forward (or with keep_logits, a [N, keep_pitch(V)] buffer or True,
+    fkl_forward_keep) with loss options: per-row weights, hard labels (< 0:
+    none) and the KL/cross-entropy mixing weight alpha. Returns a
+    ForwardResult whose lse1 is set when labels are given (the backward needs
+    it), plus the kept logits in keep mode: (result, logits)."""
+    N, d = hidden.shape
+    V, K = weight.shape[0], topk_idx.shape[1]
+    code = dtype_code(hidden.dtype)
+    for t, n, dt in ((hidden, "hidden", None), (weight, "weight", hidden.dtype),
+                     (topk_idx, "topk_idx", torch.int32), (topk_logit, "topk_logit", torch.float32)):
+        _require(t, n, dt)
+    dev = hidden.device
+    fw, _ = fkl_workspace_size(N, d, V, K, chunk, code)
+    ws = workspace if workspace is not None else _workspace(fw, dev)
+    lse1 = torch.empty(N, dtype=torch.float32, device=dev) if labels is not None else None
+    o, alive = _loss_options(N, row_weight, labels, alpha, lse1)
+    out = ForwardResult(torch.empty((), dtype=torch.float32, device=dev),
+                        torch.empty(N, dtype=torch.float32, device=dev),
+                        torch.empty(N, dtype=torch.float32, device=dev),
+                        torch.empty(N, K, dtype=torch.float32, device=dev), lse1)
+    flags = FKL_FLAG_VALIDATE_IDX if validate else 0
+    common = (_ptr(hidden), _ptr(weight), _ptr(topk_idx), _ptr(topk_logit), float(T), chunk, N, d,
+              V, K, code, flags, ctypes.byref(o), _ptr(out.loss), _ptr(out.lse),
+              _ptr(out.row_loss), _ptr(out.topk_z))
+    if keep_logits is None or keep_logits is False:
+        _check(lib().fkl_forward_ex(*common, _ptr(ws), ws.numel(), _stream(dev)))
+        return out
+    z = keep_logits if isinstance(keep_logits, torch.Tensor) else \
+        torch.empty(N, keep_pitch(V), dtype=hidden.dtype, device=dev)
+    _require(z, "logits", hidden.dtype)
+    _check(lib().fkl_forward_keep_ex(*common, _ptr(z), z.numel() * z.element_size(), _ptr(ws),
+                                     ws.numel(), _stream(dev)))
+    del alive
+    return out, z
+
+
+def fkl_backward_ex(hidden, weight, topk_idx, topk_logit, lse, T: float, chunk: int, *,
+                    topk_z=None, grad_loss=None, row_weight=None, labels=None,
+                    alpha: float = 1.0, lse1=None, logits=None, grad_weight=None,
+                    accumulate: bool = False, validate: bool = False, workspace=None):
+    """fkl_backward (or, given the kept logits, fkl_backward_keep) with loss
+    options; lse1 is the forward's (required with labels when T != 1)."""
+    N, d = hidden.shape
+    V, K = weight.shape[0], topk_idx.shape[1]
+    code = dtype_code(hidden.dtype)
+    for t, n, dt in ((hidden, "hidden", None), (weight, "weight", hidden.dtype),
+                     (topk_idx, "topk_idx", torch.int32), (topk_logit, "topk_logit", torch.float32),
+                     (lse, "lse", torch.float32)):
+        _require(t, n, dt)
+    dev = hidden.device
+    if logits is None:
+        _, bw = fkl_workspace_size(N, d, V, K, chunk, code)
+    else:
+        _require(logits, "logits", hidden.dtype)
+        _, bw = fkl_keep_sizes(N, d, V, K, code)
+    ws = workspace if workspace is not None else _workspace(bw, dev)
+    o, alive = _loss_options(N, row_weight, labels, alpha, lse1)
+    grad_hidden = torch.empty_like(hidden)
+    if grad_weight is None:
+        grad_weight = torch.empty(V, d, dtype=torch.float32, device=dev)
+    flags = (FKL_FLAG_ACCUMULATE_GRAD_W if accumulate else 0) | \
+        (FKL_FLAG_VALIDATE_IDX if validate else 0)
+    head = (_ptr(hidden), _ptr(weight), _ptr(topk_idx), _ptr(topk_logit), _ptr(lse),
+            _ptr(topk_z), _ptr(grad_loss), float(T))
+    if logits is None:
+        _check(lib().fkl_backward_ex(*head, chunk, N, d, V, K, code, flags, ctypes.byref(o),
+                                     _ptr(grad_hidden), _ptr(grad_weight), _ptr(ws), ws.numel(),
+                                     _stream(dev)))
+    else:
+        _check(lib().fkl_backward_keep_ex(*head, N, d, V, K, code, flags, ctypes.byref(o),
+                                          _ptr(logits), logits.numel() * logits.element_size(),
+                                          _ptr(grad_hidden), _ptr(grad_weight), _ptr(ws),
+                                          ws.numel(), _stream(dev)))
+    del alive
+    return grad_hidden, grad_weight
+
+
+def fkl_forward_keep_ex(hidden, weight, topk_idx, topk_logit, T, chunk, *, logits=None, **opts):
+    """fkl_forward_keep with loss options; returns (ForwardResult, logits)."""
+    return fkl_forward_ex(hidden, weight, topk_idx, topk_logit, T, chunk,
+                          keep_logits=True if logits is None else logits, **opts)
+
+
+def fkl_backward_keep_ex(hidden, weight, topk_idx, topk_logit, lse, T, logits, **opts):
+    """fkl_backward_keep with loss options (the kept logits are consumed)."""
+    return fkl_backward_ex(hidden, weight, topk_idx, topk_logit, lse, T, 1, logits=logits, **opts)
+
+
 def fkl_timing_enable(on: bool) -> bool:
     """Turns per-kernel event timing on or off; returns the previous state."""
     return bool(lib().fkl_timing_enable(1 if on else 0))
@@ -372,32 +502,47 @@ class FusedChunkedKL(torch.autograd.Function):
     logits instead and its backward skips the recompute."""
 
     @staticmethod
-    def forward(ctx, hidden, weight, topk_idx, topk_logit, T, chunk, keep):
+    def forward(ctx, hidden, weight, topk_idx, topk_logit, T, chunk, keep, row_weight, labels,
+                alpha):
         shape = hidden.shape
         h2 = hidden.reshape(-1, shape[-1]).contiguous()
-        idx = topk_idx.reshape(h2.shape[0], -1).to(torch.int32).contiguous()
-        lg = topk_logit.reshape(h2.shape[0], -1).to(torch.float32).contiguous()
+        N = h2.shape[0]
+        idx = topk_idx.reshape(N, -1).to(torch.int32).contiguous()
+        lg = topk_logit.reshape(N, -1).to(torch.float32).contiguous()
         w = weight.contiguous()
-        if keep:
-            out, z = fkl_forward_keep(h2, w, idx, lg, T, chunk)
-            ctx.save_for_backward(h2, w, idx, lg, out.lse, out.topk_z, z)
+        rw = None if row_weight is None else row_weight.reshape(N).to(torch.float32).contiguous()
+        y = None if labels is None else labels.reshape(N).to(torch.int32).contiguous()
+        z = None
+        if rw is None and y is None:
+            if keep:
+                out, z = fkl_forward_keep(h2, w, idx, lg, T, chunk)
+            else:
+                out = fkl_forward(h2, w, idx, lg, T, chunk)
         else:
-            out = fkl_forward(h2, w, idx, lg, T, chunk)
-            ctx.save_for_backward(h2, w, idx, lg, out.lse, out.topk_z)
-        ctx.T, ctx.chunk, ctx.shape, ctx.keep = T, chunk, shape, keep
+            res = fkl_forward_ex(h2, w, idx, lg, T, chunk, row_weight=rw, labels=y, alpha=alpha,
+                                 keep_logits=True if keep else None)
+            out, z = res if keep else (res, None)
+        ctx.save_for_backward(h2, w, idx, lg, out.lse, out.topk_z, z, rw, y, out.lse1)
+        ctx.T, ctx.chunk, ctx.shape, ctx.alpha = T, chunk, shape, alpha
         return out.loss
 
     @staticmethod
     @torch.autograd.function.once_differentiable
     def backward(ctx, grad_loss):
         g = grad_loss.to(torch.float32).reshape(()).contiguous()
-        if ctx.keep:
-            h2, w, idx, lg, lse, zk, z = ctx.saved_tensors
-            gh, gw = fkl_backward_keep(h2, w, idx, lg, lse, ctx.T, z, topk_z=zk, grad_loss=g)
+        h2, w, idx, lg, lse, zk, z, rw, y, lse1 = ctx.saved_tensors
+        if rw is None and y is None:
+            if z is not None:
+                gh, gw = fkl_backward_keep(h2, w, idx, lg, lse, ctx.T, z, topk_z=zk, grad_loss=g)
+            else:
+                gh, gw = fkl_backward(h2, w, idx, lg, lse, ctx.T, ctx.chunk, topk_z=zk,
+                                      grad_loss=g)
         else:
-            h2, w, idx, lg, lse, zk = ctx.saved_tensors
-            gh, gw = fkl_backward(h2, w, idx, lg, lse, ctx.T, ctx.chunk, topk_z=zk, grad_loss=g)
-        return gh.reshape(ctx.shape), gw.to(w.dtype), None, None, None, None, None
+            gh, gw = fkl_backward_ex(h2, w, idx, lg, lse, ctx.T, ctx.chunk, topk_z=zk, grad_loss=g,
+                                     row_weight=rw, labels=y, alpha=ctx.alpha, lse1=lse1,
+                                     logits=z)
+        return (gh.reshape(ctx.shape), gw.to(w.dtype), None, None, None, None, None, None, None,
+                None)
 
 
 def choose_keep(N: int, d: int, V: int, K: int, dtype: torch.dtype, budget: int | None,
@@ -414,8 +559,9 @@ def choose_keep(N: int, d: int, V: int, K: int, dtype: torch.dtype, budget: int 
 
 def fused_chunked_kl(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Tensor,
                      topk_logit: torch.Tensor, T: float = 1.0, chunk: int = 2048, *,
-                     keep_logits: bool | str = False,
-                     memory_budget: int | None = None) -> torch.Tensor:
+                     keep_logits: bool | str = False, memory_budget: int | None = None,
+                     row_weight: torch.Tensor | None = None, labels: torch.Tensor | None = None,
+                     alpha: float = 0.5) -> torch.Tensor:
     """Sum over tokens of T^2 KL(teacher top-K softmax || student softmax) at temperature T.
 
     hidden [..., d] (bf16 or fp32), weight [V, d] (LM head, nn.Linear layout),
@@ -427,6 +573,11 @@ def fused_chunked_kl(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch
     backward (the forward-chunked variant: no recompute, N * V elements more
     memory); "auto" keeps them when they fit in memory_budget bytes (default:
     half of the free device memory).
+
+    row_weight [...] weights each token's term (0 masks padding; mask /
+    mask.sum() gives the mean over valid tokens). labels [...] (hard labels,
+    < 0 for none) add the cross-entropy at temperature 1: the loss becomes
+    sum_r w_r (alpha T^2 KL_r + (1 - alpha) CE_r).
     """
     keep = keep_logits
     if keep == "auto":
@@ -437,4 +588,4 @@ def fused_chunked_kl(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch
     elif not isinstance(keep, bool):
         raise ValueError(f"keep_logits must be True, False or 'auto' (got {keep_logits!r})")
     return FusedChunkedKL.apply(hidden, weight, topk_idx, topk_logit, float(T), int(chunk),
-                                bool(keep))
+                                bool(keep), row_weight, labels, float(alpha))

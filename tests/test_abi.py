@@ -47,8 +47,9 @@ def test_workspace_is_bounded_by_chunk_times_vocab_and_never_rows_times_vocab():
     Vpad = (V + 7) // 8 * 8
     for N in (8192, 32768, 65536, 131072):
         f, b = fkl.fkl_workspace_size(N, d, V, K, chunk, fkl.FKL_BF16)
-        # forward: per-chunk partials (one float2 per row and 128-wide slice) + per-row scratch
-        assert f <= chunk * ((V + 255) // 256) * 2 * 8 + N * (4 + 4 * K) + (1 << 16)
+        # forward: per-chunk partials (one float2 per row and 128-wide slice, at T and at
+        # temperature 1 for the cross-entropy option) + per-row scratch
+        assert f <= 2 * chunk * ((V + 255) // 256) * 2 * 8 + N * (8 + 4 * K) + (1 << 16)
         # backward: one logit-gradient block within the chunk x V budget (its rows padded
         # by fewer than 64 elements to whole 128-byte lines), plus per-row scratch of a
         # row block (fp32 grad_hidden accumulator, teacher coefficients)
@@ -152,8 +153,8 @@ def test_keep_sizes_are_rows_times_padded_vocab():
         z, b = fkl.fkl_keep_sizes(N, d, V, K, dt)
         assert z == N * fkl.keep_pitch(V) * eb
         assert fkl.keep_pitch(V) % 64 == 0 and 0 <= fkl.keep_pitch(V) - V < 64
-        # per-row coefficients (p, z at the ids, two scalars) and the fp32 grad_hidden rows
-        assert N * (8 * K + 8 + 4 * d) <= b <= N * (8 * K + 8 + 4 * d) + 6 * 256
+        # per-row coefficients (p, z at the ids, six scalars) and the fp32 grad_hidden rows
+        assert N * (8 * K + 24 + 4 * d) <= b <= N * (8 * K + 24 + 4 * d) + 10 * 256
 
 
 def test_keep_sizes_reject_a_vocabulary_too_large_to_keep():
@@ -250,3 +251,36 @@ def _topk(**over):
 def test_teacher_topk_validation(over, code):
     assert _topk(**over) == code
     assert fkl.fkl_last_error() != ""
+
+
+def _fwd_ex(opts, **over):
+    args = dict(hidden=A, weight=A, idx=A, logit=A, T=2.0, chunk=4, N=10, d=16, V=100, K=5,
+                dtype=fkl.FKL_BF16, flags=0, opts=opts, loss=A, lse=A, row_loss=None, topk_z=None,
+                ws=A, ws_bytes=1 << 40, stream=None)
+    args.update(over)
+    return fkl.lib().fkl_forward_ex(*args.values())
+
+
+def _bwd_ex(opts, **over):
+    args = dict(hidden=A, weight=A, idx=A, logit=A, lse=A, topk_z=None, grad_loss=None, T=2.0,
+                chunk=4, N=10, d=16, V=100, K=5, dtype=fkl.FKL_BF16, flags=0, opts=opts, gh=A,
+                gw=A, ws=A, ws_bytes=1 << 40, stream=None)
+    args.update(over)
+    return fkl.lib().fkl_backward_ex(*args.values())
+
+
+def test_loss_options_validation():
+    import ctypes
+    ok = fkl.LossOptions(A, A, 0.5, A)
+    bad_alpha = fkl.LossOptions(None, A, float("nan"), A)
+    bad_align = fkl.LossOptions(A + 2, None, 0.5, None)
+    no_lse1 = fkl.LossOptions(None, A, 0.5, None)
+    assert _fwd_ex(ctypes.byref(bad_alpha)) == fkl.FKL_E_ARG
+    assert _fwd_ex(ctypes.byref(bad_align)) == fkl.FKL_E_ARG
+    assert _bwd_ex(ctypes.byref(bad_alpha)) == fkl.FKL_E_ARG
+    # with labels and T != 1 the backward needs the forward's lse1 ...
+    assert _bwd_ex(ctypes.byref(no_lse1)) == fkl.FKL_E_ARG
+    assert "lse1" in fkl.fkl_last_error()
+    # ... but not at T = 1 (same softmax); these stop at the workspace check
+    assert _bwd_ex(ctypes.byref(no_lse1), T=1.0, ws_bytes=16) == fkl.FKL_E_WORKSPACE
+    assert _bwd_ex(ctypes.byref(ok), ws_bytes=16) == fkl.FKL_E_WORKSPACE

@@ -1,0 +1,140 @@
+"""Loss options on the GPU against the fp64 oracle: per-row weights (with
+zero-weight padding rows whose teacher logits are all -inf), hard labels (some
+rows without one, some equal to a teacher id) mixed in with alpha at T = 1
+(one softmax) and T != 1 (a separate temperature-1 softmax), for the fused
+path and the kept-logits path, plus the autograd wrapper. Same tolerances as
+the plain parity tests."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_top_kl_amd import fkl, synth
+from tests.gpu_helpers import TOL, announce, compare, elementwise_ok, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(name, n, d, V, K, T, dtype, chunk, seed=None):
+    w = synth.small_workload(name, n=n, d=d, V=V, K=K, T=T, dtype=dtype, chunk=chunk,
+                             seed=zlib.crc32(name.encode()) % 1000 if seed is None else seed)
+    return synth.make_inputs(w)
+
+
+def _options(inp, weights, labels, rng):
+    n, V = inp["hidden"].shape[0], inp["weight"].shape[0]
+    wr = y = None
+    if weights:
+        wr = rng.uniform(0.25, 2.0, size=n).astype(np.float32)
+        pad = rng.choice(n, size=max(1, n // 10), replace=False)
+        wr[pad] = 0.0
+        inp["topk_logit"][pad] = -np.inf                  # padding rows: no teacher entries
+    if labels:
+        y = rng.integers(0, V, size=n).astype(np.int32)
+        y[rng.choice(n, size=max(1, n // 8), replace=False)] = -1                   # no label
+        same = rng.choice(n, size=max(1, n // 8), replace=False)
+        y[same] = inp["topk_idx"][same, 2]                # label equal to a teacher id
+    return wr, y
+
+
+def _run(inp, wr, y, alpha, keep, grad_scale=None):
+    T, chunk = inp["T"], inp["chunk"]
+    h, W, idx, lg = upload(inp)
+    dev = h.device
+    rwt = None if wr is None else torch.from_numpy(wr).to(dev)
+    yt = None if y is None else torch.from_numpy(y).to(dev)
+    g = None if grad_scale is None else torch.tensor(float(grad_scale), device=dev)
+    if keep:
+        out, z = fkl.fkl_forward_keep_ex(h, W, idx, lg, T, chunk, row_weight=rwt, labels=yt,
+                                         alpha=alpha)
+        gh, gw = fkl.fkl_backward_keep_ex(h, W, idx, lg, out.lse, T, z, topk_z=out.topk_z,
+                                          grad_loss=g, row_weight=rwt, labels=yt, alpha=alpha,
+                                          lse1=out.lse1)
+    else:
+        out = fkl.fkl_forward_ex(h, W, idx, lg, T, chunk, row_weight=rwt, labels=yt, alpha=alpha)
+        gh, gw = fkl.fkl_backward_ex(h, W, idx, lg, out.lse, T, chunk, topk_z=out.topk_z,
+                                     grad_loss=g, row_weight=rwt, labels=yt, alpha=alpha,
+                                     lse1=out.lse1)
+    torch.cuda.synchronize()
+    res = {
+        "loss": out.loss.item(),
+        "lse": out.lse.double().cpu().numpy(),
+        "row_loss": out.row_loss.double().cpu().numpy(),
+        "topk_z": out.topk_z.double().cpu().numpy(),
+        "grad_hidden": gh.double().cpu().numpy(),
+        "grad_w": gw.double().cpu().numpy(),
+    }
+    if out.lse1 is not None:
+        res["lse1"] = out.lse1.double().cpu().numpy()
+    return res
+
+
+CASES = [
+    # name, n, d, V, K, T, dtype, chunk, weights, labels, alpha
+    ("weights_bf16", 600, 264, 3001, 100, 1.5, "bf16", 256, True, False, 1.0),
+    ("weights_fp32", 300, 128, 2000, 60, 2.0, "fp32", 128, True, False, 1.0),
+    ("labels_T2_bf16", 600, 264, 3001, 100, 2.0, "bf16", 256, False, True, 0.3),
+    ("labels_T2_fp32", 300, 128, 2000, 60, 2.0, "fp32", 100, True, True, 0.7),
+    ("labels_T1_bf16", 500, 256, 2500, 100, 1.0, "bf16", 200, True, True, 0.6),
+    ("pure_ce_T15_bf16", 400, 128, 1800, 40, 1.5, "bf16", 128, False, True, 0.0),
+]
+
+
+@pytest.mark.parametrize("keep", [False, True], ids=["fused", "keep"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_options_against_oracle(gpu_device, case, keep):
+    name, n, d, V, K, T, dtype, chunk, weights, labels, alpha = case
+    announce(f"{name} ({'kept logits' if keep else 'fused'}): n={n} d={d} V={V} K={K} T={T} "
+             f"{dtype} weights={weights} labels={labels} alpha={alpha}")
+    inp = _inputs(name, n, d, V, K, T, dtype, chunk)
+    wr, y = _options(inp, weights, labels, np.random.default_rng(zlib.crc32(name.encode())))
+    res = _run(inp, wr, y, alpha, keep, grad_scale=-0.8)
+    ref = oracle.forward_backward(inp["hidden"], inp["weight"], inp["topk_idx"],
+                                  inp["topk_logit"], T, grad_scale=-0.8, row_weight=wr,
+                                  labels=y, alpha=alpha)
+    assert np.all(np.isfinite(res["grad_w"])) and np.all(np.isfinite(res["row_loss"]))
+    compare(res, ref, dtype)
+    if y is not None:
+        err = elementwise_ok(res["lse1"], ref["lse1"], TOL[dtype]["loss"])
+        assert err <= TOL[dtype]["loss"], err
+    if wr is not None:
+        assert np.all(res["row_loss"][wr == 0] == 0.0)
+        assert np.all(res["grad_hidden"][wr == 0] == 0.0)
+
+
+def test_autograd_with_options(gpu_device):
+    announce("autograd: row weights + labels, bf16, T = 2")
+    inp = _inputs("opt_autograd", 2 * 150, 128, 2200, 50, 2.0, "bf16", 128)
+    wr, y = _options(inp, True, True, np.random.default_rng(5))
+    h, W, idx, lg = upload(inp)
+    hh = h.detach().clone().reshape(2, 150, -1).requires_grad_(True)
+    WW = W.detach().clone().requires_grad_(True)
+    loss = fkl.fused_chunked_kl(hh, WW, idx.reshape(2, 150, -1), lg.reshape(2, 150, -1), T=2.0,
+                                chunk=128, row_weight=torch.from_numpy(wr).cuda().reshape(2, 150),
+                                labels=torch.from_numpy(y).cuda().reshape(2, 150), alpha=0.4)
+    loss.backward()
+    torch.cuda.synchronize()
+    ref = oracle.forward_backward(inp["hidden"], inp["weight"], inp["topk_idx"],
+                                  inp["topk_logit"], 2.0, row_weight=wr, labels=y, alpha=0.4)
+    assert abs(loss.item() - ref["loss"]) <= TOL["bf16"]["loss"] * abs(ref["loss"])
+    gh = hh.grad.reshape(300, -1).double().cpu().numpy()
+    gw = WW.grad.double().cpu().numpy()
+    assert np.abs(gh - ref["grad_hidden"]).max() / np.abs(ref["grad_hidden"]).max() <= 2e-2
+    assert np.abs(gw - ref["grad_w"]).max() / np.abs(ref["grad_w"]).max() <= 2e-2
+
+
+def test_validate_flag_rejects_a_label_out_of_range(gpu_device):
+    announce("validate: label >= V")
+    inp = _inputs("opt_validate", 50, 64, 500, 10, 1.0, "fp32", 32)
+    h, W, idx, lg = upload(inp)
+    y = torch.zeros(50, dtype=torch.int32, device=h.device)
+    y[7] = 500
+    with pytest.raises(fkl.FklError) as e:
+        fkl.fkl_forward_ex(h, W, idx, lg, 1.0, 32, labels=y, alpha=0.5, validate=True)
+    assert e.value.status == fkl.FKL_E_INDEX
+    y[7] = -1                                     # no label: allowed
+    fkl.fkl_forward_ex(h, W, idx, lg, 1.0, 32, labels=y, alpha=0.5, validate=True)
+    torch.cuda.synchronize()
