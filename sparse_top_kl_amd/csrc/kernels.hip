@@ -29,6 +29,17 @@
 //   k_reduce_gh    (per row block) accumulator -> grad_hidden rows.
 //   k_grad_w       MFMA product G^T . H_block into the fp32 grad_W rows of the
 //                  slice, accumulated over the row blocks.
+// Loss options (per-row weights, hard labels mixed in with alpha) change the
+// per-row coefficients (k_merge_loss, k_bwd_prep), add a second set of LSE
+// partials at temperature 1 when T != 1 (k_logits_lse<..., CE2>) and a second
+// softmax term to the G producers (GradValue<CE2>), and the label entry to the
+// exact entries (k_fixup, k_g_from_z).
+// Forward-chunked variant (the logits are kept instead of recomputed):
+//   k_logits_lse<..., KEEP>  also stores the tile's logits in the input dtype;
+//   k_g_from_z               turns a kept row into its G row in place;
+//   then k_grad_hidden over all rows and k_grad_w over row blocks.
+// Teacher top-K cache (section further down): k_teacher_logits,
+// k_topk_threshold, k_topk_collect, k_topk_final.
 #include <math.h>
 
 #include <cstdlib>
