@@ -38,6 +38,16 @@ the cross-entropy is taken at temperature 1, as in the classic recipe the
 page describes, and the mixture is convex). Rows with w_r = 0 contribute
 nothing, whatever their teacher logits.
 
+Teacher tail (an alternative to renormalising the teacher over its K
+entries, which the pages leave open): given the teacher's full-vocabulary
+log-sum-exp at T per row (``teacher_lse``, cached beside its top-K), the
+teacher probabilities of the cached ids are p_k = exp(l_k / T - teacher_lse)
+(not renormalised), the rest of the teacher's mass is one tail bucket
+p_tail = 1 - sum_k p_k, the student's is 1 - S with S = sum_k q_(idx_k), and
+the KL is taken between these K + 1 buckets:
+
+    KL_r = sum_k p_k (log p_k - log q_(idx_k)) + p_tail (log p_tail - log(1 - S)).
+
 Readings taken where the pages are silent (each listed in the design notes):
 forward KL(p_t || p_s); the teacher softmax is renormalised over its K cached
 entries; the student is normalised over the full vocabulary; tokens are summed
@@ -110,7 +120,7 @@ def teacher_log_probs(topk_logit, T: float):
 def forward_backward(hidden, w_store, topk_idx, topk_logit, T: float,
                      grad_scale: float = 1.0, want_grads: bool = True,
                      block_rows: int = 128, row_weight=None, labels=None,
-                     alpha: float = 1.0) -> dict:
+                     alpha: float = 1.0, teacher_lse=None) -> dict:
     """Loss, per-row pieces and gradients of the top-K KL loss, in fp64.
 
     hidden [N, d], w_store [V, d] (any float dtype; upcast exactly),
@@ -146,7 +156,17 @@ def forward_backward(hidden, w_store, topk_idx, topk_logit, T: float,
     # teacher logits so that a padding row of -inf entries stays harmless
     tl = np.array(topk_logit, dtype=np.float64)
     tl[wr == 0] = 0.0
-    log_p, p = teacher_log_probs(tl, T)
+    if teacher_lse is None:
+        log_p, p = teacher_log_probs(tl, T)
+        p_tail = np.zeros(n)
+    else:
+        # the cached ids' share of the teacher's full distribution, and the rest
+        tlse = _f64(teacher_lse).reshape(n)
+        tlse = np.where(wr == 0, 0.0, tlse)
+        with np.errstate(invalid="ignore"):
+            log_p = tl / T - tlse[:, None]
+        p = np.exp(log_p)
+        p_tail = np.maximum(0.0, 1.0 - p.sum(axis=1))
 
     row_loss = np.zeros(n)
     lse = np.zeros(n)
@@ -165,7 +185,13 @@ def forward_backward(hidden, w_store, topk_idx, topk_logit, T: float,
         pb, lpb = p[r0:r1], log_p[r0:r1]
         # p * (log p - log p_s), with the 0 * log 0 = 0 convention
         term = np.where(pb > 0, pb * (np.where(pb > 0, lpb, 0.0) - log_ps), 0.0)
-        kl = T * T * term.sum(axis=1)
+        ptb = p_tail[r0:r1]
+        S = np.exp(log_ps).sum(axis=1)                     # student mass on the cached ids
+        one_s = np.maximum(1.0 - S, 1e-300)
+        with np.errstate(divide="ignore"):
+            tail = np.where(ptb > 0, ptb * (np.log(np.where(ptb > 0, ptb, 1.0)) - np.log(one_s)),
+                            0.0)
+        kl = T * T * (term.sum(axis=1) + tail)
         lse1_b = logsumexp_rows(z)
         yb = y[r0:r1]
         has = yb >= 0
@@ -182,6 +208,12 @@ def forward_backward(hidden, w_store, topk_idx, topk_logit, T: float,
             rows = np.repeat(np.arange(r1 - r0), idx.shape[1])
             np.add.at(P, (rows, idx[r0:r1].ravel()), pb.ravel())
             G = a_kl * T * (q * pb.sum(axis=1, keepdims=True) - P)
+            if teacher_lse is not None:
+                # d/dz of p_tail (log p_tail - log(1 - S)): T p_tail (Q - q S) / (1 - S),
+                # Q_v = q_v times the number of cached ids equal to v
+                M = np.zeros_like(q)
+                np.add.at(M, (rows, idx[r0:r1].ravel()), 1.0)
+                G = G + a_kl * T * (ptb / one_s)[:, None] * (M * q - q * S[:, None])
             if a_ce != 0.0:
                 q1 = np.exp(z - lse1_b[:, None])
                 E = np.zeros_like(q1)
@@ -206,7 +238,7 @@ def forward_backward(hidden, w_store, topk_idx, topk_logit, T: float,
 
 def brute_force(hidden, w_store, topk_idx, topk_logit, T: float,
                 grad_scale: float = 1.0, row_weight=None, labels=None,
-                alpha: float = 1.0) -> dict:
+                alpha: float = 1.0, teacher_lse=None) -> dict:
     """The same quantities written as scalar Python loops (tiny inputs only).
 
     No NumPy arithmetic: every sum is ``math.fsum`` over Python floats, so a
@@ -236,13 +268,22 @@ def brute_force(hidden, w_store, topk_idx, topk_logit, T: float,
             grad_h.append([0.0] * d)
             continue
         a = [x / T for x in L[r]]
-        ma = max(a)
-        ln = ma + math.log(math.fsum(math.exp(x - ma) for x in a if x != -math.inf))
+        if teacher_lse is None:
+            ma = max(a)
+            ln = ma + math.log(math.fsum(math.exp(x - ma) for x in a if x != -math.inf))
+        else:
+            ln = float(teacher_lse[r])
         pt = [0.0 if x == -math.inf else math.exp(x - ln) for x in a]
         terms = []
         for k, c in enumerate(I[r]):
             if pt[k] > 0.0:
                 terms.append(pt[k] * ((a[k] - ln) - (z[c] / T - lse)))
+        ptail, S = 0.0, 0.0
+        if teacher_lse is not None:
+            ptail = max(0.0, 1.0 - math.fsum(pt))
+            S = math.fsum(math.exp(z[c] / T - lse) for c in I[r])
+            if ptail > 0.0:
+                terms.append(ptail * (math.log(ptail) - math.log(1.0 - S)))
         ce = (lse1 - z[Y[r]]) if Y[r] >= 0 else 0.0
         row_loss.append(Wr[r] * (a_kl * T * T * math.fsum(terms) + a_ce * ce))
         lse_all.append(lse)
@@ -252,6 +293,9 @@ def brute_force(hidden, w_store, topk_idx, topk_logit, T: float,
             q = math.exp(z[c] / T - lse)
             Pc = math.fsum(pt[k] for k, cc in enumerate(I[r]) if cc == c)
             g = a_kl * T * (q * sp - Pc)
+            if ptail > 0.0:
+                mult = sum(1 for cc in I[r] if cc == c)
+                g += a_kl * T * ptail * (mult * q - q * S) / (1.0 - S)
             if Y[r] >= 0:
                 g += a_ce * (math.exp(z[c] - lse1) - (1.0 if c == Y[r] else 0.0))
             G.append(grad_scale * Wr[r] * g)

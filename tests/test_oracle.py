@@ -514,3 +514,137 @@ def test_option_pins_accept_the_oracle():
 @pytest.mark.parametrize("mutant", _option_mutants(), ids=lambda f: f.__name__)
 def test_planted_option_mistakes_are_caught(mutant):
     assert not all(_option_pin_suite(mutant))
+
+
+# ------------------------------------------------------------- teacher tail
+
+def _teacher_with_tail(seed, n=5, d=6, v=40, k=7, T=1.5):
+    """A full teacher (V logits per row) cached as its top-K plus its lse at T."""
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((n, d))
+    w = rng.standard_normal((v, d)) / math.sqrt(d)
+    full = rng.standard_normal((n, v)) * 2.0
+    idx = np.argsort(-full, axis=1)[:, :k].astype(np.int32)
+    logit = np.take_along_axis(full, idx.astype(np.int64), axis=1)
+    tlse = scipy.special.logsumexp(full / T, axis=1)
+    return h, w, idx, logit, tlse, full
+
+
+@pytest.mark.parametrize("T", [1.0, 2.0])
+def test_tail_bucket_equals_scipy_relative_entropy(T):
+    h, w, idx, logit, tlse, full = _teacher_with_tail(31, T=T)
+    out = _run(h, w, idx, logit, T, teacher_lse=tlse)
+    pt = scipy.special.softmax(full / T, axis=1)
+    qs = scipy.special.softmax((h @ w.T) / T, axis=1)
+    ii = idx.astype(np.int64)
+    P = np.concatenate([np.take_along_axis(pt, ii, 1), 1 - np.take_along_axis(pt, ii, 1).sum(1,
+                        keepdims=True)], axis=1)
+    Q = np.concatenate([np.take_along_axis(qs, ii, 1), 1 - np.take_along_axis(qs, ii, 1).sum(1,
+                        keepdims=True)], axis=1)
+    ref = T * T * scipy.special.rel_entr(P, Q).sum(axis=1)
+    np.testing.assert_allclose(out["row_loss"], ref, rtol=1e-10)
+
+
+def test_tail_bucket_with_the_whole_vocabulary_is_the_full_kl():
+    rng = np.random.default_rng(32)
+    n, d, v, T = 4, 5, 9, 1.7
+    h, w = rng.standard_normal((n, d)), rng.standard_normal((v, d))
+    idx = np.stack([rng.permutation(v) for _ in range(n)]).astype(np.int32)
+    logit = rng.standard_normal((n, v)) * 2.0
+    tlse = scipy.special.logsumexp(logit / T, axis=1)
+    out = _run(h, w, idx, logit, T, teacher_lse=tlse)
+    z = torch.from_numpy(h) @ torch.from_numpy(w).T
+    dense = torch.empty(n, v, dtype=torch.float64)
+    dense.scatter_(1, torch.from_numpy(idx).long(), torch.from_numpy(logit))
+    ref = torch.nn.functional.kl_div(torch.log_softmax(z / T, 1), torch.log_softmax(dense / T, 1),
+                                     log_target=True, reduction="sum") * T * T
+    assert out["loss"] == pytest.approx(ref.item(), rel=1e-10)
+
+
+def test_tail_bucket_reduces_to_renormalised_when_the_cache_holds_all_mass():
+    h, w, idx, logit = _rand_problem(33, n=5, d=6, v=15, k=5)
+    T = 1.3
+    tlse = scipy.special.logsumexp(logit / T, axis=1)      # "the top-K are everything"
+    a = _run(h, w, idx, logit, T, teacher_lse=tlse)
+    b = _run(h, w, idx, logit, T)
+    assert a["loss"] == pytest.approx(b["loss"], rel=1e-12)
+    np.testing.assert_allclose(a["grad_hidden"], b["grad_hidden"], rtol=1e-9, atol=1e-13)
+
+
+@pytest.mark.parametrize("T", [1.0, 2.5])
+def test_tail_bucket_gradients_and_brute_force(T):
+    h, w, idx, logit, tlse, _ = _teacher_with_tail(34, n=3, d=4, v=11, k=4, T=T)
+    kw = dict(teacher_lse=tlse, row_weight=np.array([1.0, 0.5, 2.0]),
+              labels=np.array([3, -1, 7]), alpha=0.7, grad_scale=1.3)
+    out = _run(h, w, idx, logit, T, **kw)
+    bf = kl_oracle.brute_force(h, w, idx, logit, T, **kw)
+    assert out["loss"] == pytest.approx(bf["loss"], rel=1e-12)
+    np.testing.assert_allclose(out["grad_w"], bf["grad_w"], rtol=1e-10, atol=1e-13)
+
+    def f():
+        return 1.3 * _run(h, w, idx, logit, T, want_grads=False,
+                          **{k: v for k, v in kw.items() if k != "grad_scale"})["loss"]
+
+    np.testing.assert_allclose(out["grad_hidden"], _fd_grad(f, h), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(out["grad_w"], _fd_grad(f, w), rtol=1e-6, atol=1e-8)
+
+
+def _tail_mutants():
+    base = kl_oracle.forward_backward
+
+    def tail_term_sign(h, w, idx, logit, T, teacher_lse=None, **k):
+        out = dict(base(h, w, idx, logit, T, teacher_lse=teacher_lse, **k))
+        if teacher_lse is not None:   # the tail bucket's term with the opposite sign
+            z = np.asarray(h, np.float64) @ np.asarray(w, np.float64).T
+            q = scipy.special.softmax(z / T, axis=1)
+            S = np.take_along_axis(q, np.asarray(idx, np.int64), 1).sum(1)
+            pk = np.exp(np.asarray(logit, np.float64) / T - np.asarray(teacher_lse)[:, None])
+            pt = np.maximum(0.0, 1.0 - pk.sum(1))
+            tail = np.where(pt > 0, pt * (np.log(np.where(pt > 0, pt, 1.0)) - np.log(1 - S)), 0.0)
+            out["loss"] = out["loss"] - 2.0 * T * T * float(tail.sum())
+        return out
+
+    def no_tail_gradient(h, w, idx, logit, T, teacher_lse=None, **k):
+        out = dict(base(h, w, idx, logit, T, teacher_lse=teacher_lse, **k))
+        if teacher_lse is not None and k.get("want_grads", True):
+            # gradients of the teacher-normalised KL without the tail bucket
+            tl = np.asarray(logit, np.float64)
+            z = np.asarray(h, np.float64) @ np.asarray(w, np.float64).T
+            lse = scipy.special.logsumexp(z / T, axis=1, keepdims=True)
+            q = np.exp(z / T - lse)
+            p = np.exp(tl / T - np.asarray(teacher_lse)[:, None])
+            P = np.zeros_like(q)
+            np.put_along_axis(P, np.asarray(idx, np.int64), p, axis=1)
+            G = k.get("grad_scale", 1.0) * T * (q * p.sum(1, keepdims=True) - P)
+            out["grad_hidden"] = G @ np.asarray(w, np.float64)
+        return out
+
+    return [tail_term_sign, no_tail_gradient]
+
+
+def _tail_pin_suite(fb):
+    h, w, idx, logit, tlse, full = _teacher_with_tail(35, T=2.0)
+    out = fb(h, w, idx, logit, 2.0, teacher_lse=tlse)
+    pt = scipy.special.softmax(full / 2.0, axis=1)
+    qs = scipy.special.softmax((h @ w.T) / 2.0, axis=1)
+    ii = idx.astype(np.int64)
+    P = np.concatenate([np.take_along_axis(pt, ii, 1), 1 - np.take_along_axis(pt, ii, 1).sum(1,
+                        keepdims=True)], axis=1)
+    Q = np.concatenate([np.take_along_axis(qs, ii, 1), 1 - np.take_along_axis(qs, ii, 1).sum(1,
+                        keepdims=True)], axis=1)
+    ok = [math.isclose(out["loss"], 4.0 * scipy.special.rel_entr(P, Q).sum(), rel_tol=1e-10)]
+
+    def f():
+        return fb(h, w, idx, logit, 2.0, teacher_lse=tlse, want_grads=False)["loss"]
+
+    ok.append(np.allclose(out["grad_hidden"], _fd_grad(f, h), rtol=1e-5, atol=1e-7))
+    return ok
+
+
+def test_tail_pins_accept_the_oracle():
+    assert all(_tail_pin_suite(kl_oracle.forward_backward))
+
+
+@pytest.mark.parametrize("mutant", _tail_mutants(), ids=lambda f: f.__name__)
+def test_planted_tail_mistakes_are_caught(mutant):
+    assert not all(_tail_pin_suite(mutant))
