@@ -160,6 +160,16 @@ typedef struct fkl_loss_options {
                               written by the forward when non-NULL; read by
                               the backward, which requires it when labels are
                               given and T != 1 (else it may be NULL) */
+  const float* teacher_lse; /* [N] fp32 teacher ln sum_v exp(l_rv / T) over the
+                              full vocabulary (fkl_teacher_topk_ex can write
+                              it), or NULL. Given, the teacher is not
+                              renormalised over its K entries: p_k = exp(l_k / T
+                              - teacher_lse) and the rest of its mass forms a
+                              tail bucket, p_tail = 1 - sum_k p_k, matched by
+                              the student's mass outside the cached ids,
+                              1 - S with S = sum_k q_(idx_k):
+                              KL_r = sum_k p_k ln(p_k / q_k)
+                                     + p_tail ln(p_tail / (1 - S)). */
 } fkl_loss_options;
 
 /* fkl_forward, fkl_backward, fkl_forward_keep and fkl_backward_keep with loss
@@ -270,6 +280,14 @@ int32_t fkl_backward_keep_ex(const void* hidden, const void* weight, const int32
  * e.g. massive ties) take an exact but slower path. */
 int32_t fkl_topk_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk,
                                 int32_t dtype, size_t* bytes);
+/* fkl_teacher_topk plus, when teacher_lse is non-NULL, the teacher's
+ * full-vocabulary log-sum-exp at temperature T per row, teacher_lse[r] =
+ * ln sum_v exp(l_rv / T) (fp32; the tail-bucket input of fkl_loss_options).
+ * T must be finite and > 0 when teacher_lse is requested. */
+int32_t fkl_teacher_topk_ex(const void* hidden, const void* weight, int64_t N, int64_t d,
+                            int64_t V, int32_t K, int64_t chunk, int32_t dtype, uint32_t flags,
+                            float T, int32_t* topk_idx, float* topk_logit, float* teacher_lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
 int32_t fkl_teacher_topk(const void* hidden, const void* weight, int64_t N, int64_t d, int64_t V,
                          int32_t K, int64_t chunk, int32_t dtype, uint32_t flags,
                          int32_t* topk_idx, float* topk_logit, void* workspace,

@@ -47,8 +47,8 @@ struct Plan {
   // forward workspace offsets
   size_t f_part, f_part_ce, f_rowloss, f_topkz, f_zy, f_flag, f_total;
   // backward workspace offsets
-  size_t b_G, b_ghacc, b_pcoef, b_acoef, b_lse2, b_zk, b_bcoef, b_lse12, b_ycoef, b_zy, b_flag,
-      b_total;
+  size_t b_G, b_ghacc, b_pcoef, b_acoef, b_lse2, b_zk, b_bcoef, b_lse12, b_ycoef, b_zy, b_tcoef,
+      b_flag, b_total;
 };
 
 // Predicted cost of the backward contractions for row blocks of rc rows and
@@ -182,6 +182,8 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_
   off = align_up(off + rows * 4);
   p.b_zy = off;
   off = align_up(off + rows * 4);
+  p.b_tcoef = off;
+  off = align_up(off + rows * 4);
   p.b_flag = off;
   off = align_up(off + 4);
   p.b_total = off;
@@ -230,7 +232,7 @@ int32_t check_keep(int64_t V, int32_t dtype) {
 // Workspace of fkl_backward_keep: per-row teacher coefficients, z at the ids
 // and the fp32 grad_hidden accumulator, for all N rows.
 struct KeepPlan {
-  size_t pcoef, acoef, lse2, zk, ghacc, bcoef, lse12, ycoef, zy, flag, total;
+  size_t pcoef, acoef, lse2, zk, ghacc, bcoef, lse12, ycoef, zy, tcoef, flag, total;
 };
 KeepPlan make_keep_plan(int64_t N, int64_t d, int32_t K) {
   KeepPlan q{};
@@ -254,6 +256,8 @@ KeepPlan make_keep_plan(int64_t N, int64_t d, int32_t K) {
   off = align_up(off + n * 4);
   q.zy = off;
   off = align_up(off + n * 4);
+  q.tcoef = off;
+  off = align_up(off + n * 4);
   q.flag = off;
   off = align_up(off + 4);
   q.total = off;
@@ -265,8 +269,9 @@ KeepPlan make_keep_plan(int64_t N, int64_t d, int32_t K) {
 int32_t check_options(const fkl_loss_options* o, float T, bool backward) {
   if (!o) return FKL_OK;
   if (!std::isfinite(o->alpha)) return fail(FKL_E_ARG, "alpha must be finite");
-  if (!aligned(o->row_weight, 4) || !aligned(o->labels, 4) || !aligned(o->lse1, 4))
-    return fail(FKL_E_ARG, "row_weight, labels and lse1 must be 4-byte aligned");
+  if (!aligned(o->row_weight, 4) || !aligned(o->labels, 4) || !aligned(o->lse1, 4) ||
+      !aligned(o->teacher_lse, 4))
+    return fail(FKL_E_ARG, "row_weight, labels, lse1 and teacher_lse must be 4-byte aligned");
   if (backward && o->labels && T != 1.0f && !o->lse1)
     return fail(FKL_E_ARG, "lse1 (from the forward) is required with labels when T != 1");
   return FKL_OK;
@@ -332,6 +337,7 @@ int32_t forward_impl(const void* hidden, const void* weight, const int32_t* topk
   mo.a_kl = labels ? o->alpha : 1.0f;
   mo.a_ce = labels ? 1.0f - o->alpha : 0.0f;
   mo.lse1 = o ? o->lse1 : nullptr;
+  mo.teacher_lse = o ? o->teacher_lse : nullptr;
 
   fkl::launch_gather_dot(dtype, weight, hidden, topk_idx, d, 0, N, K, zk, s);
   if (labels) {
@@ -477,6 +483,8 @@ static int32_t backward_impl(const void* hidden, const void* weight, const int32
   float* lse12 = reinterpret_cast<float*>(ws + p.b_lse12);
   float* ycoef = reinterpret_cast<float*>(ws + p.b_ycoef);
   float* zy = reinterpret_cast<float*>(ws + p.b_zy);
+  const float* tlse = o ? o->teacher_lse : nullptr;
+  float* tcoef = reinterpret_cast<float*>(ws + p.b_tcoef);
   float* ghacc = reinterpret_cast<float*>(ws + p.b_ghacc);
   float* pcoef = reinterpret_cast<float*>(ws + p.b_pcoef);
   float* acoef = reinterpret_cast<float*>(ws + p.b_acoef);
@@ -500,12 +508,12 @@ static int32_t backward_impl(const void* hidden, const void* weight, const int32
       fkl::launch_gather_dot(dtype, weight, static_cast<const unsigned char*>(hidden) + row0 * d * eb,
                              labels + row0, d, 0, nrows, 1, zy, s);
     fkl::launch_bwd_prep(topk_logit, lse, grad_loss, row0, nrows, K, T, row_weight, labels, a_kl,
-                         a_ce, o ? o->lse1 : nullptr, two_sm, pcoef, acoef, lse2,
+                         a_ce, o ? o->lse1 : nullptr, two_sm, tlse, zk, pcoef, acoef, lse2,
                          two_sm ? bcoef : nullptr, two_sm ? lse12 : nullptr,
-                         labels ? ycoef : nullptr, s);
+                         labels ? ycoef : nullptr, tlse ? tcoef : nullptr, s);
     fkl::RowCoef rc{pcoef, acoef, lse2, two_sm ? bcoef : nullptr, two_sm ? lse12 : nullptr,
                     labels ? ycoef : nullptr, labels ? labels + row0 : nullptr,
-                    labels ? zy : nullptr};
+                    labels ? zy : nullptr, tlse ? tcoef : nullptr};
     for (int64_t v0 = 0; v0 < p.Vpad; v0 += p.bw_width) {
       const int64_t Vw = (p.Vpad - v0) < p.bw_width ? (p.Vpad - v0) : p.bw_width;
       const int64_t Vlim = (V - v0) < Vw ? (V - v0) : Vw;
@@ -625,13 +633,16 @@ static int32_t backward_keep_impl(const void* hidden, const void* weight,
   float* lse12 = reinterpret_cast<float*>(ws + q.lse12);
   float* ycoef = reinterpret_cast<float*>(ws + q.ycoef);
   float* zy = reinterpret_cast<float*>(ws + q.zy);
+  const float* tlse = o ? o->teacher_lse : nullptr;
+  float* tcoef = reinterpret_cast<float*>(ws + q.tcoef);
   if (labels) fkl::launch_gather_dot(dtype, weight, hidden, labels, d, 0, N, 1, zy, s);
   fkl::launch_bwd_prep(topk_logit, lse, grad_loss, 0, N, K, T, o ? o->row_weight : nullptr, labels,
-                       a_kl, a_ce, o ? o->lse1 : nullptr, two_sm, pcoef, acoef, lse2,
+                       a_kl, a_ce, o ? o->lse1 : nullptr, two_sm, tlse, zk, pcoef, acoef, lse2,
                        two_sm ? bcoef : nullptr, two_sm ? lse12 : nullptr,
-                       labels ? ycoef : nullptr, s);
+                       labels ? ycoef : nullptr, tlse ? tcoef : nullptr, s);
   const fkl::RowCoef rc{pcoef, acoef, lse2, two_sm ? bcoef : nullptr, two_sm ? lse12 : nullptr,
-                        labels ? ycoef : nullptr, labels, labels ? zy : nullptr};
+                        labels ? ycoef : nullptr, labels, labels ? zy : nullptr,
+                        tlse ? tcoef : nullptr};
   fkl::launch_g_from_z(dtype, logits, zpitch, V, topk_idx, zk, rc, N, K, c2, s);
   // grad_hidden over all rows in one launch (tiles of 256 rows reach 256 * zld bytes)
   fkl::launch_grad_hidden(dtype, logits, zpitch, weight, d, 0, zpitch, V, N, false, ghacc, s);
@@ -681,7 +692,7 @@ namespace {
 // maxima [chunk][sm_ld], thresholds, candidate lists and their counts.
 struct TopkPlan {
   int64_t chunk_cap, lt_ld, nslots, sm_ld;
-  size_t lt, smax, theta, count, cand, total;
+  size_t lt, smax, theta, count, cand, part, total;
 };
 
 TopkPlan make_topk_plan(int64_t N, int64_t V, int64_t chunk) {
@@ -703,6 +714,8 @@ TopkPlan make_topk_plan(int64_t N, int64_t V, int64_t chunk) {
   off = align_up(off + rows * 4);
   q.cand = off;
   off = align_up(off + rows * fkl::topk_capacity() * 8);
+  q.part = off;  // teacher LSE partials [slot][lt_ld] (optional output)
+  off = align_up(off + static_cast<size_t>(fkl::lse_slots(V)) * q.lt_ld * 8);
   q.total = off;
   return q;
 }
@@ -726,13 +739,16 @@ int32_t fkl_topk_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K, int6
   return FKL_OK;
 }
 
-int32_t fkl_teacher_topk(const void* hidden, const void* weight, int64_t N, int64_t d, int64_t V,
-                         int32_t K, int64_t chunk, int32_t dtype, uint32_t flags,
-                         int32_t* topk_idx, float* topk_logit, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  g_last_error[0] = 0;
+static int32_t teacher_topk_impl(const void* hidden, const void* weight, int64_t N, int64_t d,
+                                 int64_t V, int32_t K, int64_t chunk, int32_t dtype,
+                                 uint32_t flags, float T, int32_t* topk_idx, float* topk_logit,
+                                 float* teacher_lse, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   int32_t r = check_topk(N, d, V, K, chunk, dtype);
   if (r) return r;
+  if (teacher_lse && (!std::isfinite(T) || !(T > 0.0f)))
+    return fail(FKL_E_ARG, "T must be finite and > 0");
+  if (!aligned(teacher_lse, 4)) return fail(FKL_E_ARG, "teacher_lse must be 4-byte aligned");
   if (flags != 0) return fail(FKL_E_ARG, "unknown flag bits");
   if (!weight || !workspace) return fail(FKL_E_ARG, "null pointer argument");
   if (N > 0 && (!hidden || !topk_idx || !topk_logit))
@@ -754,14 +770,36 @@ int32_t fkl_teacher_topk(const void* hidden, const void* weight, int64_t N, int6
   uint32_t* theta = reinterpret_cast<uint32_t*>(ws + q.theta);
   uint32_t* count = reinterpret_cast<uint32_t*>(ws + q.count);
   uint64_t* cand = reinterpret_cast<uint64_t*>(ws + q.cand);
+  float2* part = teacher_lse ? reinterpret_cast<float2*>(ws + q.part) : nullptr;
+  const float c2 = teacher_lse ? 1.4426950408889634f / T : 0.0f;
   for (int64_t row0 = 0; row0 < N; row0 += q.chunk_cap) {
     const int64_t nrows = (N - row0) < q.chunk_cap ? (N - row0) : q.chunk_cap;
     fkl::launch_teacher_logits(dtype, weight, hidden, d, V, row0, nrows, LT, q.lt_ld, smax, q.sm_ld,
-                               s);
+                               c2, part, s);
     fkl::launch_topk_select(LT, q.lt_ld, V, smax, q.sm_ld, q.nslots, nrows, K, theta, cand, count,
                             topk_idx + row0 * K, topk_logit + row0 * K, s);
+    if (teacher_lse)
+      fkl::launch_merge_lse_rows(part, q.lt_ld, q.nslots, nrows, teacher_lse + row0, s);
   }
   return hip_check("teacher top-K launch");
+}
+
+int32_t fkl_teacher_topk(const void* hidden, const void* weight, int64_t N, int64_t d, int64_t V,
+                         int32_t K, int64_t chunk, int32_t dtype, uint32_t flags,
+                         int32_t* topk_idx, float* topk_logit, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  return teacher_topk_impl(hidden, weight, N, d, V, K, chunk, dtype, flags, 1.0f, topk_idx,
+                           topk_logit, nullptr, workspace, workspace_bytes, stream);
+}
+
+int32_t fkl_teacher_topk_ex(const void* hidden, const void* weight, int64_t N, int64_t d,
+                            int64_t V, int32_t K, int64_t chunk, int32_t dtype, uint32_t flags,
+                            float T, int32_t* topk_idx, float* topk_logit, float* teacher_lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  return teacher_topk_impl(hidden, weight, N, d, V, K, chunk, dtype, flags, T, topk_idx,
+                           topk_logit, teacher_lse, workspace, workspace_bytes, stream);
 }
 
 int32_t fkl_timing_enable(int32_t on) { return fkl::timing_set(on != 0) ? 1 : 0; }

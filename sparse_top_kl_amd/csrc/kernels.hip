@@ -393,19 +393,35 @@ __global__ __launch_bounds__(256) void k_merge_loss(const float2* __restrict__ p
     const float invT = 1.0f / T;
     const float* lg = logit + row * K;
     const float* z = zk + row * K;
-    float ma = -INFINITY;
-    for (int k = lane; k < K; k += 64) ma = fmaxf(ma, lg[k] * invT);
-    ma = wave_max(ma);
-    float zsum = 0.f;
-    for (int k = lane; k < K; k += 64) zsum += expf(lg[k] * invT - ma);
-    zsum = wave_sum(zsum);
-    const float logZ = logf(zsum);
+    // log p_k = lg/T - logZ: renormalised over the K entries, or (tail bucket)
+    // the cached ids' share of the teacher's full distribution
+    float logZ;
+    if (o.teacher_lse) {
+      logZ = o.teacher_lse[ar];
+    } else {
+      float ma = -INFINITY;
+      for (int k = lane; k < K; k += 64) ma = fmaxf(ma, lg[k] * invT);
+      ma = wave_max(ma);
+      float zsum = 0.f;
+      for (int k = lane; k < K; k += 64) zsum += expf(lg[k] * invT - ma);
+      logZ = ma + logf(wave_sum(zsum));
+    }
+    float psum = 0.f, S = 0.f;
     for (int k = lane; k < K; k += 64) {
-      const float a = lg[k] * invT - ma;
-      const float p = expf(a) / zsum;
-      if (p > 0.f) term += p * ((a - logZ) - (z[k] * invT - lse));
+      const float lp = lg[k] * invT - logZ;
+      const float p = expf(lp);
+      const float lq = z[k] * invT - lse;
+      if (p > 0.f) term += p * (lp - lq);
+      psum += p;
+      S += expf(lq);
     }
     term = wave_sum(term);
+    if (o.teacher_lse) {  // the tail bucket: p_tail (log p_tail - log(1 - S))
+      psum = wave_sum(psum);
+      S = wave_sum(S);
+      const float pt = fmaxf(0.f, 1.f - psum);
+      if (pt > 0.f) term += pt * (logf(pt) - log1pf(-fminf(S, 1.f - 1e-7f)));
+    }
   }
   if (lane == 0) {
     lse_out[row] = lse;
@@ -444,9 +460,11 @@ __global__ __launch_bounds__(256) void k_bwd_prep(
     const float* __restrict__ logit, const float* __restrict__ lse,
     const float* __restrict__ grad_loss, int64_t row0, int64_t nrows, int K, float T,
     const float* __restrict__ row_weight, const int32_t* __restrict__ labels, float a_kl,
-    float a_ce, const float* __restrict__ lse1, bool two_sm, float* __restrict__ pcoef,
-    float* __restrict__ acoef, float* __restrict__ lse2, float* __restrict__ bcoef,
-    float* __restrict__ lse1_2, float* __restrict__ ycoef) {
+    float a_ce, const float* __restrict__ lse1, bool two_sm,
+    const float* __restrict__ teacher_lse, const float* __restrict__ zk,
+    float* __restrict__ pcoef, float* __restrict__ acoef, float* __restrict__ lse2,
+    float* __restrict__ bcoef, float* __restrict__ lse1_2, float* __restrict__ ycoef,
+    float* __restrict__ tcoef) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= nrows) return;
@@ -456,27 +474,45 @@ __global__ __launch_bounds__(256) void k_bwd_prep(
   const bool has_y = labels && labels[ar] >= 0;
   const float yc = has_y ? s * w * a_ce : 0.f;
   const float scale = s * w * a_kl * T;
-  float psum = 0.f;
+  float psum = 0.f, tail = 0.f, tc = 0.f;
   if (w != 0.f) {  // uniform per wave
     const float invT = 1.0f / T;
     const float* lg = logit + row * K;
-    float ma = -INFINITY;
-    for (int k = lane; k < K; k += 64) ma = fmaxf(ma, lg[k] * invT);
-    ma = wave_max(ma);
-    float zsum = 0.f;
-    for (int k = lane; k < K; k += 64) zsum += expf(lg[k] * invT - ma);
-    zsum = wave_sum(zsum);
+    float logZ;  // as in k_merge_loss
+    if (teacher_lse) {
+      logZ = teacher_lse[ar];
+    } else {
+      float ma = -INFINITY;
+      for (int k = lane; k < K; k += 64) ma = fmaxf(ma, lg[k] * invT);
+      ma = wave_max(ma);
+      float zsum = 0.f;
+      for (int k = lane; k < K; k += 64) zsum += expf(lg[k] * invT - ma);
+      logZ = ma + logf(wave_sum(zsum));
+    }
+    float S = 0.f;
     for (int k = lane; k < K; k += 64) {
-      const float p = expf(lg[k] * invT - ma) / zsum;
+      const float p = expf(lg[k] * invT - logZ);
       psum += p;
       pcoef[row * K + k] = scale * p;
+      if (teacher_lse) S += expf(zk[row * K + k] * invT - lse[row]);
     }
     psum = wave_sum(psum);
+    if (teacher_lse) {
+      // tail bucket: d/dz of p_tail (log p_tail - log(1 - S)) is
+      // T p_tail (Q - q S) / (1 - S): the dense coefficient loses
+      // p_tail S / (1 - S), each cached id gains p_tail / (1 - S)
+      S = wave_sum(S);
+      const float pt = fmaxf(0.f, 1.f - psum);
+      const float inv = 1.f / fmaxf(1.f - S, 1e-7f);
+      tail = pt * S * inv;
+      tc = scale * pt * inv;
+    }
   } else {
     for (int k = lane; k < K; k += 64) pcoef[row * K + k] = 0.f;
   }
   if (lane == 0) {
-    acoef[row] = scale * psum + (two_sm ? 0.f : yc);
+    acoef[row] = scale * (psum - tail) + (two_sm ? 0.f : yc);
+    if (tcoef) tcoef[row] = tc;
     lse2[row] = lse[row] * kLog2e;
     if (bcoef) bcoef[row] = two_sm ? yc : 0.f;
     if (lse1_2) lse1_2[row] = two_sm ? lse1[ar] * kLog2e : 0.f;
@@ -531,7 +567,8 @@ __device__ __forceinline__ void store_one(unsigned char* grow, int64_t col, floa
 
 // The exact entries of one row of G inside columns [v0, v0 + Vw): at each
 // teacher id v, dense(z_v) - (sum of pcoef over the ids equal to v) - (ycoef
-// if v is the label); at a label that is no teacher id, dense(z_y) - ycoef.
+// if v is the label) + (tail bucket) tcoef * q_v per cached copy of v; at a
+// label that is no teacher id, dense(z_y) - ycoef.
 // z at an id or the label is the fp32 gathered logit, so every entry is
 // rounded once. sid / sp hold the row's ids and pcoef (LDS); threads
 // t = 0 .. nthreads - 1 of the workgroup share the work.
@@ -540,13 +577,20 @@ __device__ __forceinline__ void write_exact_entries(unsigned char* grow, int64_t
                                                     const int32_t* sid, const float* sp, int K,
                                                     const float* zk_row, const DenseCoef& dc,
                                                     float c2, int32_t y, float yc, float zy,
-                                                    int t, int nthreads) {
+                                                    float tc, int t, int nthreads) {
   for (int k = t; k < K; k += nthreads) {
     const int32_t v = sid[k];
     if (v < v0 || v >= v0 + Vw) continue;
-    float sum = 0.f;
-    for (int k2 = 0; k2 < K; ++k2) sum += (sid[k2] == v) ? sp[k2] : 0.f;
-    store_one<P>(grow, v - v0, dense_g(dc, zk_row[k], c2) - sum - (v == y ? yc : 0.f));
+    float sum = 0.f, mult = 0.f;
+    for (int k2 = 0; k2 < K; ++k2) {
+      const bool eq = sid[k2] == v;
+      sum += eq ? sp[k2] : 0.f;
+      mult += eq ? 1.f : 0.f;
+    }
+    const float z = zk_row[k];
+    float g = dense_g(dc, z, c2) - sum - (v == y ? yc : 0.f);
+    if (tc != 0.f) g += tc * mult * fast_exp2(z * c2 - dc.l2);
+    store_one<P>(grow, v - v0, g);
   }
   if (t == 0 && y >= 0 && y >= v0 && y < v0 + Vw) {
     bool found = false;
@@ -576,7 +620,7 @@ __global__ __launch_bounds__(64) void k_fixup(unsigned char* __restrict__ G, int
   const int32_t y = rc.labels ? rc.labels[row] : -1;
   write_exact_entries<P>(G + row * gpitch * P::kBytes, v0, Vw, sid, sp, K, zk + row * K,
                          row_dense(rc, row), c2, y, rc.ycoef ? rc.ycoef[row] : 0.f,
-                         y >= 0 ? rc.zy[row] : 0.f, lane, 64);
+                         y >= 0 ? rc.zy[row] : 0.f, rc.tcoef ? rc.tcoef[row] : 0.f, lane, 64);
 }
 
 // Kept-logits backward, one workgroup per row: turns the row's kept logits
@@ -640,8 +684,8 @@ __global__ __launch_bounds__(kGzThreads) void k_g_from_z(unsigned char* __restri
   __syncthreads();  // the dense stores of the row are done before the exact entries are written
   const int32_t y = rc.labels ? rc.labels[row] : -1;
   write_exact_entries<P>(zr, 0, zcols, sid, sp, K, zk + row * K, dc, c2, y,
-                         rc.ycoef ? rc.ycoef[row] : 0.f, y >= 0 ? rc.zy[row] : 0.f, t,
-                         kGzThreads);
+                         rc.ycoef ? rc.ycoef[row] : 0.f, y >= 0 ? rc.zy[row] : 0.f,
+                         rc.tcoef ? rc.tcoef[row] : 0.f, t, kGzThreads);
 }
 
 // acc[row][col] (+)= sum over the slice of G[row][v - v0] W[v][col], for the rows
@@ -758,11 +802,14 @@ __device__ __forceinline__ uint64_t topk_key(uint32_t ord, int64_t id) {
   return (static_cast<uint64_t>(ord) << 32) | (0xffffffffu - static_cast<uint32_t>(id));
 }
 
-template <class P, class C>
+// With LSE the tile also leaves its per-(128-vocab slice, token) log-sum-exp
+// partials at temperature 1/(c2 ln 2) in part (the teacher's lse for the tail
+// bucket of the loss).
+template <class P, class C, bool LSE>
 __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_teacher_logits(
     const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
     int64_t nrows, int64_t n_vt, int64_t n_tt, float* __restrict__ LT, int64_t lt_ld,
-    uint32_t* __restrict__ smax, int64_t sm_ld) {
+    uint32_t* __restrict__ smax, int64_t sm_ld, float c2, float2* __restrict__ part) {
   static_assert(C::kWM == kSliceVocab, "one slice maximum per wave row-slice");
   int64_t vt, tt;
   if (!TileGroups<4, 8>::coords(n_vt, n_tt, &vt, &tt)) return;
@@ -778,6 +825,8 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_teacher_log
   const int lane = threadIdx.x & 63;
   const int64_t v0 = vt * kBM + C::wave_m() * C::kWM;
   if (v0 >= V) return;
+  if constexpr (LSE)
+    lse_partials<C>(acc, v0, V, tt * kBN + C::wave_n() * C::kWN, nrows, c2, part, lt_ld);
   const int64_t slot = v0 / kSliceVocab;
   const bool full = v0 + C::kWM <= V;
   const int vlim = full ? C::kWM : static_cast<int>(V - v0);
@@ -919,6 +968,16 @@ __global__ __launch_bounds__(256) void k_topk_collect(const float* __restrict__ 
       }
     }
   }
+}
+
+// One wave per row: the natural-log log-sum-exp from its slice partials.
+__global__ __launch_bounds__(256) void k_merge_lse_rows(const float2* __restrict__ part,
+                                                        int64_t part_ld, int64_t nslots,
+                                                        int64_t nrows, float* __restrict__ out) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  const float lse = merge_lse(part, part_ld, nslots, row);
+  if ((threadIdx.x & 63) == 0) out[row] = lse;
 }
 
 constexpr int kTopkCap = 2048;  // candidate keys per token (LDS of the final kernel)
@@ -1123,13 +1182,14 @@ void launch_reduce_loss(const float* row_loss, int64_t N, float* loss, hipStream
 void launch_bwd_prep(const float* logit, const float* lse, const float* grad_loss, int64_t row0,
                      int64_t nrows, int K, float T, const float* row_weight,
                      const int32_t* labels, float a_kl, float a_ce, const float* lse1,
-                     bool two_sm, float* pcoef, float* acoef, float* lse2, float* bcoef,
-                     float* lse1_2, float* ycoef, hipStream_t s) {
+                     bool two_sm, const float* teacher_lse, const float* zk, float* pcoef,
+                     float* acoef, float* lse2, float* bcoef, float* lse1_2, float* ycoef,
+                     float* tcoef, hipStream_t s) {
   ScopedTimer timer_(KID_BWD_PREP, s);
   const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, 4));
   k_bwd_prep<<<blocks, 256, 0, s>>>(logit + row0 * K, lse + row0, grad_loss, row0, nrows, K, T,
-                                    row_weight, labels, a_kl, a_ce, lse1, two_sm, pcoef, acoef,
-                                    lse2, bcoef, lse1_2, ycoef);
+                                    row_weight, labels, a_kl, a_ce, lse1, two_sm, teacher_lse, zk,
+                                    pcoef, acoef, lse2, bcoef, lse1_2, ycoef, tcoef);
 }
 
 void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t v0,
@@ -1229,14 +1289,28 @@ void launch_grad_w(int dtype, const void* G, int64_t gpitch, const void* H, int6
 
 void launch_teacher_logits(int dtype, const void* W, const void* H, int64_t d, int64_t V,
                            int64_t row0, int64_t nrows, float* LT, int64_t lt_ld,
-                           uint32_t* smax, int64_t sm_ld, hipStream_t s) {
+                           uint32_t* smax, int64_t sm_ld, float c2, float2* part,
+                           hipStream_t s) {
   ScopedTimer timer_(KID_TEACHER_LOGITS, s);
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(V, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
+  const unsigned char* Wc = static_cast<const unsigned char*>(W);
   const unsigned grid = grouped_grid<4, 8>(n_vt, n_tt);
-  FKL_LAUNCH_GEMM(k_teacher_logits, dtype, grid, s, static_cast<const unsigned char*>(W), Hc, d,
-                  V, nrows, n_vt, n_tt, LT, lt_ld, smax, sm_ld);
+#define FKL_TEACHER(LSE)                                                                          \
+  do {                                                                                            \
+    if (dtype == 1)                                                                               \
+      k_teacher_logits<BF16, Cfg8, LSE><<<grid, Cfg8::kThreads, 0, s>>>(                          \
+          Wc, Hc, d, V, nrows, n_vt, n_tt, LT, lt_ld, smax, sm_ld, c2, part);                     \
+    else                                                                                          \
+      k_teacher_logits<F32, Cfg4, LSE><<<grid, Cfg4::kThreads, 0, s>>>(                           \
+          Wc, Hc, d, V, nrows, n_vt, n_tt, LT, lt_ld, smax, sm_ld, c2, part);                     \
+  } while (0)
+  if (part)
+    FKL_TEACHER(true);
+  else
+    FKL_TEACHER(false);
+#undef FKL_TEACHER
 }
 
 void launch_topk_select(const float* LT, int64_t lt_ld, int64_t V, const uint32_t* smax,
@@ -1268,6 +1342,14 @@ void launch_topk_select(const float* LT, int64_t lt_ld, int64_t V, const uint32_
 }
 
 int topk_capacity() { return kTopkCap; }
+
+void launch_merge_lse_rows(const float2* part, int64_t part_ld, int64_t nslots, int64_t nrows,
+                           float* out, hipStream_t s) {
+  if (nrows <= 0) return;
+  ScopedTimer timer_(KID_MERGE_LOSS, s);
+  k_merge_lse_rows<<<static_cast<unsigned>(ceil_div(nrows, 4)), 256, 0, s>>>(part, part_ld, nslots,
+                                                                            nrows, out);
+}
 
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
   if (n <= 0) return;

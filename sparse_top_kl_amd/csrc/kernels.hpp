@@ -17,11 +17,13 @@ struct MergeOpts {
   const float* row_weight;   // [rows] or null (weight 1)
   float a_kl, a_ce;          // weights of the KL and cross-entropy terms
   float* lse1;               // [rows] out: ln sum exp(z) at temperature 1, or null
+  const float* teacher_lse;  // [rows] teacher's full-vocabulary lse at T (tail bucket), or null
 };
 
 // Per-row coefficients of the logit gradient (backward), rows of one block:
 //   dense G = acoef * 2^(z*c2 - lse2) [+ bcoef * 2^(z*log2(e) - lse1_2)]
-//   at the teacher ids minus pcoef_k, at the label minus ycoef.
+//   at the teacher ids minus pcoef_k plus (tail bucket) tcoef * 2^(z*c2 - lse2)
+//   per cached copy of the id, at the label minus ycoef.
 struct RowCoef {
   const float* pcoef;      // [rows][K]
   const float* acoef;      // [rows]
@@ -31,6 +33,7 @@ struct RowCoef {
   const float* ycoef;      // [rows] or null (no labels)
   const int32_t* labels;   // [rows] or null
   const float* zy;         // [rows] z at the label, or null
+  const float* tcoef;      // [rows] or null (no tail bucket)
 };
 
 // Rows of a (vocab-slice, token) partial: running max and sum of 2^(z*c2).
@@ -65,11 +68,14 @@ void launch_reduce_loss(const float* row_loss, int64_t N, float* loss, hipStream
 // row0): row_weight, labels and lse1 are indexed by absolute row; bcoef,
 // lse1_2 and ycoef may be null (not needed); two_sm selects the separate
 // temperature-1 softmax of the cross-entropy term.
+// With teacher_lse (absolute rows) the tail bucket's coefficients need zk
+// (block rows) and go to tcoef.
 void launch_bwd_prep(const float* logit, const float* lse, const float* grad_loss, int64_t row0,
                      int64_t nrows, int K, float T, const float* row_weight,
                      const int32_t* labels, float a_kl, float a_ce, const float* lse1,
-                     bool two_sm, float* pcoef, float* acoef, float* lse2, float* bcoef,
-                     float* lse1_2, float* ycoef, hipStream_t s);
+                     bool two_sm, const float* teacher_lse, const float* zk, float* pcoef,
+                     float* acoef, float* lse2, float* bcoef, float* lse1_2, float* ycoef,
+                     float* tcoef, hipStream_t s);
 // Recompute the logit block rows [row0, row0 + nrows) x vocabulary [v0, v0 + Vw) into
 // the dense part of G (pitch gpitch elements).
 void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t v0,
@@ -98,9 +104,14 @@ void launch_grad_w(int dtype, const void* G, int64_t gpitch, const void* H, int6
 // Teacher top-K cache, per chunk of rows [row0, row0 + nrows): the chunk's
 // fp32 logits LT[v][r] (pitch lt_ld floats) and per (row, 128-vocab slice)
 // maxima smax[r][slot] (pitch sm_ld) ...
+// With part non-null also the LSE partials at c2 = log2(e)/T ([slot][lt_ld]).
 void launch_teacher_logits(int dtype, const void* W, const void* H, int64_t d, int64_t V,
                            int64_t row0, int64_t nrows, float* LT, int64_t lt_ld,
-                           uint32_t* smax, int64_t sm_ld, hipStream_t s);
+                           uint32_t* smax, int64_t sm_ld, float c2, float2* part,
+                           hipStream_t s);
+// out[r] = natural-log log-sum-exp of row r's slice partials.
+void launch_merge_lse_rows(const float2* part, int64_t part_ld, int64_t nslots, int64_t nrows,
+                           float* out, hipStream_t s);
 // ... then per row the K largest (ids, values) sorted, ties to the lower id;
 // theta [nrows], cand [nrows][topk_capacity()] and count [nrows] are scratch.
 void launch_topk_select(const float* LT, int64_t lt_ld, int64_t V, const uint32_t* smax,

@@ -62,7 +62,8 @@ _sz = ctypes.c_size_t
 class LossOptions(ctypes.Structure):
     """Mirror of fkl_loss_options (include/fkl.h)."""
     _fields_ = [("row_weight", ctypes.c_void_p), ("labels", ctypes.c_void_p),
-                ("alpha", ctypes.c_float), ("lse1", ctypes.c_void_p)]
+                ("alpha", ctypes.c_float), ("lse1", ctypes.c_void_p),
+                ("teacher_lse", ctypes.c_void_p)]
 
 
 _opt = ctypes.POINTER(LossOptions)
@@ -95,6 +96,8 @@ _SIGNATURES = {
                                    _u32, _opt, _p, _p, _p, _p, _p, _sz, _p, _sz, _p]),
     "fkl_backward_keep_ex": (_i32, [_p, _p, _p, _p, _p, _p, _p, _f32, _i64, _i64, _i64, _i32,
                                     _i32, _u32, _opt, _p, _sz, _p, _p, _p, _sz, _p]),
+    "fkl_teacher_topk_ex": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _i64, _i32, _u32, _f32, _p,
+                                   _p, _p, _p, _sz, _p]),
     "fkl_timing_enable": (_i32, [_i32]),
     "fkl_timing_reset": (_i32, []),
     "fkl_timing_read": (_i32, [_i32, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]),
@@ -181,7 +184,7 @@ class ForwardResult:
     lse1: torch.Tensor | None = None   # [N] fp32, temperature-1 lse (with labels)
 
 
-def _loss_options(N, row_weight, labels, alpha, lse1):
+def _loss_options(N, row_weight, labels, alpha, lse1, teacher_lse=None):
     """(LossOptions, keep-alive tensors) for the *_ex entry points."""
     keep = []
     if row_weight is not None:
@@ -199,7 +202,13 @@ def _loss_options(N, row_weight, labels, alpha, lse1):
     if lse1 is not None:
         _require(lse1, "lse1", torch.float32)
         keep.append(lse1)
-    o = LossOptions(_ptr(row_weight), _ptr(labels), float(alpha), _ptr(lse1))
+    if teacher_lse is not None:
+        teacher_lse = teacher_lse.reshape(-1).to(torch.float32).contiguous()
+        _require(teacher_lse, "teacher_lse", torch.float32)
+        if teacher_lse.numel() != N:
+            raise FklError(FKL_E_ARG, "teacher_lse must have N entries")
+        keep.append(teacher_lse)
+    o = LossOptions(_ptr(row_weight), _ptr(labels), float(alpha), _ptr(lse1), _ptr(teacher_lse))
     return o, keep
 
 
@@ -371,8 +380,8 @@ def fkl_teacher_topk(hidden: torch.Tensor, weight: torch.Tensor, K: int, chunk: 
 
 
 def fkl_forward_ex(hidden, weight, topk_idx, topk_logit, T: float, chunk: int, *,
-                   row_weight=None, labels=None, alpha: float = 1.0, keep_logits=None,
-                   validate: bool = False, workspace=None):
+                   row_weight=None, labels=None, alpha: float = 1.0, teacher_lse=None,
+                   keep_logits=None, validate: bool = False, workspace=None):
     """fkl_forward (or with keep_logits, a [N, keep_pitch(V)] buffer or True,
     fkl_forward_keep) with loss options: per-row weights, hard labels (< 0:
     none) and the KL/cross-entropy mixing weight alpha. Returns a
@@ -388,7 +397,7 @@ def fkl_forward_ex(hidden, weight, topk_idx, topk_logit, T: float, chunk: int, *
     fw, _ = fkl_workspace_size(N, d, V, K, chunk, code)
     ws = workspace if workspace is not None else _workspace(fw, dev)
     lse1 = torch.empty(N, dtype=torch.float32, device=dev) if labels is not None else None
-    o, alive = _loss_options(N, row_weight, labels, alpha, lse1)
+    o, alive = _loss_options(N, row_weight, labels, alpha, lse1, teacher_lse)
     out = ForwardResult(torch.empty((), dtype=torch.float32, device=dev),
                         torch.empty(N, dtype=torch.float32, device=dev),
                         torch.empty(N, dtype=torch.float32, device=dev),
@@ -411,8 +420,9 @@ def fkl_forward_ex(hidden, weight, topk_idx, topk_logit, T: float, chunk: int, *
 
 def fkl_backward_ex(hidden, weight, topk_idx, topk_logit, lse, T: float, chunk: int, *,
                     topk_z=None, grad_loss=None, row_weight=None, labels=None,
-                    alpha: float = 1.0, lse1=None, logits=None, grad_weight=None,
-                    accumulate: bool = False, validate: bool = False, workspace=None):
+                    alpha: float = 1.0, lse1=None, teacher_lse=None, logits=None,
+                    grad_weight=None, accumulate: bool = False, validate: bool = False,
+                    workspace=None):
     """fkl_backward (or, given the kept logits, fkl_backward_keep) with loss
     options; lse1 is the forward's (required with labels when T != 1)."""
     N, d = hidden.shape
@@ -429,7 +439,7 @@ def fkl_backward_ex(hidden, weight, topk_idx, topk_logit, lse, T: float, chunk: 
         _require(logits, "logits", hidden.dtype)
         _, bw = fkl_keep_sizes(N, d, V, K, code)
     ws = workspace if workspace is not None else _workspace(bw, dev)
-    o, alive = _loss_options(N, row_weight, labels, alpha, lse1)
+    o, alive = _loss_options(N, row_weight, labels, alpha, lse1, teacher_lse)
     grad_hidden = torch.empty_like(hidden)
     if grad_weight is None:
         grad_weight = torch.empty(V, d, dtype=torch.float32, device=dev)
@@ -459,6 +469,27 @@ def fkl_forward_keep_ex(hidden, weight, topk_idx, topk_logit, T, chunk, *, logit
 def fkl_backward_keep_ex(hidden, weight, topk_idx, topk_logit, lse, T, logits, **opts):
     """fkl_backward_keep with loss options (the kept logits are consumed)."""
     return fkl_backward_ex(hidden, weight, topk_idx, topk_logit, lse, T, 1, logits=logits, **opts)
+
+
+def fkl_teacher_topk_ex(hidden: torch.Tensor, weight: torch.Tensor, K: int, chunk: int = 2048,
+                        *, T: float = 1.0, workspace: torch.Tensor | None = None):
+    """fkl_teacher_topk plus the teacher's full-vocabulary log-sum-exp at T:
+    returns (ids int32 [N, K], logits fp32 [N, K], teacher_lse fp32 [N])."""
+    N, d = hidden.shape
+    V = weight.shape[0]
+    code = dtype_code(hidden.dtype)
+    _require(hidden, "hidden")
+    _require(weight, "weight", hidden.dtype)
+    dev = hidden.device
+    nb = fkl_topk_workspace_size(N, d, V, K, chunk, code)
+    ws = workspace if workspace is not None else _workspace(nb, dev)
+    idx = torch.empty(N, K, dtype=torch.int32, device=dev)
+    val = torch.empty(N, K, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    _check(lib().fkl_teacher_topk_ex(_ptr(hidden), _ptr(weight), N, d, V, K, chunk, code, 0,
+                                     float(T), _ptr(idx), _ptr(val), _ptr(lse), _ptr(ws),
+                                     ws.numel(), _stream(dev)))
+    return idx, val, lse
 
 
 def fkl_timing_enable(on: bool) -> bool:

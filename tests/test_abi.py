@@ -153,8 +153,8 @@ def test_keep_sizes_are_rows_times_padded_vocab():
         z, b = fkl.fkl_keep_sizes(N, d, V, K, dt)
         assert z == N * fkl.keep_pitch(V) * eb
         assert fkl.keep_pitch(V) % 64 == 0 and 0 <= fkl.keep_pitch(V) - V < 64
-        # per-row coefficients (p, z at the ids, six scalars) and the fp32 grad_hidden rows
-        assert N * (8 * K + 24 + 4 * d) <= b <= N * (8 * K + 24 + 4 * d) + 10 * 256
+        # per-row coefficients (p, z at the ids, seven scalars) and the fp32 grad_hidden rows
+        assert N * (8 * K + 28 + 4 * d) <= b <= N * (8 * K + 28 + 4 * d) + 11 * 256
 
 
 def test_keep_sizes_reject_a_vocabulary_too_large_to_keep():
@@ -224,8 +224,10 @@ def test_topk_workspace_holds_one_chunk_of_fp32_logits():
     for N, d, V, K, chunk in ((32768, 4096, 128256, 100, 2048), (100, 64, 1000, 10, 4096)):
         b = fkl.fkl_topk_workspace_size(N, d, V, K, chunk, fkl.FKL_BF16)
         rows = min(N, chunk)
-        lt = V * ((rows + 63) // 64 * 64) * 4
-        assert lt <= b <= lt + rows * (4 * ((V + 127) // 128 + 4) + 8 + 2048 * 8) + 6 * 256
+        ld = (rows + 63) // 64 * 64
+        lt = V * ld * 4
+        part = ((V + 255) // 256) * 2 * ld * 8     # teacher lse partials (optional output)
+        assert lt <= b <= lt + part + rows * (4 * ((V + 127) // 128 + 4) + 8 + 2048 * 8) + 7 * 256
 
 
 def _topk(**over):

@@ -175,3 +175,21 @@ def test_topk_full_size(gpu_device, name):
     _check_valid_topk(g_idx, g_val, logits, tol)
     at = np.take_along_axis(logits, g_idx.astype(np.int64), axis=1)
     assert np.max(np.abs(at - ref_val) / np.maximum(np.abs(ref_val), 1.0)) <= 2 * tol
+
+
+@pytest.mark.parametrize("values,dtype,T", [("integer", "bf16", 2.0), ("normal", "fp32", 0.7)])
+def test_teacher_lse_output(gpu_device, values, dtype, T):
+    announce(f"teacher lse at T={T}: {values} {dtype}")
+    w = synth.small_teacher_workload("lse_" + values, n=333, d=136, V=3100, K=50, dtype=dtype,
+                                     chunk=128, values=values)
+    inp = synth.make_teacher_inputs(w)
+    h, W = _upload(inp)
+    idx, val, lse = fkl.fkl_teacher_topk_ex(h, W, w.K, w.chunk, T=T)
+    idx0, val0 = fkl.fkl_teacher_topk(h, W, w.K, w.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx0) and torch.equal(val, val0)   # the lse changes nothing else
+    u = oracle.teacher_logits(inp["hidden"], inp["weight"]) / T
+    m = u.max(axis=1)
+    ref = m + np.log(np.exp(u - m[:, None]).sum(axis=1))
+    got = lse.double().cpu().numpy()
+    assert np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1.0)) <= 1e-5
