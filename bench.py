@@ -289,6 +289,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--keep-logits", action="store_true",
                     help="time the forward-chunked variant (kept logits, no recompute)")
+    ap.add_argument("--options", action="store_true",
+                    help="time the loss with its options on: hard labels for every row mixed "
+                         "in with alpha 0.5 and a teacher-tail bucket (teacher lse = lse of the "
+                         "cached logits + ln 2)")
     ap.add_argument("--teacher-topk", action="store_true",
                     help="time the teacher top-K cache producer instead of the loss "
                          "(workload teacher_llama8b_32k unless --workload names a teacher one)")
@@ -336,7 +340,23 @@ def main():
     gw = torch.empty(w.V, w.d, dtype=torch.float32, device=dev)
     zbuf = torch.empty(w.N, fkl.keep_pitch(w.V), dtype=dt, device=dev) if keep else None
 
+    opts = {}
+    if args.options:
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed)
+        labels = torch.randint(0, w.V, (w.N,), device=dev, generator=g, dtype=torch.int32)
+        tlse = (torch.logsumexp(lg / w.T, dim=1) + math.log(2.0)).contiguous()
+        opts = dict(labels=labels, alpha=0.5, teacher_lse=tlse)
+
     def step():
+        if opts:
+            res = fkl.fkl_forward_ex(h, W, idx, lg, w.T, w.chunk, keep_logits=zbuf if keep else None,
+                                     workspace=ws_f, **opts)
+            out, z = res if keep else (res, None)
+            gh, _ = fkl.fkl_backward_ex(h, W, idx, lg, out.lse, w.T, w.chunk, topk_z=out.topk_z,
+                                        lse1=out.lse1, logits=z, grad_weight=gw, workspace=ws_b,
+                                        **opts)
+            return out, gh
         if keep:
             out, z = fkl.fkl_forward_keep(h, W, idx, lg, w.T, w.chunk, logits=zbuf, workspace=ws_f)
             gh, _ = fkl.fkl_backward_keep(h, W, idx, lg, out.lse, w.T, z, topk_z=out.topk_z,
@@ -410,7 +430,7 @@ def main():
                     "unit": "GB/s", "frac": None, "traffic": load_traffic(dom, traffic_key),
                     "avg_launch_ms": avg_ms}
 
-    if args.no_cpu_baseline:
+    if args.no_cpu_baseline or args.options:
         base, parity = None, None
     else:
         log("[bench] oracle on the host (cpu_baseline and sampled parity)")
@@ -432,7 +452,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "S": w.S, "N": w.N, "d": w.d, "V": w.V,
                    "K": w.K, "T": w.T, "chunk": w.chunk, "teacher_ids": w.ids,
-                   "variant": "forward-chunked, kept logits" if keep else "fused chunked"},
+                   "variant": "forward-chunked, kept logits" if keep else "fused chunked",
+                   "options": "labels (alpha 0.5) + teacher tail" if args.options else None},
         "mfma_frac_step": flops_step / (ms_step * 1e-3) / (peak_tf * 1e12),
         "flops_per_step": flops_step,
         "roofline": roofline,

@@ -1346,7 +1346,7 @@ int topk_capacity() { return kTopkCap; }
 void launch_merge_lse_rows(const float2* part, int64_t part_ld, int64_t nslots, int64_t nrows,
                            float* out, hipStream_t s) {
   if (nrows <= 0) return;
-  ScopedTimer timer_(KID_MERGE_LOSS, s);
+  ScopedTimer timer_(KID_MERGE_LSE, s);
   k_merge_lse_rows<<<static_cast<unsigned>(ceil_div(nrows, 4)), 256, 0, s>>>(part, part_ld, nslots,
                                                                             nrows, out);
 }

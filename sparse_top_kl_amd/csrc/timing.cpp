@@ -55,7 +55,7 @@ const char* kernel_name(int32_t kid) {
       "k_bwd_prep",   "k_gprod",      "k_fixup",      "k_grad_hidden",
       "k_reduce_gh",  "k_grad_w",     "k_fill_f32",   "k_validate_idx",
       "k_g_from_z",   "k_teacher_logits", "k_topk_threshold", "k_topk_collect",
-      "k_topk_final"};
+      "k_topk_final", "k_merge_lse_rows"};
   return (kid >= 0 && kid < KID_COUNT) ? names[kid] : nullptr;
 }
 

@@ -25,6 +25,7 @@ enum KernelId : int32_t {
   KID_TOPK_THRESHOLD,
   KID_TOPK_COLLECT,
   KID_TOPK_FINAL,
+  KID_MERGE_LSE,
   KID_COUNT
 };
 
