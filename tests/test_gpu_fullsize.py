@@ -67,17 +67,21 @@ def _torch_grad_w_rows(h32, w32, idx, lg, T, vocab, chunk=2048):
     return (G.t().contiguous() @ h32).double().cpu().numpy()          # [S, d]
 
 
-# (workload, keep): keep=True runs the forward-chunked variant (kept logits)
-CASES = [(n, False) for n in FULL_WORKLOADS] + [("long32k", True), ("stress_b4_32k", True)]
+# (workload, keep, options): keep=True runs the forward-chunked variant (kept
+# logits); options=True adds hard labels (alpha 0.5) and the teacher-tail bucket
+CASES = ([(n, False, False) for n in FULL_WORKLOADS] +
+         [("long32k", True, False), ("stress_b4_32k", True, False), ("long32k", False, True)])
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,keep", CASES,
-                         ids=[n + ("-keep" if k else "") for n, k in CASES])
-def test_full_size_parity(name, keep, gpu_device):
+@pytest.mark.parametrize("name,keep,options", CASES,
+                         ids=[n + ("-keep" if k else "") + ("-options" if o else "")
+                              for n, k, o in CASES])
+def test_full_size_parity(name, keep, options, gpu_device):
     w = synth.WORKLOADS[name]
     tol = TOL[w.dtype]
-    announce(f"full size {name}{' (kept logits)' if keep else ''}: N={w.N} d={w.d} V={w.V} "
+    announce(f"full size {name}{' (kept logits)' if keep else ''}"
+             f"{' (labels + tail)' if options else ''}: N={w.N} d={w.d} V={w.V} "
              f"K={w.K} T={w.T} chunk={w.chunk} {w.dtype} ids={w.ids} (generating inputs)")
     inp = synth.make_inputs(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -86,8 +90,23 @@ def test_full_size_parity(name, keep, gpu_device):
     idx = torch.from_numpy(inp["topk_idx"]).to(gpu_device)
     lg = torch.from_numpy(inp["topk_logit"]).to(gpu_device)
 
+    opts = {}
+    if options:
+        rng_o = np.random.default_rng(99)
+        y = rng_o.integers(0, w.V, size=w.N).astype(np.int32)
+        lg64 = inp["topk_logit"].astype(np.float64) / w.T
+        mx = lg64.max(axis=1)
+        tlse = (mx + np.log(np.exp(lg64 - mx[:, None]).sum(axis=1)) + np.log(2.0)).astype(
+            np.float32)
+        opts = dict(labels=y, alpha=0.5, teacher_lse=tlse)
     announce(f"full size {name}: HIP forward + backward")
-    if keep:
+    if options:
+        topts = dict(labels=torch.from_numpy(y).to(gpu_device), alpha=0.5,
+                     teacher_lse=torch.from_numpy(tlse).to(gpu_device))
+        out = fkl.fkl_forward_ex(h, W, idx, lg, w.T, w.chunk, **topts)
+        gh, gw = fkl.fkl_backward_ex(h, W, idx, lg, out.lse, w.T, w.chunk, topk_z=out.topk_z,
+                                     lse1=out.lse1, **topts)
+    elif keep:
         out, z = fkl.fkl_forward_keep(h, W, idx, lg, w.T, w.chunk)
         ref_out = fkl.fkl_forward(h, W, idx, lg, w.T, w.chunk)
         for field in ("loss", "lse", "row_loss", "topk_z"):
@@ -113,8 +132,11 @@ def test_full_size_parity(name, keep, gpu_device):
     rng = np.random.default_rng(20261203)
     rows = _sample_rows(w, rng)
     announce(f"full size {name}: oracle on rows {rows.tolist()}")
+    sub = {k: v[rows] for k, v in opts.items() if k != "alpha"}
+    if options:
+        sub["alpha"] = opts["alpha"]
     ref = oracle.forward_backward(inp["hidden"][rows], inp["weight"], inp["topk_idx"][rows],
-                                  inp["topk_logit"][rows], w.T)
+                                  inp["topk_logit"][rows], w.T, **sub)
     sel = torch.as_tensor(rows, device=gpu_device)
     errs = {
         "lse": elementwise_ok(out.lse[sel].double().cpu().numpy(), ref["lse"], tol["loss"]),
@@ -141,6 +163,14 @@ def test_full_size_parity(name, keep, gpu_device):
     scale = float((gw.double().abs() * W.double().abs()).sum().item())
     errs["<gW,W>-<gH,H>"] = abs(a - b) / max(scale, 1e-30)
 
+    limits = {"lse": tol["loss"], "row_loss": tol["loss"], "topk_z": tol["loss"],
+              "grad_hidden": tol["grad"], "grad_w_colsum/bound": 1.0,
+              "<gW,W>-<gH,H>": tol["grad"], "grad_w_rows": tol["grad"]}
+    if options:  # the torch fp32 grad_W rows below implement the plain loss only
+        print("    errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+        bad = {k: (errs[k], limits[k]) for k in errs if not errs[k] <= limits[k]}
+        assert not bad, f"outside tolerance: {bad}"
+        return
     # grad_W rows of sampled vocabulary ids (teacher ids included) against torch fp32
     teacher = inp["topk_idx"][rows[0]][:N_SAMPLE_VOCAB // 2]
     vocab = np.unique(np.concatenate([teacher, rng.choice(w.V, N_SAMPLE_VOCAB // 2, replace=False),
@@ -150,9 +180,5 @@ def test_full_size_parity(name, keep, gpu_device):
     errs["grad_w_rows"] = max_rel_to_max(gw[torch.as_tensor(vocab, device=gpu_device)]
                                          .double().cpu().numpy(), ref_gw)
     print("    errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-
-    limits = {"lse": tol["loss"], "row_loss": tol["loss"], "topk_z": tol["loss"],
-              "grad_hidden": tol["grad"], "grad_w_colsum/bound": 1.0,
-              "<gW,W>-<gH,H>": tol["grad"], "grad_w_rows": tol["grad"]}
     bad = {k: (errs[k], limits[k]) for k in limits if not errs[k] <= limits[k]}
     assert not bad, f"outside tolerance: {bad}"
