@@ -8,7 +8,9 @@ JSON line: throughput in tokens/s, the MFMA roofline of the dominant kernel
 peak HBM of one step, a sampled parity check against the fp64 oracle and the
 oracle's own host throughput on a bounded sample of the same rows.
 
-With --teacher-topk it times the teacher top-K cache producer
+With --memory-sweep it measures the peak HBM of one step at 4096 .. 65536
+tokens and fits it linearly (memory grows linearly with sequence length, no
+N x V buffer). With --teacher-topk it times the teacher top-K cache producer
 (fkl_teacher_topk over a teacher workload) and prints that line instead.
 With --keep-logits the step is the forward-chunked variant instead
 (fkl_forward_keep + fkl_backward_keep: the logits are kept in an N x V buffer
@@ -279,6 +281,62 @@ def run_teacher_topk(args, torch, fkl, synth, dev):
     print(json.dumps(result), flush=True)
 
 
+def memory_sweep(args, torch, fkl, dev):
+    """Peak HBM of one training step (inputs, outputs, workspaces, grad_W, autograd-saved
+    tensors) through fused_chunked_kl at S in {4096 .. 65536} tokens, gpt-oss-20B
+    student shape (d 2880, V 201088, K 100, chunk 2048, bf16); a linear fit
+    peak = a + b S, and the largest single allocation of the step against one
+    N x V bf16 matrix."""
+    d, V, K, chunk, T = 2880, 201088, 100, 2048, 1.0
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    W = (torch.randn(V, d, device=dev, generator=g) / d ** 0.5).to(torch.bfloat16)
+    W.requires_grad_(True)
+    points = []
+    for S in (4096, 8192, 16384, 32768, 65536):
+        h = torch.randn(1, S, d, device=dev, generator=g).to(torch.bfloat16).requires_grad_(True)
+        idx = torch.randint(0, V, (1, S, K), device=dev, generator=g, dtype=torch.int32)
+        lg = torch.randn(1, S, K, device=dev, generator=g)
+        W.grad = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        torch.cuda.memory._record_memory_history(max_entries=100000)
+        loss = fkl.fused_chunked_kl(h, W, idx, lg, T=T, chunk=chunk)
+        loss.backward()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated(dev)
+        snap = torch.cuda.memory._snapshot()
+        torch.cuda.memory._record_memory_history(enabled=None)
+        largest = 0
+        for trace in snap.get("device_traces", []):
+            for ev in trace:
+                if ev.get("action") == "alloc":
+                    largest = max(largest, int(ev.get("size", 0)))
+        points.append({"S": S, "peak_bytes": peak, "largest_alloc_bytes": largest,
+                       "nxv_bf16_bytes": S * V * 2})
+        log(f"[bench] S={S}: peak {peak / 2**30:.3f} GiB, largest allocation "
+            f"{largest / 2**30:.3f} GiB (one N x V bf16 matrix: {S * V * 2 / 2**30:.2f} GiB)")
+        del h, idx, lg, loss
+    xs = np.array([p["S"] for p in points], dtype=np.float64)
+    ys = np.array([p["peak_bytes"] for p in points], dtype=np.float64)
+    b, a = np.polyfit(xs, ys, 1)
+    r2 = 1.0 - float(np.sum((ys - (a + b * xs)) ** 2) / np.sum((ys - ys.mean()) ** 2))
+    result = {
+        "metric": "peak HBM of one fwd+bwd step vs tokens (linear fit)",
+        "config": {"workload": "gptoss20b shape", "d": d, "V": V, "K": K, "chunk": chunk,
+                   "dtype": "bf16", "path": "fused_chunked_kl (autograd)"},
+        "points": points,
+        "fit": {"intercept_bytes": a, "slope_bytes_per_token": b, "r2": r2},
+        # the largest buffer is the fp32 grad_W (V x d x 4 bytes) at every S
+        "largest_alloc_is_grad_w": bool(all(p["largest_alloc_bytes"] <= V * d * 4 * 1.01
+                                            for p in points)),
+        "grad_w_fp32_bytes": V * d * 4,
+        "data": "synthetic",
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +351,9 @@ def main():
                     help="time the loss with its options on: hard labels for every row mixed "
                          "in with alpha 0.5 and a teacher-tail bucket (teacher lse = lse of the "
                          "cached logits + ln 2)")
+    ap.add_argument("--memory-sweep", action="store_true",
+                    help="measure peak HBM of one step at S = 4096 .. 65536 (gpt-oss-20B student "
+                         "shape) and fit it linearly instead of timing")
     ap.add_argument("--teacher-topk", action="store_true",
                     help="time the teacher top-K cache producer instead of the loss "
                          "(workload teacher_llama8b_32k unless --workload names a teacher one)")
@@ -317,6 +378,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.teacher_topk:
         run_teacher_topk(args, torch, fkl, synth, dev)
+        return
+    if args.memory_sweep:
+        memory_sweep(args, torch, fkl, dev)
         return
     w = synth.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name}: N={w.N} d={w.d} V={w.V} K={w.K} T={w.T} "
