@@ -123,6 +123,7 @@ def cpu_baseline(inp, gpu_rows: dict, budget_s: float):
         "value": n / t,
         "unit": "tokens/s",
         "cores": int(threads),
+        "gflops_fp64": 6.0 * n * w.d * w.V / t / 1e9,   # the oracle needs no recompute
         "kind": "oracle",
         "sample": f"first {n} of {w.N} rows of {w.name}, forward+backward in fp64 "
                   f"(NumPy BLAS), {t:.1f} s; grad_W restricted to those rows",
@@ -476,6 +477,7 @@ def main():
     ms_step = elapsed / args.steps * 1e3
     kernels = {k: {"launches_per_step": n / args.steps, "avg_ms": ms / n,
                    "ms_per_step": ms / args.steps} for k, (n, ms) in ktimes.items()}
+    kernel_ms_step = sum(v["ms_per_step"] for v in kernels.values())
     dom = max(ktimes, key=lambda k: ktimes[k][1])
     n_launch, dom_ms = ktimes[dom]
     avg_ms = dom_ms / n_launch
@@ -519,6 +521,9 @@ def main():
                    "variant": "forward-chunked, kept logits" if keep else "fused chunked",
                    "options": "labels (alpha 0.5) + teacher tail" if args.options else None},
         "mfma_frac_step": flops_step / (ms_step * 1e-3) / (peak_tf * 1e12),
+        # the same over the summed kernel durations of a step (HIP events), i.e. without gaps
+        "kernel_ms_per_step": kernel_ms_step,
+        "mfma_frac_kernel_time": flops_step / (kernel_ms_step * 1e-3) / (peak_tf * 1e12),
         "flops_per_step": flops_step,
         "roofline": roofline,
         "cpu_baseline": base,
