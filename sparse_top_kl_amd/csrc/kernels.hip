@@ -316,11 +316,22 @@ __global__ __launch_bounds__(256) void k_gather_dot(const unsigned char* __restr
       continue;
     }
     const unsigned char* wr = W + v * rb;
-    float acc = 0.f;
-    for (int64_t j = li; j < nvec; j += 16) {
-      const u32x4_t hv = STAGE ? lds_load16(h + j * 16) : load16(h + j * 16);
-      acc = dot16<P>(hv, load16(wr + j * 16), acc);
+    // four independent loads and partial sums in flight per lane
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    int64_t j = li;
+    for (; j + 48 < nvec; j += 64) {
+      const u32x4_t w0 = load16(wr + j * 16), w1 = load16(wr + (j + 16) * 16);
+      const u32x4_t w2 = load16(wr + (j + 32) * 16), w3 = load16(wr + (j + 48) * 16);
+      a0 = dot16<P>(STAGE ? lds_load16(h + j * 16) : load16(h + j * 16), w0, a0);
+      a1 = dot16<P>(STAGE ? lds_load16(h + (j + 16) * 16) : load16(h + (j + 16) * 16), w1, a1);
+      a2 = dot16<P>(STAGE ? lds_load16(h + (j + 32) * 16) : load16(h + (j + 32) * 16), w2, a2);
+      a3 = dot16<P>(STAGE ? lds_load16(h + (j + 48) * 16) : load16(h + (j + 48) * 16), w3, a3);
     }
+    for (; j < nvec; j += 16) {
+      const u32x4_t hv = STAGE ? lds_load16(h + j * 16) : load16(h + j * 16);
+      a0 = dot16<P>(hv, load16(wr + j * 16), a0);
+    }
+    float acc = (a0 + a1) + (a2 + a3);
     acc += __shfl_xor(acc, 8);
     acc += __shfl_xor(acc, 4);
     acc += __shfl_xor(acc, 2);
