@@ -22,9 +22,31 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max and sum of 2^(z * c2 - max) over the accumulator rows of token column
+// ni that this lane holds (rows below vlim unless kAll). c2 > 0, so the max of
+// z * c2 is c2 times the max of z, bit for bit.
+template <class C, bool kAll>
+__device__ __forceinline__ float2 lane_lse(const f32x16_t (&acc)[C::kMI][C::kNI], int ni, int lane,
+                                           int vlim, float c2) {
+  float mz = -INFINITY;
+#pragma unroll
+  for (int mi = 0; mi < C::kMI; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (kAll || acc_row(mi, r, lane) < vlim) mz = fmaxf(mz, acc[mi][ni][r]);
+  const float m = mz * c2;
+  float s = 0.f;
+#pragma unroll
+  for (int mi = 0; mi < C::kMI; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (kAll || acc_row(mi, r, lane) < vlim) s += fast_exp2(fmaf(acc[mi][ni][r], c2, -m));
+  return make_float2(m, s);
+}
+
 // Per token of the wave's sub-tile: running max and sum of 2^(z * c2) over its
 // 128 vocabulary rows v0.. (those below V), stored as the partial of slot
-// v0 / 128.
+// v0 / 128. c2 > 0.
 template <class C>
 __device__ __forceinline__ void lse_partials(const f32x16_t (&acc)[C::kMI][C::kNI], int64_t v0,
                                              int64_t V, int64_t t0, int64_t nrows, float c2,
@@ -35,18 +57,9 @@ __device__ __forceinline__ void lse_partials(const f32x16_t (&acc)[C::kMI][C::kN
   const int vlim = full ? C::kWM : static_cast<int>(V - v0);
 #pragma unroll
   for (int ni = 0; ni < C::kNI; ++ni) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int mi = 0; mi < C::kMI; ++mi)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (full || acc_row(mi, r, lane) < vlim) m = fmaxf(m, acc[mi][ni][r] * c2);
-    float s = 0.f;
-#pragma unroll
-    for (int mi = 0; mi < C::kMI; ++mi)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (full || acc_row(mi, r, lane) < vlim) s += fast_exp2(acc[mi][ni][r] * c2 - m);
+    const float2 ms = full ? lane_lse<C, true>(acc, ni, lane, vlim, c2)
+                           : lane_lse<C, false>(acc, ni, lane, vlim, c2);
+    const float m = ms.x, s = ms.y;
     // the other lane half holds the other 4-row groups of the same token
     const float mo = __shfl_xor(m, 32);
     const float so = __shfl_xor(s, 32);

@@ -760,10 +760,16 @@ __device__ __forceinline__ int64_t xcd_tile_index(int64_t total) {
   return (b & 7) * per + (b >> 3);
 }
 
+// Two fp32 values rounded to nearest-even bf16 and packed (lo in bits 0-15):
+// one v_cvt_pk_bf16_f32. Over every non-NaN fp32 input it gives the same bits
+// as adding 0x7fff plus the lowest kept bit and truncating.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.f));
 }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __builtin_bit_cast(float, static_cast<uint32_t>(h) << 16);

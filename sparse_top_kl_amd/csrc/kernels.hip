@@ -43,6 +43,7 @@
 #include <math.h>
 
 #include <cstdlib>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "gemm_core.hpp"
@@ -67,10 +68,8 @@ __device__ __forceinline__ void accumulate_out(float* p, float v, int accumulate
 template <class P>
 __device__ __forceinline__ void store4(unsigned char* p, const float (&v)[4]) {
   if constexpr (P::kBytes == 2) {
-    const uint32_t lo = f32_to_bf16_rne(v[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
-    const uint32_t hi = f32_to_bf16_rne(v[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{lo, hi};
+    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   } else {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   }
@@ -83,8 +82,9 @@ struct LogitValue {  // z itself, zero in the padding columns >= vlim
   int64_t vlim;
   struct Row {};
   __device__ __forceinline__ Row row(int64_t) const { return Row{}; }
-  __device__ __forceinline__ float operator()(const Row&, float z, int64_t col) const {
-    return col < vlim ? z : 0.f;
+  __device__ __forceinline__ float value(const Row&, float z) const { return z; }
+  __device__ __forceinline__ float operator()(const Row& r, float z, int64_t col) const {
+    return col < vlim ? value(r, z) : 0.f;
   }
 };
 // Dense part of the logit gradient, acoef * 2^(z*c2 - lse2), plus with CE2
@@ -107,19 +107,21 @@ struct GradValue {
     if constexpr (CE2) return Row{acoef[tok], lse2[tok], bcoef[tok], lse1_2[tok]};
     return Row{acoef[tok], lse2[tok], 0.f, 0.f};
   }
-  __device__ __forceinline__ float operator()(const Row& r, float z, int64_t col) const {
-    if (col >= vlim) return 0.f;
+  __device__ __forceinline__ float value(const Row& r, float z) const {
     float g = r.a * fast_exp2(z * c2 - r.l2);
     if constexpr (CE2) g += r.b * fast_exp2(z * kLog2e - r.l1);
     return g;
+  }
+  __device__ __forceinline__ float operator()(const Row& r, float z, int64_t col) const {
+    return col < vlim ? value(r, z) : 0.f;
   }
 };
 
 // Writes f(z) for the wave's sub-tile of a logit tile (accumulator rows =
 // output columns w0.., accumulator columns = tokens t0..) into Out[token][column]
-// (row pitch out_ld bytes), for tokens < nrows and columns < ncols. Called by
-// every thread of the workgroup after the k-loop. NT marks the stores
-// nontemporal (data not read again soon).
+// (row pitch out_ld bytes), for tokens < nrows and columns < ncols; f gives 0
+// at columns >= f.vlim. Called by every thread of the workgroup after the
+// k-loop. NT marks the stores nontemporal (data not read again soon).
 template <class P, class C, bool NT = false, class F>
 __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::kMI][C::kNI], const F& f,
                                                  int64_t w0, int64_t t0, int64_t nrows,
@@ -136,32 +138,47 @@ __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::kMI][C
     // of t is set, so the 32 rows one write instruction touches hit 32
     // distinct 8-byte bank positions.
     static_assert(C::kWM == 128 && C::kWN == 64, "transpose layout of the eight-wave tile");
+    typedef __attribute__((address_space(3))) unsigned char lds_u8;
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     __syncthreads();  // every wave has drained its loads: the stage LDS is free
     const int w = static_cast<int>(threadIdx.x >> 6);
-    unsigned char* tp =
-        PingPongLoop<C, false, false>::stage_arrays().s[w >> 2] + (w & 3) * (kDStageBytes / 4);
+    const auto st = PingPongLoop<C, false, false>::stage_arrays();
+    // an LDS-space pointer, so the staging uses ds_write / ds_read
+    lds_u8* const tp = (lds_u8*)(w < 4 ? st.s[0] : st.s[1]) +
+                       (w & 3) * (kDStageBytes / 4);
+    // Sub-tiles whose columns all lie below f.vlim (all but the vocabulary's
+    // last) skip the per-element column test.
+    auto fill = [&](auto all_cols) {
+      constexpr bool kAll = decltype(all_cols)::value;
 #pragma unroll
-    for (int ni = 0; ni < C::kNI; ++ni) {
-      const int tl = ni * 32 + (lane & 31);
-      const typename F::Row rw = f.row(t0 + tl);
-      const int half = (lane >> 5) ^ ((tl >> 4) & 1);
+      for (int ni = 0; ni < C::kNI; ++ni) {
+        const int tl = ni * 32 + (lane & 31);
+        const typename F::Row rw = f.row(t0 + tl);
+        const int half = (lane >> 5) ^ ((tl >> 4) & 1);
 #pragma unroll
-      for (int mi = 0; mi < C::kMI; ++mi)
+        for (int mi = 0; mi < C::kMI; ++mi)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int64_t col = w0 + mi * 32 + 8 * g4 + 4 * (lane >> 5);
-          float v[4];
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int64_t col = w0 + mi * 32 + 8 * g4 + 4 * (lane >> 5);
+            float v[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = f(rw, acc[mi][ni][4 * g4 + j], col + j);
-          const int unit = (mi * 4 + g4) ^ (tl & 15);
-          store4<P>(tp + tl * 256 + unit * 16 + half * 8, v);
-        }
-    }
+            for (int j = 0; j < 4; ++j)
+              v[j] = kAll ? f.value(rw, acc[mi][ni][4 * g4 + j]) : f(rw, acc[mi][ni][4 * g4 + j], col + j);
+            const int unit = (mi * 4 + g4) ^ (tl & 15);
+            *(__attribute__((address_space(3))) u32x2_t*)(tp + tl * 256 + unit * 16 + half * 8) =
+                u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          }
+      }
+    };
+    if (w0 + C::kWM <= f.vlim)
+      fill(std::true_type{});
+    else
+      fill(std::false_type{});
     if (w0 >= ncols) return;
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int tl = it * 4 + (lane >> 4), u = lane & 15;
-      u32x4_t x = lds_load16(tp + tl * 256 + (u ^ (tl & 15)) * 16);
+      u32x4_t x = *(const __attribute__((address_space(3))) u32x4_t*)(tp + tl * 256 + (u ^ (tl & 15)) * 16);
       if ((tl >> 4) & 1) x = u32x4_t{x[2], x[3], x[0], x[1]};
       const int64_t tok = t0 + tl, col = w0 + u * 8;
       if (tok < nrows && col < ncols) {
@@ -594,7 +611,7 @@ __global__ __launch_bounds__(kGzThreads) void k_g_from_z(unsigned char* __restri
           const float z0 = as_f32(x[u][e] << 16), z1 = as_f32(x[u][e] & 0xffff0000u);
           const float g0 = v + 2 * e < V ? dense_g(dc, z0, c2) : 0.f;
           const float g1 = v + 2 * e + 1 < V ? dense_g(dc, z1, c2) : 0.f;
-          y[e] = f32_to_bf16_rne(g0) | (static_cast<uint32_t>(f32_to_bf16_rne(g1)) << 16);
+          y[e] = pack_bf16x2(g0, g1);
         }
       } else {
 #pragma unroll
