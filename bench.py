@@ -338,6 +338,72 @@ def memory_sweep(args, torch, fkl, dev):
     print(json.dumps(result), flush=True)
 
 
+def vendor_gemm_step(args, torch, w, dev):
+    """hipBLASLt (torch.mm) on the plain contractions of one step of the workload, 8 N d V
+    flops in bf16 with no exp, log-sum-exp, gather or G formation: (a) per chunk of rows
+    over the whole vocabulary (logits, recomputed logits, grad_hidden, grad_W), as a PyTorch
+    version of the chunked recompute runs them; (b) the forward per chunk and the backward
+    in row blocks x vocabulary slices of the given shape (--vendor-block; 16384 x 16032 is
+    what the library plans for long32k). A reference time for the same flops through the
+    vendor GEMMs under the same board power limit, not a product path."""
+    N, d, V, chunk = w.N, w.d, w.V, w.chunk
+    R, S = (int(x) for x in args.vendor_block.split(","))
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    H = torch.randn(N, d, device=dev, generator=g).to(bf)
+    W = (torch.randn(V, d, device=dev, generator=g) / d ** 0.5).to(bf)
+    Z = torch.empty(chunk, V, device=dev, dtype=bf)
+    gh = torch.empty(max(R, chunk), d, device=dev, dtype=bf)
+    gw = torch.empty(V, d, device=dev, dtype=bf)
+    G = torch.empty(R, S, device=dev, dtype=bf)
+
+    def chunked():
+        for r0 in range(0, N, chunk):
+            torch.mm(H[r0:r0 + chunk], W.t(), out=Z)
+        for r0 in range(0, N, chunk):
+            h = H[r0:r0 + chunk]
+            torch.mm(h, W.t(), out=Z)
+            torch.mm(Z, W, out=gh[:chunk])
+            torch.mm(Z.t(), h, out=gw)
+
+    def blocked():
+        for r0 in range(0, N, chunk):
+            torch.mm(H[r0:r0 + chunk], W.t(), out=Z)
+        for r0 in range(0, N, R):
+            h = H[r0:r0 + R]
+            for v0 in range(0, V, S):
+                ws = W[v0:v0 + S]
+                gg = G[:h.shape[0], :ws.shape[0]]
+                if ws.shape[0] == S and h.shape[0] == R:
+                    torch.mm(h, ws.t(), out=gg)
+                    torch.mm(gg, ws, out=gh[:R])
+                    torch.mm(gg.t(), h, out=gw[v0:v0 + S])
+                else:
+                    gg = torch.mm(h, ws.t())
+                    torch.mm(gg, ws)
+                    torch.mm(gg.t(), h)
+
+    out = {}
+    for name, fn in (("chunked", chunked), ("blocked", blocked)):
+        for _ in range(args.warmup + 1):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / args.steps * 1e3
+        tf = 8.0 * N * d * V / ms / 1e9
+        out[name] = {"ms_per_step": ms, "tflops": tf, "frac_of_peak": tf / PEAK_TFLOPS["bf16"]}
+        log(f"[bench] hipBLASLt {name}: {ms:.2f} ms/step, {tf:.1f} TFLOP/s over 8NdV")
+    print(json.dumps({"metric": "vendor GEMM time for the step's contractions",
+                      "config": {"workload": w.name, "N": N, "d": d, "V": V, "chunk": chunk,
+                                 "block": [R, S], "dtype": "bf16"},
+                      "steps": args.steps, "warmup": args.warmup, **out, "data": "synthetic"}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,6 +424,12 @@ def main():
     ap.add_argument("--teacher-topk", action="store_true",
                     help="time the teacher top-K cache producer instead of the loss "
                          "(workload teacher_llama8b_32k unless --workload names a teacher one)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time hipBLASLt (torch.mm) on the plain contractions of one step "
+                         "(8NdV flops, no exp/LSE/gather) instead of the library")
+    ap.add_argument("--vendor-block", default="16384,16032",
+                    help="row block and vocabulary slice of the blocked backward for "
+                         "--vendor-gemm (the library's plan for long32k)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy this many MiB once on the device (a plain "
                          "copy of known size for calibrating rocprofv3 byte counters)")
@@ -384,6 +456,9 @@ def main():
         memory_sweep(args, torch, fkl, dev)
         return
     w = synth.WORKLOADS[args.workload]
+    if args.vendor_gemm:
+        vendor_gemm_step(args, torch, w, dev)
+        return
     log(f"[bench] generating {w.name}: N={w.N} d={w.d} V={w.V} K={w.K} T={w.T} "
         f"chunk={w.chunk} {w.dtype}")
     inp = synth.make_inputs(w)
