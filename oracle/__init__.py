@@ -10,7 +10,9 @@ method's arithmetic.
 Every function in ``kl_oracle`` is pinned by a CPU test against something
 other than itself (library routines, closed forms, brute force, finite
 differences); see ``tests/test_oracle.py``. ``topk_oracle`` (the teacher
-top-K cache) is pinned the same way in ``tests/test_oracle_topk.py``.
+top-K cache) is pinned the same way in ``tests/test_oracle_topk.py``, and
+``renorm_oracle`` (the student-renormalised loss option) in
+``tests/test_oracle_renorm.py``.
 """
 
 from .kl_oracle import (  # noqa: F401
@@ -21,3 +23,4 @@ from .kl_oracle import (  # noqa: F401
     teacher_log_probs,
 )
 from .topk_oracle import teacher_logits, teacher_topk, topk_rows  # noqa: F401,E402
+from .renorm_oracle import renorm_brute_force, renorm_forward_backward  # noqa: F401,E402
