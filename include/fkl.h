@@ -293,6 +293,58 @@ int32_t fkl_teacher_topk(const void* hidden, const void* weight, int64_t N, int6
                          int32_t* topk_idx, float* topk_logit, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Student-renormalised top-K loss: an alternative reading of how the cache's
+ * tail is treated, which the pages leave open (the cache itself:
+ * "Multiverse Computing ... (iitak.ru)", third paragraph; "Wissensdestillation
+ * mit deutlich weniger GPU-Speicher", section "Teacher-Ausgaben einmalig
+ * zwischenspeichern"; softening by T and the T^2 factor: "Дистилляция и
+ * сжатие моделей", section "Как это работает: мягкие метки и температура").
+ * Teacher and student are both softened by T and renormalised over the K
+ * cached entries of the row, so only the student's logits at the cached ids
+ * enter: no vocabulary-wide log-sum-exp and no vocabulary GEMM. Per row r,
+ * over the entries with a finite teacher logit (a -inf entry is padding and
+ * takes part in neither softmax):
+ *   p_k = softmax_k(l_rk / T),  q_k = softmax_k(z_r,idx_rk / T)
+ *   row_loss_r = w_r T^2 sum_k p_k (ln p_k - ln q_k),  loss = sum_r row_loss_r
+ *   dloss/dz_r,idx_rk = s w_r T (q_k sum_j p_j - p_k)
+ * with w_r = row_weight[r] (1 when row_weight is NULL; a row of weight 0
+ * contributes nothing, whatever its logits) and s = *grad_loss (1 when NULL).
+ * A row of nonzero weight without a finite teacher logit contributes 0.
+ * Shapes and dtypes as fkl_forward / fkl_backward (hidden [N, d] and the
+ * weight [V, d] in dtype, ids int32 [N, K] in [0, V) on every entry, padding
+ * included; teacher logits fp32 [N, K]); K <= 1024, d <= 8192,
+ * N * K < 2^31 (FKL_E_UNSUPPORTED otherwise). Duplicate ids inside a row act
+ * as separate entries. No chunk parameter: the work and the workspace are
+ * O(N * K * (1 + d / K)) and O(V) and never touch N x V.
+ *
+ * fkl_renorm_workspace_size: bytes of the forward and backward workspaces
+ *   (either pointer may be NULL). The backward workspace holds the K
+ *   coefficients per row, a counting sort of the N * K (row, entry) pairs by
+ *   id (at most 256 MiB of per-block counters) and chunk partials of grad_W.
+ * fkl_renorm_forward: writes loss[0] and, when non-NULL, row_loss [N] and
+ *   topk_z [N, K] (the student logit at each cached id, fp32 dot product of
+ *   the hidden row and the weight row). flags: 0 or FKL_FLAG_VALIDATE_IDX.
+ * fkl_renorm_backward: grad_hidden [N, d] in dtype (overwritten) and
+ *   grad_weight [V, d] fp32 (overwritten; added to under
+ *   FKL_FLAG_ACCUMULATE_GRAD_W). topk_z from the forward may be passed to skip
+ *   the gather (NULL: recomputed). grad_W is summed without float atomics in
+ *   a fixed order, so repeated calls give the same bits.
+ * Alignment, ownership, stream and error behaviour as for fkl_forward /
+ * fkl_backward; outputs must not alias inputs. */
+int32_t fkl_renorm_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K, int32_t dtype,
+                                  size_t* fwd_bytes, size_t* bwd_bytes);
+int32_t fkl_renorm_forward(const void* hidden, const void* weight, const int32_t* topk_idx,
+                           const float* topk_logit, float T, int64_t N, int64_t d, int64_t V,
+                           int32_t K, int32_t dtype, uint32_t flags, const float* row_weight,
+                           float* loss, float* row_loss, float* topk_z, void* workspace,
+                           size_t workspace_bytes, void* stream);
+int32_t fkl_renorm_backward(const void* hidden, const void* weight, const int32_t* topk_idx,
+                            const float* topk_logit, const float* topk_z, const float* grad_loss,
+                            float T, int64_t N, int64_t d, int64_t V, int32_t K, int32_t dtype,
+                            uint32_t flags, const float* row_weight, void* grad_hidden,
+                            float* grad_weight, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Per-kernel timing, a profiling aid (off by default). While enabled, every
  * kernel launch the library makes is bracketed by two HIP events recorded on
  * the launch stream; the events cost a few microseconds of GPU time each.

@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfkl.so")
 
-SOURCES = ["kernels.hip", "topk.hip", "fkl_api.cpp", "topk_api.cpp", "timing.cpp"]
+SOURCES = ["kernels.hip", "topk.hip", "renorm.hip", "fkl_api.cpp", "topk_api.cpp",
+           "renorm_api.cpp", "timing.cpp"]
 ARCH = "gfx950"
 
 

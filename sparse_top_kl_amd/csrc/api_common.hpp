@@ -11,6 +11,7 @@
 #include <cstdio>
 
 #include "fkl.h"
+#include "kernels.hpp"
 
 namespace fkl_api {
 
@@ -52,6 +53,23 @@ inline int32_t check_shapes(int64_t N, int64_t d, int64_t V, int32_t K, int64_t 
 inline int32_t hip_check(const char* where) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FKL_E_HIP, "%s: %s", where, hipGetErrorString(e));
+  return FKL_OK;
+}
+
+// Runs the device-side id check (teacher ids in [0, V), labels below V) and
+// waits for its verdict.
+inline int32_t validate_ids(const int32_t* idx, int64_t N, int32_t K, int64_t V, int32_t* dflag,
+                     hipStream_t s, const int32_t* labels = nullptr) {
+  fkl::launch_fill_f32(reinterpret_cast<float*>(dflag), 1, 0.0f, s);
+  fkl::launch_validate_idx(idx, N, K, V, false, dflag, s);
+  if (labels) fkl::launch_validate_idx(labels, N, 1, V, true, dflag, s);
+  int32_t r = hip_check("id validation launch");
+  if (r) return r;
+  int32_t host = 0;
+  hipError_t e = hipMemcpyAsync(&host, dflag, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(FKL_E_HIP, "id validation: %s", hipGetErrorString(e));
+  if (host != 0) return fail(FKL_E_INDEX, "a teacher id is outside [0, V) or a label >= V");
   return FKL_OK;
 }
 

@@ -163,23 +163,6 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_
   return p;
 }
 
-// Runs the device-side id check (teacher ids in [0, V), labels below V) and
-// waits for its verdict.
-int32_t validate_ids(const int32_t* idx, int64_t N, int32_t K, int64_t V, int32_t* dflag,
-                     hipStream_t s, const int32_t* labels = nullptr) {
-  fkl::launch_fill_f32(reinterpret_cast<float*>(dflag), 1, 0.0f, s);
-  fkl::launch_validate_idx(idx, N, K, V, false, dflag, s);
-  if (labels) fkl::launch_validate_idx(labels, N, 1, V, true, dflag, s);
-  int32_t r = hip_check("id validation launch");
-  if (r) return r;
-  int32_t host = 0;
-  hipError_t e = hipMemcpyAsync(&host, dflag, 4, hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess) return fail(FKL_E_HIP, "id validation: %s", hipGetErrorString(e));
-  if (host != 0) return fail(FKL_E_INDEX, "a teacher id is outside [0, V) or a label >= V");
-  return FKL_OK;
-}
-
 // Kept logits: each row padded to a multiple of 64 elements (128-byte lines in bf16).
 int64_t keep_pitch(int64_t V) { return fkl::round_up(V, 64); }
 size_t keep_bytes(int64_t N, int64_t V, int32_t dtype) {

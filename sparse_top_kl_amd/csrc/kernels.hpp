@@ -125,4 +125,30 @@ void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 void launch_validate_idx(const int32_t* idx, int64_t N, int K, int64_t V, bool allow_negative,
                          int32_t* flag, hipStream_t s);
 
+// ---- student-renormalised loss (renorm.hip)
+constexpr int kRenormMaxK = 1024;  // cached entries per row
+constexpr int64_t kRenormMaxD = 8192;  // hidden size (eight columns per thread, 1024 threads)
+
+// grad_W of the renormalised loss: a stable counting sort of the N * K (row,
+// entry) pairs by id in nb blocks of rows_per_block rows, then sums over
+// chunks of seg sorted pairs.
+struct RenormSortPlan {
+  int64_t nb, rows_per_block, seg, nchunks;
+};
+
+// Forward (coef_mode false): row_loss[r] = w_r T^2 KL over the row's cached
+// entries. Backward (coef_mode true): coef[r][k] = dloss/dz at entry k.
+void launch_renorm_rows(bool coef_mode, const float* zk, const float* logit,
+                        const float* row_weight, const float* grad_loss, int64_t N, int K,
+                        float T, float* row_loss, float* coef, hipStream_t s);
+// grad_hidden[r] = sum_k coef[r][k] W[idx[r][k]] in the input dtype.
+void launch_renorm_grad_h(int dtype, const void* W, const int32_t* idx, const float* coef,
+                          int64_t N, int K, int64_t d, void* gh, hipStream_t s);
+// grad_W[v] (=, or += with acc_out) sum over pairs with id v of coef * H[row];
+// hist [nb * V], total [V], start [V + 1], perm [N * K], partial [2 * nchunks * d].
+void launch_renorm_grad_w(int dtype, const void* H, const int32_t* idx, const float* coef,
+                          int64_t N, int K, int64_t d, int64_t V, const RenormSortPlan& q,
+                          int32_t* hist, int32_t* total, int32_t* start, int32_t* perm,
+                          float* partial, bool acc_out, float* gw, hipStream_t s);
+
 }  // namespace fkl

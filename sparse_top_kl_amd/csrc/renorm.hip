@@ -1,0 +1,472 @@
+// Student-renormalised top-K loss for gfx950: both distributions softened by T
+// and renormalised over the K cached entries of each row, so the loss reads
+// the student's logits at the cached ids only (no vocabulary-wide log-sum-exp
+// and no vocabulary GEMM). The pages leave open how the tail beyond the cache
+// is treated ("Multiverse Computing ... (iitak.ru)", third paragraph, and
+// "Wissensdestillation mit deutlich weniger GPU-Speicher", section
+// "Teacher-Ausgaben einmalig zwischenspeichern", describe the cache; the
+// softening and the T^2 factor follow "Дистилляция и сжатие моделей",
+// section "Как это работает: мягкие метки и температура").
+//
+// Per row r (entries with a -inf teacher logit are padding and take part in
+// neither softmax), in base-2 units with c2 = log2(e) / T:
+//   p_k = 2^(l_k c2 - la),  q_k = 2^(z_k c2 - lu)   (la, lu the log2 normalisers)
+//   row_loss = w_r T^2 ln2 sum_k p_k (log2 p_k - log2 q_k)
+//   G_rk     = s w_r T (q_k sum_j p_j - p_k)
+//   grad_h_r = sum_k G_rk W[idx_rk],  grad_W[v] = sum_{(r,k): idx_rk = v} G_rk h_r
+//
+// Kernels:
+//   k_renorm_rows    one wave per row: the two K-entry softmaxes -> row loss
+//                    (forward) or the K coefficients G_r. (backward)
+//   k_renorm_grad_h  one workgroup per row: sum_k G_rk W[idx_rk] (16-byte
+//                    loads of the K weight rows, four in flight per lane)
+//   grad_W without float atomics, bitwise deterministic:
+//   k_rs_hist        per block of rows, the count of each id (integer atomics)
+//   k_rs_colscan     per id, exclusive prefix of its counts over the blocks
+//   k_rs_scan        exclusive prefix over ids of the totals: bucket starts
+//   k_rs_place       per block, its rows in order: each pair (r, k) goes to
+//                    start[v] + (pairs of id v in earlier rows) + (copies of v
+//                    earlier in row r): a stable counting sort by id
+//   k_rs_chunks      fixed chunks of the sorted pairs: the sum of G h over each
+//                    run of one id, written to grad_W when the chunk holds the
+//                    whole bucket, else to the chunk's head or tail partial
+//   k_rs_fix         per id whose bucket crosses chunks: its partials in chunk
+//                    order; ids with no pair get a zero row
+#include <math.h>
+
+#include "device_common.hpp"
+#include "gemm_core.hpp"
+#include "kernels.hpp"
+#include "timing.hpp"
+
+namespace fkl {
+
+namespace {
+
+__device__ __forceinline__ bool finite_logit(float l) { return l > -INFINITY && l < INFINITY; }
+
+// Eight consecutive values from a bf16 (16 bytes) or fp32 (32 bytes) row.
+template <class P>
+__device__ __forceinline__ void load8(const unsigned char* p, float (&x)[8]) {
+  if constexpr (P::kBytes == 2) {
+    const u32x4_t u = load16(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = as_f32(u[e] << 16);
+      x[2 * e + 1] = as_f32(u[e] & 0xffff0000u);
+    }
+  } else {
+    const u32x4_t a = load16(p), b = load16(p + 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = as_f32(a[e]);
+      x[4 + e] = as_f32(b[e]);
+    }
+  }
+}
+
+template <class P>
+__device__ __forceinline__ void store8(unsigned char* p, const float (&x)[8]) {
+  if constexpr (P::kBytes == 2) {
+    *reinterpret_cast<u32x4_t*>(p) = u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                             pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+  } else {
+    *reinterpret_cast<u32x4_t*>(p) = u32x4_t{__builtin_bit_cast(uint32_t, x[0]),
+                                             __builtin_bit_cast(uint32_t, x[1]),
+                                             __builtin_bit_cast(uint32_t, x[2]),
+                                             __builtin_bit_cast(uint32_t, x[3])};
+    *reinterpret_cast<u32x4_t*>(p + 16) = u32x4_t{__builtin_bit_cast(uint32_t, x[4]),
+                                                  __builtin_bit_cast(uint32_t, x[5]),
+                                                  __builtin_bit_cast(uint32_t, x[6]),
+                                                  __builtin_bit_cast(uint32_t, x[7])};
+  }
+}
+
+constexpr int kRowWaves = 4;  // rows per k_renorm_rows block
+
+}  // namespace
+
+template <bool COEF>
+__global__ __launch_bounds__(64 * kRowWaves) void k_renorm_rows(
+    const float* __restrict__ zk, const float* __restrict__ logit,
+    const float* __restrict__ row_weight, const float* __restrict__ grad_loss, int64_t N, int K,
+    float T, float* __restrict__ row_loss, float* __restrict__ coef) {
+  // l c2 and z c2 must be rounded products, not fused into the following
+  // subtraction, so that an entry at the maximum is exactly 0 after the shift
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kRowWaves + (threadIdx.x >> 6);
+  if (r >= N) return;
+  const float* lr = logit + r * K;
+  const float* zr = zk + r * K;
+  const float w = row_weight ? row_weight[r] : 1.f;
+  const float c2 = kLog2e / T;
+  float ma = -INFINITY, mu = -INFINITY;
+  for (int k = lane; k < K; k += 64) {
+    const float l = lr[k];
+    if (finite_logit(l)) {
+      ma = fmaxf(ma, (l * c2));
+      mu = fmaxf(mu, (zr[k] * c2));
+    }
+  }
+  ma = wave_max(ma);
+  mu = wave_max(mu);
+  if (w == 0.f || ma == -INFINITY) {  // zero weight or no cached entry: nothing
+    if constexpr (COEF) {
+      for (int k = lane; k < K; k += 64) coef[r * K + k] = 0.f;
+    } else {
+      if (lane == 0) row_loss[r] = 0.f;
+    }
+    return;
+  }
+  float sa = 0.f, su = 0.f;
+  for (int k = lane; k < K; k += 64) {
+    const float l = lr[k];
+    if (finite_logit(l)) {
+      sa += fast_exp2((l * c2) - ma);
+      su += fast_exp2((zr[k] * c2) - mu);
+    }
+  }
+  sa = wave_sum(sa);
+  su = wave_sum(su);
+  const float lsa = log2f(sa), lsu = log2f(su);
+  if constexpr (!COEF) {
+    // log2 p_k - log2 q_k = (l_k c2 - ma) - (z_k c2 - mu) - (log2 sa - log2 su): each
+    // side shifted by its own max first (exact at the max), so a one-entry row
+    // gives exactly 0
+    const float C = lsa - lsu;
+    float acc = 0.f;
+    for (int k = lane; k < K; k += 64) {
+      const float l = lr[k];
+      if (finite_logit(l)) {
+        const float ea = (l * c2) - ma;
+        acc += fast_exp2(ea) * ((ea - ((zr[k] * c2) - mu)) - C);
+      }
+    }
+    acc = wave_sum(acc) / sa;
+    if (lane == 0) row_loss[r] = w * T * T * kLn2 * acc;
+  } else {
+    float ps = 0.f;
+    for (int k = lane; k < K; k += 64) {
+      const float l = lr[k];
+      if (finite_logit(l)) ps += fast_exp2((l * c2) - ma - lsa);
+    }
+    ps = wave_sum(ps);
+    const float sc = (grad_loss ? *grad_loss : 1.f) * w * T;
+    for (int k = lane; k < K; k += 64) {
+      const float l = lr[k];
+      float g = 0.f;
+      if (finite_logit(l))
+        g = sc * (fast_exp2((zr[k] * c2) - mu - lsu) * ps -
+                  fast_exp2((l * c2) - ma - lsa));
+      coef[r * K + k] = g;
+    }
+  }
+}
+
+// grad_hidden row r = sum_k coef[r, k] W[idx[r, k]]: one workgroup per row,
+// thread t owns columns 8t .. 8t + 7 (blockDim.x * 8 >= d).
+template <class P>
+__global__ __launch_bounds__(1024) void k_renorm_grad_h(const unsigned char* __restrict__ W,
+                                                        const int32_t* __restrict__ idx,
+                                                        const float* __restrict__ coef, int K,
+                                                        int64_t d, unsigned char* __restrict__ gh) {
+  __shared__ int32_t sid[kRenormMaxK];
+  __shared__ float sg[kRenormMaxK];
+  const int64_t r = blockIdx.x;
+  for (int k = threadIdx.x; k < K; k += blockDim.x) {
+    sid[k] = idx[r * K + k];
+    sg[k] = coef[r * K + k];
+  }
+  __syncthreads();
+  const int64_t c0 = static_cast<int64_t>(threadIdx.x) * 8;
+  if (c0 >= d) return;
+  const int64_t ld = d * P::kBytes;
+  const unsigned char* wc = W + c0 * P::kBytes;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 4 <= K; k += 4) {
+    float x0[8], x1[8], x2[8], x3[8];
+    load8<P>(wc + sid[k] * ld, x0);
+    load8<P>(wc + sid[k + 1] * ld, x1);
+    load8<P>(wc + sid[k + 2] * ld, x2);
+    load8<P>(wc + sid[k + 3] * ld, x3);
+    const float g0 = sg[k], g1 = sg[k + 1], g2 = sg[k + 2], g3 = sg[k + 3];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      acc[e] = fmaf(g3, x3[e], fmaf(g2, x2[e], fmaf(g1, x1[e], fmaf(g0, x0[e], acc[e]))));
+  }
+  for (; k < K; ++k) {
+    float x[8];
+    load8<P>(wc + sid[k] * ld, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(sg[k], x[e], acc[e]);
+  }
+  store8<P>(gh + r * ld + c0 * P::kBytes, acc);
+}
+
+// Counts of each id per block of rows: hist[b][v], b = pair / pairs_per_block.
+__global__ __launch_bounds__(256) void k_rs_hist(const int32_t* __restrict__ idx, int64_t NK,
+                                                 int64_t pairs_per_block, int64_t V,
+                                                 int32_t* __restrict__ hist) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; p < NK;
+       p += stride)
+    atomicAdd(&hist[(p / pairs_per_block) * V + idx[p]], 1);
+}
+
+// Per id v: hist[b][v] <- sum of hist[b'][v] for b' < b; total[v] <- sum over all b.
+__global__ __launch_bounds__(256) void k_rs_colscan(int32_t* __restrict__ hist, int64_t nb,
+                                                    int64_t V, int32_t* __restrict__ total) {
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (v >= V) return;
+  int32_t acc = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    const int32_t c = hist[b * V + v];
+    hist[b * V + v] = acc;
+    acc += c;
+  }
+  total[v] = acc;
+}
+
+// start[v] = sum of total[v'] for v' < v, start[V] = the grand total. One
+// workgroup of 1024 threads, each owning a contiguous segment of ids.
+__global__ __launch_bounds__(1024) void k_rs_scan(const int32_t* __restrict__ total, int64_t V,
+                                                  int32_t* __restrict__ start) {
+  __shared__ int32_t wsum[16];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int64_t seg = (V + 1023) / 1024;
+  const int64_t a = t * seg, e = a + seg < V ? a + seg : V;
+  int32_t s = 0;
+  for (int64_t v = a; v < e; ++v) s += total[v];
+  // inclusive scan of s over the workgroup
+  int32_t x = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  int32_t before = 0;
+  for (int i = 0; i < wv; ++i) before += wsum[i];
+  int32_t run = before + x - s;  // exclusive prefix of this thread's segment
+  for (int64_t v = a; v < e; ++v) {
+    start[v] = run;
+    run += total[v];
+  }
+  if (t == 1023) start[V] = before + x;
+}
+
+// Stable placement: block b walks its rows in order; within a row each id's
+// first copy reserves its copies' slots with one returning atomic on the
+// block's cursor hist[b][v] (private to the block, so the values returned
+// follow the row order), and every copy lands at start[v] + base + (earlier
+// copies in the row).
+__global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ idx, int64_t N,
+                                                  int K, int64_t rows_per_block, int64_t V,
+                                                  int32_t* __restrict__ hist,
+                                                  const int32_t* __restrict__ start,
+                                                  int32_t* __restrict__ perm) {
+  __shared__ int32_t sid[kRenormMaxK];
+  __shared__ int32_t sbase[kRenormMaxK];
+  constexpr int kPer = kRenormMaxK / 256;
+  const int64_t b = blockIdx.x;
+  const int64_t r0 = b * rows_per_block;
+  const int64_t r1 = r0 + rows_per_block < N ? r0 + rows_per_block : N;
+  int32_t* cur = hist + b * V;
+  const int t = threadIdx.x;
+  for (int64_t r = r0; r < r1; ++r) {
+    for (int k = t; k < K; k += 256) sid[k] = idx[r * K + k];
+    __syncthreads();
+    int dup[kPer], first[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int k = t + 256 * j;
+      dup[j] = 0;
+      first[j] = k;
+      if (k < K) {
+        const int32_t v = sid[k];
+        int mult = 0, fst = -1;
+        for (int k2 = 0; k2 < K; ++k2) {
+          const bool eq = sid[k2] == v;
+          mult += eq ? 1 : 0;
+          dup[j] += (eq && k2 < k) ? 1 : 0;
+          if (eq && fst < 0) fst = k2;
+        }
+        first[j] = fst;
+        if (dup[j] == 0) sbase[k] = atomicAdd(&cur[v], mult);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int k = t + 256 * j;
+      if (k < K) perm[start[sid[k]] + sbase[first[j]] + dup[j]] = static_cast<int32_t>(r * K + k);
+    }
+    __syncthreads();
+  }
+}
+
+// Chunk c covers sorted positions [c * seg, min(NK, (c + 1) * seg)). For each
+// run of one id v inside it, the sum of coef[p] * H[p / K] over the run's pairs
+// p in sorted order goes to grad_W[v] (written, or added with ACC) when the
+// chunk holds v's whole bucket, else to partial[c][0] (the bucket began in an
+// earlier chunk) or partial[c][1] (it begins here and continues).
+template <class P>
+__global__ __launch_bounds__(1024) void k_rs_chunks(
+    const unsigned char* __restrict__ H, const int32_t* __restrict__ idx,
+    const float* __restrict__ coef, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ start, int64_t NK, int K, int64_t d, int64_t seg, bool acc_out,
+    float* __restrict__ gw, float* __restrict__ partial) {
+  const int64_t c = blockIdx.x;
+  const int64_t a = c * seg, e = a + seg < NK ? a + seg : NK;
+  const int64_t c0 = static_cast<int64_t>(threadIdx.x) * 8;
+  const bool mine = c0 < d;
+  const int64_t ld = d * P::kBytes;
+  const unsigned char* hc = H + c0 * P::kBytes;
+  int64_t pos = a;
+  while (pos < e) {
+    const int32_t v = idx[perm[pos]];
+    const int64_t bs = start[v], be = start[v + 1];
+    const int64_t run_end = be < e ? be : e;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (mine) {
+      int64_t q = pos;
+      for (; q + 4 <= run_end; q += 4) {
+        const int32_t p0 = perm[q], p1 = perm[q + 1], p2 = perm[q + 2], p3 = perm[q + 3];
+        float x0[8], x1[8], x2[8], x3[8];
+        load8<P>(hc + (p0 / K) * ld, x0);
+        load8<P>(hc + (p1 / K) * ld, x1);
+        load8<P>(hc + (p2 / K) * ld, x2);
+        load8<P>(hc + (p3 / K) * ld, x3);
+        const float g0 = coef[p0], g1 = coef[p1], g2 = coef[p2], g3 = coef[p3];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[j] = fmaf(g3, x3[j], fmaf(g2, x2[j], fmaf(g1, x1[j], fmaf(g0, x0[j], acc[j]))));
+      }
+      for (; q < run_end; ++q) {
+        const int32_t p = perm[q];
+        float x[8];
+        load8<P>(hc + (p / K) * ld, x);
+        const float g = coef[p];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, x[j], acc[j]);
+      }
+      float* dst;
+      bool add = false;
+      if (bs < a)
+        dst = partial + (2 * c) * d + c0;
+      else if (be > e)
+        dst = partial + (2 * c + 1) * d + c0;
+      else {
+        dst = gw + static_cast<int64_t>(v) * d + c0;
+        add = acc_out;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j] = add ? dst[j] + acc[j] : acc[j];
+    }
+    pos = run_end;
+  }
+}
+
+// One workgroup per id: a bucket spanning chunks c0 < c1 sums the tail partial
+// of c0, the head partials of c0 + 1 .. c1 in order; an id with no pair gets
+// a zero row unless grad_W is accumulated.
+__global__ __launch_bounds__(256) void k_rs_fix(const int32_t* __restrict__ start, int64_t d,
+                                                int64_t seg, bool acc_out,
+                                                const float* __restrict__ partial,
+                                                float* __restrict__ gw) {
+  const int64_t v = blockIdx.x;
+  const int64_t bs = start[v], be = start[v + 1];
+  float* row = gw + v * d;
+  if (be == bs) {
+    if (!acc_out)
+      for (int64_t j = threadIdx.x; j < d; j += blockDim.x) row[j] = 0.f;
+    return;
+  }
+  const int64_t c0 = bs / seg, c1 = (be - 1) / seg;
+  if (c0 == c1) return;
+  for (int64_t j = threadIdx.x; j < d; j += blockDim.x) {
+    float s = partial[(2 * c0 + 1) * d + j];
+    for (int64_t c = c0 + 1; c <= c1; ++c) s += partial[(2 * c) * d + j];
+    row[j] = acc_out ? row[j] + s : s;
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+void launch_renorm_rows(bool coef_mode, const float* zk, const float* logit,
+                        const float* row_weight, const float* grad_loss, int64_t N, int K,
+                        float T, float* row_loss, float* coef, hipStream_t s) {
+  if (N <= 0) return;
+  ScopedTimer timer_(KID_RENORM_ROWS, s);
+  const unsigned grid = static_cast<unsigned>(ceil_div(N, kRowWaves));
+  if (coef_mode)
+    k_renorm_rows<true><<<grid, 64 * kRowWaves, 0, s>>>(zk, logit, row_weight, grad_loss, N, K, T,
+                                                         row_loss, coef);
+  else
+    k_renorm_rows<false><<<grid, 64 * kRowWaves, 0, s>>>(zk, logit, row_weight, grad_loss, N, K,
+                                                          T, row_loss, coef);
+}
+
+static unsigned column_threads(int64_t d) {
+  return static_cast<unsigned>(round_up(ceil_div(d, 8), 64));
+}
+
+void launch_renorm_grad_h(int dtype, const void* W, const int32_t* idx, const float* coef,
+                          int64_t N, int K, int64_t d, void* gh, hipStream_t s) {
+  if (N <= 0) return;
+  ScopedTimer timer_(KID_RENORM_GRAD_H, s);
+  const unsigned threads = column_threads(d);
+  const unsigned char* Wc = static_cast<const unsigned char*>(W);
+  unsigned char* out = static_cast<unsigned char*>(gh);
+  if (dtype == 1)
+    k_renorm_grad_h<BF16><<<static_cast<unsigned>(N), threads, 0, s>>>(Wc, idx, coef, K, d, out);
+  else
+    k_renorm_grad_h<F32><<<static_cast<unsigned>(N), threads, 0, s>>>(Wc, idx, coef, K, d, out);
+}
+
+void launch_renorm_grad_w(int dtype, const void* H, const int32_t* idx, const float* coef,
+                          int64_t N, int K, int64_t d, int64_t V, const RenormSortPlan& q,
+                          int32_t* hist, int32_t* total, int32_t* start, int32_t* perm,
+                          float* partial, bool acc_out, float* gw, hipStream_t s) {
+  const int64_t NK = N * K;
+  if (NK > 0) {
+    launch_fill_f32(reinterpret_cast<float*>(hist), q.nb * V, 0.0f, s);  // integer zero
+    {
+      ScopedTimer timer_(KID_RS_HIST, s);
+      const int64_t blocks = ceil_div(NK, 256) < 8192 ? ceil_div(NK, 256) : 8192;
+      k_rs_hist<<<static_cast<unsigned>(blocks), 256, 0, s>>>(idx, NK, q.rows_per_block * K, V,
+                                                              hist);
+    }
+    {
+      ScopedTimer timer_(KID_RS_SCAN, s);
+      k_rs_colscan<<<static_cast<unsigned>(ceil_div(V, 256)), 256, 0, s>>>(hist, q.nb, V, total);
+      k_rs_scan<<<1, 1024, 0, s>>>(total, V, start);
+    }
+    {
+      ScopedTimer timer_(KID_RS_PLACE, s);
+      k_rs_place<<<static_cast<unsigned>(q.nb), 256, 0, s>>>(idx, N, K, q.rows_per_block, V, hist,
+                                                             start, perm);
+    }
+    {
+      ScopedTimer timer_(KID_RS_CHUNKS, s);
+      const unsigned threads = column_threads(d);
+      const unsigned char* Hc = static_cast<const unsigned char*>(H);
+      if (dtype == 1)
+        k_rs_chunks<BF16><<<static_cast<unsigned>(q.nchunks), threads, 0, s>>>(
+            Hc, idx, coef, perm, start, NK, K, d, q.seg, acc_out, gw, partial);
+      else
+        k_rs_chunks<F32><<<static_cast<unsigned>(q.nchunks), threads, 0, s>>>(
+            Hc, idx, coef, perm, start, NK, K, d, q.seg, acc_out, gw, partial);
+    }
+  } else {
+    // no pairs: every bucket is empty
+    launch_fill_f32(reinterpret_cast<float*>(start), V + 1, 0.0f, s);
+  }
+  ScopedTimer timer_(KID_RS_FIX, s);
+  k_rs_fix<<<static_cast<unsigned>(V), 256, 0, s>>>(start, d, q.seg, acc_out, partial, gw);
+}
+
+}  // namespace fkl

@@ -26,6 +26,13 @@ enum KernelId : int32_t {
   KID_TOPK_COLLECT,
   KID_TOPK_FINAL,
   KID_MERGE_LSE,
+  KID_RENORM_ROWS,
+  KID_RENORM_GRAD_H,
+  KID_RS_HIST,
+  KID_RS_SCAN,
+  KID_RS_PLACE,
+  KID_RS_CHUNKS,
+  KID_RS_FIX,
   KID_COUNT
 };
 

@@ -98,6 +98,12 @@ _SIGNATURES = {
                                     _i32, _u32, _opt, _p, _sz, _p, _p, _p, _sz, _p]),
     "fkl_teacher_topk_ex": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _i64, _i32, _u32, _f32, _p,
                                    _p, _p, _p, _sz, _p]),
+    "fkl_renorm_workspace_size": (_i32, [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_sz),
+                                         ctypes.POINTER(_sz)]),
+    "fkl_renorm_forward": (_i32, [_p, _p, _p, _p, _f32, _i64, _i64, _i64, _i32, _i32, _u32, _p,
+                                  _p, _p, _p, _p, _sz, _p]),
+    "fkl_renorm_backward": (_i32, [_p, _p, _p, _p, _p, _p, _f32, _i64, _i64, _i64, _i32, _i32,
+                                   _u32, _p, _p, _p, _p, _sz, _p]),
     "fkl_timing_enable": (_i32, [_i32]),
     "fkl_timing_reset": (_i32, []),
     "fkl_timing_read": (_i32, [_i32, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]),
@@ -492,6 +498,85 @@ def fkl_teacher_topk_ex(hidden: torch.Tensor, weight: torch.Tensor, K: int, chun
     return idx, val, lse
 
 
+def fkl_renorm_workspace_size(N, d, V, K, dtype) -> tuple[int, int]:
+    """(forward, backward) workspace bytes of the student-renormalised loss."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    f, b = _sz(0), _sz(0)
+    _check(lib().fkl_renorm_workspace_size(N, d, V, K, code, ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
+
+
+@dataclass
+class RenormResult:
+    loss: torch.Tensor      # [] fp32
+    row_loss: torch.Tensor  # [N] fp32
+    topk_z: torch.Tensor    # [N, K] fp32 student logits at the cached ids
+
+
+def fkl_renorm_forward(hidden, weight, topk_idx, topk_logit, T: float, *,
+                       row_weight: torch.Tensor | None = None, validate: bool = False,
+                       workspace: torch.Tensor | None = None) -> RenormResult:
+    """Student-renormalised top-K loss (both softmaxes over the K cached
+    entries): fkl_renorm_forward of include/fkl.h."""
+    N, d = hidden.shape
+    V = weight.shape[0]
+    K = topk_idx.shape[1]
+    code = dtype_code(hidden.dtype)
+    _require(hidden, "hidden")
+    _require(weight, "weight", hidden.dtype)
+    _require(topk_idx, "topk_idx", torch.int32)
+    _require(topk_logit, "topk_logit", torch.float32)
+    if row_weight is not None:
+        _require(row_weight, "row_weight", torch.float32)
+    dev = hidden.device
+    fw, _ = fkl_renorm_workspace_size(N, d, V, K, code)
+    ws = workspace if workspace is not None else _workspace(fw, dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    row_loss = torch.empty(N, dtype=torch.float32, device=dev)
+    topk_z = torch.empty(N, K, dtype=torch.float32, device=dev)
+    flags = FKL_FLAG_VALIDATE_IDX if validate else 0
+    _check(lib().fkl_renorm_forward(_ptr(hidden), _ptr(weight), _ptr(topk_idx), _ptr(topk_logit),
+                                    float(T), N, d, V, K, code, flags, _ptr(row_weight),
+                                    _ptr(loss), _ptr(row_loss), _ptr(topk_z), _ptr(ws),
+                                    ws.numel(), _stream(dev)))
+    return RenormResult(loss, row_loss, topk_z)
+
+
+def fkl_renorm_backward(hidden, weight, topk_idx, topk_logit, T: float, *,
+                        topk_z: torch.Tensor | None = None,
+                        grad_loss: torch.Tensor | None = None,
+                        row_weight: torch.Tensor | None = None,
+                        grad_weight: torch.Tensor | None = None, accumulate: bool = False,
+                        validate: bool = False, workspace: torch.Tensor | None = None):
+    """Gradients of the student-renormalised loss: (grad_hidden [N, d] in the
+    input dtype, grad_weight [V, d] fp32)."""
+    N, d = hidden.shape
+    V = weight.shape[0]
+    K = topk_idx.shape[1]
+    code = dtype_code(hidden.dtype)
+    _require(hidden, "hidden")
+    _require(weight, "weight", hidden.dtype)
+    _require(topk_idx, "topk_idx", torch.int32)
+    _require(topk_logit, "topk_logit", torch.float32)
+    for t, name in ((topk_z, "topk_z"), (grad_loss, "grad_loss"), (row_weight, "row_weight")):
+        if t is not None:
+            _require(t, name, torch.float32)
+    dev = hidden.device
+    _, bw = fkl_renorm_workspace_size(N, d, V, K, code)
+    ws = workspace if workspace is not None else _workspace(bw, dev)
+    gh = torch.empty(N, d, dtype=hidden.dtype, device=dev)
+    gw = grad_weight if grad_weight is not None else torch.empty(V, d, dtype=torch.float32,
+                                                                 device=dev)
+    _require(gw, "grad_weight", torch.float32)
+    flags = (FKL_FLAG_ACCUMULATE_GRAD_W if accumulate else 0) | (
+        FKL_FLAG_VALIDATE_IDX if validate else 0)
+    _check(lib().fkl_renorm_backward(_ptr(hidden), _ptr(weight), _ptr(topk_idx),
+                                     _ptr(topk_logit), _ptr(topk_z), _ptr(grad_loss), float(T),
+                                     N, d, V, K, code, flags, _ptr(row_weight), _ptr(gh), _ptr(gw),
+                                     _ptr(ws), ws.numel(), _stream(dev)))
+    return gh, gw
+
+
 def fkl_timing_enable(on: bool) -> bool:
     """Turns per-kernel event timing on or off; returns the previous state."""
     return bool(lib().fkl_timing_enable(1 if on else 0))
@@ -574,6 +659,43 @@ class FusedChunkedKL(torch.autograd.Function):
                                      logits=z)
         return (gh.reshape(ctx.shape), gw.to(w.dtype), None, None, None, None, None, None, None,
                 None)
+
+
+class RenormTopKKL(torch.autograd.Function):
+    """Autograd wrapper of the student-renormalised loss: saves the gathered
+    student logits; the backward needs no vocabulary-wide work."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, topk_idx, topk_logit, T, row_weight):
+        shape = hidden.shape
+        h2 = hidden.reshape(-1, shape[-1]).contiguous()
+        N = h2.shape[0]
+        idx = topk_idx.reshape(N, -1).to(torch.int32).contiguous()
+        lg = topk_logit.reshape(N, -1).to(torch.float32).contiguous()
+        w = weight.contiguous()
+        rw = None if row_weight is None else row_weight.reshape(N).to(torch.float32).contiguous()
+        out = fkl_renorm_forward(h2, w, idx, lg, T, row_weight=rw)
+        ctx.save_for_backward(h2, w, idx, lg, out.topk_z, rw)
+        ctx.T, ctx.shape = T, shape
+        return out.loss
+
+    @staticmethod
+    @torch.autograd.function.once_differentiable
+    def backward(ctx, grad_loss):
+        g = grad_loss.to(torch.float32).reshape(()).contiguous()
+        h2, w, idx, lg, zk, rw = ctx.saved_tensors
+        gh, gw = fkl_renorm_backward(h2, w, idx, lg, ctx.T, topk_z=zk, grad_loss=g, row_weight=rw)
+        return gh.reshape(ctx.shape), gw.to(w.dtype), None, None, None, None
+
+
+def renorm_topk_kl(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Tensor,
+                   topk_logit: torch.Tensor, T: float = 1.0, *,
+                   row_weight: torch.Tensor | None = None) -> torch.Tensor:
+    """Sum over tokens of w_r T^2 KL(teacher || student) with both softmaxes
+    taken over the K cached entries of each token (entries with a -inf teacher
+    logit are padding). Shapes as fused_chunked_kl; no chunk parameter, since
+    nothing of size N x V is formed."""
+    return RenormTopKKL.apply(hidden, weight, topk_idx, topk_logit, float(T), row_weight)
 
 
 def choose_keep(N: int, d: int, V: int, K: int, dtype: torch.dtype, budget: int | None,

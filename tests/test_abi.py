@@ -286,3 +286,75 @@ def test_loss_options_validation():
     # ... but not at T = 1 (same softmax); these stop at the workspace check
     assert _bwd_ex(ctypes.byref(no_lse1), T=1.0, ws_bytes=16) == fkl.FKL_E_WORKSPACE
     assert _bwd_ex(ctypes.byref(ok), ws_bytes=16) == fkl.FKL_E_WORKSPACE
+
+
+# ------------------------------------------------ student-renormalised loss
+
+def test_renorm_workspace_is_linear_in_pairs_and_never_rows_times_vocab():
+    for N, d, V, K in ((32768, 3072, 128256, 100), (131072, 2880, 201088, 100), (300, 64, 999, 7)):
+        f, b = fkl.fkl_renorm_workspace_size(N, d, V, K, fkl.FKL_BF16)
+        NK = N * K
+        # forward: gathered logits + per-row losses
+        assert NK * 4 <= f <= NK * 4 + N * 4 + 4 * 256
+        # backward: coefficients, gathered logits, sorted pairs, per-id starts, at most 256 MiB
+        # of per-block id counters (or one block), and two d-wide partials per chunk of at least
+        # 256 sorted pairs, at most 4096 chunks beyond the first
+        counters = max(256 << 20, V * 4)
+        chunks = min(4097, NK // 256 + 1)
+        assert 3 * NK * 4 + (2 * V + 1) * 4 <= b
+        assert b <= 3 * NK * 4 + (2 * V + 1) * 4 + counters + chunks * 2 * d * 4 + 16 * 256
+        assert b < N * V * 2 / 4 or N < 4096
+
+
+def _rfwd(**over):
+    args = dict(hidden=A, weight=A, idx=A, logit=A, T=1.0, N=10, d=16, V=100, K=5,
+                dtype=fkl.FKL_BF16, flags=0, row_weight=None, loss=A, row_loss=None, topk_z=None,
+                ws=A, ws_bytes=1 << 40, stream=None)
+    args.update(over)
+    return fkl.lib().fkl_renorm_forward(*args.values())
+
+
+def _rbwd(**over):
+    args = dict(hidden=A, weight=A, idx=A, logit=A, topk_z=None, grad_loss=None, T=1.0, N=10,
+                d=16, V=100, K=5, dtype=fkl.FKL_BF16, flags=0, row_weight=None, gh=A, gw=A, ws=A,
+                ws_bytes=1 << 40, stream=None)
+    args.update(over)
+    return fkl.lib().fkl_renorm_backward(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(hidden=None), fkl.FKL_E_ARG),
+    (dict(loss=None), fkl.FKL_E_ARG),
+    (dict(hidden=A + 2), fkl.FKL_E_ARG),
+    (dict(row_weight=A + 2), fkl.FKL_E_ARG),
+    (dict(topk_z=A + 2), fkl.FKL_E_ARG),
+    (dict(T=0.0), fkl.FKL_E_ARG),
+    (dict(T=float("nan")), fkl.FKL_E_ARG),
+    (dict(K=0), fkl.FKL_E_ARG),
+    (dict(K=101), fkl.FKL_E_ARG),
+    (dict(K=1025, V=5000), fkl.FKL_E_UNSUPPORTED),
+    (dict(d=8200), fkl.FKL_E_UNSUPPORTED),
+    (dict(d=12), fkl.FKL_E_UNSUPPORTED),
+    (dict(N=1 << 22, K=1000, V=5000), fkl.FKL_E_UNSUPPORTED),
+    (dict(flags=1), fkl.FKL_E_ARG),
+    (dict(ws_bytes=16), fkl.FKL_E_WORKSPACE),
+])
+def test_renorm_forward_validation(over, code):
+    assert _rfwd(**over) == code
+    assert fkl.fkl_last_error() != ""
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(gh=None), fkl.FKL_E_ARG),
+    (dict(gw=None), fkl.FKL_E_ARG),
+    (dict(gw=A + 4), fkl.FKL_E_ARG),
+    (dict(grad_loss=A + 1), fkl.FKL_E_ARG),
+    (dict(logit=None), fkl.FKL_E_ARG),
+    (dict(T=-2.0), fkl.FKL_E_ARG),
+    (dict(flags=4), fkl.FKL_E_ARG),
+    (dict(K=2000, V=5000), fkl.FKL_E_UNSUPPORTED),
+    (dict(ws_bytes=1024), fkl.FKL_E_WORKSPACE),
+])
+def test_renorm_backward_validation(over, code):
+    assert _rbwd(**over) == code
+    assert fkl.fkl_last_error() != ""
