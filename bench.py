@@ -282,6 +282,150 @@ def run_teacher_topk(args, torch, fkl, synth, dev):
     print(json.dumps(result), flush=True)
 
 
+def cpu_baseline_renorm(inp, gpu_rows, budget_s: float):
+    """Time the fp64 oracle of the student-renormalised loss on a bounded
+    prefix of the rows (forward + backward of those rows) and compare them."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    w = inp["workload"]
+
+    def run(n):
+        t0 = time.perf_counter()
+        out = oracle.renorm_forward_backward(inp["hidden"][:n], inp["weight"], inp["topk_idx"][:n],
+                                             inp["topk_logit"][:n], w.T)
+        return out, time.perf_counter() - t0
+
+    _, t1 = run(64)
+    _, t2 = run(128)
+    per_row = max((t2 - t1) / 64, 1e-6)
+    fixed = max(t1 - 64 * per_row, 0.0)
+    n = int((budget_s - fixed) / per_row) // 64 * 64
+    n = max(64, min(w.N, n))
+    ref, t = run(n)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    errs = {"row_loss_rel_err": float(np.max(np.abs(gpu_rows["row_loss"][:n] - ref["row_loss"]) /
+                                             np.maximum(np.abs(ref["row_loss"]), 1.0))),
+            "grad_hidden_err_over_max": float(np.abs(gpu_rows["grad_hidden"][:n] -
+                                                     ref["grad_hidden"]).max() /
+                                              np.abs(ref["grad_hidden"]).max())}
+    tol = 1e-3 if w.dtype == "bf16" else 1e-5
+    gtol = 2e-2 if w.dtype == "bf16" else 1e-4
+    parity = {"rows": n, **errs,
+              "ok": bool(errs["row_loss_rel_err"] <= tol and
+                         errs["grad_hidden_err_over_max"] <= gtol)}
+    base = {"value": n / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {w.N} rows of {w.name}: the renormalised loss forward + "
+                      f"backward in fp64 (NumPy), {t:.1f} s; grad_W restricted to those rows"}
+    return base, parity
+
+
+def run_renorm(args, torch, fkl, synth, dev):
+    """Benchmark of the student-renormalised loss (fkl_renorm_forward + backward)."""
+    w = synth.WORKLOADS[args.workload]
+    log(f"[bench] generating {w.name}: N={w.N} d={w.d} V={w.V} K={w.K} T={w.T} {w.dtype}")
+    inp = synth.make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    h = torch.from_numpy(inp["hidden"]).to(dev).to(dt).contiguous()
+    W = torch.from_numpy(inp["weight"]).to(dev).to(dt).contiguous()
+    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    lg = torch.from_numpy(inp["topk_logit"]).to(dev)
+    torch.cuda.synchronize()
+    input_bytes = sum(t.numel() * t.element_size() for t in (h, W, idx, lg))
+    fw, bw = fkl.fkl_renorm_workspace_size(w.N, w.d, w.V, w.K, dt)
+    ws_f = torch.empty(fw, dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(bw, dtype=torch.uint8, device=dev)
+    gw = torch.empty(w.V, w.d, dtype=torch.float32, device=dev)
+
+    def step():
+        out = fkl.fkl_renorm_forward(h, W, idx, lg, w.T, workspace=ws_f)
+        gh, _ = fkl.fkl_renorm_backward(h, W, idx, lg, w.T, topk_z=out.topk_z, grad_weight=gw,
+                                        workspace=ws_b)
+        return out, gh
+
+    calibration_copy(args, torch, dev)
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    out, gh = step()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev)
+    gpu_rows = {"row_loss": out.row_loss.double().cpu().numpy(),
+                "grad_hidden": gh.double().cpu().numpy()}
+    del out, gh
+
+    log(f"[bench] timing {args.steps} steps")
+    fkl.fkl_timing_reset()
+    fkl.fkl_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fkl.fkl_timing_enable(False)
+    ktimes = fkl.kernel_times()
+    ms_step = elapsed / args.steps * 1e3
+    log(f"[bench] {ms_step:.2f} ms/step")
+    kernels = {k: {"launches_per_step": n / args.steps, "avg_ms": ms / n,
+                   "ms_per_step": ms / args.steps} for k, (n, ms) in ktimes.items()}
+    dom = max(ktimes, key=lambda k: ktimes[k][1])
+    n_launch, dom_ms = ktimes[dom]
+    avg_ms = dom_ms / n_launch
+    eb = 2 if w.dtype == "bf16" else 4
+    NK = w.N * w.K
+    # compulsory bytes per launch (every input byte once, every output byte once) and the
+    # bytes the kernel gathers (one weight or hidden row of d values per cached entry)
+    compulsory = {
+        "k_gather_dot": (w.V * w.d * eb + w.N * w.d * eb + NK * 8, NK * w.d * eb),
+        "k_renorm_grad_h": (w.V * w.d * eb + NK * 8 + w.N * w.d * eb, NK * w.d * eb),
+        "k_rs_chunks": (w.N * w.d * eb + NK * 12 + w.V * w.d * 4, NK * w.d * eb),
+    }
+    if dom in compulsory:
+        cb, gathered = compulsory[dom]
+        achieved = cb / (avg_ms * 1e-3) / 1e9
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                    "traffic": load_traffic(dom, w.name + "/renorm"), "bytes_per_launch": cb,
+                    "gathered_bytes_per_launch": gathered,
+                    "gathered_gbs": gathered / (avg_ms * 1e-3) / 1e9, "avg_launch_ms": avg_ms}
+    else:
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": None, "traffic": None, "avg_launch_ms": avg_ms}
+    if args.no_cpu_baseline:
+        base, parity = None, None
+    else:
+        log("[bench] oracle on the host (cpu_baseline and sampled parity)")
+        base, parity = cpu_baseline_renorm(inp, gpu_rows, args.cpu_seconds)
+    result = {
+        "metric": "student-renormalised top-K KL fwd+bwd tokens/s",
+        "value": w.N * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "N": w.N, "d": w.d, "V": w.V,
+                   "K": w.K, "T": w.T, "ids": w.ids, "loss": "student renormalised over K"},
+        "roofline": roofline,
+        "cpu_baseline": base,
+        "parity_sampled": parity,
+        "peak_hbm_gib": peak / 2**30,
+        "peak_hbm_path_gib": (peak - input_bytes) / 2**30,
+        "workspace_gib": (fw + bw) / 2**30,
+        "kernels": kernels,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def memory_sweep(args, torch, fkl, dev):
     """Peak HBM of one training step (inputs, outputs, workspaces, grad_W, autograd-saved
     tensors) through fused_chunked_kl at S in {4096 .. 65536} tokens, gpt-oss-20B
@@ -424,6 +568,9 @@ def main():
     ap.add_argument("--teacher-topk", action="store_true",
                     help="time the teacher top-K cache producer instead of the loss "
                          "(workload teacher_llama8b_32k unless --workload names a teacher one)")
+    ap.add_argument("--renorm", action="store_true",
+                    help="time the student-renormalised loss (both softmaxes over the K "
+                         "cached entries; no vocabulary GEMM) instead of the main loss")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="time hipBLASLt (torch.mm) on the plain contractions of one step "
                          "(8NdV flops, no exp/LSE/gather) instead of the library")
@@ -458,6 +605,9 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.vendor_gemm:
         vendor_gemm_step(args, torch, w, dev)
+        return
+    if args.renorm:
+        run_renorm(args, torch, fkl, synth, dev)
         return
     log(f"[bench] generating {w.name}: N={w.N} d={w.d} V={w.V} K={w.K} T={w.T} "
         f"chunk={w.chunk} {w.dtype}")

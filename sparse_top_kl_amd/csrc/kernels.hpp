@@ -128,6 +128,7 @@ void launch_validate_idx(const int32_t* idx, int64_t N, int K, int64_t V, bool a
 // ---- student-renormalised loss (renorm.hip)
 constexpr int kRenormMaxK = 1024;  // cached entries per row
 constexpr int64_t kRenormMaxD = 8192;  // hidden size (eight columns per thread, 1024 threads)
+constexpr int kRenormMaxSeg = 2048;    // sorted pairs per grad_W chunk
 
 // grad_W of the renormalised loss: a stable counting sort of the N * K (row,
 // entry) pairs by id in nb blocks of rows_per_block rows, then sums over

@@ -19,7 +19,7 @@
 //   k_renorm_rows    one wave per row: the two K-entry softmaxes -> row loss
 //                    (forward) or the K coefficients G_r. (backward)
 //   k_renorm_grad_h  one workgroup per row: sum_k G_rk W[idx_rk] (16-byte
-//                    loads of the K weight rows, four in flight per lane)
+//                    loads of the K weight rows, eight in flight per lane)
 //   grad_W without float atomics, bitwise deterministic:
 //   k_rs_hist        per block of rows, the count of each id (integer atomics)
 //   k_rs_colscan     per id, exclusive prefix of its counts over the blocks
@@ -185,16 +185,14 @@ __global__ __launch_bounds__(1024) void k_renorm_grad_h(const unsigned char* __r
   const unsigned char* wc = W + c0 * P::kBytes;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   int k = 0;
-  for (; k + 4 <= K; k += 4) {
-    float x0[8], x1[8], x2[8], x3[8];
-    load8<P>(wc + sid[k] * ld, x0);
-    load8<P>(wc + sid[k + 1] * ld, x1);
-    load8<P>(wc + sid[k + 2] * ld, x2);
-    load8<P>(wc + sid[k + 3] * ld, x3);
-    const float g0 = sg[k], g1 = sg[k + 1], g2 = sg[k + 2], g3 = sg[k + 3];
+  for (; k + 8 <= K; k += 8) {
+    float x[8][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      acc[e] = fmaf(g3, x3[e], fmaf(g2, x2[e], fmaf(g1, x1[e], fmaf(g0, x0[e], acc[e]))));
+    for (int u = 0; u < 8; ++u) load8<P>(wc + sid[k + u] * ld, x[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(sg[k + u], x[u][e], acc[e]);
   }
   for (; k < K; ++k) {
     float x[8];
@@ -308,65 +306,74 @@ __global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ id
   }
 }
 
-// Chunk c covers sorted positions [c * seg, min(NK, (c + 1) * seg)). For each
-// run of one id v inside it, the sum of coef[p] * H[p / K] over the run's pairs
-// p in sorted order goes to grad_W[v] (written, or added with ACC) when the
-// chunk holds v's whole bucket, else to partial[c][0] (the bucket began in an
-// earlier chunk) or partial[c][1] (it begins here and continues).
+// Chunk c covers sorted positions [c * seg, min(NK, (c + 1) * seg)), seg <=
+// kRenormMaxSeg. Its pairs' rows, coefficients and ids are first staged in LDS
+// (one coalesced pass, the gathers all in flight at once). For each run of one
+// id v inside it, the sum of coef[p] * H[p / K] over the run's pairs p in sorted
+// order goes to grad_W[v] (written, or added with ACC) when the chunk holds v's
+// whole bucket, else to partial[c][0] (the bucket began in an earlier chunk) or
+// partial[c][1] (it begins here and continues).
 template <class P>
 __global__ __launch_bounds__(1024) void k_rs_chunks(
     const unsigned char* __restrict__ H, const int32_t* __restrict__ idx,
     const float* __restrict__ coef, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ start, int64_t NK, int K, int64_t d, int64_t seg, bool acc_out,
     float* __restrict__ gw, float* __restrict__ partial) {
+  __shared__ int32_t srow[kRenormMaxSeg];
+  __shared__ int32_t sv[kRenormMaxSeg];
+  __shared__ float sc[kRenormMaxSeg];
   const int64_t c = blockIdx.x;
   const int64_t a = c * seg, e = a + seg < NK ? a + seg : NK;
+  const int n = static_cast<int>(e - a);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int32_t p = perm[a + i];
+    srow[i] = p / K;
+    sv[i] = idx[p];
+    sc[i] = coef[p];
+  }
+  __syncthreads();
   const int64_t c0 = static_cast<int64_t>(threadIdx.x) * 8;
-  const bool mine = c0 < d;
+  if (c0 >= d) return;
   const int64_t ld = d * P::kBytes;
   const unsigned char* hc = H + c0 * P::kBytes;
-  int64_t pos = a;
-  while (pos < e) {
-    const int32_t v = idx[perm[pos]];
+  int i = 0;
+  while (i < n) {
+    const int32_t v = sv[i];
     const int64_t bs = start[v], be = start[v + 1];
-    const int64_t run_end = be < e ? be : e;
+    const int run_end = static_cast<int>((be < e ? be : e) - a);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (mine) {
-      int64_t q = pos;
-      for (; q + 4 <= run_end; q += 4) {
-        const int32_t p0 = perm[q], p1 = perm[q + 1], p2 = perm[q + 2], p3 = perm[q + 3];
-        float x0[8], x1[8], x2[8], x3[8];
-        load8<P>(hc + (p0 / K) * ld, x0);
-        load8<P>(hc + (p1 / K) * ld, x1);
-        load8<P>(hc + (p2 / K) * ld, x2);
-        load8<P>(hc + (p3 / K) * ld, x3);
-        const float g0 = coef[p0], g1 = coef[p1], g2 = coef[p2], g3 = coef[p3];
+    int q = i;
+    for (; q + 8 <= run_end; q += 8) {
+      float x[8][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          acc[j] = fmaf(g3, x3[j], fmaf(g2, x2[j], fmaf(g1, x1[j], fmaf(g0, x0[j], acc[j]))));
-      }
-      for (; q < run_end; ++q) {
-        const int32_t p = perm[q];
-        float x[8];
-        load8<P>(hc + (p / K) * ld, x);
-        const float g = coef[p];
+      for (int u = 0; u < 8; ++u) load8<P>(hc + srow[q + u] * ld, x[u]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, x[j], acc[j]);
-      }
-      float* dst;
-      bool add = false;
-      if (bs < a)
-        dst = partial + (2 * c) * d + c0;
-      else if (be > e)
-        dst = partial + (2 * c + 1) * d + c0;
-      else {
-        dst = gw + static_cast<int64_t>(v) * d + c0;
-        add = acc_out;
-      }
+      for (int u = 0; u < 8; ++u) {
+        const float g = sc[q + u];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dst[j] = add ? dst[j] + acc[j] : acc[j];
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, x[u][j], acc[j]);
+      }
     }
-    pos = run_end;
+    for (; q < run_end; ++q) {
+      float x[8];
+      load8<P>(hc + srow[q] * ld, x);
+      const float g = sc[q];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, x[j], acc[j]);
+    }
+    float* dst;
+    bool add = false;
+    if (bs < a)
+      dst = partial + (2 * c) * d + c0;
+    else if (be > e)
+      dst = partial + (2 * c + 1) * d + c0;
+    else {
+      dst = gw + static_cast<int64_t>(v) * d + c0;
+      add = acc_out;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[j] = add ? dst[j] + acc[j] : acc[j];
+    i = run_end;
   }
 }
 

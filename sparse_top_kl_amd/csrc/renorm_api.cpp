@@ -15,7 +15,7 @@ namespace {
 
 // Sizes of the pair sort: blocks of rows whose per-id counters take at most
 // 256 MiB in all (and at least 16 rows each), chunks of sorted pairs sized for
-// about 4096 workgroups.
+// about 4096 workgroups (256 to 2048 pairs each).
 fkl::RenormSortPlan sort_plan(int64_t N, int32_t K, int64_t V) {
   fkl::RenormSortPlan q{};
   const int64_t nn = N > 0 ? N : 1;
@@ -28,6 +28,7 @@ fkl::RenormSortPlan sort_plan(int64_t N, int32_t K, int64_t V) {
   const int64_t NK = N * K;
   q.seg = fkl::round_up(fkl::ceil_div(NK > 0 ? NK : 1, 4096), 64);
   if (q.seg < 256) q.seg = 256;
+  if (q.seg > fkl::kRenormMaxSeg) q.seg = fkl::kRenormMaxSeg;
   q.nchunks = NK > 0 ? fkl::ceil_div(NK, q.seg) : 0;
   return q;
 }

@@ -297,10 +297,10 @@ def test_renorm_workspace_is_linear_in_pairs_and_never_rows_times_vocab():
         # forward: gathered logits + per-row losses
         assert NK * 4 <= f <= NK * 4 + N * 4 + 4 * 256
         # backward: coefficients, gathered logits, sorted pairs, per-id starts, at most 256 MiB
-        # of per-block id counters (or one block), and two d-wide partials per chunk of at least
-        # 256 sorted pairs, at most 4096 chunks beyond the first
+        # of per-block id counters (or one block), and two d-wide partials per chunk of 256 to
+        # 2048 sorted pairs, about 4096 chunks unless the 2048 cap needs more
         counters = max(256 << 20, V * 4)
-        chunks = min(4097, NK // 256 + 1)
+        chunks = max(min(4097, NK // 256 + 1), NK // 2048 + 1)
         assert 3 * NK * 4 + (2 * V + 1) * 4 <= b
         assert b <= 3 * NK * 4 + (2 * V + 1) * 4 + counters + chunks * 2 * d * 4 + 16 * 256
         assert b < N * V * 2 / 4 or N < 4096
