@@ -133,8 +133,26 @@ constexpr int kRenormMaxSeg = 2048;    // sorted pairs per grad_W chunk
 // grad_W of the renormalised loss: a stable counting sort of the N * K (row,
 // entry) pairs by id in nb blocks of rows_per_block rows, then sums over
 // chunks of seg sorted pairs.
+constexpr int32_t kRenormHotCap = 2048;  // ids summed by the dense product (at most)
+constexpr int32_t kRenormHotMin = 64;    // pairs an id needs to be one of them
+
 struct RenormSortPlan {
   int64_t nb, rows_per_block, seg, nchunks;
+  int64_t hot_max;   // ids the dense product can take: one round of 256 x 256 tiles
+  int64_t hot_rows;  // rows per dense-product block
+};
+// Workspace arrays of launch_renorm_grad_w.
+struct RenormBuffers {
+  int32_t* hist;        // [nb * V] per-block id counters
+  int32_t* total;       // [V] pairs per id
+  int32_t* start;       // [V + 1] cold bucket starts
+  int32_t* perm;        // [N * K] sorted cold pairs
+  int32_t* slot;        // [V] hot slot or -1
+  int32_t* hot_ids;     // [hot_max]
+  int32_t* info;        // [4] number of hot ids
+  float* partial;       // [2 * nchunks * d] chunk partials
+  unsigned char* hot_c; // [hot_rows * hot_max] coefficients, input dtype
+  float* hot_prod;      // [hot_max * d] C^T H
 };
 
 // Forward (coef_mode false): row_loss[r] = w_r T^2 KL over the row's cached
@@ -145,11 +163,9 @@ void launch_renorm_rows(bool coef_mode, const float* zk, const float* logit,
 // grad_hidden[r] = sum_k coef[r][k] W[idx[r][k]] in the input dtype.
 void launch_renorm_grad_h(int dtype, const void* W, const int32_t* idx, const float* coef,
                           int64_t N, int K, int64_t d, void* gh, hipStream_t s);
-// grad_W[v] (=, or += with acc_out) sum over pairs with id v of coef * H[row];
-// hist [nb * V], total [V], start [V + 1], perm [N * K], partial [2 * nchunks * d].
+// grad_W[v] (=, or += with acc_out) sum over pairs with id v of coef * H[row].
 void launch_renorm_grad_w(int dtype, const void* H, const int32_t* idx, const float* coef,
                           int64_t N, int K, int64_t d, int64_t V, const RenormSortPlan& q,
-                          int32_t* hist, int32_t* total, int32_t* start, int32_t* perm,
-                          float* partial, bool acc_out, float* gw, hipStream_t s);
+                          const RenormBuffers& b, bool acc_out, float* gw, hipStream_t s);
 
 }  // namespace fkl

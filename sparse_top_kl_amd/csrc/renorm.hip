@@ -23,15 +23,25 @@
 //   grad_W without float atomics, bitwise deterministic:
 //   k_rs_hist        per block of rows, the count of each id (integer atomics)
 //   k_rs_colscan     per id, exclusive prefix of its counts over the blocks
-//   k_rs_scan        exclusive prefix over ids of the totals: bucket starts
-//   k_rs_place       per block, its rows in order: each pair (r, k) goes to
-//                    start[v] + (pairs of id v in earlier rows) + (copies of v
-//                    earlier in row r): a stable counting sort by id
+//   k_rs_hot         picks the frequent ("hot") ids: count >= tau, tau the
+//                    smallest power of two >= kRenormHotMin that leaves at
+//                    most hot_max of them (as many as one round of 256 x 256
+//                    product tiles takes); gives each a slot, and the
+//                    exclusive prefix over the other ("cold") ids of their
+//                    counts: bucket starts of the cold pairs
+//   hot ids, a dense product: k_rs_hot_coef scatters each row's hot
+//   coefficients into C [rows x hot_max] (copies of one id in a row
+//   summed in entry order), k_grad_w (the loss's MFMA kernel) forms C^T H,
+//   and k_rs_hot_rows copies each hot id's row into grad_W
+//   cold ids, a sort:
+//   k_rs_place       per block, its rows in order: each cold pair (r, k) goes
+//                    to start[v] + (pairs of id v in earlier rows) + (copies of
+//                    v earlier in row r): a stable counting sort by id
 //   k_rs_chunks      fixed chunks of the sorted pairs: the sum of G h over each
 //                    run of one id, written to grad_W when the chunk holds the
 //                    whole bucket, else to the chunk's head or tail partial
-//   k_rs_fix         per id whose bucket crosses chunks: its partials in chunk
-//                    order; ids with no pair get a zero row
+//   k_rs_fix         per cold id whose bucket crosses chunks: its partials in
+//                    chunk order; ids with no pair get a zero row
 #include <math.h>
 
 #include "device_common.hpp"
@@ -227,33 +237,88 @@ __global__ __launch_bounds__(256) void k_rs_colscan(int32_t* __restrict__ hist, 
   total[v] = acc;
 }
 
-// start[v] = sum of total[v'] for v' < v, start[V] = the grand total. One
-// workgroup of 1024 threads, each owning a contiguous segment of ids.
-__global__ __launch_bounds__(1024) void k_rs_scan(const int32_t* __restrict__ total, int64_t V,
-                                                  int32_t* __restrict__ start) {
-  __shared__ int32_t wsum[16];
+// Hot ids and the cold bucket starts, one workgroup of 1024 threads, each
+// owning a contiguous segment of ids. tau = the smallest power of two >=
+// hot_min with at most hot_max ids of count >= tau (no id is hot when even
+// the largest power of two leaves more). slot[v] = the hot id's index (in id
+// order) or -1, hot_ids[slot] = v, info[0] = the number of hot ids;
+// start[v] = sum of the counts of cold ids below v, start[V] = the number of
+// cold pairs.
+__global__ __launch_bounds__(1024) void k_rs_hot(const int32_t* __restrict__ total, int64_t V,
+                                                 int32_t hot_min, int32_t hot_max,
+                                                 int32_t* __restrict__ slot,
+                                                 int32_t* __restrict__ hot_ids,
+                                                 int32_t* __restrict__ info,
+                                                 int32_t* __restrict__ start) {
+  __shared__ int32_t bins[32];
+  __shared__ int32_t s_tau;
+  __shared__ int32_t wsum[16][2];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  if (t < 32) bins[t] = 0;
+  __syncthreads();
   const int64_t seg = (V + 1023) / 1024;
   const int64_t a = t * seg, e = a + seg < V ? a + seg : V;
-  int32_t s = 0;
-  for (int64_t v = a; v < e; ++v) s += total[v];
-  // inclusive scan of s over the workgroup
-  int32_t x = s;
+  for (int64_t v = a; v < e; ++v) {
+    const int32_t c = total[v];
+    if (c >= hot_min) atomicAdd(&bins[31 - __clz(c)], 1);
+  }
+  __syncthreads();
+  if (t == 0) {
+    // ge = ids (of count >= hot_min) whose count is >= 2^b
+    int32_t tau = 0x7fffffff, ge = bins[31];
+    for (int b = 30; b >= 0; --b) {
+      ge += bins[b];
+      if (ge > hot_max) break;
+      const int32_t lo = int32_t(1) << b;
+      tau = lo < hot_min ? hot_min : lo;
+      if (lo <= hot_min) break;
+    }
+    s_tau = tau;
+  }
+  __syncthreads();
+  const int32_t tau = s_tau;
+  int32_t nh = 0, nc = 0;
+  for (int64_t v = a; v < e; ++v) {
+    const int32_t c = total[v];
+    if (c >= tau) ++nh; else nc += c;
+  }
+  // exclusive prefixes of (hot count, cold pairs) over the workgroup
+  int32_t xh = nh, xc = nc;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
+    const int32_t yh = __shfl_up(xh, o), yc = __shfl_up(xc, o);
+    if (lane >= o) {
+      xh += yh;
+      xc += yc;
+    }
   }
-  if (lane == 63) wsum[wv] = x;
+  if (lane == 63) {
+    wsum[wv][0] = xh;
+    wsum[wv][1] = xc;
+  }
   __syncthreads();
-  int32_t before = 0;
-  for (int i = 0; i < wv; ++i) before += wsum[i];
-  int32_t run = before + x - s;  // exclusive prefix of this thread's segment
-  for (int64_t v = a; v < e; ++v) {
-    start[v] = run;
-    run += total[v];
+  int32_t bh = 0, bc = 0;
+  for (int i = 0; i < wv; ++i) {
+    bh += wsum[i][0];
+    bc += wsum[i][1];
   }
-  if (t == 1023) start[V] = before + x;
+  int32_t h = bh + xh - nh, run = bc + xc - nc;
+  for (int64_t v = a; v < e; ++v) {
+    const int32_t c = total[v];
+    start[v] = run;
+    if (c >= tau) {
+      slot[v] = h;
+      hot_ids[h] = static_cast<int32_t>(v);
+      ++h;
+    } else {
+      slot[v] = -1;
+      run += c;
+    }
+  }
+  if (t == 1023) {
+    start[V] = bc + xc;
+    info[0] = bh + xh;
+  }
 }
 
 // Stable placement: block b walks its rows in order; within a row each id's
@@ -263,6 +328,7 @@ __global__ __launch_bounds__(1024) void k_rs_scan(const int32_t* __restrict__ to
 // copies in the row).
 __global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ idx, int64_t N,
                                                   int K, int64_t rows_per_block, int64_t V,
+                                                  const int32_t* __restrict__ slot,
                                                   int32_t* __restrict__ hist,
                                                   const int32_t* __restrict__ start,
                                                   int32_t* __restrict__ perm) {
@@ -275,7 +341,10 @@ __global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ id
   int32_t* cur = hist + b * V;
   const int t = threadIdx.x;
   for (int64_t r = r0; r < r1; ++r) {
-    for (int k = t; k < K; k += 256) sid[k] = idx[r * K + k];
+    for (int k = t; k < K; k += 256) {
+      const int32_t v = idx[r * K + k];
+      sid[k] = slot[v] < 0 ? v : -1;  // hot pairs take no part in the sort
+    }
     __syncthreads();
     int dup[kPer], first[kPer];
 #pragma unroll
@@ -283,7 +352,7 @@ __global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ id
       const int k = t + 256 * j;
       dup[j] = 0;
       first[j] = k;
-      if (k < K) {
+      if (k < K && sid[k] >= 0) {
         const int32_t v = sid[k];
         int mult = 0, fst = -1;
         for (int k2 = 0; k2 < K; ++k2) {
@@ -300,7 +369,8 @@ __global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ id
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int k = t + 256 * j;
-      if (k < K) perm[start[sid[k]] + sbase[first[j]] + dup[j]] = static_cast<int32_t>(r * K + k);
+      if (k < K && sid[k] >= 0)
+        perm[start[sid[k]] + sbase[first[j]] + dup[j]] = static_cast<int32_t>(r * K + k);
     }
     __syncthreads();
   }
@@ -317,13 +387,15 @@ template <class P>
 __global__ __launch_bounds__(1024) void k_rs_chunks(
     const unsigned char* __restrict__ H, const int32_t* __restrict__ idx,
     const float* __restrict__ coef, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ start, int64_t NK, int K, int64_t d, int64_t seg, bool acc_out,
+    const int32_t* __restrict__ start, int64_t V, int K, int64_t d, int64_t seg, bool acc_out,
     float* __restrict__ gw, float* __restrict__ partial) {
   __shared__ int32_t srow[kRenormMaxSeg];
+  const int64_t NK = start[V];  // sorted (cold) pairs; chunks past them have nothing to do
   __shared__ int32_t sv[kRenormMaxSeg];
   __shared__ float sc[kRenormMaxSeg];
   const int64_t c = blockIdx.x;
   const int64_t a = c * seg, e = a + seg < NK ? a + seg : NK;
+  if (a >= NK) return;
   const int n = static_cast<int>(e - a);
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int32_t p = perm[a + i];
@@ -380,11 +452,13 @@ __global__ __launch_bounds__(1024) void k_rs_chunks(
 // One workgroup per id: a bucket spanning chunks c0 < c1 sums the tail partial
 // of c0, the head partials of c0 + 1 .. c1 in order; an id with no pair gets
 // a zero row unless grad_W is accumulated.
-__global__ __launch_bounds__(256) void k_rs_fix(const int32_t* __restrict__ start, int64_t d,
+__global__ __launch_bounds__(256) void k_rs_fix(const int32_t* __restrict__ start,
+                                                const int32_t* __restrict__ slot, int64_t d,
                                                 int64_t seg, bool acc_out,
                                                 const float* __restrict__ partial,
                                                 float* __restrict__ gw) {
   const int64_t v = blockIdx.x;
+  if (slot[v] >= 0) return;  // a hot id: its row comes from the dense product
   const int64_t bs = start[v], be = start[v + 1];
   float* row = gw + v * d;
   if (be == bs) {
@@ -399,6 +473,50 @@ __global__ __launch_bounds__(256) void k_rs_fix(const int32_t* __restrict__ star
     for (int64_t c = c0 + 1; c <= c1; ++c) s += partial[(2 * c) * d + j];
     row[j] = acc_out ? row[j] + s : s;
   }
+}
+
+// Rows [r0, r0 + nrows): C[r - r0][slot[v]] = sum of coef[r][k] over the
+// entries k of row r with hot id v, in entry order (one wave per row; C is
+// zero elsewhere, filled beforehand; row pitch `pitch` elements).
+template <class P>
+__global__ __launch_bounds__(256) void k_rs_hot_coef(const int32_t* __restrict__ idx,
+                                                     const float* __restrict__ coef,
+                                                     const int32_t* __restrict__ slot, int64_t r0,
+                                                     int64_t nrows, int K, int64_t pitch,
+                                                     unsigned char* __restrict__ C) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rl = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (rl >= nrows) return;
+  const int32_t* ir = idx + (r0 + rl) * K;
+  const float* cr = coef + (r0 + rl) * K;
+  for (int k = lane; k < K; k += 64) {
+    const int32_t v = ir[k];
+    const int32_t sl = slot[v];
+    if (sl < 0) continue;
+    bool first = true;
+    for (int k2 = 0; k2 < k && first; ++k2) first = ir[k2] != v;
+    if (!first) continue;
+    float g = 0.f;
+    for (int k2 = k; k2 < K; ++k2)
+      if (ir[k2] == v) g += cr[k2];
+    unsigned char* dst = C + (rl * pitch + sl) * P::kBytes;
+    if constexpr (P::kBytes == 2)
+      *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16_rne(g);
+    else
+      *reinterpret_cast<float*>(dst) = g;
+  }
+}
+
+// grad_W[hot_ids[j]] (=, or += with acc_out) prod[j] for j < info[0].
+__global__ __launch_bounds__(256) void k_rs_hot_rows(const int32_t* __restrict__ hot_ids,
+                                                     const int32_t* __restrict__ info,
+                                                     const float* __restrict__ prod, int64_t d,
+                                                     bool acc_out, float* __restrict__ gw) {
+  const int64_t j = blockIdx.x;
+  if (j >= info[0]) return;
+  float* row = gw + static_cast<int64_t>(hot_ids[j]) * d;
+  const float* src = prod + j * d;
+  for (int64_t c = threadIdx.x; c < d; c += blockDim.x) row[c] = acc_out ? row[c] + src[c] : src[c];
 }
 
 // ------------------------------------------------------------------ launchers
@@ -436,26 +554,28 @@ void launch_renorm_grad_h(int dtype, const void* W, const int32_t* idx, const fl
 
 void launch_renorm_grad_w(int dtype, const void* H, const int32_t* idx, const float* coef,
                           int64_t N, int K, int64_t d, int64_t V, const RenormSortPlan& q,
-                          int32_t* hist, int32_t* total, int32_t* start, int32_t* perm,
-                          float* partial, bool acc_out, float* gw, hipStream_t s) {
+                          const RenormBuffers& b, bool acc_out, float* gw, hipStream_t s) {
   const int64_t NK = N * K;
+  const int64_t eb = dtype == 1 ? 2 : 4;
   if (NK > 0) {
-    launch_fill_f32(reinterpret_cast<float*>(hist), q.nb * V, 0.0f, s);  // integer zero
+    launch_fill_f32(reinterpret_cast<float*>(b.hist), q.nb * V, 0.0f, s);  // integer zero
     {
       ScopedTimer timer_(KID_RS_HIST, s);
       const int64_t blocks = ceil_div(NK, 256) < 8192 ? ceil_div(NK, 256) : 8192;
       k_rs_hist<<<static_cast<unsigned>(blocks), 256, 0, s>>>(idx, NK, q.rows_per_block * K, V,
-                                                              hist);
+                                                              b.hist);
     }
     {
       ScopedTimer timer_(KID_RS_SCAN, s);
-      k_rs_colscan<<<static_cast<unsigned>(ceil_div(V, 256)), 256, 0, s>>>(hist, q.nb, V, total);
-      k_rs_scan<<<1, 1024, 0, s>>>(total, V, start);
+      k_rs_colscan<<<static_cast<unsigned>(ceil_div(V, 256)), 256, 0, s>>>(b.hist, q.nb, V,
+                                                                          b.total);
+      k_rs_hot<<<1, 1024, 0, s>>>(b.total, V, kRenormHotMin, static_cast<int32_t>(q.hot_max),
+                                   b.slot, b.hot_ids, b.info, b.start);
     }
     {
       ScopedTimer timer_(KID_RS_PLACE, s);
-      k_rs_place<<<static_cast<unsigned>(q.nb), 256, 0, s>>>(idx, N, K, q.rows_per_block, V, hist,
-                                                             start, perm);
+      k_rs_place<<<static_cast<unsigned>(q.nb), 256, 0, s>>>(idx, N, K, q.rows_per_block, V,
+                                                             b.slot, b.hist, b.start, b.perm);
     }
     {
       ScopedTimer timer_(KID_RS_CHUNKS, s);
@@ -463,17 +583,41 @@ void launch_renorm_grad_w(int dtype, const void* H, const int32_t* idx, const fl
       const unsigned char* Hc = static_cast<const unsigned char*>(H);
       if (dtype == 1)
         k_rs_chunks<BF16><<<static_cast<unsigned>(q.nchunks), threads, 0, s>>>(
-            Hc, idx, coef, perm, start, NK, K, d, q.seg, acc_out, gw, partial);
+            Hc, idx, coef, b.perm, b.start, V, K, d, q.seg, acc_out, gw, b.partial);
       else
         k_rs_chunks<F32><<<static_cast<unsigned>(q.nchunks), threads, 0, s>>>(
-            Hc, idx, coef, perm, start, NK, K, d, q.seg, acc_out, gw, partial);
+            Hc, idx, coef, b.perm, b.start, V, K, d, q.seg, acc_out, gw, b.partial);
     }
   } else {
-    // no pairs: every bucket is empty
-    launch_fill_f32(reinterpret_cast<float*>(start), V + 1, 0.0f, s);
+    // no pairs: every bucket is empty and no id is hot
+    launch_fill_f32(reinterpret_cast<float*>(b.start), V + 1, 0.0f, s);
+    launch_fill_f32(reinterpret_cast<float*>(b.slot), V, __builtin_bit_cast(float, -1), s);
   }
-  ScopedTimer timer_(KID_RS_FIX, s);
-  k_rs_fix<<<static_cast<unsigned>(V), 256, 0, s>>>(start, d, q.seg, acc_out, partial, gw);
+  {
+    ScopedTimer timer_(KID_RS_FIX, s);
+    k_rs_fix<<<static_cast<unsigned>(V), 256, 0, s>>>(b.start, b.slot, d, q.seg, acc_out,
+                                                      b.partial, gw);
+  }
+  if (NK == 0) return;
+  // hot ids: C^T H over row blocks of q.hot_rows rows, then the rows into grad_W
+  for (int64_t r0 = 0; r0 < N; r0 += q.hot_rows) {
+    const int64_t nr = N - r0 < q.hot_rows ? N - r0 : q.hot_rows;
+    launch_fill_f32(reinterpret_cast<float*>(b.hot_c), nr * q.hot_max * eb / 4, 0.0f, s);
+    {
+      ScopedTimer timer_(KID_RS_HOT, s);
+      const unsigned grid = static_cast<unsigned>(ceil_div(nr, 4));
+      if (dtype == 1)
+        k_rs_hot_coef<BF16><<<grid, 256, 0, s>>>(idx, coef, b.slot, r0, nr, K, q.hot_max,
+                                                 b.hot_c);
+      else
+        k_rs_hot_coef<F32><<<grid, 256, 0, s>>>(idx, coef, b.slot, r0, nr, K, q.hot_max, b.hot_c);
+    }
+    launch_grad_w(dtype, b.hot_c, q.hot_max, H, d, 0, q.hot_max, q.hot_max, r0, nr, r0 > 0,
+                  b.hot_prod, s);
+  }
+  ScopedTimer timer_(KID_RS_HOT, s);
+  k_rs_hot_rows<<<static_cast<unsigned>(q.hot_max), 256, 0, s>>>(b.hot_ids, b.info, b.hot_prod,
+                                                                 d, acc_out, gw);
 }
 
 }  // namespace fkl

@@ -15,8 +15,9 @@ namespace {
 
 // Sizes of the pair sort: blocks of rows whose per-id counters take at most
 // 256 MiB in all (and at least 16 rows each), chunks of sorted pairs sized for
-// about 4096 workgroups (256 to 2048 pairs each).
-fkl::RenormSortPlan sort_plan(int64_t N, int32_t K, int64_t V) {
+// about 4096 workgroups (256 to 2048 pairs each); rows per block of the hot
+// ids' dense product.
+fkl::RenormSortPlan sort_plan(int64_t N, int64_t d, int32_t K, int64_t V, int64_t eb) {
   fkl::RenormSortPlan q{};
   const int64_t nn = N > 0 ? N : 1;
   int64_t max_nb = (int64_t(256) << 20) / (V * 4);
@@ -30,6 +31,20 @@ fkl::RenormSortPlan sort_plan(int64_t N, int32_t K, int64_t V) {
   if (q.seg < 256) q.seg = 256;
   if (q.seg > fkl::kRenormMaxSeg) q.seg = fkl::kRenormMaxSeg;
   q.nchunks = NK > 0 ? fkl::ceil_div(NK, q.seg) : 0;
+  // The dense product's output is hot_max x d. An id costs the product a full
+  // column, 2 N d flops (~0.17 us at 32K x 3072), and the sorted walk one
+  // d-wide row read per pair (~1.2 ns): the break-even is ~140 pairs, which on
+  // Zipf ids of a 128K vocabulary the ~2000 most frequent ids reach. So at most
+  // 2048 ids, and no more than one round of 256 x 256 tiles on the 256 CUs
+  // (the product's time is set by its contraction over rows up to one round).
+  const int64_t d_tiles = fkl::ceil_div(d, 256);
+  q.hot_max = (256 / d_tiles) * 256;
+  if (q.hot_max < 256) q.hot_max = 256;
+  if (q.hot_max > fkl::kRenormHotCap) q.hot_max = fkl::kRenormHotCap;
+  // row blocks of the product: 256 MiB of hot coefficients at most, equal sizes
+  const int64_t max_rows = (int64_t(256) << 20) / (q.hot_max * eb);
+  const int64_t nblk = fkl::ceil_div(nn, max_rows);
+  q.hot_rows = fkl::ceil_div(nn, nblk);
   return q;
 }
 
@@ -38,12 +53,14 @@ struct RenormPlan {
   // forward workspace
   size_t f_zk, f_rowloss, f_flag, f_total;
   // backward workspace
-  size_t b_coef, b_zk, b_hist, b_total_ids, b_start, b_perm, b_partial, b_flag, b_total;
+  size_t b_coef, b_zk, b_hist, b_total_ids, b_start, b_perm, b_partial, b_slot, b_hot_ids,
+      b_info, b_hot_c, b_hot_prod, b_flag, b_total;
 };
 
-RenormPlan make_renorm_plan(int64_t N, int64_t d, int64_t V, int32_t K) {
+RenormPlan make_renorm_plan(int64_t N, int64_t d, int64_t V, int32_t K, int32_t dtype) {
   RenormPlan p{};
-  p.sort = sort_plan(N, K, V);
+  const int64_t eb = dtype == FKL_BF16 ? 2 : 4;
+  p.sort = sort_plan(N, d, K, V, eb);
   const size_t NK = static_cast<size_t>(N) * K;
   size_t off = 0;
   p.f_zk = off;
@@ -68,6 +85,16 @@ RenormPlan make_renorm_plan(int64_t N, int64_t d, int64_t V, int32_t K) {
   off = align_up(off + NK * 4);
   p.b_partial = off;
   off = align_up(off + static_cast<size_t>(2 * p.sort.nchunks) * d * 4);
+  p.b_slot = off;
+  off = align_up(off + static_cast<size_t>(V) * 4);
+  p.b_hot_ids = off;
+  off = align_up(off + static_cast<size_t>(p.sort.hot_max) * 4);
+  p.b_info = off;
+  off = align_up(off + 16);
+  p.b_hot_c = off;
+  off = align_up(off + static_cast<size_t>(p.sort.hot_rows) * p.sort.hot_max * eb);
+  p.b_hot_prod = off;
+  off = align_up(off + static_cast<size_t>(p.sort.hot_max) * d * 4);
   p.b_flag = off;
   off = align_up(off + 4);
   p.b_total = off;
@@ -108,7 +135,7 @@ extern "C" int32_t fkl_renorm_workspace_size(int64_t N, int64_t d, int64_t V, in
   g_last_error[0] = 0;
   const int32_t r = check_renorm(N, d, V, K, dtype);
   if (r) return r;
-  const RenormPlan p = make_renorm_plan(N, d, V, K);
+  const RenormPlan p = make_renorm_plan(N, d, V, K, dtype);
   if (fwd_bytes) *fwd_bytes = p.f_total;
   if (bwd_bytes) *bwd_bytes = p.b_total;
   return FKL_OK;
@@ -129,7 +156,7 @@ extern "C" int32_t fkl_renorm_forward(const void* hidden, const void* weight,
   if (!loss) return fail(FKL_E_ARG, "null pointer argument");
   if (!aligned(loss, 4) || !aligned(row_loss, 4) || !aligned(topk_z, 4))
     return fail(FKL_E_ARG, "fp32/int32 arrays must be 4-byte aligned");
-  const RenormPlan p = make_renorm_plan(N, d, V, K);
+  const RenormPlan p = make_renorm_plan(N, d, V, K, dtype);
   if (workspace_bytes < p.f_total)
     return fail(FKL_E_WORKSPACE, "forward workspace needs %zu bytes, got %zu", p.f_total,
                 workspace_bytes);
@@ -171,7 +198,7 @@ extern "C" int32_t fkl_renorm_backward(const void* hidden, const void* weight,
     return fail(FKL_E_ARG, "grad_hidden and grad_weight must be 16-byte aligned");
   if (!aligned(topk_z, 4) || !aligned(grad_loss, 4))
     return fail(FKL_E_ARG, "fp32/int32 arrays must be 4-byte aligned");
-  const RenormPlan p = make_renorm_plan(N, d, V, K);
+  const RenormPlan p = make_renorm_plan(N, d, V, K, dtype);
   if (workspace_bytes < p.b_total)
     return fail(FKL_E_WORKSPACE, "backward workspace needs %zu bytes, got %zu", p.b_total,
                 workspace_bytes);
@@ -194,12 +221,18 @@ extern "C" int32_t fkl_renorm_backward(const void* hidden, const void* weight,
                             s);
     fkl::launch_renorm_grad_h(dtype, weight, topk_idx, coef, N, K, d, grad_hidden, s);
   }
-  fkl::launch_renorm_grad_w(dtype, hidden, topk_idx, coef, N, K, d, V, p.sort,
-                            reinterpret_cast<int32_t*>(ws + p.b_hist),
-                            reinterpret_cast<int32_t*>(ws + p.b_total_ids),
-                            reinterpret_cast<int32_t*>(ws + p.b_start),
-                            reinterpret_cast<int32_t*>(ws + p.b_perm),
-                            reinterpret_cast<float*>(ws + p.b_partial),
+  fkl::RenormBuffers b{};
+  b.hist = reinterpret_cast<int32_t*>(ws + p.b_hist);
+  b.total = reinterpret_cast<int32_t*>(ws + p.b_total_ids);
+  b.start = reinterpret_cast<int32_t*>(ws + p.b_start);
+  b.perm = reinterpret_cast<int32_t*>(ws + p.b_perm);
+  b.slot = reinterpret_cast<int32_t*>(ws + p.b_slot);
+  b.hot_ids = reinterpret_cast<int32_t*>(ws + p.b_hot_ids);
+  b.info = reinterpret_cast<int32_t*>(ws + p.b_info);
+  b.partial = reinterpret_cast<float*>(ws + p.b_partial);
+  b.hot_c = ws + p.b_hot_c;
+  b.hot_prod = reinterpret_cast<float*>(ws + p.b_hot_prod);
+  fkl::launch_renorm_grad_w(dtype, hidden, topk_idx, coef, N, K, d, V, p.sort, b,
                             (flags & FKL_FLAG_ACCUMULATE_GRAD_W) != 0, grad_weight, s);
   return hip_check("renormalised backward launch");
 }

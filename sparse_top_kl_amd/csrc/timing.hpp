@@ -33,6 +33,7 @@ enum KernelId : int32_t {
   KID_RS_PLACE,
   KID_RS_CHUNKS,
   KID_RS_FIX,
+  KID_RS_HOT,
   KID_COUNT
 };
 
