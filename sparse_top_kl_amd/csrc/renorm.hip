@@ -237,13 +237,16 @@ __global__ __launch_bounds__(256) void k_rs_colscan(int32_t* __restrict__ hist, 
   total[v] = acc;
 }
 
-// Hot ids and the cold bucket starts, one workgroup of 1024 threads, each
-// owning a contiguous segment of ids. tau = the smallest power of two >=
-// hot_min with at most hot_max ids of count >= tau (no id is hot when even
-// the largest power of two leaves more). slot[v] = the hot id's index (in id
-// order) or -1, hot_ids[slot] = v, info[0] = the number of hot ids;
-// start[v] = sum of the counts of cold ids below v, start[V] = the number of
-// cold pairs.
+// Hot ids and the cold bucket starts, one workgroup of 1024 threads. tau =
+// the smallest power of two >= hot_min with at most hot_max ids of count >=
+// tau (no id is hot when even the largest power of two leaves more).
+// slot[v] = the hot id's index (in id order) or -1, hot_ids[slot] = v,
+// info[0] = the number of hot ids; start[v] = sum of the counts of cold ids
+// below v, start[V] = the number of cold pairs. The ids go through LDS in
+// tiles of kHotTile: read and written with consecutive threads on
+// consecutive ids, scanned with each thread owning 8 consecutive ids.
+constexpr int kHotTile = 8192;
+
 __global__ __launch_bounds__(1024) void k_rs_hot(const int32_t* __restrict__ total, int64_t V,
                                                  int32_t hot_min, int32_t hot_max,
                                                  int32_t* __restrict__ slot,
@@ -253,12 +256,15 @@ __global__ __launch_bounds__(1024) void k_rs_hot(const int32_t* __restrict__ tot
   __shared__ int32_t bins[32];
   __shared__ int32_t s_tau;
   __shared__ int32_t wsum[16][2];
+  __shared__ int32_t s_carry[2];
+  __shared__ int32_t tc[kHotTile];   // counts of the tile, then bucket starts
+  __shared__ int32_t tsl[kHotTile];  // slots of the tile
+  constexpr int kPer = kHotTile / 1024;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   if (t < 32) bins[t] = 0;
+  if (t < 2) s_carry[t] = 0;
   __syncthreads();
-  const int64_t seg = (V + 1023) / 1024;
-  const int64_t a = t * seg, e = a + seg < V ? a + seg : V;
-  for (int64_t v = a; v < e; ++v) {
+  for (int64_t v = t; v < V; v += 1024) {
     const int32_t c = total[v];
     if (c >= hot_min) atomicAdd(&bins[31 - __clz(c)], 1);
   }
@@ -277,47 +283,66 @@ __global__ __launch_bounds__(1024) void k_rs_hot(const int32_t* __restrict__ tot
   }
   __syncthreads();
   const int32_t tau = s_tau;
-  int32_t nh = 0, nc = 0;
-  for (int64_t v = a; v < e; ++v) {
-    const int32_t c = total[v];
-    if (c >= tau) ++nh; else nc += c;
-  }
-  // exclusive prefixes of (hot count, cold pairs) over the workgroup
-  int32_t xh = nh, xc = nc;
+  for (int64_t base = 0; base < V; base += kHotTile) {
+    const int n = V - base < kHotTile ? static_cast<int>(V - base) : kHotTile;
+    for (int i = t; i < kHotTile; i += 1024) tc[i] = i < n ? total[base + i] : 0;
+    __syncthreads();
+    int32_t nh = 0, nc = 0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int32_t yh = __shfl_up(xh, o), yc = __shfl_up(xc, o);
-    if (lane >= o) {
-      xh += yh;
-      xc += yc;
+    for (int j = 0; j < kPer; ++j) {
+      const int i = t * kPer + j;
+      const int32_t c = tc[i];
+      if (i < n && c >= tau) ++nh; else nc += c;
     }
-  }
-  if (lane == 63) {
-    wsum[wv][0] = xh;
-    wsum[wv][1] = xc;
-  }
-  __syncthreads();
-  int32_t bh = 0, bc = 0;
-  for (int i = 0; i < wv; ++i) {
-    bh += wsum[i][0];
-    bc += wsum[i][1];
-  }
-  int32_t h = bh + xh - nh, run = bc + xc - nc;
-  for (int64_t v = a; v < e; ++v) {
-    const int32_t c = total[v];
-    start[v] = run;
-    if (c >= tau) {
-      slot[v] = h;
-      hot_ids[h] = static_cast<int32_t>(v);
-      ++h;
-    } else {
-      slot[v] = -1;
-      run += c;
+    // exclusive prefixes of (hot ids, cold pairs) over the workgroup
+    int32_t xh = nh, xc = nc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t yh = __shfl_up(xh, o), yc = __shfl_up(xc, o);
+      if (lane >= o) {
+        xh += yh;
+        xc += yc;
+      }
     }
+    if (lane == 63) {
+      wsum[wv][0] = xh;
+      wsum[wv][1] = xc;
+    }
+    __syncthreads();
+    int32_t bh = s_carry[0], bc = s_carry[1];
+    for (int i = 0; i < wv; ++i) {
+      bh += wsum[i][0];
+      bc += wsum[i][1];
+    }
+    int32_t h = bh + xh - nh, run = bc + xc - nc;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = t * kPer + j;
+      const int32_t c = tc[i];
+      tc[i] = run;
+      if (i < n && c >= tau) {
+        tsl[i] = h;
+        hot_ids[h] = static_cast<int32_t>(base + i);
+        ++h;
+      } else {
+        tsl[i] = -1;
+        run += c;
+      }
+    }
+    __syncthreads();
+    for (int i = t; i < n; i += 1024) {
+      start[base + i] = tc[i];
+      slot[base + i] = tsl[i];
+    }
+    if (t == 1023) {  // carry the tile's totals into the next
+      s_carry[0] = bh + xh;
+      s_carry[1] = bc + xc;
+    }
+    __syncthreads();
   }
-  if (t == 1023) {
-    start[V] = bc + xc;
-    info[0] = bh + xh;
+  if (t == 0) {
+    start[V] = s_carry[1];
+    info[0] = s_carry[0];
   }
 }
 
