@@ -376,21 +376,21 @@ def run_renorm(args, torch, fkl, synth, dev):
     avg_ms = dom_ms / n_launch
     eb = 2 if w.dtype == "bf16" else 4
     NK = w.N * w.K
-    # compulsory bytes per launch (every input byte once, every output byte once) and the
-    # bytes the kernel gathers (one weight or hidden row of d values per cached entry)
+    # compulsory bytes per launch: every input byte once, every output byte once (the
+    # kernels gather one d-wide row per cached entry; how many of those the caches serve
+    # is in the measured traffic)
     compulsory = {
-        "k_gather_dot": (w.V * w.d * eb + w.N * w.d * eb + NK * 8, NK * w.d * eb),
-        "k_renorm_grad_h": (w.V * w.d * eb + NK * 8 + w.N * w.d * eb, NK * w.d * eb),
-        "k_rs_chunks": (w.N * w.d * eb + NK * 12 + w.V * w.d * 4, NK * w.d * eb),
+        "k_gather_dot": w.V * w.d * eb + w.N * w.d * eb + NK * 8,
+        "k_renorm_grad_h": w.V * w.d * eb + NK * 8 + w.N * w.d * eb,
+        "k_rs_chunks": w.N * w.d * eb + NK * 12 + w.V * w.d * 4,
     }
     if dom in compulsory:
-        cb, gathered = compulsory[dom]
+        cb = compulsory[dom]
         achieved = cb / (avg_ms * 1e-3) / 1e9
         roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                     "traffic": load_traffic(dom, w.name + "/renorm"), "bytes_per_launch": cb,
-                    "gathered_bytes_per_launch": gathered,
-                    "gathered_gbs": gathered / (avg_ms * 1e-3) / 1e9, "avg_launch_ms": avg_ms}
+                    "avg_launch_ms": avg_ms}
     else:
         roofline = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": None, "traffic": None, "avg_launch_ms": avg_ms}
