@@ -3,7 +3,9 @@ kept-logits paths, with and without options) captured into a graph with
 preallocated workspaces and outputs, replayed several times with eager work
 and synchronisations in between, and every replay checked bitwise against the
 eager result (the kernels are deterministic). The library enqueues no memset
-nodes and never synchronises, so a captured step is the same launches."""
+nodes and never synchronises, so a captured step is the same launches. The
+student-renormalised loss is captured too, with its workspace scrambled
+between replays."""
 
 import numpy as np
 import pytest
@@ -76,3 +78,48 @@ def test_graph_replays_match_eager(gpu_device, keep, options):
         assert torch.equal(gw, gw0), f"replay {rep}: grad_W"
         _ = torch.randn(1000, device=gpu_device).sum().item()
     assert np.isfinite(loss0.item())
+
+
+def test_renorm_graph_replays_match_eager(gpu_device):
+    """The student-renormalised loss captured the same way: its counting sort
+    clears its counters with fill kernels, so every replay starts from the
+    same state and matches the eager step bitwise."""
+    announce("graph capture: student-renormalised loss")
+    w = synth.small_workload("graph_renorm", n=900, d=256, V=4000, K=100, T=2.0, dtype="bf16",
+                             chunk=256, ids="zipf", seed=37)
+    h, W, idx, lg = upload(synth.make_inputs(w))
+    N, d, V, K = h.shape[0], h.shape[1], W.shape[0], idx.shape[1]
+    fw, bw = fkl.fkl_renorm_workspace_size(N, d, V, K, torch.bfloat16)
+    ws_f = torch.empty(fw, dtype=torch.uint8, device=gpu_device)
+    ws_b = torch.empty(bw, dtype=torch.uint8, device=gpu_device)
+    gw = torch.empty(V, d, dtype=torch.float32, device=gpu_device)
+
+    def step():
+        out = fkl.fkl_renorm_forward(h, W, idx, lg, w.T, workspace=ws_f)
+        gh, _ = fkl.fkl_renorm_backward(h, W, idx, lg, w.T, topk_z=out.topk_z, grad_weight=gw,
+                                        workspace=ws_b)
+        return out.loss, out.row_loss, gh
+
+    loss0, rl0, gh0 = (t.clone() for t in step())
+    gw0 = gw.clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        loss_g, rl_g, gh_g = step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        gw.fill_(float("nan"))
+        ws_b.fill_(0xAB)                         # scramble the sort's state between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(loss_g, loss0), f"replay {rep}: loss"
+        assert torch.equal(rl_g, rl0), f"replay {rep}: row_loss"
+        assert torch.equal(gh_g, gh0), f"replay {rep}: grad_hidden"
+        assert torch.equal(gw, gw0), f"replay {rep}: grad_W"
+        _ = torch.randn(1000, device=gpu_device).sum().item()
