@@ -743,6 +743,27 @@ struct TileGroups {
     *tn = gn_i * GB + (j / GA);
     return *tm < mt && *tn < nt;
   }
+  // The same with `splits` copies of the tile grid (a split of the
+  // contraction): group index q runs over splits x groups, so the copies go to
+  // XCDs the first one leaves idle. splits = 1 is coords().
+  static int64_t grid_split(int64_t mt, int64_t nt, int64_t splits) {
+    const int64_t ngroups = ((mt + GA - 1) / GA) * ((nt + GB - 1) / GB) * splits;
+    return 8 * ((ngroups + 7) / 8) * 32;
+  }
+  __device__ __forceinline__ static bool coords_split(int64_t mt, int64_t nt, int64_t splits,
+                                                      int64_t* tm, int64_t* tn, int64_t* sp) {
+    // grids stay far below 2^31 blocks: 32-bit index arithmetic
+    const uint32_t b = blockIdx.x;
+    const uint32_t xcd = b & 7, local = b >> 3;
+    const uint32_t q = (local >> 5) * 8 + xcd, j = local & 31;
+    const uint32_t gn = static_cast<uint32_t>((nt + GB - 1) / GB);
+    const uint32_t ng = static_cast<uint32_t>((mt + GA - 1) / GA) * gn;
+    *sp = q / ng;
+    const uint32_t qq = q % ng;
+    *tm = (qq / gn) * GA + (j % GA);
+    *tn = (qq % gn) * GB + (j / GA);
+    return *sp < splits && *tm < mt && *tn < nt;
+  }
 };
 
 // Row offset, inside the wave sub-tile, of accumulator element r of block mi.

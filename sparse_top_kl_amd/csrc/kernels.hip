@@ -690,9 +690,18 @@ template <class P, class C>
 __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_grad_w(
     const unsigned char* __restrict__ G, int64_t gpitch, const unsigned char* __restrict__ H,
     int64_t d, int64_t Vw, int64_t Vlim, int64_t nrows, int64_t n_vt, int64_t n_dt, int accumulate,
-    float* __restrict__ grad_w) {
-  int64_t vt, dt;
-  if (!TileGroups<8, 4>::coords(n_vt, n_dt, &vt, &dt)) return;
+    float* __restrict__ grad_w, int64_t splits, int64_t split_rows, int64_t out_split_stride) {
+  int64_t vt, dt, sp;
+  if (!TileGroups<8, 4>::coords_split(n_vt, n_dt, splits, &vt, &dt, &sp)) return;
+  // split sp contracts rows [sp * split_rows, ...) into its own output copy
+  {
+    const int64_t r0 = sp * split_rows;
+    G += r0 * gpitch * P::kBytes;
+    H += r0 * d * P::kBytes;
+    nrows = nrows - r0 < split_rows ? nrows - r0 : split_rows;
+    if (nrows < 0) nrows = 0;
+    grad_w += sp * out_split_stride;
+  }
   // A = G^T (stored [row][v], k = row), B = H (stored [row][col], k = row)
   const Operand A = make_operand(G + vt * kBM * P::kBytes, gpitch * P::kBytes, Vw - vt * kBM, nrows);
   const Operand B = make_operand(H + dt * kBN * P::kBytes, d * P::kBytes, d - dt * kBN, nrows);
@@ -905,17 +914,25 @@ void launch_reduce_grad_hidden(int dtype, const float* part, int64_t splits, int
     k_reduce_gh<F32><<<static_cast<unsigned>(blocks), 256, 0, s>>>(part, splits, nrows, d, out);
 }
 
-void launch_grad_w(int dtype, const void* G, int64_t gpitch, const void* H, int64_t d,
-                   int64_t v0, int64_t Vw, int64_t Vlim, int64_t row0, int64_t nrows,
-                   bool accumulate, float* grad_w, hipStream_t s) {
+void launch_grad_w_split(int dtype, const void* G, int64_t gpitch, const void* H, int64_t d,
+                         int64_t Vw, int64_t Vlim, int64_t row0, int64_t nrows, int64_t splits,
+                         bool accumulate, float* out, int64_t out_split_stride, hipStream_t s) {
   ScopedTimer timer_(KID_GRAD_W, s);
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(Vw, kBM), n_dt = ceil_div(d, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
-  const unsigned grid = grouped_grid<8, 4>(n_vt, n_dt);
+  const unsigned grid = static_cast<unsigned>(TileGroups<8, 4>::grid_split(n_vt, n_dt, splits));
+  const int64_t split_rows = ceil_div(nrows, splits);
   FKL_LAUNCH_GEMM(k_grad_w, dtype, grid, s,
                   static_cast<const unsigned char*>(G), gpitch, Hc, d, Vw, Vlim, nrows, n_vt, n_dt,
-                  accumulate ? 1 : 0, grad_w + v0 * d);
+                  accumulate ? 1 : 0, out, splits, split_rows, out_split_stride);
+}
+
+void launch_grad_w(int dtype, const void* G, int64_t gpitch, const void* H, int64_t d,
+                   int64_t v0, int64_t Vw, int64_t Vlim, int64_t row0, int64_t nrows,
+                   bool accumulate, float* grad_w, hipStream_t s) {
+  launch_grad_w_split(dtype, G, gpitch, H, d, Vw, Vlim, row0, nrows, 1, accumulate, grad_w + v0 * d,
+                      0, s);
 }
 
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {

@@ -100,6 +100,11 @@ void launch_reduce_grad_hidden(int dtype, const float* part, int64_t splits, int
 void launch_grad_w(int dtype, const void* G, int64_t gpitch, const void* H, int64_t d,
                    int64_t v0, int64_t Vw, int64_t Vlim, int64_t row0, int64_t nrows,
                    bool accumulate, float* grad_w, hipStream_t s);
+// The same product with its rows split in `splits` equal parts contracted in
+// parallel, split i into out + i * out_split_stride (rows [0, Vlim) of each).
+void launch_grad_w_split(int dtype, const void* G, int64_t gpitch, const void* H, int64_t d,
+                         int64_t Vw, int64_t Vlim, int64_t row0, int64_t nrows, int64_t splits,
+                         bool accumulate, float* out, int64_t out_split_stride, hipStream_t s);
 
 // Teacher top-K cache, per chunk of rows [row0, row0 + nrows): the chunk's
 // fp32 logits LT[v][r] (pitch lt_ld floats) and per (row, 128-vocab slice)
@@ -140,6 +145,7 @@ struct RenormSortPlan {
   int64_t nb, rows_per_block, seg, nchunks;
   int64_t hot_max;   // ids the dense product can take: one round of 256 x 256 tiles
   int64_t hot_rows;  // rows per dense-product block
+  int64_t hot_splits;  // row splits of the product, each into its own copy of the output
 };
 // Workspace arrays of launch_renorm_grad_w.
 struct RenormBuffers {
@@ -152,7 +158,7 @@ struct RenormBuffers {
   int32_t* info;        // [4] number of hot ids
   float* partial;       // [2 * nchunks * d] chunk partials
   unsigned char* hot_c; // [hot_rows * hot_max] coefficients, input dtype
-  float* hot_prod;      // [hot_max * d] C^T H
+  float* hot_prod;      // [hot_splits * hot_max * d] C^T H, one copy per split
 };
 
 // Forward (coef_mode false): row_loss[r] = w_r T^2 KL over the row's cached

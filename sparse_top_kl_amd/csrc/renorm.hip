@@ -31,8 +31,9 @@
 //                    counts: bucket starts of the cold pairs
 //   hot ids, a dense product: k_rs_hot_coef scatters each row's hot
 //   coefficients into C [rows x hot_max] (copies of one id in a row
-//   summed in entry order), k_grad_w (the loss's MFMA kernel) forms C^T H,
-//   and k_rs_hot_rows copies each hot id's row into grad_W
+//   summed in entry order), k_grad_w (the loss's MFMA kernel, its rows split
+//   over the XCDs its tiles alone would leave idle) forms C^T H, and
+//   k_rs_hot_rows sums the splits in order into each hot id's grad_W row
 //   cold ids, a sort:
 //   k_rs_place       per block, its rows in order: each cold pair (r, k) goes
 //                    to start[v] + (pairs of id v in earlier rows) + (copies of
@@ -532,16 +533,22 @@ __global__ __launch_bounds__(256) void k_rs_hot_coef(const int32_t* __restrict__
   }
 }
 
-// grad_W[hot_ids[j]] (=, or += with acc_out) prod[j] for j < info[0].
+// grad_W[hot_ids[j]] (=, or += with acc_out) the sum over the splits, in split
+// order, of prod[split][j], for j < info[0].
 __global__ __launch_bounds__(256) void k_rs_hot_rows(const int32_t* __restrict__ hot_ids,
                                                      const int32_t* __restrict__ info,
                                                      const float* __restrict__ prod, int64_t d,
+                                                     int64_t splits, int64_t split_stride,
                                                      bool acc_out, float* __restrict__ gw) {
   const int64_t j = blockIdx.x;
   if (j >= info[0]) return;
   float* row = gw + static_cast<int64_t>(hot_ids[j]) * d;
   const float* src = prod + j * d;
-  for (int64_t c = threadIdx.x; c < d; c += blockDim.x) row[c] = acc_out ? row[c] + src[c] : src[c];
+  for (int64_t c = threadIdx.x; c < d; c += blockDim.x) {
+    float v = src[c];
+    for (int64_t i = 1; i < splits; ++i) v += src[i * split_stride + c];
+    row[c] = acc_out ? row[c] + v : v;
+  }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -637,12 +644,12 @@ void launch_renorm_grad_w(int dtype, const void* H, const int32_t* idx, const fl
       else
         k_rs_hot_coef<F32><<<grid, 256, 0, s>>>(idx, coef, b.slot, r0, nr, K, q.hot_max, b.hot_c);
     }
-    launch_grad_w(dtype, b.hot_c, q.hot_max, H, d, 0, q.hot_max, q.hot_max, r0, nr, r0 > 0,
-                  b.hot_prod, s);
+    launch_grad_w_split(dtype, b.hot_c, q.hot_max, H, d, q.hot_max, q.hot_max, r0, nr,
+                        q.hot_splits, r0 > 0, b.hot_prod, q.hot_max * d, s);
   }
   ScopedTimer timer_(KID_RS_HOT, s);
-  k_rs_hot_rows<<<static_cast<unsigned>(q.hot_max), 256, 0, s>>>(b.hot_ids, b.info, b.hot_prod,
-                                                                 d, acc_out, gw);
+  k_rs_hot_rows<<<static_cast<unsigned>(q.hot_max), 256, 0, s>>>(
+      b.hot_ids, b.info, b.hot_prod, d, q.hot_splits, q.hot_max * d, acc_out, gw);
 }
 
 }  // namespace fkl

@@ -45,6 +45,12 @@ fkl::RenormSortPlan sort_plan(int64_t N, int64_t d, int32_t K, int64_t V, int64_
   const int64_t max_rows = (int64_t(256) << 20) / (q.hot_max * eb);
   const int64_t nblk = fkl::ceil_div(nn, max_rows);
   q.hot_rows = fkl::ceil_div(nn, nblk);
+  // its 256 x 256 tiles form groups of 32, one group per XCD: split the rows
+  // so that the groups' copies fill the 8 XCDs (at least 1024 rows a split)
+  const int64_t groups = fkl::ceil_div(q.hot_max / 256, 8) * fkl::ceil_div(d_tiles, 4);
+  q.hot_splits = groups >= 8 ? 1 : 8 / groups;
+  const int64_t by_rows = q.hot_rows / 1024 > 0 ? q.hot_rows / 1024 : 1;
+  if (q.hot_splits > by_rows) q.hot_splits = by_rows;
   return q;
 }
 
@@ -94,7 +100,7 @@ RenormPlan make_renorm_plan(int64_t N, int64_t d, int64_t V, int32_t K, int32_t 
   p.b_hot_c = off;
   off = align_up(off + static_cast<size_t>(p.sort.hot_rows) * p.sort.hot_max * eb);
   p.b_hot_prod = off;
-  off = align_up(off + static_cast<size_t>(p.sort.hot_max) * d * 4);
+  off = align_up(off + static_cast<size_t>(p.sort.hot_splits) * p.sort.hot_max * d * 4);
   p.b_flag = off;
   off = align_up(off + 4);
   p.b_total = off;

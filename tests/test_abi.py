@@ -301,12 +301,14 @@ def test_renorm_workspace_is_linear_in_pairs_and_never_rows_times_vocab():
         # 2048 sorted pairs, about 4096 chunks unless the 2048 cap needs more; for the ids
         # summed by a dense product (as many as one round of 256 x 256 tiles of its hot x d
         # output takes), per-id slots, their coefficients for at most 256 MiB of rows and their
-        # product
+        # product (one copy per row split of the product)
         counters = max(256 << 20, V * 4)
         chunks = max(min(4097, NK // 256 + 1), NK // 2048 + 1)
         hot_max = min(2048, max(256, (256 // -(-d // 256)) * 256))
         rows = min(N, (256 << 20) // (hot_max * 2))
-        hot = rows * hot_max * 2 + hot_max * d * 4 + hot_max * 4 + V * 4
+        groups = -(-hot_max // 2048) * -(-(-(-d // 256)) // 4)
+        splits = min(1 if groups >= 8 else 8 // groups, max(1, rows // 1024))
+        hot = rows * hot_max * 2 + splits * hot_max * d * 4 + hot_max * 4 + V * 4
         assert 3 * NK * 4 + (2 * V + 1) * 4 + hot - rows * hot_max * 2 <= b
         assert b <= 3 * NK * 4 + (2 * V + 1) * 4 + counters + chunks * 2 * d * 4 + hot + 20 * 256
         assert b < N * V * 2 / 4 or N < 4096
