@@ -5,8 +5,9 @@ fkl_renorm_backward through the C ABI) against the fp64 oracle
 Small shapes compare every output element: bf16 and fp32, uniform and
 Zipf-skewed ids (hot ids whose pairs span several sort chunks), duplicate ids
 in a row, -inf padding entries, zero-weight padding rows, K from 1 to 1024,
-odd hidden sizes, a negative upstream scale. Then: grad_W and grad_hidden
-are bitwise repeatable, the accumulate flag adds, passing the forward's
+odd hidden sizes, a negative upstream scale, and enough rows that the
+frequent ids' dense product is split over rows and blocked. Then: grad_W and
+grad_hidden are bitwise repeatable, the accumulate flag adds, passing the forward's
 gathered logits changes nothing, an empty batch zeroes grad_W, the autograd
 wrapper matches, and at the long32k size sampled rows match the oracle while
 the whole grad_W matches an independent fp32 PyTorch computation."""
@@ -79,6 +80,12 @@ CASES = [
     ("bf16_K1", 200, 64, 500, 1, 1.0, "bf16", "uniform", False, False, False, None),
     ("fp32_K300", 150, 72, 1200, 300, 3.0, "fp32", "zipf", True, True, False, None),
     ("bf16_K1024_d8192", 40, 8192, 2048, 1024, 1.0, "bf16", "uniform", False, True, False, None),
+    # many rows: the frequent ids' dense product runs in 8 row splits, and for fp32 its
+    # coefficient matrix (at most 256 MiB) takes three row blocks accumulated in turn
+    ("bf16_40k_rows_hot_splits", 40000, 64, 3000, 16, 2.0, "bf16", "zipf", True, False, False,
+     None),
+    ("fp32_70k_rows_hot_blocks", 70000, 64, 3000, 16, 1.0, "fp32", "zipf", False, True, True,
+     0.5),
 ]
 
 
