@@ -320,7 +320,9 @@ int32_t fkl_teacher_topk(const void* hidden, const void* weight, int64_t N, int6
  * fkl_renorm_workspace_size: bytes of the forward and backward workspaces
  *   (either pointer may be NULL). The backward workspace holds the K
  *   coefficients per row, a counting sort of the N * K (row, entry) pairs by
- *   id (at most 256 MiB of per-block counters) and chunk partials of grad_W.
+ *   id (at most 256 MiB of per-block counters), chunk partials of grad_W, and
+ *   for the (at most 2048) ids with the most pairs a dense coefficient matrix
+ *   (at most 256 MiB) with its product's output copies.
  * fkl_renorm_forward: writes loss[0] and, when non-NULL, row_loss [N] and
  *   topk_z [N, K] (the student logit at each cached id, fp32 dot product of
  *   the hidden row and the weight row). flags: 0 or FKL_FLAG_VALIDATE_IDX.
