@@ -37,6 +37,9 @@ CASES = [
     ("one_row_fp32", 1, 128, 1000, 7, 0.5, "fp32", 1, "uniform"),
     ("k1_bf16", 257, 128, 2000, 1, 1.0, "bf16", 100, "uniform"),
     ("wide_d_bf16", 300, 1032, 1500, 50, 1.0, "bf16", 128, "uniform"),
+    # the largest K the library takes (4096), and a large hidden size
+    ("max_k_bf16", 96, 256, 6000, 4096, 1.0, "bf16", 40, "uniform"),
+    ("d8192_fp32", 130, 8192, 1100, 64, 2.0, "fp32", 64, "zipf"),
 ]
 
 
