@@ -40,6 +40,8 @@ CASES = [
     # the largest K the library takes (4096), and a large hidden size
     ("max_k_bf16", 96, 256, 6000, 4096, 1.0, "bf16", 40, "uniform"),
     ("d8192_fp32", 130, 8192, 1100, 64, 2.0, "fp32", 64, "zipf"),
+    # a vocabulary smaller than one 256-row tile
+    ("tiny_vocab_bf16", 200, 128, 7, 5, 1.5, "bf16", 64, "uniform"),
 ]
 
 

@@ -86,6 +86,8 @@ CASES = [
      None),
     ("fp32_70k_rows_hot_blocks", 70000, 64, 3000, 16, 1.0, "fp32", "zipf", False, True, True,
      0.5),
+    # a 7-id vocabulary: every id is frequent, the sorted walk gets no pair at all
+    ("bf16_tiny_vocab_all_hot", 400, 64, 7, 5, 1.0, "bf16", "uniform", True, True, False, None),
 ]
 
 
