@@ -6,6 +6,7 @@ The library is written next to this file; the binding loads it from there.
 
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -44,15 +45,19 @@ def compile_flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, jobs: int | None = None) -> str:
     cc = hipcc()
-    objs = []
     os.makedirs(os.path.join(HERE, "_objs"), exist_ok=True)
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(HERE, "_objs", os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *compile_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
-        _run(cmd, verbose)
+        cmds.append([cc, *compile_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    # one hipcc process per source, a few at a time
+    jobs = jobs or min(len(cmds), max(1, min(4, (os.cpu_count() or 1) // 2)))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as pool:
+        for fut in [pool.submit(_run, c, verbose) for c in cmds]:
+            fut.result()
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

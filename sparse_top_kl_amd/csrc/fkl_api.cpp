@@ -73,7 +73,9 @@ void plan_backward_blocks(int64_t N, int64_t Vpad, int64_t d, int64_t chunk_cap,
   int64_t budget = chunk_cap * Vpad;
   // rows * pitch * eb must stay below kMaxBlockBytes with up to 63 pad elements per row
   if (budget > kMaxBlockBytes / eb - 64 * N) budget = kMaxBlockBytes / eb - 64 * N;
-  if (budget >= N * Vpad) {  // one block covers everything
+  // grad_W reads the block's hidden rows through 32-bit offsets as well
+  const int64_t max_rows = kMaxBlockBytes / (d * eb);
+  if (budget >= N * Vpad && N <= max_rows) {  // one block covers everything
     *rows = N;
     *width = Vpad;
     return;
@@ -84,7 +86,7 @@ void plan_backward_blocks(int64_t N, int64_t Vpad, int64_t d, int64_t chunk_cap,
   const int64_t max_blocks = fkl::ceil_div(N, 256);
   for (int64_t nb = 1; nb <= max_blocks; ++nb) {
     const int64_t rc = nb == 1 ? N : fkl::round_up(fkl::ceil_div(N, nb), 256);
-    if (rc > N || rc * kGran > budget) continue;
+    if (rc > N || rc * kGran > budget || rc > max_rows) continue;
     if (nb > 1 && fkl::ceil_div(N, rc) != nb) continue;  // same blocking as a smaller nb
     const int64_t vs_max = budget / rc;
     const int64_t vm = vs_max >= Vpad ? Vpad : vs_max / kGran * kGran;
@@ -100,8 +102,10 @@ void plan_backward_blocks(int64_t N, int64_t Vpad, int64_t d, int64_t chunk_cap,
       }
     }
   }
-  if (best == 1e300) {  // tiny budget: one row per block, whole vocabulary
-    *rows = budget / Vpad > 0 ? (budget / Vpad < N ? budget / Vpad : N) : 1;
+  if (best == 1e300) {  // tiny budget: as many rows as fit, whole vocabulary
+    int64_t r = budget / Vpad > 0 ? (budget / Vpad < N ? budget / Vpad : N) : 1;
+    if (r > max_rows) r = max_rows;
+    *rows = r;
     *width = Vpad;
   }
 }
@@ -279,7 +283,9 @@ int32_t forward_impl(const void* hidden, const void* weight, const int32_t* topk
   float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + p.f_rowloss);
   float* zk = topk_z ? topk_z : reinterpret_cast<float*>(ws + p.f_topkz);
   const float c2 = 1.4426950408889634f / T;
-  const bool two_sm = labels && T != 1.0f;  // the cross-entropy needs its own softmax
+  // a second set of partials at temperature 1 when T != 1 and something needs
+  // that softmax: the cross-entropy term, or the caller's lse1 output
+  const bool two_sm = (labels || (o && o->lse1)) && T != 1.0f;
   fkl::MergeOpts mo{};
   mo.part_ce = two_sm ? reinterpret_cast<float2*>(ws + p.f_part_ce) : nullptr;
   mo.labels = labels;
@@ -597,8 +603,9 @@ static int32_t backward_keep_impl(const void* hidden, const void* weight,
   // grad_hidden over all rows in one launch (tiles of 256 rows reach 256 * zld bytes)
   fkl::launch_grad_hidden(dtype, logits, zpitch, weight, d, 0, zpitch, V, N, false, ghacc, s);
   fkl::launch_reduce_grad_hidden(dtype, ghacc, 1, N, d, grad_hidden, 0, s);
-  // grad_W over row blocks whose rows stay within the 32-bit offsets of one operand
-  const int64_t rmax = kMaxBlockBytes / zld;
+  // grad_W over row blocks whose rows stay within the 32-bit offsets of both
+  // operands (the kept rows and the hidden rows)
+  const int64_t rmax = kMaxBlockBytes / (zld > d * eb ? zld : d * eb);
   const int64_t nb = fkl::ceil_div(N, rmax);
   int64_t rb = fkl::round_up(fkl::ceil_div(N, nb), 64);
   if (rb > rmax) rb = fkl::ceil_div(N, nb);

@@ -207,6 +207,8 @@ def _loss_options(N, row_weight, labels, alpha, lse1, teacher_lse=None):
         keep.append(labels)
     if lse1 is not None:
         _require(lse1, "lse1", torch.float32)
+        if lse1.numel() != N:
+            raise FklError(FKL_E_ARG, "lse1 must have N entries")
         keep.append(lse1)
     if teacher_lse is not None:
         teacher_lse = teacher_lse.reshape(-1).to(torch.float32).contiguous()
@@ -387,12 +389,13 @@ def fkl_teacher_topk(hidden: torch.Tensor, weight: torch.Tensor, K: int, chunk: 
 
 def fkl_forward_ex(hidden, weight, topk_idx, topk_logit, T: float, chunk: int, *,
                    row_weight=None, labels=None, alpha: float = 1.0, teacher_lse=None,
-                   keep_logits=None, validate: bool = False, workspace=None):
+                   lse1=None, keep_logits=None, validate: bool = False, workspace=None):
     """fkl_forward (or with keep_logits, a [N, keep_pitch(V)] buffer or True,
     fkl_forward_keep) with loss options: per-row weights, hard labels (< 0:
     none) and the KL/cross-entropy mixing weight alpha. Returns a
-    ForwardResult whose lse1 is set when labels are given (the backward needs
-    it), plus the kept logits in keep mode: (result, logits)."""
+    ForwardResult whose lse1 (the temperature-1 lse) is set when labels are
+    given (the backward needs it) or an [N] fp32 lse1 buffer is passed, plus
+    the kept logits in keep mode: (result, logits)."""
     N, d = hidden.shape
     V, K = weight.shape[0], topk_idx.shape[1]
     code = dtype_code(hidden.dtype)
@@ -402,7 +405,8 @@ def fkl_forward_ex(hidden, weight, topk_idx, topk_logit, T: float, chunk: int, *
     dev = hidden.device
     fw, _ = fkl_workspace_size(N, d, V, K, chunk, code)
     ws = workspace if workspace is not None else _workspace(fw, dev)
-    lse1 = torch.empty(N, dtype=torch.float32, device=dev) if labels is not None else None
+    if lse1 is None and labels is not None:
+        lse1 = torch.empty(N, dtype=torch.float32, device=dev)
     o, alive = _loss_options(N, row_weight, labels, alpha, lse1, teacher_lse)
     out = ForwardResult(torch.empty((), dtype=torch.float32, device=dev),
                         torch.empty(N, dtype=torch.float32, device=dev),
@@ -640,6 +644,9 @@ class FusedChunkedKL(torch.autograd.Function):
             out, z = res if keep else (res, None)
         ctx.save_for_backward(h2, w, idx, lg, out.lse, out.topk_z, z, rw, y, out.lse1)
         ctx.T, ctx.chunk, ctx.shape, ctx.alpha = T, chunk, shape, alpha
+        # the kept logits are overwritten with G by the backward (through a raw
+        # pointer, which torch's version counter does not see): one backward only
+        ctx.logits_consumed = False
         return out.loss
 
     @staticmethod
@@ -647,6 +654,13 @@ class FusedChunkedKL(torch.autograd.Function):
     def backward(ctx, grad_loss):
         g = grad_loss.to(torch.float32).reshape(()).contiguous()
         h2, w, idx, lg, lse, zk, z, rw, y, lse1 = ctx.saved_tensors
+        if z is not None:
+            if ctx.logits_consumed:
+                raise RuntimeError(
+                    "fused_chunked_kl(keep_logits=...): the kept logits were consumed by the "
+                    "first backward pass; a second backward through the same graph needs "
+                    "keep_logits=False")
+            ctx.logits_consumed = True
         if rw is None and y is None:
             if z is not None:
                 gh, gw = fkl_backward_keep(h2, w, idx, lg, lse, ctx.T, z, topk_z=zk, grad_loss=g)

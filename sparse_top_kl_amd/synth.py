@@ -202,6 +202,21 @@ def make_inputs(name_or_workload, n_rows: int | None = None) -> dict:
     }
 
 
+def make_loss_options(w: Workload, seed: int = 99) -> dict:
+    """Inputs of the loss options at a workload's size: a hard label per row
+    (uniform over the vocabulary, stream ``default_rng(seed)``), the mixing
+    weight 0.5, and a teacher full-vocabulary log-sum-exp at T per row chosen
+    so that the cached entries hold half of the teacher's mass (the log-sum-exp
+    of the cached logits / T over the K entries, plus ln 2, in fp64, rounded
+    to fp32). Only input data; the loss itself is computed elsewhere."""
+    y = np.random.default_rng(seed).integers(0, w.V, size=w.N).astype(np.int32)
+    logit = _teacher_logits(_rng(w.seed, 3), w.N, w.K)
+    a = logit.astype(np.float64) / w.T
+    mx = a.max(axis=1)
+    tlse = (mx + np.log(np.exp(a - mx[:, None]).sum(axis=1)) + np.log(2.0)).astype(np.float32)
+    return {"labels": y, "alpha": 0.5, "teacher_lse": tlse}
+
+
 def small_workload(name="small", n=300, d=64, V=1000, K=100, T=1.0, dtype="fp32",
                    chunk=128, ids="uniform", seed=7) -> Workload:
     """A custom (usually tiny) workload with the same recipe."""

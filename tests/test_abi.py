@@ -62,6 +62,26 @@ def test_workspace_is_bounded_by_chunk_times_vocab_and_never_rows_times_vocab():
     assert b2 > 1.5 * b1
 
 
+def test_backward_row_blocks_keep_hidden_rows_within_32_bit_offsets():
+    """grad_W reads a row block's hidden rows through 32-bit buffer offsets, so
+    rows * d * element size stays below 2 GiB even when the chunk x V budget
+    would allow more rows (small vocabulary, large hidden size). The backward
+    workspace holds, per row of a block, the G row (padded to 64 elements),
+    the fp32 grad_hidden accumulator, two K-entry coefficient rows and seven
+    scalars, so the planned block size can be read back from its size."""
+    for dtype, eb in ((fkl.FKL_BF16, 2), (fkl.FKL_F32, 4)):
+        N, d, V, K = 200000, 8192, 1024, 16
+        _, b = fkl.fkl_workspace_size(N, d, V, K, N, dtype)
+        per_row = ((V + 63) // 64 * 64) * eb + 4 * d + 8 * K + 7 * 4
+        rows = b // per_row
+        assert rows * d * eb < 2 ** 31, (dtype, rows)
+        assert rows >= 256
+        # a smaller batch still fits in one block
+        n_small = (2 ** 31 - 2 ** 20) // (d * eb) // 2
+        _, b_small = fkl.fkl_workspace_size(n_small, d, V, K, n_small, dtype)
+        assert b_small // per_row == n_small
+
+
 def test_workspace_size_rejects_bad_shapes():
     with pytest.raises(fkl.FklError) as e:
         fkl.fkl_workspace_size(10, 12, 100, 5, 4, fkl.FKL_BF16)

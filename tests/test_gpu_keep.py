@@ -179,3 +179,31 @@ def test_autograd_keep_matches_fused(gpu_device):
         assert (gw1 - gw0).abs().max() / gw0.abs().max() <= TOL["bf16"]["grad"]
     with pytest.raises(ValueError):
         fkl.fused_chunked_kl(h, W, idx, lg, keep_logits="always")
+
+
+def test_second_backward_through_kept_logits_is_refused(gpu_device):
+    """The kept logits become G in the first backward; a second backward on
+    the same graph (retain_graph) must raise instead of reading G as logits.
+    The first backward's gradients equal the recompute path's."""
+    announce("autograd: a second backward through consumed kept logits raises")
+    w = synth.small_workload("keep_twice", n=300, d=128, V=1500, K=32, T=2.0,
+                             dtype="fp32", chunk=128)
+    inp = synth.make_inputs(w)
+    h, W, idx, lg = upload(inp)
+    grads = {}
+    for keep in (False, True):
+        hh = h.detach().clone().requires_grad_(True)
+        WW = W.detach().clone().requires_grad_(True)
+        loss = fkl.fused_chunked_kl(hh, WW, idx, lg, T=w.T, chunk=w.chunk, keep_logits=keep)
+        loss.backward(retain_graph=True)
+        torch.cuda.synchronize()
+        grads[keep] = (hh.grad.double().cpu(), WW.grad.double().cpu())
+        if keep:
+            with pytest.raises(RuntimeError, match="consumed"):
+                loss.backward()
+        else:  # the recompute path may run backward again and gives the same gradient twice
+            loss.backward()
+            torch.cuda.synchronize()
+            assert torch.equal(hh.grad.double().cpu(), 2 * grads[False][0])
+    for a, b in zip(grads[True], grads[False]):
+        assert (a - b).abs().max() / b.abs().max() <= TOL["fp32"]["grad"]

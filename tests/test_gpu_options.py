@@ -189,3 +189,22 @@ def test_teacher_cache_to_student_loss_with_tail(gpu_device):
            "topk_z": out.topk_z.double().cpu().numpy(),
            "grad_hidden": gh.double().cpu().numpy(), "grad_w": gw.double().cpu().numpy()}
     compare(res, ref, "bf16")
+
+
+@pytest.mark.parametrize("T", [1.0, 2.0])
+def test_lse1_without_labels_is_the_temperature_one_lse(gpu_device, T):
+    """lse1 requested without labels: the forward writes ln sum exp(z) at
+    temperature 1 (a second set of partials when T != 1), not the lse at T."""
+    announce(f"lse1 without labels, T={T}")
+    w = synth.small_workload("lse1_nolabels", n=300, d=64, V=1000, K=16, T=T, dtype="fp32",
+                             chunk=128)
+    inp = synth.make_inputs(w)
+    h, W, idx, lg = upload(inp)
+    lse1 = torch.empty(w.N, dtype=torch.float32, device=gpu_device)
+    out = fkl.fkl_forward_ex(h, W, idx, lg, T, w.chunk, lse1=lse1)
+    torch.cuda.synchronize()
+    ref = oracle.forward_backward(inp["hidden"], inp["weight"], inp["topk_idx"],
+                                  inp["topk_logit"], T, want_grads=False)
+    tol = TOL["fp32"]["loss"]
+    assert elementwise_ok(lse1.double().cpu().numpy(), ref["lse1"], tol) <= tol
+    assert elementwise_ok(out.lse.double().cpu().numpy(), ref["lse"], tol) <= tol
