@@ -134,6 +134,28 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
                      int64_t V, int32_t K, int32_t dtype, uint32_t flags, void* grad_hidden,
                      float* grad_weight, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward pass without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Arguments, outputs and results are those
+ * of fkl_forward (the same kernels run); the workspace is a static 64 MiB
+ * device array of the library instead, one copy per GPU, held from the
+ * library's first use on that GPU until the process ends. Its device address
+ * is looked up on the first call on each device (hipGetSymbolAddress); the
+ * call allocates nothing.
+ *   - The shapes must fit: the workspace fkl_workspace_size reports as
+ *     fwd_bytes must be at most 64 MiB (about N <= 70 000 rows at K = 100,
+ *     V = 128 256, chunk = 2048), else FKL_E_WORKSPACE before anything runs.
+ *   - stream must belong to the current device (FKL_E_ARG otherwise).
+ *   - Every call on a GPU shares that GPU's array and leaves its contents
+ *     behind: calls that overlap on one GPU (concurrent streams, or host
+ *     threads) race and give undefined results; calls ordered on one stream
+ *     are safe. */
+int32_t fkl_forward_noalloc(const void* hidden, const void* weight, const int32_t* topk_idx,
+                            const float* topk_logit, float T, int64_t chunk, int64_t N,
+                            int64_t d, int64_t V, int32_t K, int32_t dtype, uint32_t flags,
+                            float* loss, float* lse, float* row_loss, float* topk_z,
+                            void* stream);
+
 /* Loss options
  * ------------
  * The ml-book page ("Дистилляция и сжатие моделей", section "Как это

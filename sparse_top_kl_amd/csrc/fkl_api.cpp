@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "api_common.hpp"
 #include "kernels.hpp"
@@ -233,17 +234,66 @@ int32_t check_options(const fkl_loss_options* o, float T, bool backward) {
 
 // fkl_forward and fkl_forward_keep: the chunk loop, with the logits kept in
 // `logits` (N rows of keep_pitch(V) elements) when it is non-null.
+// ---- the static scratch of fkl_forward_noalloc
+//
+// A file-scope device array stands in for the workspace argument, for callers
+// that cannot allocate. In host code the name `scratch` is only a stand-in:
+// the array's device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and only that address is
+// passed to kernels. Every call on a device shares its copy.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch, looked up on its first use.
+// A non-null stream must belong to the current device.
+int32_t static_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FKL_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(FKL_E_UNSUPPORTED, "device index %d beyond %d", dev, kMaxScratchDevices);
+  if (s) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return fail(FKL_E_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(FKL_E_ARG, "the stream belongs to device %d, the current device is %d",
+                  static_cast<int>(sdev), dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(FKL_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FKL_OK;
+}
+
+// With use_static, the workspace arguments are ignored and the current
+// device's static scratch is used instead (looked up after every argument
+// check, so a rejected call touches no device).
 int32_t forward_impl(const void* hidden, const void* weight, const int32_t* topk_idx,
                      const float* topk_logit, float T, int64_t chunk, int64_t N, int64_t d,
                      int64_t V, int32_t K, int32_t dtype, uint32_t flags,
                      const fkl_loss_options* o, float* loss, float* lse, float* row_loss,
                      float* topk_z, void* logits, size_t logits_bytes, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     size_t workspace_bytes, void* stream, bool use_static = false) {
   int32_t r = check_shapes(N, d, V, K, chunk, dtype);
   if (r) return r;
   if (!std::isfinite(T) || !(T > 0.0f)) return fail(FKL_E_ARG, "T must be finite and > 0");
   if ((flags & ~FKL_FLAG_VALIDATE_IDX) != 0) return fail(FKL_E_ARG, "unknown forward flag bits");
-  if (!loss || !weight || !workspace) return fail(FKL_E_ARG, "null pointer argument");
+  if (use_static) {
+    workspace = nullptr;
+    workspace_bytes = kStaticScratchBytes;
+  }
+  if (!loss || !weight || (!workspace && !use_static)) return fail(FKL_E_ARG, "null pointer argument");
   if (N > 0 && (!hidden || !topk_idx || !topk_logit || !lse))
     return fail(FKL_E_ARG, "null pointer argument");
   if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 16))
@@ -264,9 +314,13 @@ int32_t forward_impl(const void* hidden, const void* weight, const int32_t* topk
   }
   const Plan p = make_plan(N, d, V, K, chunk, dtype);
   if (workspace_bytes < p.f_total)
-    return fail(FKL_E_WORKSPACE, "forward workspace needs %zu bytes, got %zu", p.f_total,
-                workspace_bytes);
+    return fail(FKL_E_WORKSPACE, "forward workspace needs %zu bytes, %s %zu", p.f_total,
+                use_static ? "the static scratch holds" : "got", workspace_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (use_static) {
+    r = static_scratch(s, &workspace);
+    if (r) return r;
+  }
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   (void)hipGetLastError();
 
@@ -389,6 +443,17 @@ int32_t fkl_forward_keep_ex(const void* hidden, const void* weight, const int32_
   return forward_impl(hidden, weight, topk_idx, topk_logit, T, chunk, N, d, V, K, dtype, flags,
                       opts, loss, lse, row_loss, topk_z, logits, logits_bytes, workspace,
                       workspace_bytes, stream);
+}
+
+int32_t fkl_forward_noalloc(const void* hidden, const void* weight, const int32_t* topk_idx,
+                            const float* topk_logit, float T, int64_t chunk, int64_t N,
+                            int64_t d, int64_t V, int32_t K, int32_t dtype, uint32_t flags,
+                            float* loss, float* lse, float* row_loss, float* topk_z,
+                            void* stream) {
+  g_last_error[0] = 0;
+  return forward_impl(hidden, weight, topk_idx, topk_logit, T, chunk, N, d, V, K, dtype, flags,
+                      nullptr, loss, lse, row_loss, topk_z, nullptr, 0, nullptr, 0, stream,
+                      /*use_static=*/true);
 }
 
 static int32_t backward_impl(const void* hidden, const void* weight, const int32_t* topk_idx,

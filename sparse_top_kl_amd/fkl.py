@@ -104,6 +104,8 @@ _SIGNATURES = {
                                   _p, _p, _p, _p, _sz, _p]),
     "fkl_renorm_backward": (_i32, [_p, _p, _p, _p, _p, _p, _f32, _i64, _i64, _i64, _i32, _i32,
                                    _u32, _p, _p, _p, _p, _sz, _p]),
+    "fkl_forward_noalloc": (_i32, [_p, _p, _p, _p, _f32, _i64, _i64, _i64, _i64, _i32, _i32,
+                                   _u32, _p, _p, _p, _p, _p]),
     "fkl_timing_enable": (_i32, [_i32]),
     "fkl_timing_reset": (_i32, []),
     "fkl_timing_read": (_i32, [_i32, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]),
@@ -242,6 +244,30 @@ def fkl_forward(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Tens
                              float(T), chunk, N, d, V, K, code, flags, _ptr(loss), _ptr(lse),
                              _ptr(row_loss), _ptr(topk_z), _ptr(ws), ws.numel(), _stream(dev)))
     return ForwardResult(loss, lse, row_loss, topk_z)
+
+
+def fkl_forward_noalloc(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Tensor,
+                        topk_logit: torch.Tensor, T: float, chunk: int, *, out: ForwardResult,
+                        validate: bool = False) -> ForwardResult:
+    """fkl_forward on the library's static per-device scratch (no workspace,
+    no allocation): the outputs are written into ``out`` (loss [] and lse [N]
+    required; row_loss [N] and topk_z [N, K] may be None)."""
+    N, d = hidden.shape
+    V, K = weight.shape[0], topk_idx.shape[1]
+    code = dtype_code(hidden.dtype)
+    for t, n, dt in ((hidden, "hidden", None), (weight, "weight", hidden.dtype),
+                     (topk_idx, "topk_idx", torch.int32), (topk_logit, "topk_logit", torch.float32),
+                     (out.loss, "loss", torch.float32), (out.lse, "lse", torch.float32)):
+        _require(t, n, dt)
+    for t, n in ((out.row_loss, "row_loss"), (out.topk_z, "topk_z")):
+        if t is not None:
+            _require(t, n, torch.float32)
+    flags = FKL_FLAG_VALIDATE_IDX if validate else 0
+    _check(lib().fkl_forward_noalloc(_ptr(hidden), _ptr(weight), _ptr(topk_idx),
+                                     _ptr(topk_logit), float(T), chunk, N, d, V, K, code, flags,
+                                     _ptr(out.loss), _ptr(out.lse), _ptr(out.row_loss),
+                                     _ptr(out.topk_z), _stream(hidden.device)))
+    return out
 
 
 def fkl_backward(hidden: torch.Tensor, weight: torch.Tensor, topk_idx: torch.Tensor,

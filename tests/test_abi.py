@@ -386,3 +386,18 @@ def test_renorm_forward_validation(over, code):
 def test_renorm_backward_validation(over, code):
     assert _rbwd(**over) == code
     assert fkl.fkl_last_error() != ""
+
+
+def test_noalloc_forward_refuses_before_touching_a_device():
+    """fkl_forward_noalloc checks its arguments and that the forward workspace
+    fits its static 64 MiB scratch before any device call (so it fails the
+    same way without a GPU)."""
+    call = fkl.lib().fkl_forward_noalloc
+    ok = dict(hidden=A, weight=A, idx=A, logit=A, T=1.0, chunk=2048, N=200000, d=64, V=128256,
+              K=100, dtype=fkl.FKL_BF16, flags=0, loss=A, lse=A, row_loss=None, topk_z=None,
+              stream=None)
+    assert call(*ok.values()) == fkl.FKL_E_WORKSPACE
+    assert "static scratch" in fkl.fkl_last_error()
+    assert call(*dict(ok, loss=None).values()) == fkl.FKL_E_ARG
+    assert call(*dict(ok, T=0.0).values()) == fkl.FKL_E_ARG
+    assert call(*dict(ok, d=12).values()) == fkl.FKL_E_UNSUPPORTED
