@@ -105,10 +105,11 @@ int32_t fkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K, int64_t c
  *   loss       [1]     fp32 sum of row losses (required)
  *   lse        [N]     fp32 ln sum_v exp(z_rv / T) (required; the backward needs it)
  *   row_loss   [N]     fp32 per-row loss (may be NULL)
- *   topk_z     [N, K]  fp32 raw student logits z at the given ids (may be NULL;
+ *   topk_z     [N, K]  fp32 raw student logits z at the given ids, the same
+ *                      values the logit tiles feed the log-sum-exp (may be NULL;
  *                      passing it to fkl_backward saves a recomputation)
  * The N x V logits are never stored: each chunk's logit tiles live only in
- * registers. */
+ * registers; z at the teacher ids is taken from them as they are formed. */
 int32_t fkl_forward(const void* hidden, const void* weight, const int32_t* topk_idx,
                     const float* topk_logit, float T, int64_t chunk, int64_t N, int64_t d,
                     int64_t V, int32_t K, int32_t dtype, uint32_t flags, float* loss, float* lse,
@@ -119,7 +120,10 @@ int32_t fkl_forward(const void* hidden, const void* weight, const int32_t* topk_
  *   hidden, weight, topk_idx, topk_logit, T, chunk, N, d, V, K, dtype: as in
  *                      the forward (same values)
  *   lse        [N]     from fkl_forward (required)
- *   topk_z     [N, K]  from fkl_forward, or NULL to recompute it
+ *   topk_z     [N, K]  from fkl_forward, or NULL to recompute it (by one dot
+ *                      product per id: a different summation order, so the
+ *                      gradients then agree with the saved-topk_z ones to
+ *                      rounding, not bitwise)
  *   grad_loss  [1]     device fp32 upstream gradient s, or NULL for s = 1
  *   flags              FKL_FLAG_ACCUMULATE_GRAD_W and/or FKL_FLAG_VALIDATE_IDX
  * Outputs:
@@ -143,7 +147,7 @@ int32_t fkl_backward(const void* hidden, const void* weight, const int32_t* topk
  * is looked up on the first call on each device (hipGetSymbolAddress); the
  * call allocates nothing.
  *   - The shapes must fit: the workspace fkl_workspace_size reports as
- *     fwd_bytes must be at most 64 MiB (about N <= 70 000 rows at K = 100,
+ *     fwd_bytes must be at most 64 MiB (N <= 39 168 rows at K = 100,
  *     V = 128 256, chunk = 2048), else FKL_E_WORKSPACE before anything runs.
  *   - stream must belong to the current device (FKL_E_ARG otherwise).
  *   - Every call on a GPU shares that GPU's array and leaves its contents

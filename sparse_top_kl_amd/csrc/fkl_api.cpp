@@ -34,11 +34,17 @@ struct Plan {
   int64_t slot_cap;   // partial slots allocated per row
   // backward blocking: row blocks of bw_rows x vocabulary slices of bw_width
   int64_t bw_rows, bw_width, bw_pitch;
+  // teacher-id pair index (kernels.hpp PairIndex): bucket width, buckets, row
+  // tiles, entries per row tile (room for a label per row); pair_log2 < 0 when
+  // the vocabulary is too wide to bucket (the separate gather and fixup
+  // kernels are used instead)
+  int pair_log2;
+  int64_t n_vb, n_rt, pair_cap;
   // forward workspace offsets
-  size_t f_part, f_part_ce, f_rowloss, f_topkz, f_zy, f_flag, f_total;
+  size_t f_part, f_part_ce, f_rowloss, f_topkz, f_zy, f_pstart, f_pentry, f_flag, f_total;
   // backward workspace offsets
   size_t b_G, b_ghacc, b_pcoef, b_acoef, b_lse2, b_zk, b_bcoef, b_lse12, b_ycoef, b_zy, b_tcoef,
-      b_flag, b_total;
+      b_pstart, b_pentry, b_sub, b_tmul, b_flag, b_total;
 };
 
 // Predicted cost of the backward contractions for row blocks of rc rows and
@@ -122,6 +128,13 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_
   p.slot_cap = lse_slots(V);
   plan_backward_blocks(N > 0 ? N : 1, p.Vpad, d, p.chunk_cap, eb, &p.bw_rows, &p.bw_width);
   p.bw_pitch = fkl::round_up(p.bw_width, 64);
+  p.pair_log2 = pair_bucket_log2(V);
+  const bool pairs = p.pair_log2 >= 0;
+  p.n_vb = pairs ? ceil_div(V, int64_t(1) << p.pair_log2) : 0;
+  p.n_rt = pairs ? ceil_div(N, 256) : 0;
+  p.pair_cap = 256 * (int64_t(K) + 1);
+  const size_t pstart_bytes = static_cast<size_t>(p.n_rt) * (p.n_vb + 1) * 4;
+  const size_t pentry_bytes = static_cast<size_t>(p.n_rt) * p.pair_cap * 4;
 
   size_t off = 0;
   p.f_part = off;
@@ -134,6 +147,10 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_
   off = align_up(off + static_cast<size_t>(N) * K * 4);
   p.f_zy = off;  // z at the labels
   off = align_up(off + static_cast<size_t>(N) * 4);
+  p.f_pstart = off;
+  off = align_up(off + pstart_bytes);
+  p.f_pentry = off;
+  off = align_up(off + pentry_bytes);
   p.f_flag = off;
   off = align_up(off + 4);
   p.f_total = off;
@@ -162,6 +179,14 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_
   off = align_up(off + rows * 4);
   p.b_tcoef = off;
   off = align_up(off + rows * 4);
+  p.b_pstart = off;
+  off = align_up(off + pstart_bytes);
+  p.b_pentry = off;
+  off = align_up(off + pentry_bytes);
+  p.b_sub = off;  // exact-entry constants, K + 1 per row
+  off = align_up(off + (pairs ? rows * (K + 1) * 4 : 0));
+  p.b_tmul = off;
+  off = align_up(off + (pairs ? rows * (K + 1) * 4 : 0));
   p.b_flag = off;
   off = align_up(off + 4);
   p.b_total = off;
@@ -349,16 +374,27 @@ int32_t forward_impl(const void* hidden, const void* weight, const int32_t* topk
   mo.lse1 = o ? o->lse1 : nullptr;
   mo.teacher_lse = o ? o->teacher_lse : nullptr;
 
-  fkl::launch_gather_dot(dtype, weight, hidden, topk_idx, d, 0, N, K, zk, s);
-  if (labels) {
-    float* zy = reinterpret_cast<float*>(ws + p.f_zy);
-    fkl::launch_gather_dot(dtype, weight, hidden, labels, d, 0, N, 1, zy, s);
-    mo.zy = zy;
+  float* zy = reinterpret_cast<float*>(ws + p.f_zy);
+  if (labels) mo.zy = zy;
+  // z at the teacher ids (and labels): taken from the logit tiles through the
+  // pair index, or gathered by separate dot products for vocabularies too
+  // wide to bucket
+  fkl::PairIndex pi{};
+  if (p.pair_log2 >= 0) {
+    int32_t* pstart = reinterpret_cast<int32_t*>(ws + p.f_pstart);
+    uint32_t* pentry = reinterpret_cast<uint32_t*>(ws + p.f_pentry);
+    fkl::launch_pair_index(topk_idx, labels, N, K, V, p.pair_log2, p.n_vb, pstart, pentry,
+                           p.pair_cap, zk, zy, s);
+    pi = fkl::PairIndex{pstart, pentry, p.n_vb, p.pair_cap, p.pair_log2, K};
+  } else {
+    fkl::launch_gather_dot(dtype, weight, hidden, topk_idx, d, 0, N, K, zk, s);
+    if (labels) fkl::launch_gather_dot(dtype, weight, hidden, labels, d, 0, N, 1, zy, s);
   }
   for (int64_t row0 = 0; row0 < N; row0 += p.chunk_cap) {
     const int64_t nrows = (N - row0) < p.chunk_cap ? (N - row0) : p.chunk_cap;
     fkl::launch_logits_lse(dtype, weight, hidden, d, V, row0, nrows, c2, part, p.chunk_cap,
-                           const_cast<float2*>(mo.part_ce), logits, zpitch, s);
+                           const_cast<float2*>(mo.part_ce), logits, zpitch,
+                           p.pair_log2 >= 0 ? &pi : nullptr, zk, zy, s);
     fkl::launch_merge_loss(part, p.chunk_cap, p.nslots, zk, topk_logit, row0, nrows, K, T, lse, rl,
                            mo, s);
   }
@@ -513,6 +549,20 @@ static int32_t backward_impl(const void* hidden, const void* weight, const int32
   float* zk_ws = reinterpret_cast<float*>(ws + p.b_zk);
   const float c2 = 1.4426950408889634f / T;
   const int64_t eb = dtype == FKL_BF16 ? 2 : 4;
+  // the exact G entries at the teacher ids and labels: written by the logit
+  // tiles through the pair index, or by the separate fixup kernel for
+  // vocabularies too wide to bucket
+  const bool pairs = p.pair_log2 >= 0;
+  fkl::PairIndex pi{};
+  float* sub = reinterpret_cast<float*>(ws + p.b_sub);
+  float* tmul = reinterpret_cast<float*>(ws + p.b_tmul);
+  if (pairs) {
+    int32_t* pstart = reinterpret_cast<int32_t*>(ws + p.b_pstart);
+    uint32_t* pentry = reinterpret_cast<uint32_t*>(ws + p.b_pentry);
+    fkl::launch_pair_index(topk_idx, labels, N, K, V, p.pair_log2, p.n_vb, pstart, pentry,
+                           p.pair_cap, nullptr, nullptr, s);
+    pi = fkl::PairIndex{pstart, pentry, p.n_vb, p.pair_cap, p.pair_log2, K};
+  }
 
   for (int64_t row0 = 0; row0 < N; row0 += p.bw_rows) {
     const int64_t nrows = (N - row0) < p.bw_rows ? (N - row0) : p.bw_rows;
@@ -531,15 +581,19 @@ static int32_t backward_impl(const void* hidden, const void* weight, const int32
     fkl::launch_bwd_prep(topk_logit, lse, grad_loss, row0, nrows, K, T, row_weight, labels, a_kl,
                          a_ce, o ? o->lse1 : nullptr, two_sm, tlse, zk, pcoef, acoef, lse2,
                          two_sm ? bcoef : nullptr, two_sm ? lse12 : nullptr,
-                         labels ? ycoef : nullptr, tlse ? tcoef : nullptr, s);
+                         labels ? ycoef : nullptr, tlse ? tcoef : nullptr, topk_idx + row0 * K,
+                         pairs ? sub : nullptr, pairs ? tmul : nullptr, s);
     fkl::RowCoef rc{pcoef, acoef, lse2, two_sm ? bcoef : nullptr, two_sm ? lse12 : nullptr,
                     labels ? ycoef : nullptr, labels ? labels + row0 : nullptr,
                     labels ? zy : nullptr, tlse ? tcoef : nullptr};
+    const fkl::PairPatch pp{pi, zk, zy, sub, tmul};  // zk, zy: the block's rows
     for (int64_t v0 = 0; v0 < p.Vpad; v0 += p.bw_width) {
       const int64_t Vw = (p.Vpad - v0) < p.bw_width ? (p.Vpad - v0) : p.bw_width;
       const int64_t Vlim = (V - v0) < Vw ? (V - v0) : Vw;
-      fkl::launch_gprod(dtype, weight, hidden, d, V, v0, Vw, p.bw_pitch, row0, nrows, c2, rc, G, s);
-      fkl::launch_fixup(dtype, G, p.bw_pitch, v0, Vw, topk_idx, zk, rc, row0, nrows, K, c2, s);
+      fkl::launch_gprod(dtype, weight, hidden, d, V, v0, Vw, p.bw_pitch, row0, nrows, c2, rc, G,
+                        pairs ? &pp : nullptr, s);
+      if (!pairs)
+        fkl::launch_fixup(dtype, G, p.bw_pitch, v0, Vw, topk_idx, zk, rc, row0, nrows, K, c2, s);
       fkl::launch_grad_hidden(dtype, G, p.bw_pitch, weight, d, v0, Vw, Vlim, nrows, v0 > 0, ghacc,
                               s);
       fkl::launch_grad_w(dtype, G, p.bw_pitch, hidden, d, v0, Vw, Vlim, row0, nrows,
@@ -660,7 +714,8 @@ static int32_t backward_keep_impl(const void* hidden, const void* weight,
   fkl::launch_bwd_prep(topk_logit, lse, grad_loss, 0, N, K, T, o ? o->row_weight : nullptr, labels,
                        a_kl, a_ce, o ? o->lse1 : nullptr, two_sm, tlse, zk, pcoef, acoef, lse2,
                        two_sm ? bcoef : nullptr, two_sm ? lse12 : nullptr,
-                       labels ? ycoef : nullptr, tlse ? tcoef : nullptr, s);
+                       labels ? ycoef : nullptr, tlse ? tcoef : nullptr, topk_idx, nullptr,
+                       nullptr, s);
   const fkl::RowCoef rc{pcoef, acoef, lse2, two_sm ? bcoef : nullptr, two_sm ? lse12 : nullptr,
                         labels ? ycoef : nullptr, labels, labels ? zy : nullptr,
                         tlse ? tcoef : nullptr};

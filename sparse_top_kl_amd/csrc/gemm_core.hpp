@@ -340,12 +340,19 @@ struct TileLoop {
     __syncthreads();
   }
 
+  // The loop's LDS (one array per kernel; epilogues may reuse it once every
+  // wave has left the loop).
+  __device__ __forceinline__ static unsigned char* smem() {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+    return lds;
+  }
+
   // acc = A[tile, k_begin:k_end] . B[tile, k_begin:k_end]^T. k_begin is 0 or
   // a multiple of the stage depth; the operands' k_lim zeroes anything past
   // the true end of K.
   __device__ __forceinline__ static void run(f32x16_t (&acc)[C::kMI][C::kNI], const Operand& A,
                                              const Operand& B, int k_begin, int k_end) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+    unsigned char* const lds = smem();
     const int tid = threadIdx.x, lane = tid & 63;
 #pragma unroll
     for (int mi = 0; mi < C::kMI; ++mi)

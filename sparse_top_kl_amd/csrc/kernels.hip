@@ -117,16 +117,21 @@ struct GradValue {
   }
 };
 
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
 // Writes f(z) for the wave's sub-tile of a logit tile (accumulator rows =
 // output columns w0.., accumulator columns = tokens t0..) into Out[token][column]
 // (row pitch out_ld bytes), for tokens < nrows and columns < ncols; f gives 0
 // at columns >= f.vlim. Called by every thread of the workgroup after the
-// k-loop. NT marks the stores nontemporal (data not read again soon).
-template <class P, class C, bool NT = false, class F>
+// k-loop. NT marks the stores nontemporal (data not read again soon). hook()
+// runs before the global stores are issued (loads placed there overlap them).
+template <class P, class C, bool NT = false, class F, class Hook = NoHook>
 __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::kMI][C::kNI], const F& f,
                                                  int64_t w0, int64_t t0, int64_t nrows,
                                                  int64_t ncols, unsigned char* __restrict__ out,
-                                                 int64_t out_ld) {
+                                                 int64_t out_ld, const Hook& hook = Hook{}) {
   const int lane = threadIdx.x & 63;
   if constexpr (P::kBytes == 2) {
     // A lane holds 4 consecutive columns of one token, so direct stores would
@@ -174,6 +179,7 @@ __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::kMI][C
       fill(std::true_type{});
     else
       fill(std::false_type{});
+    hook();
     if (w0 >= ncols) return;
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
@@ -191,6 +197,7 @@ __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::kMI][C
     }
     return;
   }
+  hook();
   if (w0 >= ncols) return;
 #pragma unroll
   for (int ni = 0; ni < C::kNI; ++ni) {
@@ -213,20 +220,269 @@ __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::kMI][C
 }
 
 
+// ------------------------------------------------------------------ pair index
+
+constexpr int kPairThreads = 1024;
+
+__device__ __forceinline__ uint32_t pack_pair(int k, int tl, int32_t v) {
+  return static_cast<uint32_t>(k) | (static_cast<uint32_t>(tl) << 13) |
+         (static_cast<uint32_t>(v & 2047) << 21);
+}
+
+// One workgroup per row tile t (rows 256 t .. 256 t + 255 below N): counts its
+// pairs per vocabulary bucket in LDS, scans the counts into start[t], then
+// places each pair at its bucket's cursor. Pairs without a valid id get z = 0
+// in zk / zy (when those are given) and no entry.
+__global__ __launch_bounds__(kPairThreads) void k_pair_index(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ labels, int64_t N, int K,
+    int64_t V, int bw_log2, int64_t n_vb, int32_t* __restrict__ start,
+    uint32_t* __restrict__ entry, int64_t cap, float* __restrict__ zk, float* __restrict__ zy) {
+  __shared__ int32_t cnt[kPairMaxBuckets];
+  __shared__ int32_t wsum[kPairThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 256;
+  const int rows = static_cast<int>(N - r0 < 256 ? N - r0 : 256);
+  const int Kp = K + (labels ? 1 : 0);
+  const int npairs = rows * Kp;
+  const int nb = static_cast<int>(n_vb);
+  for (int b = tid; b < nb; b += kPairThreads) cnt[b] = 0;
+  __syncthreads();
+  for (int p = tid; p < npairs; p += kPairThreads) {
+    const int rl = p / Kp, k = p - rl * Kp;
+    const int64_t r = r0 + rl;
+    const int32_t v = k < K ? idx[r * K + k] : labels[r];
+    if (v >= 0 && v < V)
+      atomicAdd(&cnt[v >> bw_log2], 1);
+    else if (k < K) {
+      if (zk) zk[r * K + k] = 0.f;
+    } else if (zy) {
+      zy[r] = 0.f;
+    }
+  }
+  __syncthreads();
+  // exclusive scan of cnt[0, nb): each thread takes a run of consecutive
+  // buckets; runs are scanned across the wave, then across the waves
+  const int per = (nb + kPairThreads - 1) / kPairThreads;
+  const int b0 = tid * per, b1 = b0 + per < nb ? b0 + per : nb;
+  int run = 0;
+  for (int b = b0; b < b1; ++b) run += cnt[b];
+  int x = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int wbase = 0;
+  for (int i = 0; i < w; ++i) wbase += wsum[i];
+  int acc = wbase + x - run;
+  int32_t* st = start + static_cast<int64_t>(blockIdx.x) * (n_vb + 1);
+  for (int b = b0; b < b1; ++b) {
+    const int c = cnt[b];
+    cnt[b] = acc;
+    st[b] = acc;
+    acc += c;
+  }
+  if (tid == kPairThreads - 1) st[nb] = wbase + x;  // all pairs of the tile
+  __syncthreads();
+  uint32_t* ent = entry + static_cast<int64_t>(blockIdx.x) * cap;
+  for (int p = tid; p < npairs; p += kPairThreads) {
+    const int rl = p / Kp, k = p - rl * Kp;
+    const int64_t r = r0 + rl;
+    const int32_t v = k < K ? idx[r * K + k] : labels[r];
+    if (v >= 0 && v < V) ent[atomicAdd(&cnt[v >> bw_log2], 1)] = pack_pair(k, rl, v);
+  }
+}
+
+// The teacher-id pairs of one logit tile: rows [g_lo, g_hi) of the batch (at
+// most 256, tile columns tl = r - g_lo) and ids [va, vb) (vb - va <= 256,
+// c = v - va). The buckets overlapping [va, vb) span fewer than 2048 ids, so
+// an entry's low 11 id bits fix its id. The entry ranges of the tile's (at
+// most two) row tiles are read when the kernel starts, so that their latency
+// hides behind the k-loop; after the loop each thread loads one pair; pairs
+// beyond one per thread (tiles of very frequent ids only) are read from memory
+// as they are visited.
+struct TilePairs {
+  int64_t g_lo, g_hi, va, vb, gt0;
+  int32_t raw[4];  // range bounds as loaded: [start, end) in the first and second row tile
+  bool two;        // the rows span a second row tile
+  int32_t e0[2];   // first entry of the range in each row tile   (set after the loop)
+  int32_t n0, n;   // pairs in the first row tile's range; in both (set after the loop)
+  uint32_t mine;   // this thread's pair: bit 31 set, k | tl << 13 | c << 21; else 0
+};
+
+// Issues the loads of the range bounds only: nothing uses them before the
+// k-loop has run, so their latency is not waited for at the start.
+__device__ __forceinline__ TilePairs tile_pairs_begin(const PairIndex& pi, int64_t g_lo,
+                                                      int64_t g_hi, int64_t va, int64_t vb) {
+  TilePairs tp;
+  tp.g_lo = g_lo;
+  tp.g_hi = g_hi;
+  tp.va = va;
+  tp.vb = vb;
+  tp.gt0 = g_lo >> 8;
+  tp.mine = 0u;
+  const bool empty = g_hi <= g_lo || vb <= va;
+  tp.two = !empty && ((g_hi - 1) >> 8) != tp.gt0;
+  int64_t b0 = 0, b1 = 0;
+  if (!empty) {
+    b0 = va >> pi.bw_log2;
+    b1 = ((vb - 1) >> pi.bw_log2) + 1;
+    if (b1 > pi.n_vb) b1 = pi.n_vb;
+  }
+  // vector (buffer) loads: their results land in VGPRs that nothing touches
+  // until after the loop (scalar loads were waited for at once to free SGPRs)
+  const Operand st = make_operand(reinterpret_cast<const unsigned char*>(
+                                      pi.start + tp.gt0 * (pi.n_vb + 1)),
+                                  0, 0, 0);
+  const uint32_t o1 = tp.two ? static_cast<uint32_t>((pi.n_vb + 1) * 4) : 0u;
+  tp.raw[0] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(st.rsrc, b0 * 4, 0, 0));
+  tp.raw[1] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(st.rsrc, b1 * 4, 0, 0));
+  tp.raw[2] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(st.rsrc, o1 + b0 * 4, 0, 0));
+  tp.raw[3] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(st.rsrc, o1 + b1 * 4, 0, 0));
+  return tp;
+}
+
+// Pair i (0 <= i < tp.n) in the packed form, or 0 if it lies outside the tile.
+__device__ __forceinline__ uint32_t tile_pair_at(const PairIndex& pi, const TilePairs& tp,
+                                                 int32_t i) {
+  const bool first = i < tp.n0;
+  const int64_t gt = first ? tp.gt0 : tp.gt0 + 1;
+  const uint32_t e = pi.entry[gt * pi.cap + (first ? tp.e0[0] + i : tp.e0[1] + (i - tp.n0))];
+  const int64_t r = gt * 256 + ((e >> 13) & 0xffu);
+  const int64_t c = (static_cast<int64_t>(e >> 21) - tp.va) & 2047;
+  if (r < tp.g_lo || r >= tp.g_hi || tp.va + c >= tp.vb) return 0u;
+  return 0x80000000u | (e & 0x1fffu) | (static_cast<uint32_t>(r - tp.g_lo) << 13) |
+         (static_cast<uint32_t>(c) << 21);
+}
+
+// After the k-loop: the ranges, and thread t's pair.
+__device__ __forceinline__ void tile_pairs_load(const PairIndex& pi, TilePairs& tp, int t) {
+  tp.e0[0] = tp.raw[0];
+  tp.n0 = tp.raw[1] - tp.raw[0];
+  tp.e0[1] = tp.raw[2];
+  tp.n = tp.n0 + (tp.two ? tp.raw[3] - tp.raw[2] : 0);
+  tp.mine = t < tp.n ? tile_pair_at(pi, tp, t) : 0u;
+}
+
+__device__ __forceinline__ int pair_tl(uint32_t m) { return (m >> 13) & 0xffu; }
+__device__ __forceinline__ int pair_k(uint32_t m) { return m & 0x1fffu; }
+__device__ __forceinline__ int pair_c(uint32_t m) { return (m >> 21) & 0xffu; }
+
+// f(m) for every pair m of the tile: thread t's own, then those beyond one
+// per thread (threads t = 0 .. nth - 1 share them).
+template <class F>
+__device__ __forceinline__ void tile_pairs_each(const PairIndex& pi, const TilePairs& tp, int t,
+                                                int nth, F&& f) {
+  if (tp.mine) f(tp.mine);
+  for (int32_t i = nth + t; i < tp.n; i += nth) {
+    const uint32_t m = tile_pair_at(pi, tp, i);
+    if (m) f(m);
+  }
+}
+
+// The two 64 KiB halves of the idle k-loop LDS of a tile kernel (the
+// instantiation the kernels' gemm_tile<P, C, false, false> uses).
+template <class P, class C>
+__device__ __forceinline__ void loop_lds_halves(unsigned char** lo, unsigned char** hi) {
+  if constexpr (P::kBytes == 2) {
+    const auto st = PingPongLoop<C, false, false>::stage_arrays();
+    *lo = st.s[0];
+    *hi = st.s[1];
+  } else {
+    unsigned char* l = TileLoop<P, C, false, false>::smem();
+    *lo = l;
+    *hi = l + 65536;
+  }
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// z at the teacher-id pairs inside a logit tile (TilePairs, the thread's own
+// pair loaded): the pairs' positions are marked in a per-tile bitmap, the
+// waves holding marked accumulators write them (in groups of four vocabulary
+// rows) to an fp32 staging area [token][128 vocabulary] in the idle k-loop LDS,
+// one vocabulary half at a time, and the pair's thread reads its value back
+// and stores it: zk[r][k] (k < K) or zy[r] (k = K, the label).
+template <class P, class C>
+__device__ __forceinline__ void gather_tile_pairs(const f32x16_t (&acc)[C::kMI][C::kNI],
+                                                  const PairIndex& pi, const TilePairs& tp,
+                                                  float* __restrict__ zk, float* __restrict__ zy) {
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  __shared__ uint32_t bits[256 * 8];
+  const int tid = threadIdx.x, lane = tid & 63;
+  constexpr int nth = C::kThreads;
+  unsigned char *glo, *ghi;
+  loop_lds_halves<P, C>(&glo, &ghi);
+  lds_u8* const stage_lo = (lds_u8*)glo;
+  lds_u8* const stage_hi = (lds_u8*)ghi;
+  for (int i = tid; i < 256 * 8; i += nth) bits[i] = 0u;
+  __syncthreads();  // every wave has left the k-loop: its LDS is free
+  tile_pairs_each(pi, tp, tid, nth, [&](uint32_t m) {
+    const int c = pair_c(m);
+    atomicOr(&bits[pair_tl(m) * 8 + (c >> 5)], 1u << (c & 31));
+  });
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (C::wave_m() == h) {  // this wave holds tile rows 128 h .. 128 h + 127
+#pragma unroll
+      for (int ni = 0; ni < C::kNI; ++ni) {
+        const int tl = C::wave_n() * C::kWN + ni * 32 + (lane & 31);
+        lds_u8* const row = (tl < 128 ? stage_lo : stage_hi) + (tl & 127) * 512;
+#pragma unroll
+        for (int mi = 0; mi < C::kMI; ++mi)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int vl = mi * 32 + 8 * g4 + 4 * (lane >> 5);  // row within the half
+            const uint32_t word = bits[tl * 8 + h * 4 + (vl >> 5)];
+            if ((word >> (vl & 31)) & 0xfu)
+              *(__attribute__((address_space(3))) f32x4_t*)(row + vl * 4) =
+                  f32x4_t{acc[mi][ni][4 * g4], acc[mi][ni][4 * g4 + 1], acc[mi][ni][4 * g4 + 2],
+                          acc[mi][ni][4 * g4 + 3]};
+          }
+      }
+    }
+    __syncthreads();
+    tile_pairs_each(pi, tp, tid, nth, [&](uint32_t m) {
+      const int c = pair_c(m) - h * 128;
+      if (c < 0 || c >= 128) return;
+      const int tl = pair_tl(m), k = pair_k(m);
+      const float z = *(const __attribute__((address_space(3))) float*)(
+          (tl < 128 ? stage_lo : stage_hi) + (tl & 127) * 512 + c * 4);
+      const int64_t r = tp.g_lo + tl;
+      if (k < pi.K)
+        zk[r * pi.K + k] = z;
+      else
+        zy[r] = z;
+    });
+    __syncthreads();
+  }
+}
+
 // With KEEP the tile's logits are also written, rounded to the element type,
 // into Z[token][v] (row pitch zld bytes) for v < zcols, as zero for v >= V
 // (streaming stores: the backward reads them much later).
 // With CE2 the partials at temperature 1 (c = log2(e)) go to part_ce as well.
+// With pi.entry non-null, z at the teacher-id pairs of the tile goes to zk /
+// zy (gather_tile_pairs); row0 is the batch row of the chunk's first row.
 template <class P, class C, bool KEEP, bool CE2>
 __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_logits_lse(
     const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
     int64_t nrows, int64_t n_vt, int64_t n_tt, float c2, float2* __restrict__ part,
     int64_t part_ld, float2* __restrict__ part_ce, unsigned char* __restrict__ Z, int64_t zld,
-    int64_t zcols) {
+    int64_t zcols, PairIndex pi, int64_t row0, float* __restrict__ zk, float* __restrict__ zy) {
   static_assert(C::kWM == kSliceVocab, "one LSE partial per wave row-slice");
   int64_t vt, tt;
   if (!TileGroups<4, 8>::coords(n_vt, n_tt, &vt, &tt)) return;
   const int64_t ld = d * P::kBytes;
+  TilePairs tp;
+  if (pi.entry) {
+    const int64_t va = vt * kBM, ntok = nrows - tt * kBN < kBN ? nrows - tt * kBN : kBN;
+    tp = tile_pairs_begin(pi, row0 + tt * kBN, row0 + tt * kBN + ntok, va,
+                          va + kBM < V ? va + kBM : V);
+  }
   // MFMA rows = vocabulary entries (weight rows), columns = tokens, so each
   // lane's accumulators belong to one token and the reduction over the
   // vocabulary is mostly in-lane.
@@ -234,6 +490,7 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_logits_lse(
   const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
   f32x16_t acc[C::kMI][C::kNI];
   gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
+  if (pi.entry) tile_pairs_load(pi, tp, static_cast<int>(threadIdx.x));
 
   const int64_t v0 = vt * kBM + C::wave_m() * C::kWM;
   if (v0 < V) {
@@ -242,6 +499,7 @@ __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_logits_lse(
       lse_partials<C>(acc, v0, V, tt * kBN + C::wave_n() * C::kWN, nrows, kLog2e, part_ce,
                       part_ld);
   }
+  if (pi.entry) gather_tile_pairs<P, C>(acc, pi, tp, zk, zy);
   if constexpr (KEEP)
     store_token_rows<P, C, true>(acc, LogitValue{V}, v0, tt * kBN + C::wave_n() * C::kWN, nrows, zcols,
                            Z, zld);
@@ -392,15 +650,21 @@ __global__ __launch_bounds__(1024) void k_reduce_loss(const float* __restrict__ 
 
 // ------------------------------------------------------------------ backward
 
-// One wave per row, coefficients of its logit gradient with s the upstream
-// scale, w the row weight and y the label:
+// One wave (workgroup) per row, coefficients of its logit gradient with s the
+// upstream scale, w the row weight and y the label:
 //   pcoef_k = s w a_kl T p_k,  ycoef = s w a_ce [y >= 0],
 //   acoef = s w a_kl T sum_k p_k (+ ycoef when the cross-entropy shares the
 //   softmax, i.e. T = 1), bcoef = ycoef when it has its own (two_sm),
 //   lse2 = lse log2(e), lse1_2 = lse1 log2(e).
-// logit, lse and the outputs start at the block's first row; row_weight,
+// With sub / tmul (row pitch K + 1; dynamic LDS of 8 K bytes) also the
+// constants of the exact entries at the row's pairs: for entry k with id v,
+//   sub_k = sum of pcoef over the entries with id v (+ ycoef if v = y),
+//   tmul_k = tcoef x (number of entries with id v);
+// for the label (entry K): sub = ycoef, tmul = 0, or NaN when y is also a
+// teacher id (those entries then carry it).
+// logit, lse, idx and the outputs start at the block's first row; row_weight,
 // labels and lse1 are indexed by absolute row (row0 + row).
-__global__ __launch_bounds__(256) void k_bwd_prep(
+__global__ __launch_bounds__(64) void k_bwd_prep(
     const float* __restrict__ logit, const float* __restrict__ lse,
     const float* __restrict__ grad_loss, int64_t row0, int64_t nrows, int K, float T,
     const float* __restrict__ row_weight, const int32_t* __restrict__ labels, float a_kl,
@@ -408,9 +672,13 @@ __global__ __launch_bounds__(256) void k_bwd_prep(
     const float* __restrict__ teacher_lse, const float* __restrict__ zk,
     float* __restrict__ pcoef, float* __restrict__ acoef, float* __restrict__ lse2,
     float* __restrict__ bcoef, float* __restrict__ lse1_2, float* __restrict__ ycoef,
-    float* __restrict__ tcoef) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    float* __restrict__ tcoef, const int32_t* __restrict__ idx, float* __restrict__ sub,
+    float* __restrict__ tmul) {
+  extern __shared__ int32_t sh_prep[];
+  int32_t* sid = sh_prep;
+  float* sp = reinterpret_cast<float*>(sh_prep + K);
+  const int lane = threadIdx.x;
+  const int64_t row = blockIdx.x;
   if (row >= nrows) return;
   const int64_t ar = row0 + row;
   const float s = grad_loss ? *grad_loss : 1.0f;
@@ -419,7 +687,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(
   const float yc = has_y ? s * w * a_ce : 0.f;
   const float scale = s * w * a_kl * T;
   float psum = 0.f, tail = 0.f, tc = 0.f;
-  if (w != 0.f) {  // uniform per wave
+  if (w != 0.f) {
     const float invT = 1.0f / T;
     const float* lg = logit + row * K;
     float logZ;  // as in k_merge_loss
@@ -438,6 +706,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(
       const float p = expf(lg[k] * invT - logZ);
       psum += p;
       pcoef[row * K + k] = scale * p;
+      if (sub) sp[k] = scale * p;
       if (teacher_lse) S += expf(zk[row * K + k] * invT - lse[row]);
     }
     psum = wave_sum(psum);
@@ -452,7 +721,10 @@ __global__ __launch_bounds__(256) void k_bwd_prep(
       tc = scale * pt * inv;
     }
   } else {
-    for (int k = lane; k < K; k += 64) pcoef[row * K + k] = 0.f;
+    for (int k = lane; k < K; k += 64) {
+      pcoef[row * K + k] = 0.f;
+      if (sub) sp[k] = 0.f;
+    }
   }
   if (lane == 0) {
     acoef[row] = scale * (psum - tail) + (two_sm ? 0.f : yc);
@@ -462,31 +734,37 @@ __global__ __launch_bounds__(256) void k_bwd_prep(
     if (lse1_2) lse1_2[row] = two_sm ? lse1[ar] * kLog2e : 0.f;
     if (ycoef) ycoef[row] = yc;
   }
+  if (sub) {
+    const int Kp = K + 1;
+    const int32_t y = has_y ? labels[ar] : -1;
+    for (int k = lane; k < K; k += 64) sid[k] = idx[row * K + k];
+    // the wave's LDS writes are visible to its own later reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int k = lane; k < K; k += 64) {
+      const int32_t v = sid[k];
+      float ps = 0.f, m = 0.f;
+      for (int k2 = 0; k2 < K; ++k2) {
+        const bool eq = sid[k2] == v;
+        ps += eq ? sp[k2] : 0.f;
+        m += eq ? 1.f : 0.f;
+      }
+      sub[row * Kp + k] = ps + (v == y ? yc : 0.f);
+      tmul[row * Kp + k] = tc * m;
+    }
+    if (lane == 0) {
+      bool found = false;
+      for (int k2 = 0; k2 < K; ++k2) found |= (sid[k2] == y);
+      sub[row * Kp + K] = found ? __builtin_nanf("") : yc;
+      tmul[row * Kp + K] = 0.f;
+    }
+  }
 }
 
 // Recompute the logit tile of rows [0, nrows) x vocabulary [v0, v0 + Vw) and
 // write the dense part of G (GradValue) into the G block G[row][v - v0]
 // (row pitch gpitch elements; entries with v >= V are written as zero).
-template <class P, class C, bool CE2>
-__global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_gprod(
-    const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
-    int64_t v0, int64_t Vw, int64_t gpitch, int64_t nrows, int64_t n_vt, int64_t n_tt, float c2,
-    RowCoef rc, unsigned char* __restrict__ G) {
-  int64_t vt, tt;
-  if (!TileGroups<4, 8>::coords(n_vt, n_tt, &vt, &tt)) return;
-  const int64_t ld = d * P::kBytes;
-  const int64_t vbase = v0 + vt * kBM;  // first vocabulary entry of the tile
-  const Operand A = make_operand(W + vbase * ld, ld, V - vbase, d);
-  const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
-  f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
-
-  const int64_t w0 = vt * kBM + C::wave_m() * C::kWM;  // slice-relative column of the wave
-  const int64_t t0 = tt * kBN + C::wave_n() * C::kWN;  // first token of the wave
-  const GradValue<CE2> f{rc.acoef, rc.lse2, rc.bcoef, rc.lse1_2, c2, V - v0, nrows};
-  store_token_rows<P, C>(acc, f, w0, t0, nrows, Vw, G, gpitch * P::kBytes);
-}
-
 // Dense part of G at one logit for one row's coefficients.
 struct DenseCoef {
   float a, l2, b, l1;
@@ -507,6 +785,76 @@ __device__ __forceinline__ void store_one(unsigned char* grow, int64_t col, floa
     reinterpret_cast<uint16_t*>(grow)[col] = f32_to_bf16_rne(val);
   else
     reinterpret_cast<float*>(grow)[col] = val;
+}
+
+// With pp.pi.entry non-null, after the tile's dense entries have been stored,
+// the exact entries at the teacher-id and label pairs of the tile overwrite
+// them (PairPatch; each entry is rounded once, from the gathered fp32 logit).
+// row0 is the batch row of the block's first row.
+template <class P, class C, bool CE2>
+__global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_gprod(
+    const unsigned char* __restrict__ W, const unsigned char* __restrict__ H, int64_t d, int64_t V,
+    int64_t v0, int64_t Vw, int64_t gpitch, int64_t nrows, int64_t n_vt, int64_t n_tt, float c2,
+    RowCoef rc, unsigned char* __restrict__ G, int64_t row0, PairPatch pp) {
+  int64_t vt, tt;
+  if (!TileGroups<4, 8>::coords(n_vt, n_tt, &vt, &tt)) return;
+  const int64_t ld = d * P::kBytes;
+  const int64_t vbase = v0 + vt * kBM;  // first vocabulary entry of the tile
+  TilePairs tp;
+  if (pp.pi.entry) {
+    int64_t vb = vbase + kBM;
+    if (vb > v0 + Vw) vb = v0 + Vw;
+    if (vb > V) vb = V;
+    const int64_t ntok = nrows - tt * kBN < kBN ? nrows - tt * kBN : kBN;
+    tp = tile_pairs_begin(pp.pi, row0 + tt * kBN, row0 + tt * kBN + ntok, vbase, vb);
+  }
+  const Operand A = make_operand(W + vbase * ld, ld, V - vbase, d);
+  const Operand B = make_operand(H + tt * kBN * ld, ld, nrows - tt * kBN, d);
+  f32x16_t acc[C::kMI][C::kNI];
+  gemm_tile<P, C, false, false>(acc, A, B, static_cast<int>(d));
+  if (pp.pi.entry) tile_pairs_load(pp.pi, tp, static_cast<int>(threadIdx.x));
+
+  const int64_t w0 = vt * kBM + C::wave_m() * C::kWM;  // slice-relative column of the wave
+  const int64_t t0 = tt * kBN + C::wave_n() * C::kWN;  // first token of the wave
+  const GradValue<CE2> f{rc.acoef, rc.lse2, rc.bcoef, rc.lse1_2, c2, V - v0, nrows};
+  if (!pp.pi.entry) {
+    store_token_rows<P, C>(acc, f, w0, t0, nrows, Vw, G, gpitch * P::kBytes);
+    return;
+  }
+  // Exact entries at the tile's pairs: the values a pair needs are loaded
+  // while the dense part is staged and written, and the exact entry replaces
+  // the dense one once every dense store of the tile has completed (a thread's
+  // stores complete in order; the wait and the barrier order them across the
+  // workgroup).
+  const int Kp = pp.pi.K + 1;
+  struct Vals {
+    float z, sub, tmul;
+    DenseCoef dc;
+  };
+  auto vals = [&](uint32_t m) {
+    const int64_t rb = tt * kBN + pair_tl(m);  // row of the block
+    const int k = pair_k(m);
+    return Vals{k < pp.pi.K ? pp.zk[rb * pp.pi.K + k] : pp.zy[rb], pp.sub[rb * Kp + k],
+                pp.tmul[rb * Kp + k], row_dense(rc, rb)};
+  };
+  auto put = [&](uint32_t m, const Vals& x) {
+    if (x.sub != x.sub) return;  // a label that is also a teacher id: its entries write it
+    float g = dense_g(x.dc, x.z, c2) - x.sub;
+    if (x.tmul != 0.f) g += x.tmul * fast_exp2(x.z * c2 - x.dc.l2);
+    const int64_t rb = tt * kBN + pair_tl(m);
+    store_one<P>(G + rb * gpitch * P::kBytes, vt * kBM + pair_c(m), g);
+  };
+  Vals mine{};
+  store_token_rows<P, C>(acc, f, w0, t0, nrows, Vw, G, gpitch * P::kBytes, [&]() {
+    if (tp.mine) mine = vals(tp.mine);
+  });
+  wait_vmcnt_lgkm0<0>();
+  __syncthreads();
+  if (tp.mine) put(tp.mine, mine);
+  for (int32_t i = C::kThreads + static_cast<int>(threadIdx.x); i < tp.n; i += C::kThreads) {
+    const uint32_t m = tile_pair_at(pp.pi, tp, i);
+    if (m) put(m, vals(m));
+  }
 }
 
 // The exact entries of one row of G inside columns [v0, v0 + Vw): at each
@@ -746,10 +1094,21 @@ __global__ __launch_bounds__(256) void k_validate_idx(const int32_t* __restrict_
 
 // ------------------------------------------------------------------ launchers
 
+void launch_pair_index(const int32_t* idx, const int32_t* labels, int64_t N, int K, int64_t V,
+                       int bw_log2, int64_t n_vb, int32_t* start, uint32_t* entry, int64_t cap,
+                       float* zk, float* zy, hipStream_t s) {
+  if (N <= 0) return;
+  ScopedTimer timer_(KID_PAIR_INDEX, s);
+  k_pair_index<<<static_cast<unsigned>(ceil_div(N, 256)), kPairThreads, 0, s>>>(
+      idx, labels, N, K, V, bw_log2, n_vb, start, entry, cap, zk, zy);
+}
+
 void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64_t V,
                        int64_t row0, int64_t nrows, float c2, float2* part, int64_t part_ld,
-                       float2* part_ce, void* Z, int64_t zpitch, hipStream_t s) {
+                       float2* part_ce, void* Z, int64_t zpitch, const PairIndex* pi, float* zk,
+                       float* zy, hipStream_t s) {
   ScopedTimer timer_(KID_LOGITS_LSE, s);
+  const PairIndex pix = pi ? *pi : PairIndex{};
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(V, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
@@ -761,10 +1120,12 @@ void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64
   do {                                                                                            \
     if (dtype == 1)                                                                               \
       k_logits_lse<BF16, Cfg8, KEEP, CE2><<<grid, Cfg8::kThreads, 0, s>>>(                        \
-          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, part_ce, Zc, zld, zpitch);          \
+          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, part_ce, Zc, zld, zpitch, pix,      \
+          row0, zk, zy);                                                                          \
     else                                                                                          \
       k_logits_lse<F32, Cfg4, KEEP, CE2><<<grid, Cfg4::kThreads, 0, s>>>(                         \
-          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, part_ce, Zc, zld, zpitch);          \
+          Wc, Hc, d, V, nrows, n_vt, n_tt, c2, part, part_ld, part_ce, Zc, zld, zpitch, pix,      \
+          row0, zk, zy);                                                                          \
   } while (0)
   if (Z && part_ce)
     FKL_LOGITS(true, true);
@@ -824,18 +1185,21 @@ void launch_bwd_prep(const float* logit, const float* lse, const float* grad_los
                      const int32_t* labels, float a_kl, float a_ce, const float* lse1,
                      bool two_sm, const float* teacher_lse, const float* zk, float* pcoef,
                      float* acoef, float* lse2, float* bcoef, float* lse1_2, float* ycoef,
-                     float* tcoef, hipStream_t s) {
+                     float* tcoef, const int32_t* idx, float* sub, float* tmul, hipStream_t s) {
+  if (nrows <= 0) return;
   ScopedTimer timer_(KID_BWD_PREP, s);
-  const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, 4));
-  k_bwd_prep<<<blocks, 256, 0, s>>>(logit + row0 * K, lse + row0, grad_loss, row0, nrows, K, T,
-                                    row_weight, labels, a_kl, a_ce, lse1, two_sm, teacher_lse, zk,
-                                    pcoef, acoef, lse2, bcoef, lse1_2, ycoef, tcoef);
+  const size_t shm = sub ? static_cast<size_t>(K) * 8 : 0;
+  k_bwd_prep<<<static_cast<unsigned>(nrows), 64, shm, s>>>(
+      logit + row0 * K, lse + row0, grad_loss, row0, nrows, K, T, row_weight, labels, a_kl, a_ce,
+      lse1, two_sm, teacher_lse, zk, pcoef, acoef, lse2, bcoef, lse1_2, ycoef, tcoef, idx, sub,
+      tmul);
 }
 
 void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t v0,
                   int64_t Vw, int64_t gpitch, int64_t row0, int64_t nrows, float c2,
-                  const RowCoef& rc, void* G, hipStream_t s) {
+                  const RowCoef& rc, void* G, const PairPatch* pp, hipStream_t s) {
   ScopedTimer timer_(KID_GPROD, s);
+  const PairPatch ppx = pp ? *pp : PairPatch{};
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_vt = ceil_div(Vw, kBM), n_tt = ceil_div(nrows, kBN);
   const unsigned char* Hc = static_cast<const unsigned char*>(H) + row0 * d * eb;
@@ -845,11 +1209,11 @@ void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V,
 #define FKL_GPROD(CE2)                                                                            \
   do {                                                                                            \
     if (dtype == 1)                                                                               \
-      k_gprod<BF16, Cfg8, CE2><<<grid, Cfg8::kThreads, 0, s>>>(Wc, Hc, d, V, v0, Vw, gpitch,       \
-                                                               nrows, n_vt, n_tt, c2, rc, Gc);    \
+      k_gprod<BF16, Cfg8, CE2><<<grid, Cfg8::kThreads, 0, s>>>(                                   \
+          Wc, Hc, d, V, v0, Vw, gpitch, nrows, n_vt, n_tt, c2, rc, Gc, row0, ppx);                \
     else                                                                                          \
-      k_gprod<F32, Cfg4, CE2><<<grid, Cfg4::kThreads, 0, s>>>(Wc, Hc, d, V, v0, Vw, gpitch, nrows, \
-                                                              n_vt, n_tt, c2, rc, Gc);            \
+      k_gprod<F32, Cfg4, CE2><<<grid, Cfg4::kThreads, 0, s>>>(                                    \
+          Wc, Hc, d, V, v0, Vw, gpitch, nrows, n_vt, n_tt, c2, rc, Gc, row0, ppx);                \
   } while (0)
   if (rc.bcoef)
     FKL_GPROD(true);

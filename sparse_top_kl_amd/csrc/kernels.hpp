@@ -36,6 +36,39 @@ struct RowCoef {
   const float* tcoef;      // [rows] or null (no tail bucket)
 };
 
+// Teacher-id pairs of the batch, bucketed so that a logit tile finds the
+// pairs it holds in one contiguous range: for each tile of 256 rows (global
+// row / 256) the pairs sorted by vocabulary bucket (id >> bw_log2), with
+// start[t][b] .. start[t][b + 1] the bucket's entries in the tile's block of
+// `cap` entries. An entry packs the pair's entry index k (bits 0-12; k = K is
+// the row's label when labels are indexed), its row within the tile (bits
+// 13-20) and the id's low 11 bits (21-31), which fix the id inside any window
+// of fewer than 2048 ids. Order inside a bucket is unspecified (each pair has
+// its own output).
+struct PairIndex {
+  const int32_t* start;   // [n_rt][n_vb + 1]
+  const uint32_t* entry;  // [n_rt][cap]
+  int64_t n_vb;           // vocabulary buckets
+  int64_t cap;            // entries per row tile: 256 * Kp
+  int32_t bw_log2;        // bucket width 2^bw_log2 (32 .. 512)
+  int32_t K;              // teacher entries per row (pair K is the label)
+};
+constexpr int kPairMaxBuckets = 16384;  // buckets one row tile sorts in LDS
+// Bucket width (log2) for a vocabulary of V ids: the smallest power of two
+// >= 32 with at most kPairMaxBuckets buckets; -1 if V needs buckets wider than 512.
+inline int pair_bucket_log2(int64_t V) {
+  for (int b = 5; b <= 9; ++b)
+    if (((V + (int64_t(1) << b) - 1) >> b) <= kPairMaxBuckets) return b;
+  return -1;
+}
+
+// Builds the pair index of rows [0, N) (ids [N][K], optional labels [N]; a
+// label < 0 or an id outside [0, V) is no pair: its z output is set to 0 in
+// zk [N][K] / zy [N] instead). One workgroup per row tile.
+void launch_pair_index(const int32_t* idx, const int32_t* labels, int64_t N, int K, int64_t V,
+                       int bw_log2, int64_t n_vb, int32_t* start, uint32_t* entry, int64_t cap,
+                       float* zk, float* zy, hipStream_t s);
+
 // Rows of a (vocab-slice, token) partial: running max and sum of 2^(z*c2).
 constexpr int kSliceVocab = 128;  // vocabulary entries per partial slot
 
@@ -49,9 +82,12 @@ inline int64_t lse_slots(int64_t V) { return ceil_div(V, 256) * 2; }
 // With Z non-null the chunk's logits are also kept: Z[row0 + r][v] (pitch zpitch
 // elements of the dtype) = z rounded to the dtype for v < V, zero for V <= v < zpitch.
 // With part_ce non-null, partials at temperature 1 are written there too.
+// With pi non-null the tile also writes z at the teacher-id pairs of its rows
+// and vocabulary: zk[r][k] (global row r) and, for label pairs, zy[r].
 void launch_logits_lse(int dtype, const void* W, const void* H, int64_t d, int64_t V,
                        int64_t row0, int64_t nrows, float c2, float2* part, int64_t part_ld,
-                       float2* part_ce, void* Z, int64_t zpitch, hipStream_t s);
+                       float2* part_ce, void* Z, int64_t zpitch, const PairIndex* pi, float* zk,
+                       float* zy, hipStream_t s);
 // z at the teacher ids for rows [row0, row0 + nrows) (an id < 0 gives 0).
 void launch_gather_dot(int dtype, const void* W, const void* H, const int32_t* idx, int64_t d,
                        int64_t row0, int64_t nrows, int K, float* zk, hipStream_t s);
@@ -70,17 +106,32 @@ void launch_reduce_loss(const float* row_loss, int64_t N, float* loss, hipStream
 // temperature-1 softmax of the cross-entropy term.
 // With teacher_lse (absolute rows) the tail bucket's coefficients need zk
 // (block rows) and go to tcoef.
+// With sub / tmul non-null (pitch K + 1 per row) also the per-pair constants of
+// the exact entries (PairPatch); idx starts at the block's first row.
 void launch_bwd_prep(const float* logit, const float* lse, const float* grad_loss, int64_t row0,
                      int64_t nrows, int K, float T, const float* row_weight,
                      const int32_t* labels, float a_kl, float a_ce, const float* lse1,
                      bool two_sm, const float* teacher_lse, const float* zk, float* pcoef,
                      float* acoef, float* lse2, float* bcoef, float* lse1_2, float* ycoef,
-                     float* tcoef, hipStream_t s);
+                     float* tcoef, const int32_t* idx, float* sub, float* tmul, hipStream_t s);
+// Exact entries of G at the teacher-id and label pairs (backward): the entry
+// of pair (r, k) is dense(z) - sub[k] + tmul[k] 2^(z c2 - lse2) with z the
+// gathered logit; sub and tmul are [rows][K + 1] (entry K is the label's, NaN
+// in sub when the label is also a teacher id, whose entries then write it).
+// zk [rows][K], zy [rows], sub and tmul start at the block's first row.
+struct PairPatch {
+  PairIndex pi;
+  const float* zk;
+  const float* zy;
+  const float* sub;
+  const float* tmul;
+};
 // Recompute the logit block rows [row0, row0 + nrows) x vocabulary [v0, v0 + Vw) into
-// the dense part of G (pitch gpitch elements).
+// the dense part of G (pitch gpitch elements); with pp non-null, then the exact
+// entries at the pairs inside the tile.
 void launch_gprod(int dtype, const void* W, const void* H, int64_t d, int64_t V, int64_t v0,
                   int64_t Vw, int64_t gpitch, int64_t row0, int64_t nrows, float c2,
-                  const RowCoef& rc, void* G, hipStream_t s);
+                  const RowCoef& rc, void* G, const PairPatch* pp, hipStream_t s);
 // Exact G entries at the teacher ids and the label that fall inside the slice.
 void launch_fixup(int dtype, void* G, int64_t gpitch, int64_t v0, int64_t Vw, const int32_t* idx,
                   const float* zk, const RowCoef& rc, int64_t row0, int64_t nrows, int K,

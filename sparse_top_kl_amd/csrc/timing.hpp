@@ -34,6 +34,7 @@ enum KernelId : int32_t {
   KID_RS_CHUNKS,
   KID_RS_FIX,
   KID_RS_HOT,
+  KID_PAIR_INDEX,
   KID_COUNT
 };
 

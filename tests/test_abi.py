@@ -42,18 +42,29 @@ def test_abi_version_and_status_strings():
     assert fkl.fkl_status_string(12345) == "unknown status"
 
 
+def pair_index_bytes(N, V, K):
+    """The teacher-id pair index both passes build: per tile of 256 rows, one
+    offset per 32-id vocabulary bucket (+1) and room for 256 (K + 1) packed
+    pairs (the +1: a hard label per row)."""
+    tiles = (N + 255) // 256
+    return tiles * ((V + 31) // 32 + 1) * 4 + tiles * 256 * (K + 1) * 4
+
+
 def test_workspace_is_bounded_by_chunk_times_vocab_and_never_rows_times_vocab():
     d, V, K, chunk = 3072, 128256, 100, 2048
     Vpad = (V + 7) // 8 * 8
     for N in (8192, 32768, 65536, 131072):
         f, b = fkl.fkl_workspace_size(N, d, V, K, chunk, fkl.FKL_BF16)
         # forward: per-chunk partials (one float2 per row and 128-wide slice, at T and at
-        # temperature 1 for the cross-entropy option) + per-row scratch
-        assert f <= 2 * chunk * ((V + 255) // 256) * 2 * 8 + N * (8 + 4 * K) + (1 << 16)
+        # temperature 1 for the cross-entropy option) + per-row scratch + the pair index
+        assert f <= 2 * chunk * ((V + 255) // 256) * 2 * 8 + N * (8 + 4 * K) + \
+            pair_index_bytes(N, V, K) + (1 << 16)
         # backward: one logit-gradient block within the chunk x V budget (its rows padded
         # by fewer than 64 elements to whole 128-byte lines), plus per-row scratch of a
-        # row block (fp32 grad_hidden accumulator, teacher coefficients)
-        assert b <= chunk * Vpad * 2 + min(N, 1 << 16) * (4 * d + 8 * K + 8 + 128) + (1 << 16)
+        # row block (fp32 grad_hidden accumulator, teacher coefficients, the constants of
+        # the exact entries) and the pair index
+        assert b <= chunk * Vpad * 2 + min(N, 1 << 16) * (4 * d + 16 * K + 16 + 128) + \
+            pair_index_bytes(N, V, K) + (1 << 16)
         if N >= 8 * chunk:
             assert b < N * V * 2 / 4  # far below one dense bf16 N x V matrix
     # a larger chunk buys a larger block
@@ -72,14 +83,16 @@ def test_backward_row_blocks_keep_hidden_rows_within_32_bit_offsets():
     for dtype, eb in ((fkl.FKL_BF16, 2), (fkl.FKL_F32, 4)):
         N, d, V, K = 200000, 8192, 1024, 16
         _, b = fkl.fkl_workspace_size(N, d, V, K, N, dtype)
-        per_row = ((V + 63) // 64 * 64) * eb + 4 * d + 8 * K + 7 * 4
-        rows = b // per_row
+        # G row, grad_hidden accumulator, K-entry coefficient rows (two of K, two of
+        # K + 1) and seven scalars; the pair index depends on N only
+        per_row = ((V + 63) // 64 * 64) * eb + 4 * d + 8 * K + 8 * (K + 1) + 7 * 4
+        rows = (b - pair_index_bytes(N, V, K)) // per_row
         assert rows * d * eb < 2 ** 31, (dtype, rows)
         assert rows >= 256
         # a smaller batch still fits in one block
         n_small = (2 ** 31 - 2 ** 20) // (d * eb) // 2
         _, b_small = fkl.fkl_workspace_size(n_small, d, V, K, n_small, dtype)
-        assert b_small // per_row == n_small
+        assert (b_small - pair_index_bytes(n_small, V, K)) // per_row == n_small
 
 
 def test_workspace_size_rejects_bad_shapes():
