@@ -14,7 +14,9 @@ N x V buffer). With --teacher-topk it times the teacher top-K cache producer
 (fkl_teacher_topk over a teacher workload) and prints that line instead.
 With --keep-logits the step is the forward-chunked variant instead
 (fkl_forward_keep + fkl_backward_keep: the logits are kept in an N x V buffer
-and not recomputed, 6 N d V flops per step).
+and not recomputed, 6 N d V flops per step). Where tests/golden holds the
+oracle's values for the workload, every row's lse and row loss, the total
+loss and the stored grad_W rows are compared with them (parity_fixture).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--keep-logits]
 """
@@ -129,6 +131,43 @@ def cpu_baseline(inp, gpu_rows: dict, budget_s: float):
                   f"(NumPy BLAS), {t:.1f} s; grad_W restricted to those rows",
     }
     return base, parity
+
+
+def fixture_parity(case: str, w, gpu_rows: dict, gw_rows):
+    """Every row's lse and row loss, the total loss and the stored grad_W rows
+    against the oracle's values for this workload (tests/golden, written by
+    tests/golden/make_fullsize_fixtures.py, which runs only the oracle);
+    None when there is no fixture for the case."""
+    path = os.path.join(ROOT, "tests", "golden", f"fullsize_{case}.npz")
+    if not os.path.exists(path):
+        return None
+    with np.load(path, allow_pickle=False) as f:
+        fx = {k: f[k] for k in f.files}
+    if (list(fx["params"]) != [w.B, w.S, w.d, w.V, w.K, w.chunk, w.seed]
+            or float(fx["T"]) != w.T):
+        return None
+    tol = 1e-3 if w.dtype == "bf16" else 1e-5
+    gtol = 2e-2 if w.dtype == "bf16" else 1e-4
+
+    def rel_floor(a, b):
+        return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), 1.0)))
+
+    out = {
+        "case": case,
+        "rows": int(w.N),
+        "lse_err": rel_floor(gpu_rows["lse"], fx["lse"].astype(np.float64)),
+        "row_loss_err": rel_floor(gpu_rows["row_loss"], fx["row_loss"].astype(np.float64)),
+        "loss_rel_err": abs(gpu_rows["loss"] - float(fx["loss"])) / abs(float(fx["loss"])),
+    }
+    for g in ("hot", "cold", "tail", "random"):
+        ref = fx[f"grad_w_{g}"].astype(np.float64)
+        out[f"grad_w_{g}_err_over_max"] = float(np.max(np.abs(gw_rows(fx[f"vocab_{g}"]) - ref)) /
+                                                np.max(np.abs(ref)))
+    out["ok"] = bool(out["lse_err"] <= tol and out["row_loss_err"] <= tol and
+                     out["loss_rel_err"] <= tol and
+                     all(out[f"grad_w_{g}_err_over_max"] <= gtol
+                         for g in ("hot", "cold", "tail", "random")))
+    return out
 
 
 def calibration_copy(args, torch, dev):
@@ -631,12 +670,10 @@ def main():
     zbuf = torch.empty(w.N, fkl.keep_pitch(w.V), dtype=dt, device=dev) if keep else None
 
     opts = {}
-    if args.options:
-        g = torch.Generator(device=dev)
-        g.manual_seed(w.seed)
-        labels = torch.randint(0, w.V, (w.N,), device=dev, generator=g, dtype=torch.int32)
-        tlse = (torch.logsumexp(lg / w.T, dim=1) + math.log(2.0)).contiguous()
-        opts = dict(labels=labels, alpha=0.5, teacher_lse=tlse)
+    if args.options:  # the generator's option inputs (those of the oracle fixture)
+        o = synth.make_loss_options(w)
+        opts = dict(labels=torch.from_numpy(o["labels"]).to(dev), alpha=o["alpha"],
+                    teacher_lse=torch.from_numpy(o["teacher_lse"]).to(dev))
 
     def step():
         if opts:
@@ -681,6 +718,10 @@ def main():
         "grad_hidden": gh.double().cpu().numpy(),
     }
     loss_val = out.loss.item()
+    gpu_rows["loss"] = loss_val
+    parity_fx = fixture_parity(
+        w.name + ("-options" if args.options else ""), w, gpu_rows,
+        lambda v: gw[torch.as_tensor(v, device=dev)].double().cpu().numpy())
     del out, gh
 
     log(f"[bench] timing {args.steps} steps")
@@ -753,6 +794,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": base,
         "parity_sampled": parity,
+        "parity_fixture": parity_fx,
         "peak_hbm_gib": peak / 2**30,
         "peak_hbm_path_gib": (peak - input_bytes) / 2**30,
         "largest_workspace_gib": largest_ws / 2**30,

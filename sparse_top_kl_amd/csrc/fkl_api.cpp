@@ -47,14 +47,17 @@ struct Plan {
       b_pstart, b_pentry, b_sub, b_tmul, b_flag, b_total;
 };
 
+// Rounds of 256 x 256 tiles a launch of `tiles` tiles takes: every XCD (8 of
+// 32 CUs) runs an equal share of the tiles, 32 at a time (TileGroups).
+inline int64_t tile_rounds(int64_t tiles) { return fkl::ceil_div(fkl::ceil_div(tiles, 8), 32); }
+
 // Predicted cost of the backward contractions for row blocks of rc rows and
 // vocabulary slices of width vs, in units of one value of the contraction
-// length on a full round of 256 x 256 tiles: a launch runs ceil(tiles / CUs)
-// rounds whose contraction length is d (logit tiles), the slice width
-// (grad_hidden) or the block's rows (grad_W); each slice adds a fixed cost for
-// its launches. The sizes are those of the loops in fkl_backward.
+// length on a round of tiles: a launch runs tile_rounds(tiles) rounds whose
+// contraction length is d (logit tiles), the slice width (grad_hidden) or the
+// block's rows (grad_W); each slice adds a fixed cost for its launches. The
+// sizes are those of the loops in fkl_backward.
 double backward_cost(int64_t N, int64_t Vpad, int64_t d, int64_t rc, int64_t vs) {
-  constexpr int64_t kCUs = 256;  // MI355X compute units
   constexpr double kSliceCost = 1000.0;
   const int64_t dt = fkl::ceil_div(d, 256);
   double c = 0.0;
@@ -64,8 +67,8 @@ double backward_cost(int64_t N, int64_t Vpad, int64_t d, int64_t rc, int64_t vs)
     for (int64_t v0 = 0; v0 < Vpad; v0 += vs) {
       const int64_t vw = Vpad - v0 < vs ? Vpad - v0 : vs;
       const int64_t vt = fkl::ceil_div(vw, 256);
-      c += double(fkl::ceil_div(rt * vt, kCUs)) * d + double(fkl::ceil_div(rt * dt, kCUs)) * vw +
-           double(fkl::ceil_div(vt * dt, kCUs)) * nr + kSliceCost;
+      c += double(tile_rounds(rt * vt)) * d + double(tile_rounds(rt * dt)) * vw +
+           double(tile_rounds(vt * dt)) * nr + kSliceCost;
     }
   }
   return c;

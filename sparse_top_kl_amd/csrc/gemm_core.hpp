@@ -728,64 +728,63 @@ __device__ __forceinline__ void gemm_tile(f32x16_t (&acc)[C::kMI][C::kNI], const
 
 // Grouped, XCD-aware tile order. Blocks are dealt round-robin over the 8 XCDs
 // (launch block b runs on XCD b % 8) and each XCD runs ~32 workgroups at a
-// time (one per CU). Output tiles are cut into groups of GA x GB = 32 tiles;
-// group q runs entirely on XCD q % 8, as 32 consecutive blocks of that XCD, so
-// the workgroups resident on an XCD share GA panels of one operand and GB of
-// the other in its L2 instead of each streaming its own. Launch with
-// grouped_grid() blocks; blocks whose tile falls outside the grid exit.
+// time (one per CU). The output tiles are laid out in strips of GB tile
+// columns, each strip row-major, and each XCD takes an equal contiguous share
+// of that order (its blocks in launch order walk its share). The 32
+// workgroups an XCD runs at once are consecutive tiles: (32 / GB) tile rows of
+// one strip (GA x GB for full strips), so one L2 serves their GA panels of one
+// operand and GB of the other instead of each streaming its own; and every
+// XCD has the same number of tiles, so a grid of T tiles takes
+// ceil(ceil(T / 8) / 32) rounds of 32 on each XCD (whole groups of 32 per XCD
+// left some XCDs a round more than others whenever the group count was not a
+// multiple of 8). Launch with grid() blocks; blocks past the grid exit.
 template <int GA, int GB>
 struct TileGroups {
-  static_assert(GA * GB == 32, "one group per XCD wave of workgroups");
-  static int64_t grid(int64_t mt, int64_t nt) {
-    const int64_t ngroups = ((mt + GA - 1) / GA) * ((nt + GB - 1) / GB);
-    return 8 * ((ngroups + 7) / 8) * 32;
+  static_assert(GA * GB == 32, "one group per XCD round of workgroups");
+  static int64_t grid(int64_t mt, int64_t nt) { return 8 * ((mt * nt + 7) / 8); }
+  // Tile of position t (0 <= t < mt * nt) in the strip order.
+  __device__ __forceinline__ static void tile_of(int64_t t, int64_t mt, int64_t nt, int64_t* tm,
+                                                 int64_t* tn) {
+    const int64_t full = (nt / GB) * GB * mt;  // tiles in full-width strips
+    if (t < full) {
+      const int64_t s = t / (GB * mt), r = t - s * (GB * mt);
+      *tm = r / GB;
+      *tn = s * GB + r % GB;
+    } else {
+      const int64_t ws = nt % GB, r = t - full;
+      *tm = r / ws;
+      *tn = (nt / GB) * GB + r % ws;
+    }
   }
   __device__ __forceinline__ static bool coords(int64_t mt, int64_t nt, int64_t* tm, int64_t* tn) {
+    const int64_t total = mt * nt, per = (total + 7) / 8;
     const int64_t b = blockIdx.x;
-    const int64_t xcd = b & 7, local = b >> 3;
-    const int64_t q = (local >> 5) * 8 + xcd, j = local & 31;
-    const int64_t gn = (nt + GB - 1) / GB;
-    const int64_t gm_i = q / gn, gn_i = q % gn;
-    *tm = gm_i * GA + (j % GA);
-    *tn = gn_i * GB + (j / GA);
-    return *tm < mt && *tn < nt;
+    const int64_t t = (b & 7) * per + (b >> 3);
+    if ((b >> 3) >= per || t >= total) return false;
+    tile_of(t, mt, nt, tm, tn);
+    return true;
   }
   // The same with `splits` copies of the tile grid (a split of the
-  // contraction): group index q runs over splits x groups, so the copies go to
-  // XCDs the first one leaves idle. splits = 1 is coords().
+  // contraction): position t runs over splits x tiles, split-major, so the
+  // copies are spread over the XCDs like any other tiles. splits = 1 is coords().
   static int64_t grid_split(int64_t mt, int64_t nt, int64_t splits) {
-    const int64_t ngroups = ((mt + GA - 1) / GA) * ((nt + GB - 1) / GB) * splits;
-    return 8 * ((ngroups + 7) / 8) * 32;
+    return 8 * ((mt * nt * splits + 7) / 8);
   }
   __device__ __forceinline__ static bool coords_split(int64_t mt, int64_t nt, int64_t splits,
                                                       int64_t* tm, int64_t* tn, int64_t* sp) {
-    // grids stay far below 2^31 blocks: 32-bit index arithmetic
-    const uint32_t b = blockIdx.x;
-    const uint32_t xcd = b & 7, local = b >> 3;
-    const uint32_t q = (local >> 5) * 8 + xcd, j = local & 31;
-    const uint32_t gn = static_cast<uint32_t>((nt + GB - 1) / GB);
-    const uint32_t ng = static_cast<uint32_t>((mt + GA - 1) / GA) * gn;
-    *sp = q / ng;
-    const uint32_t qq = q % ng;
-    *tm = (qq / gn) * GA + (j % GA);
-    *tn = (qq % gn) * GB + (j / GA);
-    return *sp < splits && *tm < mt && *tn < nt;
+    const int64_t tiles = mt * nt, total = tiles * splits, per = (total + 7) / 8;
+    const int64_t b = blockIdx.x;
+    const int64_t t = (b & 7) * per + (b >> 3);
+    if ((b >> 3) >= per || t >= total) return false;
+    *sp = t / tiles;
+    tile_of(t - *sp * tiles, mt, nt, tm, tn);
+    return true;
   }
 };
 
 // Row offset, inside the wave sub-tile, of accumulator element r of block mi.
 __device__ __forceinline__ int acc_row(int mi, int r, int lane) {
   return mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
-
-// Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8).
-// Give each XCD one contiguous range of tile indices so that tiles sharing an
-// operand panel run on the same XCD and hit its L2. The grid is launched with
-// 8 * ceil(total / 8) blocks; indices >= total exit.
-__device__ __forceinline__ int64_t xcd_tile_index(int64_t total) {
-  const int64_t b = blockIdx.x;
-  const int64_t per = (total + 7) / 8;
-  return (b & 7) * per + (b >> 3);
 }
 
 // Two fp32 values rounded to nearest-even bf16 and packed (lo in bits 0-15):
