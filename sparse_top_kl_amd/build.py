@@ -2,6 +2,9 @@
 
 Usage: ``python -m sparse_top_kl_amd.build`` (or ``__graft_entry__.build()``).
 The library is written next to this file; the binding loads it from there.
+``python -m sparse_top_kl_amd.build --sanitize`` builds a host-instrumented
+copy (ASan + UBSan) under _objs_sanitized/, which a process selects with
+FKL_LIBRARY and runs with the ASan runtime preloaded (sanitizer_runtime()).
 """
 
 from __future__ import annotations
@@ -45,23 +48,51 @@ def compile_flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the same
+# sources (the device code is compiled as usual): argument validation,
+# workspace planning and the launch loops run instrumented. Each -fsanitize=
+# is preceded by -Xarch_host so that it applies to the host compilation only.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZED_LIB = os.path.join(HERE, "_objs_sanitized", "libfkl_sanitized.so")
+
+
+def sanitizer_runtime() -> str:
+    """The clang ASan runtime (with the UBSan handlers) that a process using
+    the sanitized library must preload."""
+    llvm = os.path.join(os.path.dirname(os.path.dirname(hipcc())), "lib", "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(llvm), reverse=True):
+        path = os.path.join(llvm, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(path):
+            return path
+    raise RuntimeError("clang ASan runtime not found")
+
+
+def build(verbose: bool = False, jobs: int | None = None, sanitize: bool = False) -> str:
     cc = hipcc()
-    os.makedirs(os.path.join(HERE, "_objs"), exist_ok=True)
+    objdir = os.path.join(HERE, "_objs_sanitized" if sanitize else "_objs")
+    os.makedirs(objdir, exist_ok=True)
+    extra = ["-O1", "-g", *SANITIZE_FLAGS] if sanitize else []
     cmds, objs = [], []
     for src in SOURCES:
-        obj = os.path.join(HERE, "_objs", os.path.splitext(src)[0] + ".o")
-        cmds.append([cc, *compile_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmds.append([cc, *compile_flags(), *extra, "-x", "hip", "-c", os.path.join(CSRC, src),
+                     "-o", obj])
         objs.append(obj)
     # one hipcc process per source, a few at a time
     jobs = jobs or min(len(cmds), max(1, min(4, (os.cpu_count() or 1) // 2)))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as pool:
         for fut in [pool.submit(_run, c, verbose) for c in cmds]:
             fut.result()
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    out = SANITIZED_LIB if sanitize else LIB
+    tmp = out + ".tmp"
+    link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-shared-libsan"] if sanitize else []
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp],
+         verbose)
+    os.replace(tmp, out)
+    return out
 
 
 def _run(cmd, verbose):
@@ -77,4 +108,4 @@ def _run(cmd, verbose):
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))
