@@ -32,8 +32,10 @@ struct Plan {
   int64_t Vpad;       // vocabulary rounded up to 8
   int64_t nslots;     // vocabulary slices holding a partial (valid ones)
   int64_t slot_cap;   // partial slots allocated per row
-  // backward blocking: row blocks of bw_rows x vocabulary slices of bw_width
-  int64_t bw_rows, bw_width, bw_pitch;
+  // backward blocking: row blocks of bw_rows x vocabulary slices of bw_width;
+  // grad_hidden's contraction over a slice cut in gh_splits parts (separate
+  // fp32 accumulators) when its tiles alone would leave CUs idle
+  int64_t bw_rows, bw_width, bw_pitch, gh_splits;
   // teacher-id pair index (kernels.hpp PairIndex): bucket width, buckets, row
   // tiles, entries per row tile (room for a label per row); pair_log2 < 0 when
   // the vocabulary is too wide to bucket (the separate gather and fixup
@@ -120,6 +122,26 @@ void plan_backward_blocks(int64_t N, int64_t Vpad, int64_t d, int64_t chunk_cap,
   }
 }
 
+// Parts the grad_hidden contraction over a slice of width vs is cut into, for
+// row blocks of rc rows: the count (1 .. 4) with the fewest predicted rounds x
+// contraction length (tile_rounds), e.g. 2 when one block's 256 x 256 tiles
+// alone take 1.5 rounds of the chip.
+int64_t grad_hidden_splits(int64_t rc, int64_t vs, int64_t d) {
+  const int64_t tiles = fkl::ceil_div(rc, 256) * fkl::ceil_div(d, 256);
+  int64_t best = 1;
+  double best_cost = 1e300;
+  for (int64_t sp = 1; sp <= 4; ++sp) {
+    const int64_t kc = fkl::round_up(fkl::ceil_div(vs, sp), 64);
+    if (sp > 1 && kc * (sp - 1) >= vs) break;  // a part would be empty
+    const double c = double(tile_rounds(tiles * sp)) * double(kc) * (1.0 + 0.02 * double(sp - 1));
+    if (c < best_cost) {
+      best_cost = c;
+      best = sp;
+    }
+  }
+  return best;
+}
+
 Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_t dtype) {
   using namespace fkl;
   Plan p{};
@@ -131,6 +153,7 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_
   p.slot_cap = lse_slots(V);
   plan_backward_blocks(N > 0 ? N : 1, p.Vpad, d, p.chunk_cap, eb, &p.bw_rows, &p.bw_width);
   p.bw_pitch = fkl::round_up(p.bw_width, 64);
+  p.gh_splits = grad_hidden_splits(p.bw_rows, p.bw_width, d);
   p.pair_log2 = pair_bucket_log2(V);
   const bool pairs = p.pair_log2 >= 0;
   p.n_vb = pairs ? ceil_div(V, int64_t(1) << p.pair_log2) : 0;
@@ -163,7 +186,7 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int32_
   p.b_G = off;
   off = align_up(off + rows * p.bw_pitch * eb);
   p.b_ghacc = off;
-  off = align_up(off + rows * d * 4);
+  off = align_up(off + rows * d * 4 * static_cast<size_t>(p.gh_splits));
   p.b_pcoef = off;
   off = align_up(off + rows * K * 4);
   p.b_acoef = off;
@@ -598,11 +621,11 @@ static int32_t backward_impl(const void* hidden, const void* weight, const int32
       if (!pairs)
         fkl::launch_fixup(dtype, G, p.bw_pitch, v0, Vw, topk_idx, zk, rc, row0, nrows, K, c2, s);
       fkl::launch_grad_hidden(dtype, G, p.bw_pitch, weight, d, v0, Vw, Vlim, nrows, v0 > 0, ghacc,
-                              s);
+                              p.gh_splits, s);
       fkl::launch_grad_w(dtype, G, p.bw_pitch, hidden, d, v0, Vw, Vlim, row0, nrows,
                          accumulate || row0 > 0, grad_weight, s);
     }
-    fkl::launch_reduce_grad_hidden(dtype, ghacc, 1, nrows, d, grad_hidden, row0, s);
+    fkl::launch_reduce_grad_hidden(dtype, ghacc, p.gh_splits, nrows, d, grad_hidden, row0, s);
   }
   return hip_check("backward launch");
 }
@@ -724,7 +747,7 @@ static int32_t backward_keep_impl(const void* hidden, const void* weight,
                         tlse ? tcoef : nullptr};
   fkl::launch_g_from_z(dtype, logits, zpitch, V, topk_idx, zk, rc, N, K, c2, s);
   // grad_hidden over all rows in one launch (tiles of 256 rows reach 256 * zld bytes)
-  fkl::launch_grad_hidden(dtype, logits, zpitch, weight, d, 0, zpitch, V, N, false, ghacc, s);
+  fkl::launch_grad_hidden(dtype, logits, zpitch, weight, d, 0, zpitch, V, N, false, ghacc, 1, s);
   fkl::launch_reduce_grad_hidden(dtype, ghacc, 1, N, d, grad_hidden, 0, s);
   // grad_W over row blocks whose rows stay within the 32-bit offsets of both
   // operands (the kept rows and the hidden rows)

@@ -981,21 +981,29 @@ __global__ __launch_bounds__(kGzThreads) void k_g_from_z(unsigned char* __restri
 }
 
 // acc[row][col] (+)= sum over the slice of G[row][v - v0] W[v][col], for the rows
-// of one block; the slice is Vw entries wide (Vlim of them below V).
+// of one block; the slice is Vw entries wide (Vlim of them below V). With
+// splits > 1 the slice is cut into parts of split_k columns (a multiple of the
+// stage depth), part sp contracted into its own copy out + sp * out_split_stride
+// (each copy receives one contribution per element per launch; the copies are
+// summed in a fixed order afterwards).
 template <class P, class C>
 __global__ __launch_bounds__(C::kThreads) FKL_WAVES_PER_EU(C) void k_grad_hidden(
     const unsigned char* __restrict__ G, int64_t gpitch, const unsigned char* __restrict__ W,
     int64_t d, int64_t Vw, int64_t Vlim, int64_t nrows, int64_t n_tt, int64_t n_dt,
-    int accumulate, float* __restrict__ out) {
-  int64_t tt, dt;
-  if (!TileGroups<8, 4>::coords(n_tt, n_dt, &tt, &dt)) return;
+    int accumulate, float* __restrict__ out, int64_t splits, int64_t split_k,
+    int64_t out_split_stride) {
+  int64_t tt, dt, sp;
+  if (!TileGroups<8, 4>::coords_split(n_tt, n_dt, splits, &tt, &dt, &sp)) return;
   const int64_t gld = gpitch * P::kBytes, wld = d * P::kBytes;
+  const int64_t k0 = sp * split_k;
+  const int64_t kn = Vw - k0 < split_k ? Vw - k0 : split_k;  // columns of this part
+  out += sp * out_split_stride;
   // A = G rows of this tile (k = slice column), B = W rows of the slice (k = v), columns of
   // this tile
-  const Operand A = make_operand(G + tt * kBM * gld, gld, nrows - tt * kBM, Vw);
-  const Operand B = make_operand(W + dt * kBN * P::kBytes, wld, d - dt * kBN, Vlim);
+  const Operand A = make_operand(G + tt * kBM * gld + k0 * P::kBytes, gld, nrows - tt * kBM, kn);
+  const Operand B = make_operand(W + dt * kBN * P::kBytes + k0 * wld, wld, d - dt * kBN, Vlim - k0);
   f32x16_t acc[C::kMI][C::kNI];
-  gemm_tile<P, C, false, true>(acc, A, B, static_cast<int>(Vw));
+  gemm_tile<P, C, false, true>(acc, A, B, static_cast<int>(kn > 0 ? kn : 0));
 
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -1252,15 +1260,17 @@ void launch_g_from_z(int dtype, void* Z, int64_t zpitch, int64_t V, const int32_
 
 void launch_grad_hidden(int dtype, const void* G, int64_t gpitch, const void* W, int64_t d,
                         int64_t v0, int64_t Vw, int64_t Vlim, int64_t nrows, bool accumulate,
-                        float* acc, hipStream_t s) {
+                        float* acc, int64_t splits, hipStream_t s) {
   ScopedTimer timer_(KID_GRAD_HIDDEN, s);
   const int64_t eb = dtype == 1 ? 2 : 4;
   const int64_t n_tt = ceil_div(nrows, kBM), n_dt = ceil_div(d, kBN);
   const unsigned char* Ws = static_cast<const unsigned char*>(W) + v0 * d * eb;
-  const unsigned grid = grouped_grid<8, 4>(n_tt, n_dt);
+  if (splits < 1) splits = 1;
+  const int64_t split_k = round_up(ceil_div(Vw, splits), 64);
+  const unsigned grid = static_cast<unsigned>(TileGroups<8, 4>::grid_split(n_tt, n_dt, splits));
   FKL_LAUNCH_GEMM(k_grad_hidden, dtype, grid, s,
                   static_cast<const unsigned char*>(G), gpitch, Ws, d, Vw, Vlim, nrows, n_tt, n_dt,
-                  accumulate ? 1 : 0, acc);
+                  accumulate ? 1 : 0, acc, splits, split_k, nrows * d);
 }
 
 void launch_reduce_grad_hidden(int dtype, const float* part, int64_t splits, int64_t nrows,

@@ -141,10 +141,12 @@ void launch_fixup(int dtype, void* G, int64_t gpitch, int64_t v0, int64_t Vw, co
 void launch_g_from_z(int dtype, void* Z, int64_t zpitch, int64_t V, const int32_t* idx,
                      const float* zk, const RowCoef& rc, int64_t nrows, int K, float c2,
                      hipStream_t s);
-// acc[nrows][d] (+)= G_block . W[v0 : v0 + Vw]  (Vlim entries of the slice lie below V).
+// acc[nrows][d] (+)= G_block . W[v0 : v0 + Vw]  (Vlim entries of the slice lie below V);
+// with splits > 1 the slice's columns are cut in `splits` parts contracted into
+// `splits` copies of acc (stride nrows * d), to be summed by the reduction.
 void launch_grad_hidden(int dtype, const void* G, int64_t gpitch, const void* W, int64_t d,
                         int64_t v0, int64_t Vw, int64_t Vlim, int64_t nrows, bool accumulate,
-                        float* acc, hipStream_t s);
+                        float* acc, int64_t splits, hipStream_t s);
 void launch_reduce_grad_hidden(int dtype, const float* part, int64_t splits, int64_t nrows,
                                int64_t d, void* grad_hidden, int64_t row0, hipStream_t s);
 // grad_W[v0 : v0 + Vlim] (+)= G_block^T . H[row0 : row0 + nrows].

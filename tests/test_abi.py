@@ -62,8 +62,9 @@ def test_workspace_is_bounded_by_chunk_times_vocab_and_never_rows_times_vocab():
         # backward: one logit-gradient block within the chunk x V budget (its rows padded
         # by fewer than 64 elements to whole 128-byte lines), plus per-row scratch of a
         # row block (fp32 grad_hidden accumulator, teacher coefficients, the constants of
-        # the exact entries) and the pair index
-        assert b <= chunk * Vpad * 2 + min(N, 1 << 16) * (4 * d + 16 * K + 16 + 128) + \
+        # the exact entries; up to four fp32 accumulators when grad_hidden's contraction is
+        # split) and the pair index
+        assert b <= chunk * Vpad * 2 + min(N, 1 << 16) * (16 * d + 16 * K + 16 + 128) + \
             pair_index_bytes(N, V, K) + (1 << 16)
         if N >= 8 * chunk:
             assert b < N * V * 2 / 4  # far below one dense bf16 N x V matrix
