@@ -434,31 +434,13 @@ __global__ __launch_bounds__(1024) void k_rs_chunks(
   if (c0 >= d) return;
   const int64_t ld = d * P::kBytes;
   const unsigned char* hc = H + c0 * P::kBytes;
-  int i = 0;
-  while (i < n) {
-    const int32_t v = sv[i];
+  // The chunk's pairs are taken eight at a time whatever the runs (runs of
+  // rare ids are one to a few pairs long), so eight row loads are always in
+  // flight; a run's sum is written out when its last pair has been added.
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto flush = [&](int q) {  // q: the last pair of a run
+    const int32_t v = sv[q];
     const int64_t bs = start[v], be = start[v + 1];
-    const int run_end = static_cast<int>((be < e ? be : e) - a);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int q = i;
-    for (; q + 8 <= run_end; q += 8) {
-      float x[8][8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) load8<P>(hc + srow[q + u] * ld, x[u]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float g = sc[q + u];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, x[u][j], acc[j]);
-      }
-    }
-    for (; q < run_end; ++q) {
-      float x[8];
-      load8<P>(hc + srow[q] * ld, x);
-      const float g = sc[q];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, x[j], acc[j]);
-    }
     float* dst;
     bool add = false;
     if (bs < a)
@@ -470,8 +452,31 @@ __global__ __launch_bounds__(1024) void k_rs_chunks(
       add = acc_out;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dst[j] = add ? dst[j] + acc[j] : acc[j];
-    i = run_end;
+    for (int j = 0; j < 8; ++j) {
+      dst[j] = add ? dst[j] + acc[j] : acc[j];
+      acc[j] = 0.f;
+    }
+  };
+  int q = 0;
+  for (; q + 8 <= n; q += 8) {
+    float x[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) load8<P>(hc + srow[q + u] * ld, x[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float g = sc[q + u];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, x[u][j], acc[j]);
+      if (q + u + 1 == n || sv[q + u + 1] != sv[q + u]) flush(q + u);
+    }
+  }
+  for (; q < n; ++q) {
+    float x[8];
+    load8<P>(hc + srow[q] * ld, x);
+    const float g = sc[q];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, x[j], acc[j]);
+    if (q + 1 == n || sv[q + 1] != sv[q]) flush(q);
   }
 }
 
