@@ -593,6 +593,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="long32k")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="rows per pass instead of the workload's (a different memory budget; "
+                         "the line then names it and no stored oracle values apply)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--keep-logits", action="store_true",
@@ -642,6 +645,9 @@ def main():
         memory_sweep(args, torch, fkl, dev)
         return
     w = synth.WORKLOADS[args.workload]
+    if args.chunk > 0:
+        import dataclasses
+        w = dataclasses.replace(w, chunk=args.chunk)
     if args.vendor_gemm:
         vendor_gemm_step(args, torch, w, dev)
         return

@@ -572,23 +572,18 @@ __global__ __launch_bounds__(256) void k_gather_dot(const unsigned char* __restr
   }
 }
 
-// One wave per row of the chunk: lse at T (and at temperature 1 with
-// partials there), the teacher softmax over the K entries, the row's KL term
-// and, with labels, its cross-entropy; row_loss = w (a_kl T^2 KL + a_ce CE).
-// zk, logit, lse_out and row_loss start at the chunk's first row; the
-// option arrays are indexed by absolute row (row0 + row).
-__global__ __launch_bounds__(256) void k_merge_loss(const float2* __restrict__ part, int64_t part_ld,
-                                                    int64_t nslots, const float* __restrict__ zk,
-                                                    const float* __restrict__ logit, int64_t row0,
-                                                    int64_t nrows, int K, float T,
-                                                    float* __restrict__ lse_out,
-                                                    float* __restrict__ row_loss, MergeOpts o) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= nrows) return;
+// The loss of one row of the chunk given its lse at T and at temperature 1
+// (called by one whole wave): the teacher softmax over the K entries, the
+// row's KL term and, with labels, its cross-entropy; row_loss = w (a_kl T^2 KL
+// + a_ce CE). zk, logit, lse_out and row_loss start at the chunk's first row;
+// the option arrays are indexed by absolute row (row0 + row).
+__device__ __forceinline__ void merge_row_loss(const float* __restrict__ zk,
+                                               const float* __restrict__ logit, int64_t row0,
+                                               int64_t row, int K, float T, float lse, float lse1,
+                                               float* __restrict__ lse_out,
+                                               float* __restrict__ row_loss, const MergeOpts& o,
+                                               int lane) {
   const int64_t ar = row0 + row;
-  const float lse = merge_lse(part, part_ld, nslots, row);
-  const float lse1 = o.part_ce ? merge_lse(o.part_ce, part_ld, nslots, row) : lse;
   const float w = o.row_weight ? o.row_weight[ar] : 1.0f;
   float term = 0.f;
   if (w != 0.f) {  // uniform per wave; a weight-0 (padding) row may lack teacher entries
@@ -633,6 +628,67 @@ __global__ __launch_bounds__(256) void k_merge_loss(const float2* __restrict__ p
     if (row_loss) row_loss[row] = w != 0.f ? w * (o.a_kl * T * T * term + o.a_ce * ce) : 0.f;
   }
 }
+
+// Rows per k_merge_loss block: 16 consecutive rows share each 128-byte line of
+// the [slot][row] partials, so the merge reads whole lines.
+constexpr int kMergeRows = 16;
+
+// Per row of the chunk: lse at T (and at temperature 1 with partials there)
+// from the (vocabulary slice, row) partials, then the row's loss. A block of
+// 16 waves takes 16 rows: in the merge, lane (sub, r) of wave wv reads slots
+// 4 wv + sub + 64 j of row r, four loads in flight; the four subs of a wave,
+// then the 16 waves, are merged in a fixed order. Then wave wv computes the
+// loss of row wv.
+constexpr int kMergeWaves = 16;
+
+__global__ __launch_bounds__(64 * kMergeWaves) void k_merge_loss(
+    const float2* __restrict__ part, int64_t part_ld, int64_t nslots,
+    const float* __restrict__ zk, const float* __restrict__ logit, int64_t row0, int64_t nrows,
+    int K, float T, float* __restrict__ lse_out, float* __restrict__ row_loss, MergeOpts o) {
+  __shared__ float2 red[2][kMergeWaves][kMergeRows];
+  __shared__ float s_lse[2][kMergeRows];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t rb = static_cast<int64_t>(blockIdx.x) * kMergeRows;
+  {
+    const int r = lane & 15, sub = lane >> 4;
+    const bool valid = rb + r < nrows;
+    constexpr int kStride = 4 * kMergeWaves;
+    for (int t = 0; t < (o.part_ce ? 2 : 1); ++t) {
+      const float2* P = t ? o.part_ce : part;
+      float m = -INFINITY, sm = 0.f;
+      if (valid) {
+        for (int64_t sl = 4 * wv + sub; sl < nslots; sl += 4 * kStride) {
+          float2 q[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            q[u] = sl + u * kStride < nslots ? P[(sl + u * kStride) * part_ld + rb + r]
+                                             : make_float2(-INFINITY, 0.f);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) merge_ms(m, sm, q[u].x, q[u].y);
+        }
+      }
+#pragma unroll
+      for (int x = 16; x <= 32; x <<= 1) {
+        const float mo = __shfl_xor(m, x), so = __shfl_xor(sm, x);
+        merge_ms(m, sm, mo, so);
+      }
+      if (sub == 0) red[t][wv][r] = make_float2(m, sm);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 2 * kMergeRows) {
+    const int t = threadIdx.x / kMergeRows, r = threadIdx.x % kMergeRows;
+    float m = -INFINITY, sm = 0.f;
+    for (int i = 0; i < kMergeWaves; ++i) merge_ms(m, sm, red[t][i][r].x, red[t][i][r].y);
+    s_lse[t][r] = (m + log2f(sm)) * kLn2;
+  }
+  __syncthreads();
+  const int64_t row = rb + wv;
+  if (row < nrows)
+    merge_row_loss(zk, logit, row0, row, K, T, s_lse[0][wv], o.part_ce ? s_lse[1][wv] : s_lse[0][wv],
+                   lse_out, row_loss, o, lane);
+}
+
 
 __global__ __launch_bounds__(1024) void k_reduce_loss(const float* __restrict__ row_loss, int64_t N,
                                                       float* __restrict__ loss) {
@@ -742,10 +798,27 @@ __global__ __launch_bounds__(64) void k_bwd_prep(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    bool found = false;  // y is one of the row's ids
     for (int k = lane; k < K; k += 64) {
       const int32_t v = sid[k];
+      found |= v == y;
       float ps = 0.f, m = 0.f;
-      for (int k2 = 0; k2 < K; ++k2) {
+      int k2 = 0;
+      for (; k2 + 4 <= K; k2 += 4) {  // K is a multiple of 4 only by chance: tail below
+        int32_t ids[4];
+        float pv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ids[u] = sid[k2 + u];
+          pv[u] = sp[k2 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ps += ids[u] == v ? pv[u] : 0.f;
+          m += ids[u] == v ? 1.f : 0.f;
+        }
+      }
+      for (; k2 < K; ++k2) {
         const bool eq = sid[k2] == v;
         ps += eq ? sp[k2] : 0.f;
         m += eq ? 1.f : 0.f;
@@ -753,9 +826,8 @@ __global__ __launch_bounds__(64) void k_bwd_prep(
       sub[row * Kp + k] = ps + (v == y ? yc : 0.f);
       tmul[row * Kp + k] = tc * m;
     }
+    found = __any(found);
     if (lane == 0) {
-      bool found = false;
-      for (int k2 = 0; k2 < K; ++k2) found |= (sid[k2] == y);
       sub[row * Kp + K] = found ? __builtin_nanf("") : yc;
       tmul[row * Kp + K] = 0.f;
     }
@@ -1177,8 +1249,8 @@ void launch_merge_loss(const float2* part, int64_t part_ld, int64_t nslots, cons
                        const float* logit, int64_t row0, int64_t nrows, int K, float T,
                        float* lse, float* row_loss, const MergeOpts& opts, hipStream_t s) {
   ScopedTimer timer_(KID_MERGE_LOSS, s);
-  const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, 4));
-  k_merge_loss<<<blocks, 256, 0, s>>>(part, part_ld, nslots, zk + row0 * K, logit + row0 * K,
+  const unsigned blocks = static_cast<unsigned>(ceil_div(nrows, kMergeRows));
+  k_merge_loss<<<blocks, 64 * kMergeWaves, 0, s>>>(part, part_ld, nslots, zk + row0 * K, logit + row0 * K,
                                       row0, nrows, K, T, lse + row0,
                                       row_loss ? row_loss + row0 : nullptr, opts);
 }
