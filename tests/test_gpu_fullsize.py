@@ -1,30 +1,38 @@
-"""Parity at the full workload sizes, in the launch configuration the
-benchmark times (same chunk, library-planned blocking, bf16 inputs).
+"""Parity against the fp64 oracle at the full workload sizes, in the launch
+configuration the benchmark times (same chunk, library-planned blocking,
+bf16 inputs).
 
-The fp64 oracle cannot afford the whole N x V problem, so these tests check
-  * sampled rows against the oracle, element by element: lse, per-row loss,
-    z at the teacher ids, and the full grad_hidden row (each needs only its
-    own row of logits);
-  * properties that hold at any size: every per-row loss is a temperature-
-    scaled KL divergence (>= 0), the loss is the fixed-order sum of the
-    per-row losses, every row of the logit gradient G sums to zero so
-    sum_v grad_W[v, :] vanishes, and <grad_W, W> = <grad_hidden, H> (both
-    equal sum over rows and vocabulary of G * z);
-  * grad_W rows of sampled vocabulary ids against an independent PyTorch
-    fp32 computation that builds its own log-sum-exp over the whole
-    vocabulary (no value of the HIP path enters it).
-The forward-chunked variant (kept logits) runs on two of the workloads: its
-forward outputs must equal the fused forward's bitwise, and its gradients
-pass the same checks.
-Tolerances are those of the small-shape parity tests (bf16: 1e-3 relative on
-loss-like values, 2e-2 of the largest reference magnitude on gradients); the
-two summation properties use bounds derived in the test from bf16 rounding of
-G and fp32 accumulation.
+Expected values come from ``tests/golden/fullsize_<case>.npz``, written by
+``tests/golden/make_fullsize_fixtures.py``, which runs the oracle once over
+every row of the same seeded inputs (it imports only ``oracle`` and the input
+generator). Compared element by element:
+  * lse and the per-row loss of EVERY row, and the total loss;
+  * full grad_W rows of four groups of vocabulary ids, each measured against
+    its own largest magnitude: the ids with the most teacher-cache pairs
+    ("hot"), ids with the fewest ("cold": with Zipf ids, ids in no row's
+    top-K, whose gradient is the dense softmax term alone), the last ids of
+    the vocabulary (the ragged last tile) and uniform random ids;
+  * on sampled rows, the logits at the teacher ids and whole grad_hidden rows,
+    from the oracle run here on those rows only (each needs only its own row).
+Properties that hold at any size are checked as well: every per-row loss is a
+temperature-scaled KL divergence (>= 0), the loss is the fixed-order sum of
+the per-row losses, every row of the logit gradient G sums to zero so
+sum_v grad_W[v, :] vanishes, and <grad_W, W> = <grad_hidden, H>.
+
+The loss is motivated by the pages' isolated long-context loss test and the
+loss curves that nearly coincide with the baseline's ("Multiverse Computing
+... (iitak.ru)", fourth and fifth paragraphs). Tolerances are the stated bf16
+ones: 1e-3 relative on loss-like values (per element, with an absolute floor
+of the same size near 0), 2e-2 of the largest reference magnitude on
+gradients. The forward-chunked variant (kept logits) runs on two of the
+workloads: its forward outputs must equal the fused forward's bitwise, and its
+gradients pass the same checks.
 """
 
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -36,9 +44,26 @@ from tests.gpu_helpers import TOL, announce, elementwise_ok, max_rel_to_max
 
 pytestmark = pytest.mark.gpu
 
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 FULL_WORKLOADS = ["llama3b_8k", "long32k", "gptoss20b_32k", "stress_b1_64k", "stress_b4_32k"]
 N_SAMPLE_ROWS = 8
-N_SAMPLE_VOCAB = 48
+GROUPS = ("hot", "cold", "tail", "random")
+
+
+def load_fixture(case: str, w: synth.Workload, options: bool) -> dict:
+    """The oracle's stored values for a case, after checking that they were
+    made for exactly this workload and input generator."""
+    path = os.path.join(GOLDEN, f"fullsize_{case}.npz")
+    if not os.path.exists(path):
+        pytest.fail(f"missing {path}: run tests/golden/make_fullsize_fixtures.py {case}")
+    with np.load(path, allow_pickle=False) as f:
+        fx = {k: f[k] for k in f.files}
+    want = np.array([w.B, w.S, w.d, w.V, w.K, w.chunk, w.seed], dtype=np.int64)
+    assert np.array_equal(fx["params"], want), "fixture made for other workload parameters"
+    assert float(fx["T"]) == w.T and str(fx["dtype"]) == w.dtype and str(fx["ids"]) == w.ids
+    assert int(fx["generator_version"]) == synth.GENERATOR_VERSION, "stale fixture"
+    assert bool(fx["options"]) == options
+    return fx
 
 
 def _sample_rows(w, rng):
@@ -46,25 +71,6 @@ def _sample_rows(w, rng):
     fixed = {0, w.N - 1, min(w.chunk, w.N) - 1, min(w.chunk, w.N - 1)}
     rest = rng.choice(w.N, size=N_SAMPLE_ROWS - len(fixed), replace=False)
     return np.array(sorted(fixed | set(int(r) for r in rest)))
-
-
-def _torch_grad_w_rows(h32, w32, idx, lg, T, vocab, chunk=2048):
-    """grad_W[v, :] for the given vocabulary ids, in fp32 on the GPU: own
-    log-sum-exp over all V, teacher softmax over the K entries, then
-    G[:, v] = T * (q[:, v] * sum_k p - sum_{k: idx = v} p) and G[:, v]^T H."""
-    N = h32.shape[0]
-    lse = torch.empty(N, dtype=torch.float32, device=h32.device)
-    for r0 in range(0, N, chunk):
-        z = torch.matmul(h32[r0:r0 + chunk], w32.t())                 # fp32, 2-D
-        lse[r0:r0 + chunk] = torch.logsumexp(z / T, dim=1)
-        del z
-    p = torch.softmax(lg / T, dim=1)                                   # [N, K]
-    vv = torch.as_tensor(vocab, device=h32.device, dtype=torch.long)
-    zv = torch.matmul(h32, w32[vv].t().contiguous())                  # [N, S]
-    q = torch.exp(zv / T - lse[:, None])
-    scatter = torch.stack([(p * (idx == int(v)).float()).sum(dim=1) for v in vocab], dim=1)
-    G = T * (q * p.sum(dim=1, keepdim=True) - scatter)                # [N, S]
-    return (G.t().contiguous() @ h32).double().cpu().numpy()          # [S, d]
 
 
 # (workload, keep, options): keep=True runs the forward-chunked variant (kept
@@ -80,6 +86,8 @@ CASES = ([(n, False, False) for n in FULL_WORKLOADS] +
 def test_full_size_parity(name, keep, options, gpu_device):
     w = synth.WORKLOADS[name]
     tol = TOL[w.dtype]
+    case = name + ("-options" if options else "")
+    fx = load_fixture(case, w, options)
     announce(f"full size {name}{' (kept logits)' if keep else ''}"
              f"{' (labels + tail)' if options else ''}: N={w.N} d={w.d} V={w.V} "
              f"K={w.K} T={w.T} chunk={w.chunk} {w.dtype} ids={w.ids} (generating inputs)")
@@ -90,19 +98,12 @@ def test_full_size_parity(name, keep, options, gpu_device):
     idx = torch.from_numpy(inp["topk_idx"]).to(gpu_device)
     lg = torch.from_numpy(inp["topk_logit"]).to(gpu_device)
 
-    opts = {}
-    if options:
-        rng_o = np.random.default_rng(99)
-        y = rng_o.integers(0, w.V, size=w.N).astype(np.int32)
-        lg64 = inp["topk_logit"].astype(np.float64) / w.T
-        mx = lg64.max(axis=1)
-        tlse = (mx + np.log(np.exp(lg64 - mx[:, None]).sum(axis=1)) + np.log(2.0)).astype(
-            np.float32)
-        opts = dict(labels=y, alpha=0.5, teacher_lse=tlse)
+    opts = synth.make_loss_options(w) if options else {}
     announce(f"full size {name}: HIP forward + backward")
     if options:
-        topts = dict(labels=torch.from_numpy(y).to(gpu_device), alpha=0.5,
-                     teacher_lse=torch.from_numpy(tlse).to(gpu_device))
+        topts = dict(labels=torch.from_numpy(opts["labels"]).to(gpu_device),
+                     alpha=opts["alpha"],
+                     teacher_lse=torch.from_numpy(opts["teacher_lse"]).to(gpu_device))
         out = fkl.fkl_forward_ex(h, W, idx, lg, w.T, w.chunk, **topts)
         gh, gw = fkl.fkl_backward_ex(h, W, idx, lg, out.lse, w.T, w.chunk, topk_z=out.topk_z,
                                      lse1=out.lse1, **topts)
@@ -121,14 +122,27 @@ def test_full_size_parity(name, keep, options, gpu_device):
     torch.cuda.synchronize()
     loss = out.loss.item()
     row_loss = out.row_loss.double().cpu().numpy()
+    lse = out.lse.double().cpu().numpy()
     assert math.isfinite(loss)
     assert np.isfinite(row_loss).all()
+
+    errs = {}
+    # every row against the oracle, and the total
+    errs["lse(all rows)"] = elementwise_ok(lse, fx["lse"].astype(np.float64), tol["loss"])
+    errs["row_loss(all rows)"] = elementwise_ok(row_loss, fx["row_loss"].astype(np.float64),
+                                                tol["loss"])
+    errs["loss"] = abs(loss - float(fx["loss"])) / abs(float(fx["loss"]))
+    # grad_W rows of each vocabulary group, each against its own largest magnitude
+    for g in GROUPS:
+        vocab = fx[f"vocab_{g}"]
+        got = gw[torch.as_tensor(vocab, device=gpu_device)].double().cpu().numpy()
+        errs[f"grad_w[{g}]"] = max_rel_to_max(got, fx[f"grad_w_{g}"].astype(np.float64))
 
     # properties of the forward at full size
     assert abs(loss - math.fsum(row_loss.tolist())) <= 1e-6 * max(1.0, abs(loss))
     assert row_loss.min() >= -tol["loss"] * max(1.0, float(np.abs(row_loss).max()))
 
-    # sampled rows against the oracle
+    # sampled rows: logits at the teacher ids and whole grad_hidden rows
     rng = np.random.default_rng(20261203)
     rows = _sample_rows(w, rng)
     announce(f"full size {name}: oracle on rows {rows.tolist()}")
@@ -138,13 +152,12 @@ def test_full_size_parity(name, keep, options, gpu_device):
     ref = oracle.forward_backward(inp["hidden"][rows], inp["weight"], inp["topk_idx"][rows],
                                   inp["topk_logit"][rows], w.T, **sub)
     sel = torch.as_tensor(rows, device=gpu_device)
-    errs = {
-        "lse": elementwise_ok(out.lse[sel].double().cpu().numpy(), ref["lse"], tol["loss"]),
-        "row_loss": elementwise_ok(row_loss[rows], ref["row_loss"], tol["loss"]),
-        "topk_z": elementwise_ok(out.topk_z[sel].double().cpu().numpy(), ref["topk_z"],
-                                 tol["loss"]),
-        "grad_hidden": max_rel_to_max(gh[sel].double().cpu().numpy(), ref["grad_hidden"]),
-    }
+    errs["topk_z(rows)"] = elementwise_ok(out.topk_z[sel].double().cpu().numpy(), ref["topk_z"],
+                                          tol["loss"])
+    errs["grad_hidden(rows)"] = max_rel_to_max(gh[sel].double().cpu().numpy(),
+                                               ref["grad_hidden"])
+    # the row sample agrees with the fixture (same oracle, same rows)
+    assert elementwise_ok(ref["lse"], fx["lse"][rows].astype(np.float64), 1e-6) <= 1e-6
     del ref
 
     # grad_W: column sums vanish. Each G element is rounded to bf16 (relative
@@ -154,31 +167,15 @@ def test_full_size_parity(name, keep, options, gpu_device):
     colsum = gw.double().sum(dim=0)
     habs = h.float().abs().double().sum(dim=0)
     bound = 2.0 * (2.0 ** -9 + w.N * 2.0 ** -24) * 2.0 * w.T * habs
-    worst = float((colsum.abs() / bound).max().item())
-    errs["grad_w_colsum/bound"] = worst
-
+    errs["grad_w_colsum/bound"] = float((colsum.abs() / bound).max().item())
     # <grad_W, W> = <grad_hidden, H>
     a = float((gw.double() * W.double()).sum().item())
     b = float((gh.double() * h.double()).sum().item())
     scale = float((gw.double().abs() * W.double().abs()).sum().item())
     errs["<gW,W>-<gH,H>"] = abs(a - b) / max(scale, 1e-30)
 
-    limits = {"lse": tol["loss"], "row_loss": tol["loss"], "topk_z": tol["loss"],
-              "grad_hidden": tol["grad"], "grad_w_colsum/bound": 1.0,
-              "<gW,W>-<gH,H>": tol["grad"], "grad_w_rows": tol["grad"]}
-    if options:  # the torch fp32 grad_W rows below implement the plain loss only
-        print("    errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-        bad = {k: (errs[k], limits[k]) for k in errs if not errs[k] <= limits[k]}
-        assert not bad, f"outside tolerance: {bad}"
-        return
-    # grad_W rows of sampled vocabulary ids (teacher ids included) against torch fp32
-    teacher = inp["topk_idx"][rows[0]][:N_SAMPLE_VOCAB // 2]
-    vocab = np.unique(np.concatenate([teacher, rng.choice(w.V, N_SAMPLE_VOCAB // 2, replace=False),
-                                      [0, w.V - 1]]))
-    announce(f"full size {name}: torch fp32 grad_W on {len(vocab)} vocabulary rows")
-    ref_gw = _torch_grad_w_rows(h.float(), W.float(), idx, lg, w.T, vocab)
-    errs["grad_w_rows"] = max_rel_to_max(gw[torch.as_tensor(vocab, device=gpu_device)]
-                                         .double().cpu().numpy(), ref_gw)
+    limits = {k: (tol["grad"] if k.startswith(("grad", "<")) else tol["loss"]) for k in errs}
+    limits["grad_w_colsum/bound"] = 1.0
     print("    errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    bad = {k: (errs[k], limits[k]) for k in limits if not errs[k] <= limits[k]}
+    bad = {k: (errs[k], limits[k]) for k in errs if not errs[k] <= limits[k]}
     assert not bad, f"outside tolerance: {bad}"
