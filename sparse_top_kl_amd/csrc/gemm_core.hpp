@@ -730,8 +730,9 @@ __device__ __forceinline__ void gemm_tile(f32x16_t (&acc)[C::kMI][C::kNI], const
 // (launch block b runs on XCD b % 8) and each XCD runs ~32 workgroups at a
 // time (one per CU). The output tiles are laid out in strips of GB tile
 // columns, each strip row-major, and each XCD takes an equal contiguous share
-// of that order (its blocks in launch order walk its share), rounded up to
-// whole rounds of 32. The 32 workgroups an XCD runs at once are consecutive
+// of that order (its blocks in launch order walk its share): whole strips
+// when they split evenly over the XCDs, else a share rounded up to whole
+// rounds of 32. The 32 workgroups an XCD runs at once are consecutive
 // tiles: (32 / GB) tile rows of one strip (GA x GB for full strips), so one L2
 // serves their GA panels of one operand and GB of the other instead of each
 // streaming its own; and every XCD has at most ceil(ceil(T / 8) / 32) rounds
@@ -741,13 +742,18 @@ __device__ __forceinline__ void gemm_tile(f32x16_t (&acc)[C::kMI][C::kNI], const
 template <int GA, int GB>
 struct TileGroups {
   static_assert(GA * GB == 32, "one group per XCD round of workgroups");
-  // Tiles per XCD: an equal share rounded up to whole rounds of 32, so that
-  // each round is one aligned group of the strip order (the same number of
-  // rounds as the exact share: ceil(x / 32) = round_up(x, 32) / 32).
-  static __host__ __device__ __forceinline__ int64_t share(int64_t total) {
+  // Tiles per XCD: whole strips when the strips split evenly over the 8 XCDs
+  // (each XCD then walks its own strips from their first row); otherwise an
+  // equal share rounded up to whole rounds of 32, so that each round is one
+  // aligned group of the strip order. Either way the same number of rounds
+  // as the exact share (ceil(x / 32) = round_up(x, 32) / 32).
+  static __host__ __device__ __forceinline__ int64_t share(int64_t mt, int64_t nt,
+                                                           int64_t splits) {
+    const int64_t total = mt * nt * splits;
+    if (splits == 1 && nt % GB == 0 && (nt / GB) % 8 == 0) return total / 8;
     return ((total + 7) / 8 + 31) / 32 * 32;
   }
-  static int64_t grid(int64_t mt, int64_t nt) { return 8 * share(mt * nt); }
+  static int64_t grid(int64_t mt, int64_t nt) { return 8 * share(mt, nt, 1); }
   // Tile of position t (0 <= t < mt * nt) in the strip order.
   __device__ __forceinline__ static void tile_of(int64_t t, int64_t mt, int64_t nt, int64_t* tm,
                                                  int64_t* tn) {
@@ -763,7 +769,7 @@ struct TileGroups {
     }
   }
   __device__ __forceinline__ static bool coords(int64_t mt, int64_t nt, int64_t* tm, int64_t* tn) {
-    const int64_t total = mt * nt, per = share(total);
+    const int64_t total = mt * nt, per = share(mt, nt, 1);
     const int64_t b = blockIdx.x;
     const int64_t t = (b & 7) * per + (b >> 3);
     if ((b >> 3) >= per || t >= total) return false;
@@ -774,11 +780,11 @@ struct TileGroups {
   // contraction): position t runs over splits x tiles, split-major, so the
   // copies are spread over the XCDs like any other tiles. splits = 1 is coords().
   static int64_t grid_split(int64_t mt, int64_t nt, int64_t splits) {
-    return 8 * share(mt * nt * splits);
+    return 8 * share(mt, nt, splits);
   }
   __device__ __forceinline__ static bool coords_split(int64_t mt, int64_t nt, int64_t splits,
                                                       int64_t* tm, int64_t* tn, int64_t* sp) {
-    const int64_t tiles = mt * nt, total = tiles * splits, per = share(total);
+    const int64_t tiles = mt * nt, total = tiles * splits, per = share(mt, nt, splits);
     const int64_t b = blockIdx.x;
     const int64_t t = (b & 7) * per + (b >> 3);
     if ((b >> 3) >= per || t >= total) return false;
