@@ -186,16 +186,21 @@ void launch_validate_idx(const int32_t* idx, int64_t N, int K, int64_t V, bool a
 // ---- student-renormalised loss (renorm.hip)
 constexpr int kRenormMaxK = 1024;  // cached entries per row
 constexpr int64_t kRenormMaxD = 8192;  // hidden size (eight columns per thread, 1024 threads)
-constexpr int kRenormMaxSeg = 2048;    // sorted pairs per grad_W chunk
+constexpr int kRenormMaxSeg = 2048;    // sorted pairs per grad_W chunk (at most)
+// pairs per chunk: 64 shares of 30 with the shares' pieces fit four
+// 256-thread workgroups in a CU's 160 KiB of LDS
+constexpr int kRenormSeg = 1920;
+constexpr int kRenormSliceCols = 64;   // grad_W columns per slice of the sorted walk
 
 // grad_W of the renormalised loss: a stable counting sort of the N * K (row,
 // entry) pairs by id in nb blocks of rows_per_block rows, then sums over
-// chunks of seg sorted pairs.
+// chunks of seg sorted pairs, slice by slice of kRenormSliceCols columns.
 constexpr int32_t kRenormHotCap = 2048;  // ids summed by the dense product (at most)
 constexpr int32_t kRenormHotMin = 64;    // pairs an id needs to be one of them
 
 struct RenormSortPlan {
   int64_t nb, rows_per_block, seg, nchunks;
+  int64_t nslices;   // ceil(d / kRenormSliceCols)
   int64_t hot_max;   // ids the dense product can take: one round of 256 x 256 tiles
   int64_t hot_rows;  // rows per dense-product block
   int64_t hot_splits;  // row splits of the product, each into its own copy of the output
@@ -205,7 +210,10 @@ struct RenormBuffers {
   int32_t* hist;        // [nb * V] per-block id counters
   int32_t* total;       // [V] pairs per id
   int32_t* start;       // [V + 1] cold bucket starts
-  int32_t* perm;        // [N * K] sorted cold pairs
+  int32_t* srow;        // [N * K] sorted cold pairs: row,
+  int32_t* sid;         //   id
+  float* scoef;         //   and coefficient
+  unsigned char* hs;    // [nslices][N][kRenormSliceCols] hidden rows, slice-major
   int32_t* slot;        // [V] hot slot or -1
   int32_t* hot_ids;     // [hot_max]
   int32_t* info;        // [4] number of hot ids

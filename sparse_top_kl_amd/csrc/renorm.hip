@@ -37,9 +37,12 @@
 //   cold ids, a sort:
 //   k_rs_place       per block, its rows in order: each cold pair (r, k) goes
 //                    to start[v] + (pairs of id v in earlier rows) + (copies of
-//                    v earlier in row r): a stable counting sort by id
-//   k_rs_chunks      fixed chunks of the sorted pairs: the sum of G h over each
-//                    run of one id, written to grad_W when the chunk holds the
+//                    v earlier in row r): a stable counting sort by id, which
+//                    writes each pair's row, id and coefficient there
+//   k_rs_slices      the hidden rows copied slice-major, 32 columns a slice
+//   k_rs_chunks      fixed chunks of the sorted pairs, slice by slice, each XCD
+//                    walking one slice at a time: the sum of G h over each run
+//                    of one id, written to grad_W when the chunk holds the
 //                    whole bucket, else to the chunk's head or tail partial
 //   k_rs_fix         per cold id whose bucket crosses chunks: its partials in
 //                    chunk order; ids with no pair get a zero row
@@ -94,6 +97,9 @@ __device__ __forceinline__ void store8(unsigned char* p, const float (&x)[8]) {
 }
 
 constexpr int kRowWaves = 4;  // rows per k_renorm_rows block
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kWalkLanes = kRenormSliceCols / 8;  // lanes of a k_rs_chunks group, 8 columns each
+constexpr int kWalkGroups = 256 / kWalkLanes;     // groups (shares) per k_rs_chunks workgroup
 
 }  // namespace
 
@@ -350,15 +356,18 @@ __global__ __launch_bounds__(1024) void k_rs_hot(const int32_t* __restrict__ tot
 // Stable placement: block b walks its rows in order; within a row each id's
 // first copy reserves its copies' slots with one returning atomic on the
 // block's cursor hist[b][v] (private to the block, so the values returned
-// follow the row order), and every copy lands at start[v] + base + (earlier
-// copies in the row).
-__global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ idx, int64_t N,
+// follow the row order), and every copy lands at position start[v] + base +
+// (earlier copies in the row), where its row, id and coefficient are written.
+__global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ idx,
+                                                  const float* __restrict__ coef, int64_t N,
                                                   int K, int64_t rows_per_block, int64_t V,
                                                   const int32_t* __restrict__ slot,
                                                   int32_t* __restrict__ hist,
                                                   const int32_t* __restrict__ start,
-                                                  int32_t* __restrict__ perm) {
-  __shared__ int32_t sid[kRenormMaxK];
+                                                  int32_t* __restrict__ srow,
+                                                  int32_t* __restrict__ sid,
+                                                  float* __restrict__ scoef) {
+  __shared__ int32_t lid[kRenormMaxK];
   __shared__ int32_t sbase[kRenormMaxK];
   constexpr int kPer = kRenormMaxK / 256;
   const int64_t b = blockIdx.x;
@@ -369,7 +378,7 @@ __global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ id
   for (int64_t r = r0; r < r1; ++r) {
     for (int k = t; k < K; k += 256) {
       const int32_t v = idx[r * K + k];
-      sid[k] = slot[v] < 0 ? v : -1;  // hot pairs take no part in the sort
+      lid[k] = slot[v] < 0 ? v : -1;  // hot pairs take no part in the sort
     }
     __syncthreads();
     int dup[kPer], first[kPer];
@@ -378,11 +387,11 @@ __global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ id
       const int k = t + 256 * j;
       dup[j] = 0;
       first[j] = k;
-      if (k < K && sid[k] >= 0) {
-        const int32_t v = sid[k];
+      if (k < K && lid[k] >= 0) {
+        const int32_t v = lid[k];
         int mult = 0, fst = -1;
         for (int k2 = 0; k2 < K; ++k2) {
-          const bool eq = sid[k2] == v;
+          const bool eq = lid[k2] == v;
           mult += eq ? 1 : 0;
           dup[j] += (eq && k2 < k) ? 1 : 0;
           if (eq && fst < 0) fst = k2;
@@ -395,88 +404,208 @@ __global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ id
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int k = t + 256 * j;
-      if (k < K && sid[k] >= 0)
-        perm[start[sid[k]] + sbase[first[j]] + dup[j]] = static_cast<int32_t>(r * K + k);
+      if (k < K && lid[k] >= 0) {
+        const int32_t v = lid[k];
+        const int32_t pos = start[v] + sbase[first[j]] + dup[j];
+        srow[pos] = static_cast<int32_t>(r);
+        sid[pos] = v;
+        scoef[pos] = coef[r * K + k];
+      }
     }
     __syncthreads();
   }
 }
 
-// Chunk c covers sorted positions [c * seg, min(NK, (c + 1) * seg)), seg <=
-// kRenormMaxSeg. Its pairs' rows, coefficients and ids are first staged in LDS
-// (one coalesced pass, the gathers all in flight at once). For each run of one
-// id v inside it, the sum of coef[p] * H[p / K] over the run's pairs p in sorted
-// order goes to grad_W[v] (written, or added with ACC) when the chunk holds v's
-// whole bucket, else to partial[c][0] (the bucket began in an earlier chunk) or
-// partial[c][1] (it begins here and continues).
+// Slice-major copy of the hidden rows for the walk below: slice s holds
+// columns [32 s, 32 s + 32) of every row, one row after the other (64 bytes a
+// row in bf16), so that a slice of all N rows is one contiguous block whose
+// 128-byte lines hold only that slice. Columns past d in the last slice are
+// neither written nor read.
 template <class P>
-__global__ __launch_bounds__(1024) void k_rs_chunks(
-    const unsigned char* __restrict__ H, const int32_t* __restrict__ idx,
-    const float* __restrict__ coef, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ start, int64_t V, int K, int64_t d, int64_t seg, bool acc_out,
-    float* __restrict__ gw, float* __restrict__ partial) {
-  __shared__ int32_t srow[kRenormMaxSeg];
-  const int64_t NK = start[V];  // sorted (cold) pairs; chunks past them have nothing to do
-  __shared__ int32_t sv[kRenormMaxSeg];
-  __shared__ float sc[kRenormMaxSeg];
-  const int64_t c = blockIdx.x;
-  const int64_t a = c * seg, e = a + seg < NK ? a + seg : NK;
-  if (a >= NK) return;
-  const int n = static_cast<int>(e - a);
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int32_t p = perm[a + i];
-    srow[i] = p / K;
-    sv[i] = idx[p];
-    sc[i] = coef[p];
-  }
-  __syncthreads();
-  const int64_t c0 = static_cast<int64_t>(threadIdx.x) * 8;
-  if (c0 >= d) return;
-  const int64_t ld = d * P::kBytes;
-  const unsigned char* hc = H + c0 * P::kBytes;
-  // The chunk's pairs are taken eight at a time whatever the runs (runs of
-  // rare ids are one to a few pairs long), so eight row loads are always in
-  // flight; a run's sum is written out when its last pair has been added.
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto flush = [&](int q) {  // q: the last pair of a run
-    const int32_t v = sv[q];
-    const int64_t bs = start[v], be = start[v + 1];
-    float* dst;
-    bool add = false;
-    if (bs < a)
-      dst = partial + (2 * c) * d + c0;
-    else if (be > e)
-      dst = partial + (2 * c + 1) * d + c0;
-    else {
-      dst = gw + static_cast<int64_t>(v) * d + c0;
-      add = acc_out;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      dst[j] = add ? dst[j] + acc[j] : acc[j];
-      acc[j] = 0.f;
-    }
-  };
-  int q = 0;
-  for (; q + 8 <= n; q += 8) {
-    float x[8][8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) load8<P>(hc + srow[q + u] * ld, x[u]);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float g = sc[q + u];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, x[u][j], acc[j]);
-      if (q + u + 1 == n || sv[q + u + 1] != sv[q + u]) flush(q + u);
-    }
-  }
-  for (; q < n; ++q) {
+__global__ __launch_bounds__(256) void k_rs_slices(const unsigned char* __restrict__ H,
+                                                   int64_t N, int64_t d,
+                                                   unsigned char* __restrict__ hs) {
+  const int64_t groups = d / 8;  // eight columns each
+  const int64_t total = N * groups;
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; u < total;
+       u += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t r = u / groups, c8 = u - r * groups;
     float x[8];
-    load8<P>(hc + srow[q] * ld, x);
-    const float g = sc[q];
+    load8<P>(H + (r * d + c8 * 8) * P::kBytes, x);
+    const int64_t sl = c8 / (kRenormSliceCols / 8), part = c8 - sl * (kRenormSliceCols / 8);
+    store8<P>(hs + ((sl * N + r) * kRenormSliceCols + part * 8) * P::kBytes, x);
+  }
+}
+
+// Chunk c of the sorted cold pairs (positions [c seg, min(NK, (c + 1) seg)),
+// seg <= kRenormMaxSeg) on the 32 columns of slice s. Work items are dealt so
+// that each XCD (workgroups go to the 8 XCDs in turn) takes its slices one
+// after the other, every chunk of a slice before the next slice, and the
+// slice of the hidden rows it reads (N x 64 bytes in bf16) stays in its L2
+// (all columns at once read each pair's whole row from memory, the pairs
+// being sorted by id and their rows scattered). The grid is persistent: a
+// workgroup loops over items, their number known only on the device.
+//
+// The chunk's rows, ids and coefficients are staged in LDS; 64 groups of four
+// lanes (eight columns a lane) take equal shares of its positions and sum
+// coef * H[row] over each run (the pairs of one id) in sorted order, eight
+// row loads in flight across runs. A run that lies inside one share is
+// written out at once; the pieces of a run that crosses shares go to LDS, and
+// after a barrier the share where the run began adds them in share order.
+// A run's sum goes to grad_W[v] (or is added to it, with acc_out) when the
+// chunk holds v's whole bucket, else to the chunk's head partial (the bucket
+// began in an earlier chunk: only the chunk's first run) or tail partial (it
+// continues: only the last run).
+template <class P>
+__global__ __launch_bounds__(256, 4) void k_rs_chunks(
+    const unsigned char* __restrict__ hs, const int32_t* __restrict__ srow,
+    const int32_t* __restrict__ sid, const float* __restrict__ scoef,
+    const int32_t* __restrict__ start, int64_t N, int64_t V, int64_t d, int64_t seg,
+    int64_t nslices, bool acc_out, float* __restrict__ gw, float* __restrict__ partial) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char sh_walk[];
+  float* piece = reinterpret_cast<float*>(sh_walk);  // [shares][2][slice columns]
+  int32_t* lrow = reinterpret_cast<int32_t*>(piece + kWalkGroups * 2 * kRenormSliceCols);
+  int32_t* lid = lrow + seg;
+  float* lcoef = reinterpret_cast<float*>(lid + seg);
+  __shared__ int32_t lcont[2];  // the first run continues a bucket, the last run's continues
+  const int64_t NK = start[V];  // sorted (cold) pairs
+  const int64_t nch = (NK + seg - 1) / seg;
+  const int64_t items = (nslices + 7) / 8 * nch;
+  const int g = threadIdx.x / kWalkLanes, l = threadIdx.x % kWalkLanes;
+  constexpr int64_t ld = kRenormSliceCols * P::kBytes;
+  const int64_t xcd = blockIdx.x & 7;
+  for (int64_t j = blockIdx.x >> 3; j < items; j += gridDim.x >> 3) {
+    const int64_t s = (j / nch) * 8 + xcd, c = j - (j / nch) * nch;
+    if (s >= nslices) continue;  // uniform over the workgroup
+    const int64_t a = c * seg, e = a + seg < NK ? a + seg : NK;
+    const int n = static_cast<int>(e - a);
+    __syncthreads();  // the previous item is done with LDS
+    // four positions a thread per load, all loads in flight at once (the
+    // arrays are padded so that a quad may run past the last pair; a thread
+    // past the chunk reloads its first quad, so no load waits on a branch)
+    u32x4_t qr[kRenormMaxSeg / 1024], qi[kRenormMaxSeg / 1024], qc[kRenormMaxSeg / 1024];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, x[j], acc[j]);
-    if (q + 1 == n || sv[q + 1] != sv[q]) flush(q);
+    for (int h = 0; h < kRenormMaxSeg / 1024; ++h) {
+      const int i4 = (threadIdx.x + 256 * h) * 4;
+      const int64_t o = a + (i4 < n ? i4 : 0);
+      qr[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(srow + o));
+      qi[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(sid + o));
+      qc[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(scoef + o));
+    }
+#pragma unroll
+    for (int h = 0; h < kRenormMaxSeg / 1024; ++h) {
+      const int i4 = (threadIdx.x + 256 * h) * 4;
+      if (i4 < n) {
+        *reinterpret_cast<u32x4_t*>(lrow + i4) = qr[h];
+        *reinterpret_cast<u32x4_t*>(lid + i4) = qi[h];
+        *reinterpret_cast<u32x4_t*>(lcoef + i4) = qc[h];
+      }
+    }
+    if (threadIdx.x == 0) {
+      lcont[0] = a > 0 && sid[a - 1] == sid[a];
+      lcont[1] = e < NK && sid[e] == sid[e - 1];
+    }
+    __syncthreads();
+    const int64_t c0 = s * kRenormSliceCols + l * 8;
+    const bool live = c0 < d;  // the last slice may be narrower than 32 columns
+    const int32_t first_id = lid[0], last_id = lid[n - 1];
+    const bool head_cont = lcont[0] != 0, tail_cont = lcont[1] != 0;
+    // eight columns as two 16-byte streaming stores (c0 is a multiple of 8)
+    auto write_run = [&](int32_t v, const float (&x)[8]) {
+      float* dst;
+      bool add = false;
+      if (head_cont && v == first_id)
+        dst = partial + (2 * c) * d + c0;
+      else if (tail_cont && v == last_id)
+        dst = partial + (2 * c + 1) * d + c0;
+      else {
+        dst = gw + static_cast<int64_t>(v) * d + c0;
+        add = acc_out;
+      }
+      f32x4_t* d4 = reinterpret_cast<f32x4_t*>(dst);
+      f32x4_t lo = {x[0], x[1], x[2], x[3]}, hi = {x[4], x[5], x[6], x[7]};
+      if (add) {
+        lo += d4[0];
+        hi += d4[1];
+      }
+      __builtin_nontemporal_store(lo, d4);
+      __builtin_nontemporal_store(hi, d4 + 1);
+    };
+    const int p0 = g * n / kWalkGroups, p1 = (g + 1) * n / kWalkGroups;
+    // this share's first run began in an earlier share
+    const bool open = p0 < p1 && p0 > 0 && lid[p0] == lid[p0 - 1];
+    float* my = piece + (g * 2) * kRenormSliceCols + l * 8;
+    const unsigned char* hc = hs + (s * N * kRenormSliceCols + l * 8) * P::kBytes;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int rs = p0;  // first position of the current run inside the share
+    // eight rows in flight (four in fp32, whose rows take twice the registers)
+    constexpr int kB = P::kBytes == 2 ? 8 : 4;
+    for (int q = p0; q < p1; q += kB) {
+      const int m = p1 - q < kB ? p1 - q : kB;
+      // raw 16-byte loads, widened to fp32 as they are used (fewer registers
+      // per load in flight)
+      // Every load is issued (a position past the share reloads the first
+      // row of the batch, and a lane past d reads columns of its own slice
+      // that hold no data): loads behind a branch were each preceded by a
+      // wait for all earlier ones.
+      u32x4_t raw[kB][P::kBytes / 2];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const unsigned char* src = hc + lrow[u < m ? q + u : q] * ld;
+#pragma unroll
+        for (int h = 0; h < P::kBytes / 2; ++h) raw[u][h] = load16(src + 16 * h);
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        if (u < m) {
+          const int qq = q + u;
+          const float gg = lcoef[qq];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            float xv;
+            if constexpr (P::kBytes == 2)
+              xv = as_f32((k & 1) ? (raw[u][0][k >> 1] & 0xffff0000u) : (raw[u][0][k >> 1] << 16));
+            else
+              xv = as_f32(raw[u][k >> 2][k & 3]);
+            acc[k] = fmaf(gg, xv, acc[k]);
+          }
+          const bool run_end = qq + 1 == n || lid[qq + 1] != lid[qq];
+          if (run_end || qq + 1 == p1) {
+            if (rs == p0 && open) {  // a piece of a run that began before the share
+#pragma unroll
+              for (int k = 0; k < 8; ++k) my[k] = acc[k];
+            } else if (!run_end) {  // a run that continues past the share
+#pragma unroll
+              for (int k = 0; k < 8; ++k) my[kRenormSliceCols + k] = acc[k];
+            } else if (live) {
+              write_run(lid[qq], acc);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+            rs = qq + 1;
+          }
+        }
+      }
+    }
+    __syncthreads();  // every piece is in LDS
+    // The share whose last run began in it and continues adds the pieces of
+    // the following shares (skipping empty ones) up to the run's end.
+    if (p0 < p1 && p1 < n && lid[p1] == lid[p1 - 1] && !(open && lid[p0] == lid[p1 - 1]) &&
+        live) {
+      const int32_t v = lid[p1 - 1];
+      float sum[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sum[k] = my[kRenormSliceCols + k];
+      for (int g2 = g + 1; g2 < kWalkGroups; ++g2) {
+        const int b0 = g2 * n / kWalkGroups, b1 = (g2 + 1) * n / kWalkGroups;
+        if (b0 == b1) continue;
+        const float* pc = piece + (g2 * 2) * kRenormSliceCols + l * 8;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sum[k] += pc[k];
+        if (b1 == n || lid[b1] != v) break;
+      }
+      write_run(v, sum);
+    }
   }
 }
 
@@ -611,19 +740,34 @@ void launch_renorm_grad_w(int dtype, const void* H, const int32_t* idx, const fl
     }
     {
       ScopedTimer timer_(KID_RS_PLACE, s);
-      k_rs_place<<<static_cast<unsigned>(q.nb), 256, 0, s>>>(idx, N, K, q.rows_per_block, V,
-                                                             b.slot, b.hist, b.start, b.perm);
+      k_rs_place<<<static_cast<unsigned>(q.nb), 256, 0, s>>>(
+          idx, coef, N, K, q.rows_per_block, V, b.slot, b.hist, b.start, b.srow, b.sid, b.scoef);
+    }
+    const unsigned char* Hc = static_cast<const unsigned char*>(H);
+    {
+      ScopedTimer timer_(KID_RS_SLICES, s);
+      const int64_t blocks = ceil_div(N * (d / 8), 256) < 65536 ? ceil_div(N * (d / 8), 256)
+                                                                 : 65536;
+      if (dtype == 1)
+        k_rs_slices<BF16><<<static_cast<unsigned>(blocks), 256, 0, s>>>(Hc, N, d, b.hs);
+      else
+        k_rs_slices<F32><<<static_cast<unsigned>(blocks), 256, 0, s>>>(Hc, N, d, b.hs);
     }
     {
       ScopedTimer timer_(KID_RS_CHUNKS, s);
-      const unsigned threads = column_threads(d);
-      const unsigned char* Hc = static_cast<const unsigned char*>(H);
+      // persistent: four workgroups per CU (256 CUs), fewer when there are
+      // fewer (slice, chunk) items than that, a multiple of the 8 XCDs
+      int64_t grid = round_up(q.nslices, 8) * q.nchunks;
+      if (grid > 8 * 128) grid = 8 * 128;
+      const size_t lds = (kWalkGroups * 2 * kRenormSliceCols + 3 * q.seg) * 4;
       if (dtype == 1)
-        k_rs_chunks<BF16><<<static_cast<unsigned>(q.nchunks), threads, 0, s>>>(
-            Hc, idx, coef, b.perm, b.start, V, K, d, q.seg, acc_out, gw, b.partial);
+        k_rs_chunks<BF16><<<static_cast<unsigned>(grid), 256, lds, s>>>(
+            b.hs, b.srow, b.sid, b.scoef, b.start, N, V, d, q.seg, q.nslices, acc_out, gw,
+            b.partial);
       else
-        k_rs_chunks<F32><<<static_cast<unsigned>(q.nchunks), threads, 0, s>>>(
-            Hc, idx, coef, b.perm, b.start, V, K, d, q.seg, acc_out, gw, b.partial);
+        k_rs_chunks<F32><<<static_cast<unsigned>(grid), 256, lds, s>>>(
+            b.hs, b.srow, b.sid, b.scoef, b.start, N, V, d, q.seg, q.nslices, acc_out, gw,
+            b.partial);
     }
   } else {
     // no pairs: every bucket is empty and no id is hot

@@ -14,9 +14,8 @@ using namespace fkl_api;
 namespace {
 
 // Sizes of the pair sort: blocks of rows whose per-id counters take at most
-// 256 MiB in all (and at least 16 rows each), chunks of sorted pairs sized for
-// about 4096 workgroups (256 to 2048 pairs each); rows per block of the hot
-// ids' dense product.
+// 256 MiB in all (and at least 16 rows each), chunks of kRenormSeg sorted
+// pairs; rows per block of the hot ids' dense product.
 fkl::RenormSortPlan sort_plan(int64_t N, int64_t d, int32_t K, int64_t V, int64_t eb) {
   fkl::RenormSortPlan q{};
   const int64_t nn = N > 0 ? N : 1;
@@ -27,10 +26,9 @@ fkl::RenormSortPlan sort_plan(int64_t N, int64_t d, int32_t K, int64_t V, int64_
   q.rows_per_block = fkl::ceil_div(nn, nb);
   q.nb = fkl::ceil_div(nn, q.rows_per_block);
   const int64_t NK = N * K;
-  q.seg = fkl::round_up(fkl::ceil_div(NK > 0 ? NK : 1, 4096), 64);
-  if (q.seg < 256) q.seg = 256;
-  if (q.seg > fkl::kRenormMaxSeg) q.seg = fkl::kRenormMaxSeg;
+  q.seg = fkl::kRenormSeg;
   q.nchunks = NK > 0 ? fkl::ceil_div(NK, q.seg) : 0;
+  q.nslices = fkl::ceil_div(d, fkl::kRenormSliceCols);
   // The dense product's output is hot_max x d. An id costs the product a full
   // column, 2 N d flops (~0.17 us at 32K x 3072), and the sorted walk one
   // d-wide row read per pair (~1.2 ns): the break-even is ~140 pairs, which on
@@ -59,8 +57,8 @@ struct RenormPlan {
   // forward workspace
   size_t f_zk, f_rowloss, f_flag, f_total;
   // backward workspace
-  size_t b_coef, b_zk, b_hist, b_total_ids, b_start, b_perm, b_partial, b_slot, b_hot_ids,
-      b_info, b_hot_c, b_hot_prod, b_flag, b_total;
+  size_t b_coef, b_zk, b_hist, b_total_ids, b_start, b_srow, b_sid, b_scoef, b_hs, b_partial,
+      b_slot, b_hot_ids, b_info, b_hot_c, b_hot_prod, b_flag, b_total;
 };
 
 RenormPlan make_renorm_plan(int64_t N, int64_t d, int64_t V, int32_t K, int32_t dtype) {
@@ -87,8 +85,14 @@ RenormPlan make_renorm_plan(int64_t N, int64_t d, int64_t V, int32_t K, int32_t 
   off = align_up(off + static_cast<size_t>(V) * 4);
   p.b_start = off;
   off = align_up(off + static_cast<size_t>(V + 1) * 4);
-  p.b_perm = off;
-  off = align_up(off + NK * 4);
+  p.b_srow = off;  // each padded by a quad for the walk's 16-byte loads
+  off = align_up(off + NK * 4 + 16);
+  p.b_sid = off;
+  off = align_up(off + NK * 4 + 16);
+  p.b_scoef = off;
+  off = align_up(off + NK * 4 + 16);
+  p.b_hs = off;
+  off = align_up(off + static_cast<size_t>(N) * p.sort.nslices * fkl::kRenormSliceCols * eb);
   p.b_partial = off;
   off = align_up(off + static_cast<size_t>(2 * p.sort.nchunks) * d * 4);
   p.b_slot = off;
@@ -231,7 +235,10 @@ extern "C" int32_t fkl_renorm_backward(const void* hidden, const void* weight,
   b.hist = reinterpret_cast<int32_t*>(ws + p.b_hist);
   b.total = reinterpret_cast<int32_t*>(ws + p.b_total_ids);
   b.start = reinterpret_cast<int32_t*>(ws + p.b_start);
-  b.perm = reinterpret_cast<int32_t*>(ws + p.b_perm);
+  b.srow = reinterpret_cast<int32_t*>(ws + p.b_srow);
+  b.sid = reinterpret_cast<int32_t*>(ws + p.b_sid);
+  b.scoef = reinterpret_cast<float*>(ws + p.b_scoef);
+  b.hs = ws + p.b_hs;
   b.slot = reinterpret_cast<int32_t*>(ws + p.b_slot);
   b.hot_ids = reinterpret_cast<int32_t*>(ws + p.b_hot_ids);
   b.info = reinterpret_cast<int32_t*>(ws + p.b_info);

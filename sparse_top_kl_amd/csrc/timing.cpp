@@ -57,7 +57,7 @@ const char* kernel_name(int32_t kid) {
       "k_g_from_z",   "k_teacher_logits", "k_topk_threshold", "k_topk_collect",
       "k_topk_final", "k_merge_lse_rows", "k_renorm_rows", "k_renorm_grad_h",
       "k_rs_hist",    "k_rs_scan",    "k_rs_place",   "k_rs_chunks",
-      "k_rs_fix",     "k_rs_hot",     "k_pair_index"};
+      "k_rs_fix",     "k_rs_hot",     "k_pair_index", "k_rs_slices"};
   return (kid >= 0 && kid < KID_COUNT) ? names[kid] : nullptr;
 }
 

@@ -35,6 +35,7 @@ enum KernelId : int32_t {
   KID_RS_FIX,
   KID_RS_HOT,
   KID_PAIR_INDEX,
+  KID_RS_SLICES,
   KID_COUNT
 };
 

@@ -330,21 +330,24 @@ def test_renorm_workspace_is_linear_in_pairs_and_never_rows_times_vocab():
         NK = N * K
         # forward: gathered logits + per-row losses
         assert NK * 4 <= f <= NK * 4 + N * 4 + 4 * 256
-        # backward: coefficients, gathered logits, sorted pairs, per-id starts, at most 256 MiB
-        # of per-block id counters (or one block), and two d-wide partials per chunk of 256 to
-        # 2048 sorted pairs, about 4096 chunks unless the 2048 cap needs more; for the ids
+        # backward: coefficients, gathered logits, sorted pairs (row, id, coefficient), the
+        # hidden rows in 32-column slices, per-id starts, at most 256 MiB
+        # of per-block id counters (or one block), and two d-wide partials per chunk of 1920
+        # sorted pairs; for the ids
         # summed by a dense product (as many as one round of 256 x 256 tiles of its hot x d
         # output takes), per-id slots, their coefficients for at most 256 MiB of rows and their
         # product (one copy per row split of the product)
         counters = max(256 << 20, V * 4)
-        chunks = max(min(4097, NK // 256 + 1), NK // 2048 + 1)
+        chunks = NK // 1920 + 1
         hot_max = min(2048, max(256, (256 // -(-d // 256)) * 256))
         rows = min(N, (256 << 20) // (hot_max * 2))
         groups = -(-hot_max // 2048) * -(-(-(-d // 256)) // 4)
         splits = min(1 if groups >= 8 else 8 // groups, max(1, rows // 1024))
         hot = rows * hot_max * 2 + splits * hot_max * d * 4 + hot_max * 4 + V * 4
-        assert 3 * NK * 4 + (2 * V + 1) * 4 + hot - rows * hot_max * 2 <= b
-        assert b <= 3 * NK * 4 + (2 * V + 1) * 4 + counters + chunks * 2 * d * 4 + hot + 20 * 256
+        slices = N * -(-d // 32) * 32 * 2
+        assert 5 * NK * 4 + slices + (2 * V + 1) * 4 + hot - rows * hot_max * 2 <= b
+        assert b <= (5 * NK * 4 + slices + (2 * V + 1) * 4 + counters + chunks * 2 * d * 4 + hot
+                     + 24 * 256)
         assert b < N * V * 2 / 4 or N < 4096
 
 
