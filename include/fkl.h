@@ -347,8 +347,8 @@ int32_t fkl_teacher_topk(const void* hidden, const void* weight, int64_t N, int6
  *   (either pointer may be NULL). The backward workspace holds the K
  *   coefficients per row, a counting sort of the N * K (row, entry) pairs by
  *   id (at most 256 MiB of per-block counters; the sorted rows, ids and
- *   coefficients), a copy of the hidden rows in slices of 32 columns
- *   (N * ceil(d / 32) * 32 elements of dtype), chunk partials of grad_W, and
+ *   coefficients), a copy of the hidden rows in slices of 64 columns
+ *   (N * ceil(d / 64) * 64 elements of dtype), chunk partials of grad_W, and
  *   for the (at most 2048) ids with the most pairs a dense coefficient matrix
  *   (at most 256 MiB) with its product's output copies.
  * fkl_renorm_forward: writes loss[0] and, when non-NULL, row_loss [N] and

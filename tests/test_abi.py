@@ -331,7 +331,7 @@ def test_renorm_workspace_is_linear_in_pairs_and_never_rows_times_vocab():
         # forward: gathered logits + per-row losses
         assert NK * 4 <= f <= NK * 4 + N * 4 + 4 * 256
         # backward: coefficients, gathered logits, sorted pairs (row, id, coefficient), the
-        # hidden rows in 32-column slices, per-id starts, at most 256 MiB
+        # hidden rows in 64-column slices, per-id starts, at most 256 MiB
         # of per-block id counters (or one block), and two d-wide partials per chunk of 1920
         # sorted pairs; for the ids
         # summed by a dense product (as many as one round of 256 x 256 tiles of its hot x d
@@ -344,7 +344,7 @@ def test_renorm_workspace_is_linear_in_pairs_and_never_rows_times_vocab():
         groups = -(-hot_max // 2048) * -(-(-(-d // 256)) // 4)
         splits = min(1 if groups >= 8 else 8 // groups, max(1, rows // 1024))
         hot = rows * hot_max * 2 + splits * hot_max * d * 4 + hot_max * 4 + V * 4
-        slices = N * -(-d // 32) * 32 * 2
+        slices = N * -(-d // 64) * 64 * 2
         assert 5 * NK * 4 + slices + (2 * V + 1) * 4 + hot - rows * hot_max * 2 <= b
         assert b <= (5 * NK * 4 + slices + (2 * V + 1) * 4 + counters + chunks * 2 * d * 4 + hot
                      + 24 * 256)
