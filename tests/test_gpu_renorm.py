@@ -5,8 +5,9 @@ fkl_renorm_backward through the C ABI) against the fp64 oracle
 Small shapes compare every output element: bf16 and fp32, uniform and
 Zipf-skewed ids (hot ids whose pairs span several sort chunks), duplicate ids
 in a row, -inf padding entries, zero-weight padding rows, K from 1 to 1024,
-odd hidden sizes, a negative upstream scale, and enough rows that the
-frequent ids' dense product is split over rows and blocked. Then: grad_W and
+odd hidden sizes, a negative upstream scale, enough rows that the
+frequent ids' dense product is split over rows and blocked, and ids that are
+all below its threshold with runs of hundreds of pairs. Then: grad_W and
 grad_hidden are bitwise repeatable, the accumulate flag adds, passing the forward's
 gathered logits changes nothing, an empty batch zeroes grad_W, the autograd
 wrapper matches, and at the long32k size sampled rows match the oracle while
@@ -88,6 +89,14 @@ CASES = [
      0.5),
     # a 7-id vocabulary: every id is frequent, the sorted walk gets no pair at all
     ("bf16_tiny_vocab_all_hot", 400, 64, 7, 5, 1.0, "bf16", "uniform", True, True, False, None),
+    # every id has ~700 (~800) pairs: more ids than the dense product takes reach each
+    # power-of-two threshold below 1024, so none is frequent and the sorted walk sums runs
+    # that span many of a chunk's shares and cross chunks; d not a multiple of the walk's
+    # 64-column slices
+    ("bf16_long_cold_runs", 21000, 72, 3000, 100, 2.0, "bf16", "uniform", False, False, False,
+     None),
+    ("fp32_long_cold_runs", 20000, 40, 2500, 100, 1.0, "fp32", "uniform", True, False, False,
+     None),
 ]
 
 
