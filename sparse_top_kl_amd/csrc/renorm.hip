@@ -18,8 +18,9 @@
 // Kernels:
 //   k_renorm_rows    one wave per row: the two K-entry softmaxes -> row loss
 //                    (forward) or the K coefficients G_r. (backward)
-//   k_renorm_grad_h  one workgroup per row: sum_k G_rk W[idx_rk] (16-byte
-//                    loads of the K weight rows, eight in flight per lane)
+//   k_renorm_grad_h  one wave per (row, eighth of the columns), the eighths
+//                    dealt to the XCDs: sum_k G_rk W[idx_rk] (16-byte loads,
+//                    eight weight rows in flight per lane)
 //   grad_W without float atomics, bitwise deterministic:
 //   k_rs_hist        per block of rows, the count of each id (integer atomics)
 //   k_rs_colscan     per id, exclusive prefix of its counts over the blocks
@@ -183,41 +184,72 @@ __global__ __launch_bounds__(64 * kRowWaves) void k_renorm_rows(
 
 // grad_hidden row r = sum_k coef[r, k] W[idx[r, k]]: one workgroup per row,
 // thread t owns columns 8t .. 8t + 7 (blockDim.x * 8 >= d).
+// grad_h[r] = sum_k coef[r][k] W[idx[r][k]], one wave per (row, eighth of
+// the columns): workgroup b takes rows 4 (b >> 3) .. 4 (b >> 3) + 3, a wave
+// each, on column eighth b & 7. Workgroups are dealt to the 8 XCDs in turn,
+// so each XCD reads one eighth of every weight row it needs, and the eighths
+// of the frequent ids' rows (2048 x 768 bytes at d 3072) stay in its L2,
+// where their whole rows (12.6 MB) did not fit. Each column adds its K terms
+// in entry order, eight weight loads in flight per lane.
 template <class P>
-__global__ __launch_bounds__(1024) void k_renorm_grad_h(const unsigned char* __restrict__ W,
-                                                        const int32_t* __restrict__ idx,
-                                                        const float* __restrict__ coef, int K,
-                                                        int64_t d, unsigned char* __restrict__ gh) {
-  __shared__ int32_t sid[kRenormMaxK];
-  __shared__ float sg[kRenormMaxK];
-  const int64_t r = blockIdx.x;
-  for (int k = threadIdx.x; k < K; k += blockDim.x) {
-    sid[k] = idx[r * K + k];
-    sg[k] = coef[r * K + k];
-  }
-  __syncthreads();
-  const int64_t c0 = static_cast<int64_t>(threadIdx.x) * 8;
-  if (c0 >= d) return;
+__global__ __launch_bounds__(256) void k_renorm_grad_h(const unsigned char* __restrict__ W,
+                                                       const int32_t* __restrict__ idx,
+                                                       const float* __restrict__ coef, int64_t N,
+                                                       int K, int64_t d,
+                                                       unsigned char* __restrict__ gh) {
+  extern __shared__ int32_t sh_gh[];  // per wave: K ids, then K coefficients
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int32_t* sid = sh_gh + w * 2 * K;
+  float* sg = reinterpret_cast<float*>(sid + K);
+  const int64_t x = blockIdx.x & 7;
+  const int64_t cs = (d + 63) / 64 * 8;  // columns per eighth, a multiple of 8
+  const int64_t c_hi = (x + 1) * cs < d ? (x + 1) * cs : d;
   const int64_t ld = d * P::kBytes;
-  const unsigned char* wc = W + c0 * P::kBytes;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int k = 0;
-  for (; k + 8 <= K; k += 8) {
-    float x[8][8];
+  // groups of four rows, more than one per workgroup only when the grid is capped
+  for (int64_t rb = blockIdx.x >> 3; rb * 4 < N; rb += gridDim.x >> 3) {
+    const int64_t r = rb * 4 + w;
+    const bool valid = r < N;
+    __syncthreads();  // the previous group is done with LDS
+    if (valid)
+      for (int k = lane; k < K; k += 64) {
+        sid[k] = idx[r * K + k];
+        sg[k] = coef[r * K + k];
+      }
+    __syncthreads();
+    if (!valid) continue;
+    for (int64_t c0 = x * cs + lane * 8; c0 < c_hi; c0 += 512) {
+      const unsigned char* wc = W + c0 * P::kBytes;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < K; k += 8) {
+        // every load is issued (an entry past K reloads entry k), so that no
+        // load waits behind a branch for the ones before it
+        u32x4_t raw[8][P::kBytes / 2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load8<P>(wc + sid[k + u] * ld, x[u]);
+        for (int u = 0; u < 8; ++u) {
+          const unsigned char* src = wc + sid[k + u < K ? k + u : k] * ld;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+          for (int h = 0; h < P::kBytes / 2; ++h) raw[u][h] = load16(src + 16 * h);
+        }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(sg[k + u], x[u][e], acc[e]);
+        for (int u = 0; u < 8; ++u) {
+          if (k + u < K) {
+            const float gg = sg[k + u];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float xv;
+              if constexpr (P::kBytes == 2)
+                xv = as_f32((e & 1) ? (raw[u][0][e >> 1] & 0xffff0000u)
+                                    : (raw[u][0][e >> 1] << 16));
+              else
+                xv = as_f32(raw[u][e >> 2][e & 3]);
+              acc[e] = fmaf(gg, xv, acc[e]);
+            }
+          }
+        }
+      }
+      store8<P>(gh + r * ld + c0 * P::kBytes, acc);
+    }
   }
-  for (; k < K; ++k) {
-    float x[8];
-    load8<P>(wc + sid[k] * ld, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(sg[k], x[e], acc[e]);
-  }
-  store8<P>(gh + r * ld + c0 * P::kBytes, acc);
 }
 
 // Counts of each id per block of rows: hist[b][v], b = pair / pairs_per_block.
@@ -701,21 +733,20 @@ void launch_renorm_rows(bool coef_mode, const float* zk, const float* logit,
                                                           T, row_loss, coef);
 }
 
-static unsigned column_threads(int64_t d) {
-  return static_cast<unsigned>(round_up(ceil_div(d, 8), 64));
-}
-
 void launch_renorm_grad_h(int dtype, const void* W, const int32_t* idx, const float* coef,
                           int64_t N, int K, int64_t d, void* gh, hipStream_t s) {
   if (N <= 0) return;
   ScopedTimer timer_(KID_RENORM_GRAD_H, s);
-  const unsigned threads = column_threads(d);
+  // eight workgroups per four rows, at most 2^23 (a grid of 2^32 work-items is the limit)
+  const int64_t groups = ceil_div(N, 4) < (int64_t(1) << 20) ? ceil_div(N, 4) : int64_t(1) << 20;
+  const unsigned grid = static_cast<unsigned>(8 * groups);
   const unsigned char* Wc = static_cast<const unsigned char*>(W);
   unsigned char* out = static_cast<unsigned char*>(gh);
+  const size_t lds = static_cast<size_t>(4) * 2 * K * 4;
   if (dtype == 1)
-    k_renorm_grad_h<BF16><<<static_cast<unsigned>(N), threads, 0, s>>>(Wc, idx, coef, K, d, out);
+    k_renorm_grad_h<BF16><<<grid, 256, lds, s>>>(Wc, idx, coef, N, K, d, out);
   else
-    k_renorm_grad_h<F32><<<static_cast<unsigned>(N), threads, 0, s>>>(Wc, idx, coef, K, d, out);
+    k_renorm_grad_h<F32><<<grid, 256, lds, s>>>(Wc, idx, coef, N, K, d, out);
 }
 
 void launch_renorm_grad_w(int dtype, const void* H, const int32_t* idx, const float* coef,
