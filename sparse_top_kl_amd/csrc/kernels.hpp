@@ -216,7 +216,8 @@ struct RenormBuffers {
   unsigned char* hs;    // [nslices][N][kRenormSliceCols] hidden rows, slice-major
   int32_t* slot;        // [V] hot slot or -1
   int32_t* hot_ids;     // [hot_max]
-  int32_t* info;        // [4] number of hot ids
+  int32_t* info;        // [4] number of hot ids, tau
+  int32_t* tsum;        // [2 * ceil(V / 8192)] hot ids and cold pairs per tile of ids
   float* partial;       // [2 * nchunks * d] chunk partials
   unsigned char* hot_c; // [hot_rows * hot_max] coefficients, input dtype
   float* hot_prod;      // [hot_splits * hot_max * d] C^T H, one copy per split

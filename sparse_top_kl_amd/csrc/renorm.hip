@@ -24,10 +24,11 @@
 //   grad_W without float atomics, bitwise deterministic:
 //   k_rs_hist        per block of rows, the count of each id (integer atomics)
 //   k_rs_colscan     per id, exclusive prefix of its counts over the blocks
-//   k_rs_hot         picks the frequent ("hot") ids: count >= tau, tau the
+//   k_rs_tau, k_rs_hot_sums, k_rs_hot_place
+//                    pick the frequent ("hot") ids: count >= tau, tau the
 //                    smallest power of two >= kRenormHotMin that leaves at
 //                    most hot_max of them (as many as one round of 256 x 256
-//                    product tiles takes); gives each a slot, and the
+//                    product tiles takes); give each a slot, and the
 //                    exclusive prefix over the other ("cold") ids of their
 //                    counts: bucket starts of the cold pairs
 //   hot ids, a dense product: k_rs_hot_coef scatters each row's hot
@@ -268,7 +269,20 @@ __global__ __launch_bounds__(256) void k_rs_colscan(int32_t* __restrict__ hist, 
   const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (v >= V) return;
   int32_t acc = 0;
-  for (int64_t b = 0; b < nb; ++b) {
+  int64_t b = 0;
+  // sixteen blocks' counts loaded together, then their prefixes stored (one
+  // load at a time waited on every load in turn)
+  for (; b + 16 <= nb; b += 16) {
+    int32_t c[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) c[u] = hist[(b + u) * V + v];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      hist[(b + u) * V + v] = acc;
+      acc += c[u];
+    }
+  }
+  for (; b < nb; ++b) {
     const int32_t c = hist[b * V + v];
     hist[b * V + v] = acc;
     acc += c;
@@ -276,32 +290,25 @@ __global__ __launch_bounds__(256) void k_rs_colscan(int32_t* __restrict__ hist, 
   total[v] = acc;
 }
 
-// Hot ids and the cold bucket starts, one workgroup of 1024 threads. tau =
-// the smallest power of two >= hot_min with at most hot_max ids of count >=
-// tau (no id is hot when even the largest power of two leaves more).
-// slot[v] = the hot id's index (in id order) or -1, hot_ids[slot] = v,
-// info[0] = the number of hot ids; start[v] = sum of the counts of cold ids
-// below v, start[V] = the number of cold pairs. The ids go through LDS in
-// tiles of kHotTile: read and written with consecutive threads on
-// consecutive ids, scanned with each thread owning 8 consecutive ids.
+// Hot ids and the cold bucket starts. tau = the smallest power of two >=
+// hot_min with at most hot_max ids of count >= tau (no id is hot when even the
+// largest power of two leaves more); slot[v] = the hot id's index (in id
+// order) or -1, hot_ids[slot] = v, info[0] = the number of hot ids; start[v]
+// = sum of the counts of cold ids below v, start[V] = the number of cold
+// pairs. Three launches: k_rs_tau (one workgroup) finds tau (info[1]);
+// k_rs_hot_sums (a workgroup per tile of kHotTile ids) counts each tile's hot
+// ids and cold pairs; k_rs_hot_place (a workgroup per tile) adds the earlier
+// tiles' counts and writes the tile, its ids going through LDS read and
+// written by consecutive threads on consecutive ids and scanned with each
+// thread owning 8 consecutive ids.
 constexpr int kHotTile = 8192;
 
-__global__ __launch_bounds__(1024) void k_rs_hot(const int32_t* __restrict__ total, int64_t V,
+__global__ __launch_bounds__(1024) void k_rs_tau(const int32_t* __restrict__ total, int64_t V,
                                                  int32_t hot_min, int32_t hot_max,
-                                                 int32_t* __restrict__ slot,
-                                                 int32_t* __restrict__ hot_ids,
-                                                 int32_t* __restrict__ info,
-                                                 int32_t* __restrict__ start) {
+                                                 int32_t* __restrict__ info) {
   __shared__ int32_t bins[32];
-  __shared__ int32_t s_tau;
-  __shared__ int32_t wsum[16][2];
-  __shared__ int32_t s_carry[2];
-  __shared__ int32_t tc[kHotTile];   // counts of the tile, then bucket starts
-  __shared__ int32_t tsl[kHotTile];  // slots of the tile
-  constexpr int kPer = kHotTile / 1024;
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int t = threadIdx.x;
   if (t < 32) bins[t] = 0;
-  if (t < 2) s_carry[t] = 0;
   __syncthreads();
   for (int64_t v = t; v < V; v += 1024) {
     const int32_t c = total[v];
@@ -318,70 +325,142 @@ __global__ __launch_bounds__(1024) void k_rs_hot(const int32_t* __restrict__ tot
       tau = lo < hot_min ? hot_min : lo;
       if (lo <= hot_min) break;
     }
-    s_tau = tau;
+    info[1] = tau;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_rs_hot_sums(const int32_t* __restrict__ total,
+                                                      int64_t V,
+                                                      const int32_t* __restrict__ info,
+                                                      int32_t* __restrict__ tsum) {
+  __shared__ int32_t wsum[16][2];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int32_t tau = info[1];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kHotTile;
+  int32_t nh = 0, nc = 0;
+  for (int i = t; i < kHotTile && base + i < V; i += 1024) {
+    const int32_t c = total[base + i];
+    if (c >= tau)
+      ++nh;
+    else
+      nc += c;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    nh += __shfl_xor(nh, o);
+    nc += __shfl_xor(nc, o);
+  }
+  if (lane == 0) {
+    wsum[wv][0] = nh;
+    wsum[wv][1] = nc;
   }
   __syncthreads();
-  const int32_t tau = s_tau;
-  for (int64_t base = 0; base < V; base += kHotTile) {
-    const int n = V - base < kHotTile ? static_cast<int>(V - base) : kHotTile;
-    for (int i = t; i < kHotTile; i += 1024) tc[i] = i < n ? total[base + i] : 0;
-    __syncthreads();
-    int32_t nh = 0, nc = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = t * kPer + j;
-      const int32_t c = tc[i];
-      if (i < n && c >= tau) ++nh; else nc += c;
-    }
-    // exclusive prefixes of (hot ids, cold pairs) over the workgroup
-    int32_t xh = nh, xc = nc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int32_t yh = __shfl_up(xh, o), yc = __shfl_up(xc, o);
-      if (lane >= o) {
-        xh += yh;
-        xc += yc;
-      }
-    }
-    if (lane == 63) {
-      wsum[wv][0] = xh;
-      wsum[wv][1] = xc;
-    }
-    __syncthreads();
-    int32_t bh = s_carry[0], bc = s_carry[1];
-    for (int i = 0; i < wv; ++i) {
-      bh += wsum[i][0];
-      bc += wsum[i][1];
-    }
-    int32_t h = bh + xh - nh, run = bc + xc - nc;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = t * kPer + j;
-      const int32_t c = tc[i];
-      tc[i] = run;
-      if (i < n && c >= tau) {
-        tsl[i] = h;
-        hot_ids[h] = static_cast<int32_t>(base + i);
-        ++h;
-      } else {
-        tsl[i] = -1;
-        run += c;
-      }
-    }
-    __syncthreads();
-    for (int i = t; i < n; i += 1024) {
-      start[base + i] = tc[i];
-      slot[base + i] = tsl[i];
-    }
-    if (t == 1023) {  // carry the tile's totals into the next
-      s_carry[0] = bh + xh;
-      s_carry[1] = bc + xc;
-    }
-    __syncthreads();
-  }
   if (t == 0) {
-    start[V] = s_carry[1];
-    info[0] = s_carry[0];
+    int32_t h = 0, c = 0;
+    for (int i = 0; i < 16; ++i) {
+      h += wsum[i][0];
+      c += wsum[i][1];
+    }
+    tsum[2 * blockIdx.x] = h;
+    tsum[2 * blockIdx.x + 1] = c;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_rs_hot_place(const int32_t* __restrict__ total,
+                                                       int64_t V,
+                                                       int32_t* __restrict__ info,
+                                                       const int32_t* __restrict__ tsum,
+                                                       int32_t* __restrict__ slot,
+                                                       int32_t* __restrict__ hot_ids,
+                                                       int32_t* __restrict__ start) {
+  __shared__ int32_t wsum[16][2];
+  __shared__ int32_t s_base[2];
+  __shared__ int32_t tc[kHotTile];   // counts of the tile, then bucket starts
+  __shared__ int32_t tsl[kHotTile];  // slots of the tile
+  constexpr int kPer = kHotTile / 1024;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int32_t tau = info[1];
+  const int64_t tile = blockIdx.x, base = tile * kHotTile;
+  const int n = V - base < kHotTile ? static_cast<int>(V - base) : kHotTile;
+  // the earlier tiles' hot ids and cold pairs
+  int32_t bh = 0, bc = 0;
+  for (int64_t i = t; i < tile; i += 1024) {
+    bh += tsum[2 * i];
+    bc += tsum[2 * i + 1];
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    bh += __shfl_xor(bh, o);
+    bc += __shfl_xor(bc, o);
+  }
+  if (lane == 0) {
+    wsum[wv][0] = bh;
+    wsum[wv][1] = bc;
+  }
+  for (int i = t; i < kHotTile; i += 1024) tc[i] = i < n ? total[base + i] : 0;
+  __syncthreads();
+  if (t == 0) {
+    int32_t h = 0, c = 0;
+    for (int i = 0; i < 16; ++i) {
+      h += wsum[i][0];
+      c += wsum[i][1];
+    }
+    s_base[0] = h;
+    s_base[1] = c;
+  }
+  __syncthreads();
+  int32_t nh = 0, nc = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = t * kPer + j;
+    const int32_t c = tc[i];
+    if (i < n && c >= tau)
+      ++nh;
+    else
+      nc += c;
+  }
+  // exclusive prefixes of (hot ids, cold pairs) over the workgroup
+  int32_t xh = nh, xc = nc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t yh = __shfl_up(xh, o), yc = __shfl_up(xc, o);
+    if (lane >= o) {
+      xh += yh;
+      xc += yc;
+    }
+  }
+  if (lane == 63) {  // wsum's earlier reader (thread 0) passed the barrier above
+    wsum[wv][0] = xh;
+    wsum[wv][1] = xc;
+  }
+  __syncthreads();
+  bh = s_base[0];
+  bc = s_base[1];
+  for (int i = 0; i < wv; ++i) {
+    bh += wsum[i][0];
+    bc += wsum[i][1];
+  }
+  int32_t h = bh + xh - nh, run = bc + xc - nc;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = t * kPer + j;
+    const int32_t c = tc[i];
+    tc[i] = run;
+    if (i < n && c >= tau) {
+      tsl[i] = h;
+      hot_ids[h] = static_cast<int32_t>(base + i);
+      ++h;
+    } else {
+      tsl[i] = -1;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int i = t; i < n; i += 1024) {
+    start[base + i] = tc[i];
+    slot[base + i] = tsl[i];
+  }
+  if (t == 1023 && base + kHotTile >= V) {  // the last tile: the totals
+    start[V] = bc + xc;
+    info[0] = bh + xh;
   }
 }
 
@@ -766,8 +845,12 @@ void launch_renorm_grad_w(int dtype, const void* H, const int32_t* idx, const fl
       ScopedTimer timer_(KID_RS_SCAN, s);
       k_rs_colscan<<<static_cast<unsigned>(ceil_div(V, 256)), 256, 0, s>>>(b.hist, q.nb, V,
                                                                           b.total);
-      k_rs_hot<<<1, 1024, 0, s>>>(b.total, V, kRenormHotMin, static_cast<int32_t>(q.hot_max),
-                                   b.slot, b.hot_ids, b.info, b.start);
+      const unsigned tiles = static_cast<unsigned>(ceil_div(V, kHotTile));
+      k_rs_tau<<<1, 1024, 0, s>>>(b.total, V, kRenormHotMin, static_cast<int32_t>(q.hot_max),
+                                   b.info);
+      k_rs_hot_sums<<<tiles, 1024, 0, s>>>(b.total, V, b.info, b.tsum);
+      k_rs_hot_place<<<tiles, 1024, 0, s>>>(b.total, V, b.info, b.tsum, b.slot, b.hot_ids,
+                                            b.start);
     }
     {
       ScopedTimer timer_(KID_RS_PLACE, s);

@@ -58,7 +58,7 @@ struct RenormPlan {
   size_t f_zk, f_rowloss, f_flag, f_total;
   // backward workspace
   size_t b_coef, b_zk, b_hist, b_total_ids, b_start, b_srow, b_sid, b_scoef, b_hs, b_partial,
-      b_slot, b_hot_ids, b_info, b_hot_c, b_hot_prod, b_flag, b_total;
+      b_slot, b_hot_ids, b_info, b_tsum, b_hot_c, b_hot_prod, b_flag, b_total;
 };
 
 RenormPlan make_renorm_plan(int64_t N, int64_t d, int64_t V, int32_t K, int32_t dtype) {
@@ -101,6 +101,8 @@ RenormPlan make_renorm_plan(int64_t N, int64_t d, int64_t V, int32_t K, int32_t 
   off = align_up(off + static_cast<size_t>(p.sort.hot_max) * 4);
   p.b_info = off;
   off = align_up(off + 16);
+  p.b_tsum = off;
+  off = align_up(off + static_cast<size_t>(fkl::ceil_div(V, 8192)) * 2 * 4);
   p.b_hot_c = off;
   off = align_up(off + static_cast<size_t>(p.sort.hot_rows) * p.sort.hot_max * eb);
   p.b_hot_prod = off;
@@ -242,6 +244,7 @@ extern "C" int32_t fkl_renorm_backward(const void* hidden, const void* weight,
   b.slot = reinterpret_cast<int32_t*>(ws + p.b_slot);
   b.hot_ids = reinterpret_cast<int32_t*>(ws + p.b_hot_ids);
   b.info = reinterpret_cast<int32_t*>(ws + p.b_info);
+  b.tsum = reinterpret_cast<int32_t*>(ws + p.b_tsum);
   b.partial = reinterpret_cast<float*>(ws + p.b_partial);
   b.hot_c = ws + p.b_hot_c;
   b.hot_prod = reinterpret_cast<float*>(ws + p.b_hot_prod);
