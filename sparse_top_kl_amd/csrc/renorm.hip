@@ -464,11 +464,17 @@ __global__ __launch_bounds__(1024) void k_rs_hot_place(const int32_t* __restrict
   }
 }
 
-// Stable placement: block b walks its rows in order; within a row each id's
-// first copy reserves its copies' slots with one returning atomic on the
-// block's cursor hist[b][v] (private to the block, so the values returned
-// follow the row order), and every copy lands at position start[v] + base +
-// (earlier copies in the row), where its row, id and coefficient are written.
+// Stable placement: block b walks its rows in order, R = floor(1024 / K)
+// rows at a time (one contiguous range of at most 1024 pairs). A range's cold
+// entries are sorted in LDS by (id, entry) with a bitonic network, so each
+// id's copies form a run in pair order; the run's first element reserves its
+// copies' slots with one returning atomic on the block's cursor hist[b][v]
+// (private to the block, so the values returned follow the row order), and
+// the copy at rank i of the run lands at start[v] + base + i, where its row,
+// id and coefficient are written. A range's ids are loaded two ranges ahead
+// and their hot slots, bucket starts and coefficients one range ahead, so
+// that a range waits on its atomics alone; entries past the block load entry
+// 0 of the range (valid) and are not used, so no load sits behind a branch.
 __global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ idx,
                                                   const float* __restrict__ coef, int64_t N,
                                                   int K, int64_t rows_per_block, int64_t V,
@@ -478,59 +484,123 @@ __global__ __launch_bounds__(256) void k_rs_place(const int32_t* __restrict__ id
                                                   int32_t* __restrict__ srow,
                                                   int32_t* __restrict__ sid,
                                                   float* __restrict__ scoef) {
-  __shared__ int32_t lid[kRenormMaxK];
-  __shared__ int32_t sbase[kRenormMaxK];
-  constexpr int kPer = kRenormMaxK / 256;
+  constexpr int kN = kRenormMaxK;       // sort size (a power of two)
+  constexpr int kPer = kN / 256;
+  __shared__ uint64_t key[kN];          // (id << 11) | entry, or ~0 for no cold entry
+  __shared__ int32_t lst[kN];           // bucket start of entry e's id
+  __shared__ float lcf[kN];             // coefficient of entry e
+  __shared__ int32_t base[kN];          // at a run's first sorted position: its slots' base
   const int64_t b = blockIdx.x;
   const int64_t r0 = b * rows_per_block;
   const int64_t r1 = r0 + rows_per_block < N ? r0 + rows_per_block : N;
+  if (r0 >= r1) return;
   int32_t* cur = hist + b * V;
   const int t = threadIdx.x;
-  for (int64_t r = r0; r < r1; ++r) {
-    for (int k = t; k < K; k += 256) {
-      const int32_t v = idx[r * K + k];
-      lid[k] = slot[v] < 0 ? v : -1;  // hot pairs take no part in the sort
-    }
-    __syncthreads();
-    int dup[kPer], first[kPer];
+  const int64_t R = kN / K;           // rows per range (K <= kRenormMaxK)
+  const int64_t p1 = r1 * K;          // the block's pairs end here
+  // entry j of this thread in the range starting at pair q (clamped)
+  auto ent = [&](int64_t q, int j) {
+    const int64_t e = q + t + 256 * j;
+    return e < q + R * K && e < p1 ? e : q;
+  };
+  auto rq = [&](int64_t q) { return q < p1 ? q : r0 * K; };  // a range past the block: any valid
+  int32_t ida[kPer], idb[kPer], sl[kPer], st[kPer];
+  float cf[kPer];
+  const int64_t q0 = r0 * K;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    ida[j] = idx[ent(q0, j)];
+    idb[j] = idx[ent(rq(q0 + R * K), j)];
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    sl[j] = slot[ida[j]];
+    st[j] = start[ida[j]];
+    cf[j] = coef[ent(q0, j)];
+  }
+  for (int64_t q = q0; q < p1; q += R * K) {
+    const int n = static_cast<int>(q + R * K < p1 ? R * K : p1 - q);  // entries in the range
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int k = t + 256 * j;
-      dup[j] = 0;
-      first[j] = k;
-      if (k < K && lid[k] >= 0) {
-        const int32_t v = lid[k];
-        int mult = 0, fst = -1;
-        for (int k2 = 0; k2 < K; ++k2) {
-          const bool eq = lid[k2] == v;
-          mult += eq ? 1 : 0;
-          dup[j] += (eq && k2 < k) ? 1 : 0;
-          if (eq && fst < 0) fst = k2;
+      const int e = t + 256 * j;
+      const bool cold = e < n && sl[j] < 0;  // hot pairs skip the sort
+      key[e] = cold ? (static_cast<uint64_t>(ida[j]) << 11) | static_cast<uint64_t>(e)
+                    : ~uint64_t(0);
+      lst[e] = st[j];
+      lcf[e] = cf[j];
+    }
+    // the next range's slots, starts and coefficients, the one after's ids
+    int32_t idc[kPer], sl2[kPer], st2[kPer];
+    float cf2[kPer];
+    const int64_t qn = rq(q + R * K), qnn = rq(q + 2 * R * K);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      sl2[j] = slot[idb[j]];
+      st2[j] = start[idb[j]];
+      cf2[j] = coef[ent(qn, j)];
+      idc[j] = idx[ent(qnn, j)];
+    }
+    __syncthreads();
+    for (int size = 2; size <= kN; size <<= 1)
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+        for (int h = 0; h < kN / 512; ++h) {
+          const int c = t + 256 * h;  // compare-exchange c of kN / 2
+          const int i = 2 * stride * (c / stride) + (c % stride), i2 = i + stride;
+          const uint64_t x = key[i], y = key[i2];
+          if ((x > y) == ((i & size) == 0)) {
+            key[i] = y;
+            key[i2] = x;
+          }
         }
-        first[j] = fst;
-        if (dup[j] == 0) sbase[k] = atomicAdd(&cur[v], mult);
+        __syncthreads();
+      }
+    // run starts reserve their slots
+    uint64_t kv[kPer];
+    int rs[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = t + 256 * j;
+      kv[j] = key[i];
+      rs[j] = i;
+      if (kv[j] != ~uint64_t(0)) {
+        const uint64_t id = kv[j] >> 11;
+        while (rs[j] > 0 && (key[rs[j] - 1] >> 11) == id) --rs[j];
+        if (rs[j] == i) {
+          int m = 1;
+          while (i + m < kN && (key[i + m] >> 11) == id) ++m;
+          base[i] = atomicAdd(&cur[id], m);
+        }
       }
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int k = t + 256 * j;
-      if (k < K && lid[k] >= 0) {
-        const int32_t v = lid[k];
-        const int32_t pos = start[v] + sbase[first[j]] + dup[j];
-        srow[pos] = static_cast<int32_t>(r);
-        sid[pos] = v;
-        scoef[pos] = coef[r * K + k];
+      const int i = t + 256 * j;
+      if (kv[j] != ~uint64_t(0)) {
+        const int e = static_cast<int>(kv[j] & 2047);
+        const int32_t pos = lst[e] + base[rs[j]] + (i - rs[j]);
+        srow[pos] = static_cast<int32_t>((q + e) / K);
+        sid[pos] = static_cast<int32_t>(kv[j] >> 11);
+        scoef[pos] = lcf[e];
       }
     }
     __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      ida[j] = idb[j];
+      idb[j] = idc[j];
+      sl[j] = sl2[j];
+      st[j] = st2[j];
+      cf[j] = cf2[j];
+    }
   }
 }
 
 // Slice-major copy of the hidden rows for the walk below: slice s holds
-// columns [32 s, 32 s + 32) of every row, one row after the other (64 bytes a
-// row in bf16), so that a slice of all N rows is one contiguous block whose
-// 128-byte lines hold only that slice. Columns past d in the last slice are
+// columns [64 s, 64 s + 64) of every row, one row after the other (128 bytes
+// a row in bf16), so that a slice of all N rows is one contiguous block whose
+// lines hold only that slice. Columns past d in the last slice are
 // neither written nor read.
 template <class P>
 __global__ __launch_bounds__(256) void k_rs_slices(const unsigned char* __restrict__ H,
