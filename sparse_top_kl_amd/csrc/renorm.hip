@@ -31,9 +31,9 @@
 //                    product tiles takes); give each a slot, and the
 //                    exclusive prefix over the other ("cold") ids of their
 //                    counts: bucket starts of the cold pairs
-//   hot ids, a dense product: k_rs_hot_coef scatters each row's hot
-//   coefficients into C [rows x hot_max] (copies of one id in a row
-//   summed in entry order), k_grad_w (the loss's MFMA kernel, its rows split
+//   hot ids, a dense product: k_rs_hot_coef writes each row of C
+//   [rows x hot_max], the row's hot coefficients (copies of one id in a row
+//   summed in entry order) and zeros, k_grad_w (the loss's MFMA kernel, its rows split
 //   over the XCDs its tiles alone would leave idle) forms C^T H, and
 //   k_rs_hot_rows sums the splits in order into each hot id's grad_W row
 //   cold ids, a sort:
@@ -817,34 +817,52 @@ __global__ __launch_bounds__(256) void k_rs_fix(const int32_t* __restrict__ star
 }
 
 // Rows [r0, r0 + nrows): C[r - r0][slot[v]] = sum of coef[r][k] over the
-// entries k of row r with hot id v, in entry order (one wave per row; C is
-// zero elsewhere, filled beforehand; row pitch `pitch` elements).
+// entries k of row r with hot id v, in entry order, and 0 in the other
+// columns (the whole row is written; row pitch `pitch` elements, a multiple
+// of 8). One wave per row, four rows a workgroup: the row's ids are staged in
+// LDS, its values built in an fp32 LDS row (the first copy of an id sums its
+// copies), then written out 16 bytes a lane.
 template <class P>
 __global__ __launch_bounds__(256) void k_rs_hot_coef(const int32_t* __restrict__ idx,
                                                      const float* __restrict__ coef,
                                                      const int32_t* __restrict__ slot, int64_t r0,
                                                      int64_t nrows, int K, int64_t pitch,
                                                      unsigned char* __restrict__ C) {
-  const int lane = threadIdx.x & 63;
-  const int64_t rl = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (rl >= nrows) return;
-  const int32_t* ir = idx + (r0 + rl) * K;
-  const float* cr = coef + (r0 + rl) * K;
-  for (int k = lane; k < K; k += 64) {
-    const int32_t v = ir[k];
-    const int32_t sl = slot[v];
-    if (sl < 0) continue;
-    bool first = true;
-    for (int k2 = 0; k2 < k && first; ++k2) first = ir[k2] != v;
-    if (!first) continue;
-    float g = 0.f;
-    for (int k2 = k; k2 < K; ++k2)
-      if (ir[k2] == v) g += cr[k2];
-    unsigned char* dst = C + (rl * pitch + sl) * P::kBytes;
-    if constexpr (P::kBytes == 2)
-      *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16_rne(g);
-    else
-      *reinterpret_cast<float*>(dst) = g;
+  extern __shared__ int32_t sh_hc[];  // per wave: K ids, then pitch fp32 values
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int32_t* lid = sh_hc + w * (K + pitch);
+  float* val = reinterpret_cast<float*>(lid + K);
+  const int64_t rl = static_cast<int64_t>(blockIdx.x) * 4 + w;
+  const bool valid = rl < nrows;
+  if (valid) {
+    const int32_t* ir = idx + (r0 + rl) * K;
+    for (int k = lane; k < K; k += 64) lid[k] = ir[k];
+    for (int64_t c = lane; c < pitch; c += 64) val[c] = 0.f;
+  }
+  __syncthreads();
+  if (valid) {
+    const float* cr = coef + (r0 + rl) * K;
+    for (int k = lane; k < K; k += 64) {
+      const int32_t v = lid[k];
+      const int32_t sl = slot[v];
+      if (sl < 0) continue;
+      bool first = true;
+      for (int k2 = 0; k2 < k && first; ++k2) first = lid[k2] != v;
+      if (!first) continue;
+      float g = 0.f;
+      for (int k2 = k; k2 < K; ++k2)
+        if (lid[k2] == v) g += cr[k2];
+      val[sl] = g;
+    }
+  }
+  __syncthreads();
+  if (!valid) return;
+  unsigned char* dst = C + rl * pitch * P::kBytes;
+  for (int64_t c = lane * 8; c < pitch; c += 512) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = val[c + e];
+    store8<P>(dst + c * P::kBytes, x);
   }
 }
 
@@ -902,7 +920,6 @@ void launch_renorm_grad_w(int dtype, const void* H, const int32_t* idx, const fl
                           int64_t N, int K, int64_t d, int64_t V, const RenormSortPlan& q,
                           const RenormBuffers& b, bool acc_out, float* gw, hipStream_t s) {
   const int64_t NK = N * K;
-  const int64_t eb = dtype == 1 ? 2 : 4;
   if (NK > 0) {
     launch_fill_f32(reinterpret_cast<float*>(b.hist), q.nb * V, 0.0f, s);  // integer zero
     {
@@ -967,15 +984,16 @@ void launch_renorm_grad_w(int dtype, const void* H, const int32_t* idx, const fl
   // hot ids: C^T H over row blocks of q.hot_rows rows, then the rows into grad_W
   for (int64_t r0 = 0; r0 < N; r0 += q.hot_rows) {
     const int64_t nr = N - r0 < q.hot_rows ? N - r0 : q.hot_rows;
-    launch_fill_f32(reinterpret_cast<float*>(b.hot_c), nr * q.hot_max * eb / 4, 0.0f, s);
     {
       ScopedTimer timer_(KID_RS_HOT, s);
       const unsigned grid = static_cast<unsigned>(ceil_div(nr, 4));
+      const size_t lds = static_cast<size_t>(4) * (K + q.hot_max) * 4;
       if (dtype == 1)
-        k_rs_hot_coef<BF16><<<grid, 256, 0, s>>>(idx, coef, b.slot, r0, nr, K, q.hot_max,
-                                                 b.hot_c);
+        k_rs_hot_coef<BF16><<<grid, 256, lds, s>>>(idx, coef, b.slot, r0, nr, K, q.hot_max,
+                                                   b.hot_c);
       else
-        k_rs_hot_coef<F32><<<grid, 256, 0, s>>>(idx, coef, b.slot, r0, nr, K, q.hot_max, b.hot_c);
+        k_rs_hot_coef<F32><<<grid, 256, lds, s>>>(idx, coef, b.slot, r0, nr, K, q.hot_max,
+                                                  b.hot_c);
     }
     launch_grad_w_split(dtype, b.hot_c, q.hot_max, H, d, q.hot_max, q.hot_max, r0, nr,
                         q.hot_splits, r0 > 0, b.hot_prod, q.hot_max * d, s);
