@@ -587,6 +587,61 @@ def vendor_gemm_step(args, torch, w, dev):
           flush=True)
 
 
+def loop_probe(args, torch, fkl, synth, dev):
+    """The contraction k-loop away from the board's power limit: the loss on one
+    512-row chunk with d 8192 and V 12 288 (bf16) makes the logit kernel
+    (k_logits_lse) a launch of 2 x 48 = 96 output tiles of 256 x 256. Each XCD's
+    share is rounded up to a round of 32 tiles, so three XCDs run 32 tiles each,
+    sharing operand panels in their L2 as at full load, while 96 of the 256 CUs
+    draw power; each tile contracts over d = 8192 (128 k-blocks of 64). Reports
+    the kernel's rate per busy CU against one CU's dense bf16 MFMA peak at 2.4 GHz
+    (4096 flop per clock)."""
+    w = synth.small_workload("loop_probe", n=512, d=8192, V=12288, K=100, T=2.0,
+                             dtype="bf16", chunk=512, ids="zipf", seed=11)
+    inp = synth.make_inputs(w)
+    h = torch.from_numpy(inp["hidden"]).to(dev).to(torch.bfloat16).contiguous()
+    W = torch.from_numpy(inp["weight"]).to(dev).to(torch.bfloat16).contiguous()
+    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    lg = torch.from_numpy(inp["topk_logit"]).to(dev)
+    fw, bw = fkl.fkl_workspace_size(w.N, w.d, w.V, w.K, w.chunk, torch.bfloat16)
+    ws_f = torch.empty(fw, dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(bw, dtype=torch.uint8, device=dev)
+    gw = torch.empty(w.V, w.d, dtype=torch.float32, device=dev)
+
+    def step():
+        out = fkl.fkl_forward(h, W, idx, lg, w.T, w.chunk, workspace=ws_f)
+        fkl.fkl_backward(h, W, idx, lg, out.lse, w.T, w.chunk, topk_z=out.topk_z,
+                         grad_weight=gw, workspace=ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    fkl.fkl_timing_reset()
+    fkl.fkl_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    fkl.fkl_timing_enable(False)
+    kt = fkl.kernel_times()
+    tiles = -(-w.N // 256) * -(-w.V // 256)
+    flops = 2.0 * w.N * w.d * w.V  # per launch: one launch of each per step
+    cu_peak = 4096 * 2.4e9 / 1e12
+    res = {}
+    for k in ("k_logits_lse",):
+        n, ms = kt[k]
+        avg_ms = ms / n
+        per_cu = flops / tiles / (avg_ms * 1e-3) / 1e12
+        res[k] = {"launches_per_step": n / args.steps, "avg_launch_ms": avg_ms,
+                  "tflops_per_busy_cu": per_cu, "frac_of_cu_peak": per_cu / cu_peak}
+    print(json.dumps({
+        "metric": "contraction k-loop rate per busy CU, 96 CUs busy",
+        "value": res["k_logits_lse"]["tflops_per_busy_cu"], "unit": "TFLOP/s",
+        "cu_peak_2p4ghz": cu_peak, "busy_cus": tiles, "k_blocks": w.d // 64,
+        "flops_per_launch": flops, "kernels": res, "steps": args.steps,
+        "config": {"N": w.N, "d": w.d, "V": w.V, "K": w.K, "chunk": w.chunk, "dtype": w.dtype},
+        "source_hash": source_hash()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -619,6 +674,9 @@ def main():
     ap.add_argument("--vendor-block", default="16384,16032",
                     help="row block and vocabulary slice of the blocked backward for "
                          "--vendor-gemm (the library's plan for long32k)")
+    ap.add_argument("--loop-probe", action="store_true",
+                    help="the contraction k-loop with 96 CUs busy (below the power limit): "
+                         "the logit kernel's rate per CU against one CU's MFMA peak")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy this many MiB once on the device (a plain "
                          "copy of known size for calibrating rocprofv3 byte counters)")
@@ -643,6 +701,9 @@ def main():
         return
     if args.memory_sweep:
         memory_sweep(args, torch, fkl, dev)
+        return
+    if args.loop_probe:
+        loop_probe(args, torch, fkl, synth, dev)
         return
     w = synth.WORKLOADS[args.workload]
     if args.chunk > 0:
