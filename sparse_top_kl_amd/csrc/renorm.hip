@@ -41,7 +41,7 @@
 //                    to start[v] + (pairs of id v in earlier rows) + (copies of
 //                    v earlier in row r): a stable counting sort by id, which
 //                    writes each pair's row, id and coefficient there
-//   k_rs_slices      the hidden rows copied slice-major, 32 columns a slice
+//   k_rs_slices      the hidden rows copied slice-major, 64 columns a slice
 //   k_rs_chunks      fixed chunks of the sorted pairs, slice by slice, each XCD
 //                    walking one slice at a time: the sum of G h over each run
 //                    of one id, written to grad_W when the chunk holds the
@@ -619,18 +619,19 @@ __global__ __launch_bounds__(256) void k_rs_slices(const unsigned char* __restri
 }
 
 // Chunk c of the sorted cold pairs (positions [c seg, min(NK, (c + 1) seg)),
-// seg <= kRenormMaxSeg) on the 32 columns of slice s. Work items are dealt so
-// that each XCD (workgroups go to the 8 XCDs in turn) takes its slices one
-// after the other, every chunk of a slice before the next slice, and the
-// slice of the hidden rows it reads (N x 64 bytes in bf16) stays in its L2
+// seg <= kRenormMaxSeg) on the kRenormSliceCols (64) columns of slice s. Work
+// items are dealt so that each XCD (workgroups go to the 8 XCDs in turn) takes
+// its slices one after the other, every chunk of a slice before the next
+// slice, and the slice of the hidden rows it reads (N x 128 bytes in bf16)
+// stays in its L2
 // (all columns at once read each pair's whole row from memory, the pairs
 // being sorted by id and their rows scattered). The grid is persistent: a
 // workgroup loops over items, their number known only on the device.
 //
-// The chunk's rows, ids and coefficients are staged in LDS; 64 groups of four
-// lanes (eight columns a lane) take equal shares of its positions and sum
-// coef * H[row] over each run (the pairs of one id) in sorted order, eight
-// row loads in flight across runs. A run that lies inside one share is
+// The chunk's rows, ids and coefficients are staged in LDS; 32 groups of
+// eight lanes (eight columns a lane) take equal shares of its positions and
+// sum coef * H[row] over each run (the pairs of one id) in sorted order, eight
+// row loads in flight across runs (four in fp32). A run that lies inside one share is
 // written out at once; the pieces of a run that crosses shares go to LDS, and
 // after a barrier the share where the run began adds them in share order.
 // A run's sum goes to grad_W[v] (or is added to it, with acc_out) when the
@@ -688,7 +689,7 @@ __global__ __launch_bounds__(256, 4) void k_rs_chunks(
     }
     __syncthreads();
     const int64_t c0 = s * kRenormSliceCols + l * 8;
-    const bool live = c0 < d;  // the last slice may be narrower than 32 columns
+    const bool live = c0 < d;  // the last slice may be narrower than the others
     const int32_t first_id = lid[0], last_id = lid[n - 1];
     const bool head_cont = lcont[0] != 0, tail_cont = lcont[1] != 0;
     // eight columns as two 16-byte streaming stores (c0 is a multiple of 8)
